@@ -1,0 +1,193 @@
+/*
+ * mk — batch-1 greedy decode of a Qwen3-style decoder as one persistent HIP
+ * kernel per token on AMD MI355X (gfx950).
+ *
+ * What is computed follows the monolith project page
+ * (projects.dotslasha.me/p/monolith): "Upstream facts" gives the model
+ * (pre-norm decoder with RMSNorm, QK-norm, RoPE, grouped-query attention over
+ * a KV cache, SwiGLU MLP, tied embedding used as the LM head) and the greedy
+ * decode step; "Design decisions" gives the weight formats (FP8 E4M3 with one
+ * scale per output row; NVFP4 = E2M1 values with one E4M3 scale per 16
+ * weights and one fp32 scale per tensor; activations bf16, fp32
+ * accumulation), the bf16 KV cache, the folded LM head + argmax so that one
+ * launch yields one token, and the per-block phase timestamps ("X-ray").
+ *
+ * Conventions for every call:
+ *   - Return value: MK_OK (0) or a negative mk_status.  Calls that return a
+ *     token return it (>= 0) or a negative mk_status.  No exception or abort
+ *     crosses this boundary.
+ *   - Arguments are validated before any HIP call, so argument errors are
+ *     reported the same way with or without a GPU.
+ *   - The library allocates no device memory: the caller allocates the
+ *     buffers whose sizes mk_query_sizes reports and binds them with mk_bind.
+ *     Device pointers must be 256-byte aligned.
+ *   - All work is enqueued on the caller's stream.  One model handle must not
+ *     be used from two threads at once, and two launches on one handle must
+ *     not run concurrently (they share the bound scratch buffer).
+ *   - Matrices are [out, in] row-major (the PyTorch Linear layout).
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* mk_stream_t;  /* a hipStream_t; NULL = the null stream */
+
+enum mk_status {
+  MK_OK = 0,
+  MK_E_INVALID = -1,      /* bad argument (null, out of range, misaligned) */
+  MK_E_UNSUPPORTED = -2,  /* shape or format the kernels do not handle */
+  MK_E_STATE = -3,        /* call out of order (e.g. decode before pack) */
+  MK_E_HIP = -4,          /* a HIP runtime call failed; see mk_last_error */
+  MK_E_TIMEOUT = -5,      /* a kernel wait exceeded its spin bound and the kernel exited */
+};
+
+/* Weight formats (monolith page, "Design decisions"). */
+enum mk_wfmt {
+  MK_WFMT_BF16 = 0,     /* every matrix bf16 */
+  MK_WFMT_FP8_ROW = 1,  /* every linear and the tied embedding: E4M3, fp32 scale per row */
+  MK_WFMT_FP4_MIX = 2,  /* q, k, v, o, gate, up: NVFP4; down and the tied embedding: FP8_ROW */
+};
+
+/* Model shape.  Constraints checked by mk_create: all sizes > 0;
+ * n_q_heads % n_kv_heads == 0; head_dim in {64, 128, 256};
+ * hidden, intermediate and n_q_heads*head_dim multiples of 16;
+ * n_layers <= 160; max_ctx <= 1<<20. */
+typedef struct mk_config {
+  int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, intermediate, vocab, max_ctx;
+  float rope_theta;   /* RoPE base (Qwen3: 1e6) */
+  float rms_eps;      /* RMSNorm epsilon (Qwen3: 1e-6) */
+  int32_t wfmt;       /* mk_wfmt */
+} mk_config;
+
+/* Byte sizes of the caller-owned device buffers, plus figures used for
+ * measurement. */
+typedef struct mk_sizes {
+  size_t weights;     /* packed weight arena */
+  size_t kv;          /* KV cache: n_layers * 2 * n_kv_heads * max_ctx * head_dim * 2 (bf16) */
+  size_t rope;        /* RoPE table: max_ctx * head_dim/2 * 2 * 4 (fp32 cos, sin) */
+  size_t scratch;     /* exchange buffers, argmax slots, error word */
+  size_t trace;       /* X-ray records for one step (0 in builds without X-ray) */
+  size_t weight_bytes_per_token;  /* algorithmic weight bytes one step reads: every matrix,
+                                     its scales and the norm gains, each once */
+  size_t kv_bytes_per_position;   /* KV bytes one step reads per cached position */
+} mk_sizes;
+
+/* One X-ray record: one workgroup, one phase of one step.  Times are
+ * s_memtime ticks (the shader clock counter) except rt_*, which are
+ * s_memrealtime ticks (a 100 MHz constant-rate counter shared by all XCDs). */
+typedef struct mk_trace_rec {
+  uint32_t phase;      /* phase id: 1 embed; 2+6l+{0..5} layer l QKV, attention, merge, O,
+                          gate/up, down; 2+6L final norm + LM head; 3+6L argmax reduce */
+  uint32_t wg;         /* workgroup index */
+  uint32_t hw_id;      /* HW_ID register (CU, SE, SIMD, wave slot) */
+  uint32_t xcc;        /* XCC_ID register (which XCD) */
+  uint32_t active;     /* 1 if this workgroup had work in the phase */
+  uint32_t pad;
+  uint64_t t_start, t_wait_begin, t_wait_end, t_end;  /* s_memtime */
+  uint64_t rt_start, rt_end;                           /* s_memrealtime */
+} mk_trace_rec;
+
+typedef struct mk_model mk_model;
+
+/* Validate `cfg` and create a host-side handle (no HIP calls).  The device
+ * used is the one current at mk_bind.  Errors: MK_E_INVALID (null or
+ * non-positive sizes), MK_E_UNSUPPORTED (shape outside the constraints). */
+int mk_create(const mk_config* cfg, mk_model** out);
+
+/* Fill `out` with the buffer sizes for this model.  No HIP calls. */
+int mk_query_sizes(const mk_model* m, mk_sizes* out);
+
+/* Register caller-owned device buffers (for example torch tensors' data
+ * pointers) of at least the sizes mk_query_sizes reports; `d_trace` may be
+ * NULL.  Queries the current device's compute-unit count and sets the
+ * launch grid to one workgroup per compute unit.  The pointers are not
+ * owned and must stay valid until mk_destroy.  The scratch buffer is
+ * cleared on `s`.  Errors: MK_E_INVALID (null or not 256-byte aligned),
+ * MK_E_HIP (no device). */
+int mk_bind(mk_model* m, void* d_weights, void* d_kv, void* d_rope, void* d_scratch,
+            void* d_trace, mk_stream_t s);
+
+/* Quantize and pack the bf16 master weights into the bound arena and build
+ * the RoPE table, on the GPU.  `d_tensors` holds 2 + 11*n_layers DEVICE
+ * pointers to bf16 tensors in this order: embed [V,H]; per layer in_norm [H],
+ * q [nq*hd,H], k [nkv*hd,H], v [nkv*hd,H], q_norm [hd], k_norm [hd],
+ * o [H,nq*hd], post_norm [H], gate [I,H], up [I,H], down [H,I]; final_norm
+ * [H].  Quantization follows the page's formats: FP8 per-row scale
+ * s = absmax/448 and codes e4m3(w/s); NVFP4 tensor scale ts = absmax/2688,
+ * block scale bs = e4m3(blockmax/(6*ts)) and codes e2m1(w/(e4m3(bs)*ts)); all
+ * encodes round to nearest even and saturate.  The tensors are read during
+ * the call only.  Errors: MK_E_INVALID, MK_E_STATE (not bound), MK_E_HIP. */
+int mk_pack_weights(mk_model* m, const void* const* d_tensors, int32_t n_tensors, mk_stream_t s);
+
+/* Test hook: copy one matrix back in canonical (row-major, un-fused) form.
+ * matrix: 0 q, 1 k, 2 v, 3 o, 4 gate, 5 up, 6 down, 7 embed (layer ignored).
+ * h_codes: bf16 [N,K] (uint16), FP8 [N,K] bytes, or FP4 [N,K/2] bytes (element
+ * 2j in the low nibble of byte j).  h_scales: FP8 fp32 [N] (else unused).
+ * h_block_scales: FP4 e4m3 [N,K/16] (else unused).  h_tensor_scale: FP4 fp32
+ * (else unused).  Synchronous.  Errors: MK_E_INVALID, MK_E_STATE, MK_E_HIP. */
+int mk_read_packed(mk_model* m, int32_t layer, int32_t matrix, void* h_codes, void* h_scales,
+                   void* h_block_scales, float* h_tensor_scale);
+
+/* Run the prompt: one decode step per position 0..n-1, writing the KV cache;
+ * return the greedy token that follows the prompt (>= 0), or a negative
+ * mk_status.  Synchronous. */
+int32_t mk_prefill(mk_model* m, const int32_t* h_tokens, int32_t n, mk_stream_t s);
+
+/* One decode step: consume `token` at position `pos` (writing its K/V into
+ * the cache), attend over positions 0..pos and return the next greedy token
+ * (>= 0) or a negative mk_status (MK_E_INVALID if pos >= max_ctx or token is
+ * outside the vocabulary; MK_E_TIMEOUT if the kernel hit its spin bound).
+ * One kernel launch; synchronous (a 4-byte readback). */
+int32_t mk_decode_step(mk_model* m, int32_t token, int32_t pos, mk_stream_t s);
+
+/* The same step without any host synchronisation: the token is read from
+ * device memory `d_token` and the next token is written to `d_next` (both
+ * int32, device), so steps chain on the device.  `d_logits` (fp32 [vocab],
+ * device) receives the logits when non-NULL.  A token outside the
+ * vocabulary read from `d_token` makes the kernel record MK_E_INVALID in the
+ * device error word, which the next synchronous call reports.  Errors
+ * (immediate): MK_E_INVALID, MK_E_STATE, MK_E_HIP. */
+int mk_decode_step_async(mk_model* m, const int32_t* d_token, int32_t pos, int32_t* d_next,
+                         float* d_logits, mk_stream_t s);
+
+/* Read and clear the device error word (synchronous).  Returns MK_OK or the
+ * first error a kernel recorded. */
+int mk_check_device_error(mk_model* m, mk_stream_t s);
+
+/* Copy the X-ray records of the most recent step (X-ray builds only).
+ * Writes min(cap, available) records; *n_out receives the number available
+ * (0 in builds without X-ray).  Synchronous.  Errors: MK_E_INVALID if cap is
+ * smaller than the number available. */
+int mk_get_trace(mk_model* m, mk_trace_rec* h_out, size_t cap, size_t* n_out);
+
+/* Test hook: decode `n` codes with the kernel's own register decoders.
+ * codec 0: E4M3 bytes -> fp32; codec 1: E2M1 (one code per byte, low
+ * nibble) -> fp32.  Device buffers; enqueued on `s`.  Needs no model. */
+int mk_decode_codes(int32_t codec, const uint8_t* d_codes, int32_t n, float* d_out, mk_stream_t s);
+
+/* Tuning knobs (defaults in brackets): key 0 grid size [compute units],
+ * key 1 exchange replicas [8], key 2 attention positions per unit [64],
+ * key 3 spin bound in 100 MHz ticks [100000000 = 1 s], key 4 test hook
+ * [0]: a non-zero value shifts every tag the kernel waits for, so no wait
+ * can be satisfied and each one ends at the spin bound (used to test the
+ * MK_E_TIMEOUT path without hanging).  Keys 0 and 1 must be set before
+ * mk_bind.  Errors: MK_E_INVALID, MK_E_STATE. */
+int mk_set_option(mk_model* m, int32_t key, int64_t value);
+
+/* 1 if the library was built with the X-ray stamps, else 0. */
+int mk_has_xray(void);
+
+const char* mk_status_str(int status);
+const char* mk_last_error(const mk_model* m);
+void mk_destroy(mk_model* m);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_H */

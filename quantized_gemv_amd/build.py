@@ -1,0 +1,48 @@
+"""Build libmk (the C-ABI library with the gfx950 kernels) in-tree with hipcc.
+
+Two variants: libmk.so (headline build) and libmk_xray.so (compiled with
+MK_XRAY, the per-phase timestamp stamps).
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+SOURCES = ["mk_kernels.hip", "mk_abi.cpp"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+
+def lib_path(xray: bool = False) -> str:
+    return os.path.join(HERE, "libmk_xray.so" if xray else "libmk.so")
+
+
+def build(xray: bool = False, verbose: bool = False) -> str:
+    out = lib_path(xray)
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+           # no packed-FP32 instructions anywhere in the device code
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    if xray:
+        cmd.append("-DMK_XRAY")
+    cmd += [os.path.join(CSRC, s) for s in SOURCES]
+    cmd += ["-o", out + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"hipcc failed building {os.path.basename(out)}")
+    if verbose:
+        sys.stderr.write(r.stderr)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def build_all(verbose: bool = False):
+    return [build(False, verbose), build(True, verbose)]
+
+
+if __name__ == "__main__":
+    for p in build_all(verbose="-v" in sys.argv):
+        print(p)

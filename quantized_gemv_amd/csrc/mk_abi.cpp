@@ -1,0 +1,579 @@
+// The C-ABI of libmk: argument validation, the packed-weight and scratch
+// layouts, and the launches.  Every entry point is declared, with its
+// contract, in include/mk.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "mk.h"
+#include "mk_launch.h"
+#include "mk_shared.h"
+
+using namespace mk;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMatQ = 0, kMatK = 1, kMatV = 2, kMatO = 3, kMatGate = 4, kMatUp = 5, kMatDown = 6, kMatEmbed = 7;
+
+size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+
+struct MatSize {
+  size_t codes, scales, tscale;
+};
+
+MatSize mat_bytes(uint32_t fmt, size_t N, size_t K, int n_tscale) {
+  MatSize s{0, 0, 0};
+  if (fmt == FMT_BF16) s.codes = N * K * 2;
+  if (fmt == FMT_FP8) { s.codes = N * K; s.scales = N * 4; }
+  if (fmt == FMT_FP4) { s.codes = N * K / 2; s.scales = N * K / 16; s.tscale = 4ull * n_tscale; }
+  return s;
+}
+
+}  // namespace
+
+struct mk_model {
+  mk_config cfg;
+  uint32_t fmt_lin = FMT_BF16, fmt_down = FMT_BF16, fmt_embed = FMT_BF16;
+  Params P;                 // host copy of the kernel parameters
+  size_t weights_bytes = 0, algo_bytes = 0, layer_stride = 0;
+  size_t scratch_bytes = 0, params_off = 0, tok_off = 0;
+  size_t scratch_reported = 0;
+  void* d_weights = nullptr;
+  void* d_kv = nullptr;
+  void* d_rope = nullptr;
+  uint8_t* d_scratch = nullptr;
+  void* d_trace = nullptr;
+  bool bound = false, packed = false, params_dirty = true;
+  int device = -1, cus = 0;
+  int grid_opt = 0, replicas = 8, att_target = 64;
+  int64_t spin_limit = 100000000;
+  uint32_t tag_skew = 0;
+  uint32_t epoch = 0;
+  std::string err;
+};
+
+namespace {
+
+int fail(mk_model* m, int code, const char* fmt, ...) {
+  if (m) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    m->err = buf;
+  }
+  return code;
+}
+
+int hip_fail(mk_model* m, hipError_t e, const char* what) {
+  return fail(m, MK_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIPCK(m, call)                                         \
+  do {                                                         \
+    hipError_t e_ = (call);                                    \
+    if (e_ != hipSuccess) return hip_fail((m), e_, #call);    \
+  } while (0)
+
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) % kAlign) == 0; }
+
+// Lay out the weight arena and fill the matrix descriptors.
+void layout_weights(mk_model* m) {
+  const mk_config& c = m->cfg;
+  const size_t H = c.hidden, I = c.intermediate, V = c.vocab, hd = c.head_dim;
+  const size_t nq = c.n_q_heads, nkv = c.n_kv_heads, nqkv = (nq + 2 * nkv) * hd;
+  size_t off = 0, algo = 0;
+  auto place = [&](Mat& mt, uint32_t fmt, size_t N, size_t K, int n_ts) {
+    const MatSize s = mat_bytes(fmt, N, K, n_ts);
+    mt.fmt = fmt;
+    mt.N = (uint32_t)N;
+    mt.K = (uint32_t)K;
+    mt.codes = off;
+    off = align_up(off + s.codes);
+    mt.scales = off;
+    off = align_up(off + s.scales);
+    mt.tscale = off;
+    off = align_up(off + s.tscale);
+    mt.ts_mode = 0;
+    mt.ts_b0 = mt.ts_b1 = 0;
+    algo += s.codes + s.scales + s.tscale;
+  };
+  auto place_vec = [&](uint64_t& o, size_t n) {
+    o = off;
+    off = align_up(off + n * 2);
+    algo += n * 2;
+  };
+  Params& P = m->P;
+  place(P.embed, m->fmt_embed, V, H, 0);
+  const size_t layers_begin = off;
+  const size_t algo_before = algo;
+  Layer& L = P.layer0;
+  place(L.qkv, m->fmt_lin, nqkv, H, 3);
+  L.qkv.ts_mode = 1;
+  L.qkv.ts_b0 = (uint32_t)(nq * hd);
+  L.qkv.ts_b1 = (uint32_t)((nq + nkv) * hd);
+  place(L.o, m->fmt_lin, H, nq * hd, 1);
+  place(L.gu, m->fmt_lin, 2 * I, H, 2);
+  L.gu.ts_mode = 2;
+  place(L.down, m->fmt_down, H, I, 1);
+  place_vec(L.in_norm, H);
+  place_vec(L.post_norm, H);
+  place_vec(L.q_norm, hd);
+  place_vec(L.k_norm, hd);
+  m->layer_stride = off - layers_begin;
+  const size_t layer_algo = algo - algo_before;
+  off = layers_begin + m->layer_stride * c.n_layers;
+  algo = algo_before + layer_algo * c.n_layers;
+  place_vec(P.final_norm, H);
+  P.layer_stride = m->layer_stride;
+  m->weights_bytes = off;
+  m->algo_bytes = algo;
+}
+
+// Lay out the scratch buffer: exchange words, the params copy, token slots.
+void layout_scratch(mk_model* m, int grid, bool for_sizing = true) {
+  const mk_config& c = m->cfg;
+  Params& P = m->P;
+  Xch& X = P.x;
+  const int R = m->replicas;
+  const uint64_t H = c.hidden, hd = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads;
+  const uint64_t pad = 32;  // words between replicas, so copies start on different lines
+  uint64_t w = 0;
+  auto vec = [&](uint64_t& base, uint64_t& rep, uint64_t& par, uint64_t n) {
+    rep = n + pad;
+    par = rep * R;
+    base = w;
+    w += 2 * par;
+  };
+  uint64_t dummy_rep = 0;
+  vec(X.x_d, X.rep_x, X.par_x, H);
+  uint64_t rep2 = 0, par2 = 0;
+  vec(X.x_o, rep2, par2, H);  // same shape as x_d: same strides
+  vec(X.qkv, X.rep_qkv, X.par_qkv, (nq + 2 * nkv) * hd);
+  vec(X.o, X.rep_o, X.par_o, nq * hd / 2);
+  vec(X.h, X.rep_h, X.par_h, (uint64_t)c.intermediate / 2);
+  (void)dummy_rep;
+  int ns_max = grid / (int)nkv;
+  const int cap = kMaxVecWords / (int)(hd + 2);
+  if (ns_max > cap) ns_max = cap;
+  if (ns_max < 1) ns_max = 1;
+  P.ns_max = ns_max;
+  X.part = w;
+  X.par_part = nq * (uint64_t)ns_max * (hd + 2);
+  w += 2 * X.par_part;
+  X.arg = w;
+  w += 2ull * grid;
+  X.err = w;
+  w += 1;
+  X.amax = w;
+  w += 1;
+  w = (w + 31) / 32 * 32;
+  X.words = w;
+  m->params_off = align_up(w * 8);
+  m->tok_off = align_up(m->params_off + sizeof(Params));
+  m->scratch_bytes = align_up(m->tok_off + 4ull * ((size_t)c.max_ctx + 4));
+  if (for_sizing) m->scratch_reported = m->scratch_bytes;
+}
+
+int n_phases(const mk_config& c) { return 6 * c.n_layers + 4; }
+
+// Before mk_bind the compute-unit count is unknown, so sizes are reported for
+// the grid option if set, else for the largest grid the library launches.
+constexpr int kMaxGrid = 1024;
+int sizing_grid(const mk_model* m) { return m->grid_opt > 0 ? m->grid_opt : kMaxGrid; }
+
+int validate_cfg(const mk_config* c) {
+  if (!c) return MK_E_INVALID;
+  if (c->n_layers <= 0 || c->hidden <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 ||
+      c->intermediate <= 0 || c->vocab <= 0 || c->max_ctx <= 0 || !(c->rope_theta > 0) || !(c->rms_eps > 0))
+    return MK_E_INVALID;
+  if (c->wfmt < MK_WFMT_BF16 || c->wfmt > MK_WFMT_FP4_MIX) return MK_E_INVALID;
+  if (c->n_q_heads % c->n_kv_heads) return MK_E_UNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) return MK_E_UNSUPPORTED;
+  const int gs = c->n_q_heads / c->n_kv_heads;
+  if (gs > 4 || gs * c->head_dim > 512) return MK_E_UNSUPPORTED;
+  if (c->hidden % 16 || c->intermediate % 16 || (c->n_q_heads * c->head_dim) % 16) return MK_E_UNSUPPORTED;
+  if (c->hidden > 4096 || c->intermediate / 2 > 6144 || c->n_q_heads * c->head_dim / 2 > 6144)
+    return MK_E_UNSUPPORTED;
+  if (c->n_layers > 160 || c->max_ctx > (1 << 20)) return MK_E_UNSUPPORTED;
+  return MK_OK;
+}
+
+// Per-workgroup capacities of the kernel (LDS arrays) for a given grid.
+int check_grid(mk_model* m, int grid) {
+  const mk_config& c = m->cfg;
+  auto cdiv = [](long a, long b) { return (a + b - 1) / b; };
+  const long G = grid, nch_h = cdiv(c.hidden, 1024);
+  const long nqkv = (long)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
+  if (grid < 1) return fail(m, MK_E_INVALID, "grid must be positive");
+  if (cdiv(c.hidden, G) > kMaxOwn) return fail(m, MK_E_UNSUPPORTED, "grid %d too small for hidden %d", grid, c.hidden);
+  const long items[5] = {cdiv(nqkv, G) * nch_h, cdiv(c.hidden, G) * cdiv((long)c.n_q_heads * c.head_dim, 1024),
+                         4 * cdiv(c.intermediate / 2, G) * nch_h, cdiv(c.hidden, G) * cdiv(c.intermediate, 1024),
+                         cdiv(c.vocab, G) * nch_h};
+  for (long it : items)
+    if (it > kMaxPart) return fail(m, MK_E_UNSUPPORTED, "grid %d leaves %ld GEMV items per workgroup", grid, it);
+  if (2 * G > kMaxVecWords) return fail(m, MK_E_UNSUPPORTED, "grid %d too large", grid);
+  return MK_OK;
+}
+
+// Fill the kernel parameters that depend on the grid and the bound buffers,
+// and upload them.
+int sync_params(mk_model* m, hipStream_t s) {
+  if (!m->params_dirty) return MK_OK;
+  const mk_config& c = m->cfg;
+  Params& P = m->P;
+  P.w = static_cast<const uint8_t*>(m->d_weights);
+  P.kv = static_cast<uint16_t*>(m->d_kv);
+  P.rope = static_cast<const float*>(m->d_rope);
+  P.xch = reinterpret_cast<uint64_t*>(m->d_scratch);
+  P.trace = m->d_trace;
+  P.L = c.n_layers;
+  P.H = c.hidden;
+  P.nq = c.n_q_heads;
+  P.nkv = c.n_kv_heads;
+  P.hd = c.head_dim;
+  P.I = c.intermediate;
+  P.V = c.vocab;
+  P.max_ctx = c.max_ctx;
+  P.eps = c.rms_eps;
+  P.R = m->replicas;
+  P.att_target = m->att_target;
+  P.spin_limit = (uint64_t)m->spin_limit;
+  P.tag_skew = m->tag_skew;
+  P.n_phases = n_phases(c);
+  HIPCK(m, hipMemcpyAsync(m->d_scratch + m->params_off, &P, sizeof(Params), hipMemcpyHostToDevice, s));
+  HIPCK(m, hipStreamSynchronize(s));  // the host copy is a stack-independent member, but keep ordering simple
+  m->params_dirty = false;
+  return MK_OK;
+}
+
+int32_t read_token_and_error(mk_model* m, const int32_t* d_next, hipStream_t s) {
+  int32_t tok = -1;
+  uint32_t err = 0;
+  HIPCK(m, hipMemcpyAsync(&tok, d_next, 4, hipMemcpyDeviceToHost, s));
+  HIPCK(m, hipMemcpyAsync(&err, m->d_scratch + 8 * m->P.x.err, 4, hipMemcpyDeviceToHost, s));
+  HIPCK(m, hipStreamSynchronize(s));
+  if (err) {
+    uint32_t zero = 0;
+    HIPCK(m, hipMemcpy(m->d_scratch + 8 * m->P.x.err, &zero, 4, hipMemcpyHostToDevice));
+    if (err & 1u) return fail(m, MK_E_TIMEOUT, "a kernel wait exceeded its spin bound");
+    return fail(m, MK_E_INVALID, "the kernel read a token outside the vocabulary");
+  }
+  return tok;
+}
+
+int launch_step(mk_model* m, const int32_t* d_token, int pos, int32_t* d_next, float* d_logits, hipStream_t s) {
+  int rc = sync_params(m, s);
+  if (rc) return rc;
+  m->epoch = (m->epoch + 1) & kEpochMask;
+  if (m->epoch == 0) {  // tags would repeat: clear the exchange words and restart
+    HIPCK(m, hipMemsetAsync(m->d_scratch, 0, 8 * m->P.x.words, s));
+    m->epoch = 1;
+  }
+  const Params* dp = reinterpret_cast<const Params*>(m->d_scratch + m->params_off);
+  HIPCK(m, launch_decode(dp, m->P.grid, d_token, pos, m->epoch, d_next, d_logits, s));
+  return MK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mk_create(const mk_config* cfg, mk_model** out) {
+  if (!out) return MK_E_INVALID;
+  *out = nullptr;
+  const int v = validate_cfg(cfg);
+  if (v) return v;
+  mk_model* m = new (std::nothrow) mk_model();
+  if (!m) return MK_E_INVALID;
+  m->cfg = *cfg;
+  std::memset(&m->P, 0, sizeof(Params));
+  if (cfg->wfmt == MK_WFMT_FP8_ROW) m->fmt_lin = m->fmt_down = m->fmt_embed = FMT_FP8;
+  if (cfg->wfmt == MK_WFMT_FP4_MIX) {
+    m->fmt_lin = FMT_FP4;
+    m->fmt_down = m->fmt_embed = FMT_FP8;
+  }
+  layout_weights(m);
+  layout_scratch(m, sizing_grid(m));
+  *out = m;
+  return MK_OK;
+}
+
+int mk_query_sizes(const mk_model* m, mk_sizes* out) {
+  if (!m || !out) return MK_E_INVALID;
+  const mk_config& c = m->cfg;
+  out->weights = m->weights_bytes;
+  out->kv = (size_t)c.n_layers * 2 * c.n_kv_heads * (size_t)c.max_ctx * c.head_dim * 2;
+  out->rope = (size_t)c.max_ctx * (c.head_dim / 2) * 2 * 4;
+  out->scratch = m->scratch_reported;
+  out->trace = mk_has_xray() ? sizeof(mk_trace_rec) * (size_t)sizing_grid(m) * n_phases(c) : 0;
+  out->weight_bytes_per_token = m->algo_bytes;
+  out->kv_bytes_per_position = (size_t)c.n_layers * 2 * c.n_kv_heads * c.head_dim * 2;
+  return MK_OK;
+}
+
+int mk_bind(mk_model* m, void* d_weights, void* d_kv, void* d_rope, void* d_scratch, void* d_trace,
+            mk_stream_t stream) {
+  if (!m) return MK_E_INVALID;
+  if (!d_weights || !d_kv || !d_rope || !d_scratch)
+    return fail(m, MK_E_INVALID, "mk_bind: a required buffer is null");
+  if (!aligned(d_weights) || !aligned(d_kv) || !aligned(d_rope) || !aligned(d_scratch) ||
+      (d_trace && !aligned(d_trace)))
+    return fail(m, MK_E_INVALID, "mk_bind: buffers must be 256-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  HIPCK(m, hipGetDevice(&m->device));
+  hipDeviceProp_t prop;
+  HIPCK(m, hipGetDeviceProperties(&prop, m->device));
+  int coop = 0;
+  HIPCK(m, hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, m->device));
+  if (!coop) return fail(m, MK_E_UNSUPPORTED, "device lacks cooperative launch");
+  m->cus = prop.multiProcessorCount;
+  const int grid = m->grid_opt > 0 ? m->grid_opt : m->cus;
+  if (grid > kMaxGrid) return fail(m, MK_E_UNSUPPORTED, "grid %d above %d", grid, kMaxGrid);
+  const int gc = check_grid(m, grid);
+  if (gc) return gc;
+  layout_scratch(m, grid, false);  // never larger than the size reported for sizing_grid()
+  m->P.grid = grid;
+  m->d_weights = d_weights;
+  m->d_kv = d_kv;
+  m->d_rope = d_rope;
+  m->d_scratch = static_cast<uint8_t*>(d_scratch);
+  m->d_trace = mk_has_xray() ? d_trace : nullptr;
+  m->bound = true;
+  m->params_dirty = true;
+  m->epoch = 0;
+  HIPCK(m, hipMemsetAsync(d_scratch, 0, m->scratch_bytes, s));
+  return sync_params(m, s);
+}
+
+int mk_pack_weights(mk_model* m, const void* const* d_tensors, int32_t n_tensors, mk_stream_t stream) {
+  if (!m) return MK_E_INVALID;
+  const mk_config& c = m->cfg;
+  if (!d_tensors || n_tensors != 2 + 11 * c.n_layers)
+    return fail(m, MK_E_INVALID, "mk_pack_weights: expected %d tensors", 2 + 11 * c.n_layers);
+  for (int i = 0; i < n_tensors; ++i)
+    if (!d_tensors[i]) return fail(m, MK_E_INVALID, "mk_pack_weights: tensor %d is null", i);
+  if (!m->bound) return fail(m, MK_E_STATE, "mk_pack_weights before mk_bind");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint8_t* W = static_cast<uint8_t*>(m->d_weights);
+  uint32_t* amax = reinterpret_cast<uint32_t*>(m->d_scratch + 8 * m->P.x.amax);
+  auto T = [&](int i) { return static_cast<const uint16_t*>(d_tensors[i]); };
+  // one source matrix [N,K] into rows row_off + r*row_step of `mt`
+  auto pack = [&](const uint16_t* src, const Mat& mt, size_t layer_off, int N, int K, int row_off, int row_step,
+                  int ts_index) -> hipError_t {
+    uint8_t* codes = W + mt.codes + layer_off;
+    if (mt.fmt == FMT_BF16)
+      return launch_pack_bf16(src, N, K, reinterpret_cast<uint16_t*>(codes), row_off, row_step, s);
+    if (mt.fmt == FMT_FP8)
+      return launch_pack_fp8(src, N, K, codes, reinterpret_cast<float*>(W + mt.scales + layer_off), row_off,
+                             row_step, s);
+    return launch_pack_fp4(src, N, K, codes, W + mt.scales + layer_off,
+                           reinterpret_cast<float*>(W + mt.tscale + layer_off), ts_index, amax, row_off, row_step,
+                           s);
+  };
+  auto copy_vec = [&](const uint16_t* src, uint64_t off, size_t n) -> hipError_t {
+    return hipMemcpyAsync(W + off, src, n * 2, hipMemcpyDeviceToDevice, s);
+  };
+  const int H = c.hidden, I = c.intermediate, hd = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads;
+  const Layer& L = m->P.layer0;
+  HIPCK(m, pack(T(0), m->P.embed, 0, c.vocab, H, 0, 1, 0));
+  for (int l = 0; l < c.n_layers; ++l) {
+    const int b = 1 + 11 * l;
+    const size_t lo = (size_t)l * m->layer_stride;
+    HIPCK(m, copy_vec(T(b + 0), L.in_norm + lo, H));
+    HIPCK(m, pack(T(b + 1), L.qkv, lo, nq * hd, H, 0, 1, 0));
+    HIPCK(m, pack(T(b + 2), L.qkv, lo, nkv * hd, H, nq * hd, 1, 1));
+    HIPCK(m, pack(T(b + 3), L.qkv, lo, nkv * hd, H, (nq + nkv) * hd, 1, 2));
+    HIPCK(m, copy_vec(T(b + 4), L.q_norm + lo, hd));
+    HIPCK(m, copy_vec(T(b + 5), L.k_norm + lo, hd));
+    HIPCK(m, pack(T(b + 6), L.o, lo, H, nq * hd, 0, 1, 0));
+    HIPCK(m, copy_vec(T(b + 7), L.post_norm + lo, H));
+    HIPCK(m, pack(T(b + 8), L.gu, lo, I, H, 0, 2, 0));
+    HIPCK(m, pack(T(b + 9), L.gu, lo, I, H, 1, 2, 1));
+    HIPCK(m, pack(T(b + 10), L.down, lo, H, I, 0, 1, 0));
+  }
+  HIPCK(m, copy_vec(T(1 + 11 * c.n_layers), m->P.final_norm, H));
+  HIPCK(m, launch_rope(static_cast<float*>(m->d_rope), c.max_ctx, hd, (double)c.rope_theta, s));
+  HIPCK(m, hipStreamSynchronize(s));
+  m->packed = true;
+  return MK_OK;
+}
+
+int mk_read_packed(mk_model* m, int32_t layer, int32_t matrix, void* h_codes, void* h_scales,
+                   void* h_block_scales, float* h_tensor_scale) {
+  if (!m) return MK_E_INVALID;
+  const mk_config& c = m->cfg;
+  if (matrix < 0 || matrix > kMatEmbed || !h_codes) return fail(m, MK_E_INVALID, "mk_read_packed: bad matrix");
+  if (matrix != kMatEmbed && (layer < 0 || layer >= c.n_layers))
+    return fail(m, MK_E_INVALID, "mk_read_packed: bad layer");
+  if (!m->packed) return fail(m, MK_E_STATE, "mk_read_packed before mk_pack_weights");
+  const int H = c.hidden, I = c.intermediate, hd = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads;
+  const Layer& L = m->P.layer0;
+  const size_t lo = matrix == kMatEmbed ? 0 : (size_t)layer * m->layer_stride;
+  const Mat* mt = nullptr;
+  int N = 0, K = 0, row_off = 0, row_step = 1, ts_index = 0;
+  switch (matrix) {
+    case kMatQ: mt = &L.qkv; N = nq * hd; K = H; break;
+    case kMatK: mt = &L.qkv; N = nkv * hd; K = H; row_off = nq * hd; ts_index = 1; break;
+    case kMatV: mt = &L.qkv; N = nkv * hd; K = H; row_off = (nq + nkv) * hd; ts_index = 2; break;
+    case kMatO: mt = &L.o; N = H; K = nq * hd; break;
+    case kMatGate: mt = &L.gu; N = I; K = H; row_step = 2; break;
+    case kMatUp: mt = &L.gu; N = I; K = H; row_off = 1; row_step = 2; ts_index = 1; break;
+    case kMatDown: mt = &L.down; N = H; K = I; break;
+    default: mt = &m->P.embed; N = c.vocab; K = H; break;
+  }
+  const uint8_t* W = static_cast<const uint8_t*>(m->d_weights);
+  size_t row_bytes = mt->fmt == FMT_BF16 ? 2ull * K : (mt->fmt == FMT_FP8 ? (size_t)K : (size_t)K / 2);
+  HIPCK(m, hipMemcpy2D(h_codes, row_bytes, W + mt->codes + lo + row_bytes * row_off, row_bytes * row_step,
+                       row_bytes, N, hipMemcpyDeviceToHost));
+  if (mt->fmt == FMT_FP8) {
+    if (!h_scales) return fail(m, MK_E_INVALID, "mk_read_packed: h_scales is null");
+    HIPCK(m, hipMemcpy2D(h_scales, 4, W + mt->scales + lo + 4ull * row_off, 4ull * row_step, 4, N,
+                         hipMemcpyDeviceToHost));
+  } else if (mt->fmt == FMT_FP4) {
+    if (!h_block_scales || !h_tensor_scale) return fail(m, MK_E_INVALID, "mk_read_packed: FP4 outputs are null");
+    const size_t bsb = K / 16;
+    HIPCK(m, hipMemcpy2D(h_block_scales, bsb, W + mt->scales + lo + bsb * row_off, bsb * row_step, bsb, N,
+                         hipMemcpyDeviceToHost));
+    HIPCK(m, hipMemcpy(h_tensor_scale, W + mt->tscale + lo + 4ull * ts_index, 4, hipMemcpyDeviceToHost));
+  }
+  return MK_OK;
+}
+
+int mk_decode_step_async(mk_model* m, const int32_t* d_token, int32_t pos, int32_t* d_next, float* d_logits,
+                         mk_stream_t stream) {
+  if (!m) return MK_E_INVALID;
+  if (!d_token || !d_next || d_token == d_next)
+    return fail(m, MK_E_INVALID, "mk_decode_step_async: token buffers must be distinct and non-null");
+  if (pos < 0 || pos >= m->cfg.max_ctx) return fail(m, MK_E_INVALID, "position %d outside [0, %d)", pos, m->cfg.max_ctx);
+  if (!m->bound || !m->packed) return fail(m, MK_E_STATE, "decode before mk_bind and mk_pack_weights");
+  return launch_step(m, d_token, pos, d_next, d_logits, reinterpret_cast<hipStream_t>(stream));
+}
+
+int32_t mk_decode_step(mk_model* m, int32_t token, int32_t pos, mk_stream_t stream) {
+  if (!m) return MK_E_INVALID;
+  if (token < 0 || token >= m->cfg.vocab) return fail(m, MK_E_INVALID, "token %d outside the vocabulary", token);
+  if (pos < 0 || pos >= m->cfg.max_ctx) return fail(m, MK_E_INVALID, "position %d outside [0, %d)", pos, m->cfg.max_ctx);
+  if (!m->bound || !m->packed) return fail(m, MK_E_STATE, "decode before mk_bind and mk_pack_weights");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int32_t* tok = reinterpret_cast<int32_t*>(m->d_scratch + m->tok_off);
+  HIPCK(m, hipMemcpyAsync(tok, &token, 4, hipMemcpyHostToDevice, s));
+  int rc = launch_step(m, tok, pos, tok + 1, nullptr, s);
+  if (rc) return rc;
+  return read_token_and_error(m, tok + 1, s);
+}
+
+int32_t mk_prefill(mk_model* m, const int32_t* h_tokens, int32_t n, mk_stream_t stream) {
+  if (!m) return MK_E_INVALID;
+  if (!h_tokens || n <= 0 || n > m->cfg.max_ctx) return fail(m, MK_E_INVALID, "mk_prefill: bad prompt length %d", n);
+  for (int i = 0; i < n; ++i)
+    if (h_tokens[i] < 0 || h_tokens[i] >= m->cfg.vocab)
+      return fail(m, MK_E_INVALID, "mk_prefill: token %d outside the vocabulary", i);
+  if (!m->bound || !m->packed) return fail(m, MK_E_STATE, "prefill before mk_bind and mk_pack_weights");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int32_t* tok = reinterpret_cast<int32_t*>(m->d_scratch + m->tok_off);
+  int32_t* prompt = tok + 2;
+  HIPCK(m, hipMemcpyAsync(prompt, h_tokens, 4ull * n, hipMemcpyHostToDevice, s));
+  for (int i = 0; i < n; ++i) {
+    int rc = launch_step(m, prompt + i, i, tok + 1, nullptr, s);
+    if (rc) return rc;
+  }
+  return read_token_and_error(m, tok + 1, s);
+}
+
+int mk_check_device_error(mk_model* m, mk_stream_t stream) {
+  if (!m) return MK_E_INVALID;
+  if (!m->bound) return fail(m, MK_E_STATE, "not bound");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int32_t* next = reinterpret_cast<const int32_t*>(m->d_scratch + m->tok_off) + 1;
+  const int32_t r = read_token_and_error(m, next, s);
+  return r < 0 ? r : MK_OK;
+}
+
+int mk_get_trace(mk_model* m, mk_trace_rec* h_out, size_t cap, size_t* n_out) {
+  if (!m || !n_out) return MK_E_INVALID;
+  if (!mk_has_xray() || !m->d_trace) {
+    *n_out = 0;
+    return MK_OK;
+  }
+  const size_t n = (size_t)m->P.grid * n_phases(m->cfg);
+  *n_out = n;
+  if (!h_out || cap < n) return fail(m, MK_E_INVALID, "mk_get_trace: need room for %zu records", n);
+  HIPCK(m, hipDeviceSynchronize());
+  HIPCK(m, hipMemcpy(h_out, m->d_trace, n * sizeof(mk_trace_rec), hipMemcpyDeviceToHost));
+  return MK_OK;
+}
+
+int mk_decode_codes(int32_t codec, const uint8_t* d_codes, int32_t n, float* d_out, mk_stream_t stream) {
+  if ((codec != 0 && codec != 1) || n < 0 || (n > 0 && (!d_codes || !d_out))) return MK_E_INVALID;
+  const hipError_t e = launch_decode_codes(codec, d_codes, n, d_out, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MK_OK : MK_E_HIP;
+}
+
+int mk_set_option(mk_model* m, int32_t key, int64_t value) {
+  if (!m) return MK_E_INVALID;
+  switch (key) {
+    case 0:
+      if (value < 0) return fail(m, MK_E_INVALID, "grid %lld out of range", (long long)value);
+      if (m->bound) return fail(m, MK_E_STATE, "set the grid before mk_bind");
+      if (value > kMaxGrid) return fail(m, MK_E_INVALID, "grid above %d", kMaxGrid);
+      m->grid_opt = (int)value;
+      layout_scratch(m, sizing_grid(m));
+      break;
+    case 1:
+      if (value < 1 || value > 64) return fail(m, MK_E_INVALID, "replicas %lld out of range", (long long)value);
+      if (m->bound) return fail(m, MK_E_STATE, "set replicas before mk_bind");
+      m->replicas = (int)value;
+      layout_scratch(m, sizing_grid(m));
+      break;
+    case 2:
+      if (value < 1 || value > (1 << 20)) return fail(m, MK_E_INVALID, "attention target out of range");
+      m->att_target = (int)value;
+      break;
+    case 3:
+      if (value < 0) return fail(m, MK_E_INVALID, "spin limit must be >= 0");
+      m->spin_limit = value;
+      break;
+    case 4:
+      if (value < 0 || value > 0xFFFF) return fail(m, MK_E_INVALID, "tag skew out of range");
+      m->tag_skew = (uint32_t)value;
+      break;
+    default:
+      return fail(m, MK_E_INVALID, "unknown option %d", key);
+  }
+  m->params_dirty = true;
+  return MK_OK;
+}
+
+int mk_has_xray(void) {
+#ifdef MK_XRAY
+  return 1;
+#else
+  return 0;
+#endif
+}
+
+const char* mk_status_str(int status) {
+  switch (status) {
+    case MK_OK: return "ok";
+    case MK_E_INVALID: return "invalid argument";
+    case MK_E_UNSUPPORTED: return "unsupported shape or format";
+    case MK_E_STATE: return "call out of order";
+    case MK_E_HIP: return "HIP runtime error";
+    case MK_E_TIMEOUT: return "kernel wait timed out";
+    default: return "unknown status";
+  }
+}
+
+const char* mk_last_error(const mk_model* m) { return m ? m->err.c_str() : "null model"; }
+
+void mk_destroy(mk_model* m) { delete m; }
+
+}  // extern "C"

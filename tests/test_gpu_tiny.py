@@ -1,0 +1,253 @@
+"""GPU parity of the HIP decode path against the CPU oracle on the tiny
+decoder (2 layers, hidden 256, 4 q / 2 KV heads of 64, intermediate 768,
+vocab 4096), through the C-ABI.  Sizes span several tiles per phase and
+ragged row splits (e.g. 384 SwiGLU pairs over 256 workgroups)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle.codecs import e2m1_decode, e4m3_decode
+from oracle.model import Oracle, argmax_lowest
+from oracle.quant import quant_fp4, quant_fp8_row
+from oracle.codecs import bf16_bits_to_f32
+
+pytestmark = pytest.mark.gpu
+
+FORMATS = [synth.BF16, synth.FP8_ROW, synth.FP4_MIX]
+REL_L2 = 1e-2     # logits tolerance (relative L2), stated for this path
+GAP = 1e-3        # argmax must agree where the oracle's top-2 gap is at least this
+
+
+@pytest.fixture(scope="module")
+def native():
+    from quantized_gemv_amd import native as n
+    assert torch.cuda.is_available()
+    return n
+
+
+@pytest.fixture(scope="module")
+def master():
+    return synth.make_weights(synth.TINY, 0)
+
+
+def _decoder(native, master, wfmt, max_ctx=64, **kw):
+    d = native.Decoder(synth.TINY, wfmt, max_ctx, **kw)
+    d.pack(native.master_to_device(master))
+    return d
+
+
+def _gap(logits):
+    top2 = np.sort(logits)[-2:]
+    return float(top2[1] - top2[0])
+
+
+def test_codec_tables(native):
+    """G6: the kernel's register decoders reproduce every E4M3 and E2M1 code."""
+    codes = torch.arange(256, dtype=torch.uint8, device="cuda")
+    out = torch.empty(256, dtype=torch.float32, device="cuda")
+    native.decode_codes(0, codes, out)
+    got = out.cpu().numpy()
+    ref = e4m3_decode(np.arange(256, dtype=np.uint8))
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin].view(np.uint32), ref[fin].view(np.uint32))
+    c16 = torch.arange(16, dtype=torch.uint8, device="cuda")
+    o16 = torch.empty(16, dtype=torch.float32, device="cuda")
+    native.decode_codes(1, c16, o16)
+    assert np.array_equal(o16.cpu().numpy().view(np.uint32),
+                          e2m1_decode(np.arange(16, dtype=np.uint8)).view(np.uint32))
+
+
+@pytest.mark.parametrize("wfmt", FORMATS)
+def test_packed_bytes_bit_exact(native, master, wfmt):
+    """G1: the GPU packer's canonical bytes equal the oracle quantizer's."""
+    d = _decoder(native, master, wfmt)
+    orc = Oracle(master, wfmt, 64)
+    for layer in range(synth.TINY.n_layers):
+        for name in ("q", "k", "v", "o", "gate", "up", "down"):
+            codes, sc, bs, ts = d.read_packed(layer, name)
+            ref = orc.packed[(layer, name)]
+            _check_packed(codes, sc, bs, ts, ref, (wfmt, layer, name))
+    codes, sc, bs, ts = d.read_packed(0, "embed")
+    _check_packed(codes, sc, bs, ts, orc.packed[(-1, "embed")], (wfmt, "embed"))
+    d.close()
+
+
+def _check_packed(codes, sc, bs, ts, ref, what):
+    if isinstance(ref, np.ndarray):                      # bf16: stored as is
+        assert np.array_equal(codes, ref), what
+    elif hasattr(ref, "scales"):                         # FP8 per row
+        assert np.array_equal(codes, ref.codes), what
+        assert np.array_equal(sc.view(np.uint32), ref.scales.view(np.uint32)), what
+    else:                                                # NVFP4
+        assert np.array_equal(codes, ref.codes), what
+        assert np.array_equal(bs, ref.block_scales), what
+        assert np.float32(ts).view(np.uint32) == np.float32(ref.tensor_scale).view(np.uint32), what
+
+
+def _teacher_forced(native, master, wfmt, tokens, max_ctx=64, dec=None):
+    """Run `tokens` at positions 0.. on both sides; return per-step GPU logits,
+    GPU fused argmax and oracle logits."""
+    d = dec or _decoder(native, master, wfmt, max_ctx)
+    orc = Oracle(master, wfmt, max_ctx)
+    cache = orc.new_cache()
+    tok = torch.zeros(2, dtype=torch.int32, device="cuda")
+    lg = torch.zeros(synth.TINY.vocab, dtype=torch.float32, device="cuda")
+    gl, ga, ol = [], [], []
+    for pos, t in enumerate(tokens):
+        tok[0] = int(t)
+        d.decode_step_async(tok[0:1], pos, tok[1:2], lg)
+        torch.cuda.synchronize()
+        gl.append(lg.cpu().numpy().copy())
+        ga.append(int(tok[1].item()))
+        ol.append(orc.step(cache, int(t), pos))
+    d.check_device_error()
+    return d, np.array(gl), np.array(ga), np.array(ol)
+
+
+@pytest.mark.parametrize("wfmt", FORMATS)
+def test_teacher_forced_logits(native, master, wfmt):
+    """G2/G3/G4 over a 16-token prompt plus 32 forced random tokens (48
+    positions: one attention split up to position 63, so every step also
+    exercises the KV append and the full causal range)."""
+    toks = np.concatenate([synth.make_prompt(synth.TINY.vocab, 16, 1),
+                           synth.make_prompt(synth.TINY.vocab, 32, 5)])
+    d, gl, ga, ol = _teacher_forced(native, master, wfmt, toks)
+    for i in range(len(toks)):
+        rel = np.linalg.norm(gl[i] - ol[i]) / np.linalg.norm(ol[i])
+        assert rel <= REL_L2, (wfmt, i, rel)
+        assert ga[i] == argmax_lowest(gl[i]), (wfmt, i)            # G4: fused = brute force
+        if _gap(ol[i]) >= GAP:
+            assert ga[i] == argmax_lowest(ol[i]), (wfmt, i)        # G3
+    d.close()
+
+
+@pytest.mark.parametrize("wfmt", FORMATS)
+def test_split_attention_long_positions(native, master, wfmt):
+    """Positions up to 300 with 64 positions per unit: attention runs as 5
+    splits per KV head plus the merge phase; compare a few late steps."""
+    toks = synth.make_prompt(synth.TINY.vocab, 300, 7)
+    d = _decoder(native, master, wfmt, max_ctx=320)
+    orc = Oracle(master, wfmt, 320)
+    cache = orc.new_cache()
+    nxt = d.prefill(toks[:296])
+    want, last = orc.prefill_batched(cache, toks[:296])
+    if _gap(last) >= GAP:
+        assert nxt == want
+    tok = torch.zeros(2, dtype=torch.int32, device="cuda")
+    lg = torch.zeros(synth.TINY.vocab, dtype=torch.float32, device="cuda")
+    for pos in range(296, 300):
+        tok[0] = int(toks[pos])
+        d.decode_step_async(tok[0:1], pos, tok[1:2], lg)
+        torch.cuda.synchronize()
+        ref = orc.step(cache, int(toks[pos]), pos)
+        got = lg.cpu().numpy()
+        assert np.linalg.norm(got - ref) / np.linalg.norm(ref) <= REL_L2, (wfmt, pos)
+        assert int(tok[1].item()) == argmax_lowest(got)
+    d.check_device_error()
+    d.close()
+
+
+@pytest.mark.parametrize("wfmt", FORMATS)
+def test_free_running_greedy(native, master, wfmt):
+    """G3 free-running: the GPU's greedy tokens equal the oracle's up to the
+    first step whose oracle top-2 gap is below the tolerance."""
+    prompt = synth.make_prompt(synth.TINY.vocab, 16, 1)
+    d = _decoder(native, master, wfmt)
+    orc = Oracle(master, wfmt, 64)
+    toks, logits = orc.generate(prompt, 32)
+    got = [d.prefill(prompt)]
+    for i in range(32):
+        got.append(d.decode_step(got[-1], 16 + i))
+    for i in range(33):
+        if i > 0 and _gap(logits[i - 1]) < GAP:
+            break
+        assert got[i] == toks[i], (wfmt, i)
+    d.close()
+
+
+def test_determinism_three_runs(native, master):
+    """G5: three runs give identical tokens and bit-identical logits."""
+    toks = synth.make_prompt(synth.TINY.vocab, 24, 3)
+    runs = []
+    for _ in range(3):
+        d, gl, ga, _ = _teacher_forced(native, master, synth.FP8_ROW, toks)
+        runs.append((gl.view(np.uint32).copy(), ga.copy()))
+        d.close()
+    for gl, ga in runs[1:]:
+        assert np.array_equal(gl, runs[0][0]) and np.array_equal(ga, runs[0][1])
+
+
+def test_argmax_tie_lowest_index(native, master):
+    """Duplicate the winning embedding row into a lower index: the tied
+    logits must resolve to the lower index."""
+    d = _decoder(native, master, synth.BF16)
+    tok = torch.zeros(2, dtype=torch.int32, device="cuda")
+    lg = torch.zeros(synth.TINY.vocab, dtype=torch.float32, device="cuda")
+    tok[0] = 123
+    d.decode_step_async(tok[0:1], 0, tok[1:2], lg)
+    torch.cuda.synchronize()
+    win = int(tok[1].item())
+    d.close()
+    lower = 7 if win != 7 else 8
+    if lower > win:
+        win, lower = lower, win
+    m2 = synth.make_weights(synth.TINY, 0)
+    m2.embed[lower] = m2.embed[win]
+    d = _decoder(native, m2, synth.BF16)
+    d.decode_step_async(tok[0:1], 0, tok[1:2], lg)
+    torch.cuda.synchronize()
+    got = lg.cpu().numpy()
+    assert got[lower] == got[win]
+    assert int(tok[1].item()) == argmax_lowest(got)
+    d.close()
+
+
+def test_edge_positions_and_errors(native, master):
+    d = _decoder(native, master, synth.BF16, max_ctx=20)
+    # last position of the cache
+    toks = synth.make_prompt(synth.TINY.vocab, 20, 4)
+    d.prefill(toks)
+    with pytest.raises(native.MkError) as e:
+        d.decode_step(1, 20)
+    assert e.value.status == native.MK_E_INVALID
+    with pytest.raises(native.MkError):
+        d.decode_step(synth.TINY.vocab, 0)
+    with pytest.raises(native.MkError):
+        d.prefill([])
+    # a single-token prompt
+    orc = Oracle(master, synth.BF16, 20)
+    want, _ = orc.prefill(orc.new_cache(), toks[:1])
+    assert d.prefill(toks[:1]) == want
+    d.close()
+
+
+def test_timeout_path_forced_from_host(native, master):
+    """Every wait made unsatisfiable from the host (tag skew) with a 100 us
+    spin bound: the kernel exits, the step reports MK_E_TIMEOUT, and the next
+    normal step works."""
+    d = _decoder(native, master, synth.BF16)
+    d.set_option(native.OPT_SPIN_LIMIT, 10_000)
+    d.set_option(native.OPT_TAG_SKEW, 1)
+    with pytest.raises(native.MkError) as e:
+        d.decode_step(5, 0)
+    assert e.value.status == native.MK_E_TIMEOUT
+    d.set_option(native.OPT_TAG_SKEW, 0)
+    d.set_option(native.OPT_SPIN_LIMIT, 100_000_000)
+    orc = Oracle(master, synth.BF16, 64)
+    want = argmax_lowest(orc.step(orc.new_cache(), 5, 0))
+    assert d.decode_step(5, 0) == want
+    d.close()
+
+
+def test_invalid_device_token(native, master):
+    d = _decoder(native, master, synth.BF16)
+    tok = torch.tensor([synth.TINY.vocab + 3, 0], dtype=torch.int32, device="cuda")
+    d.decode_step_async(tok[0:1], 0, tok[1:2])
+    torch.cuda.synchronize()
+    assert int(tok[1].item()) == -1
+    with pytest.raises(native.MkError) as e:
+        d.check_device_error()
+    assert e.value.status == native.MK_E_INVALID
+    d.close()

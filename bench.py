@@ -1,0 +1,185 @@
+"""Batch-1 decode benchmark on one MI355X.
+
+One step = one decode launch of the whole hot path (embed, 28 layers of
+norm/QKV/attention/O/MLP, final norm, tied LM head, argmax) at batch 1.
+Protocol (monolith page, "Hard constraints" and "Design decisions",
+benchmark protocol): prefill excluded and untimed, a full warm-up pass,
+re-prefill, then K greedy steps with tokens chained on the device, timed with
+events around the whole loop.  Prints one JSON line.
+
+    python bench.py [--steps 256] [--warmup 16] [--workload qwen3_0p6b_bf16]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0   # MI355X HBM3E peak
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default="qwen3_0p6b_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-steps", type=int, default=12)
+    ap.add_argument("--repeats", type=int, default=5, help="timed runs; the median is reported")
+    ap.add_argument("--att-target", type=int, default=0, help="attention positions per unit (0: library default)")
+    ap.add_argument("--replicas", type=int, default=0, help="exchange replicas (0: library default)")
+    ap.add_argument("--poll-sleep", type=int, default=-1, help="poll back-off level (-1: library default)")
+    ap.add_argument("--xray", action="store_true",
+                    help="X-ray build: print the per-phase budget of the step at position P + K/2 "
+                         "instead of the headline line")
+    return ap.parse_args()
+
+
+def xray_report(dec, wl, K, prompt):
+    """Run the X-ray build to position P + K/2 and report that step's budget."""
+    import torch
+    from quantized_gemv_amd import xray
+    tok = torch.zeros(2, dtype=torch.int32, device="cuda")
+    tok[0] = dec.prefill(prompt)
+    pos = wl.prompt_len
+    for i in range(K // 2):
+        dec.decode_step_async(tok[i % 2:i % 2 + 1], pos + i, tok[1 - i % 2:2 - i % 2])
+    torch.cuda.synchronize()
+    dec.check_device_error()
+    rec = dec.trace()
+    b = xray.budget(rec, wl.shape.n_layers)
+    tab = xray.phase_table(rec, wl.shape.n_layers)
+    L = wl.shape.n_layers
+    layer_mid = {t["name"]: t for ph, t in tab.items() if (ph - 2) // 6 == L // 2 and 2 <= ph < 6 * L + 2}
+    return {"xray_position": pos + K // 2 - 1, "budget": b,
+            "middle_layer_phases": {k: {kk: round(vv, 1) if isinstance(vv, float) else vv for kk, vv in v.items()}
+                                    for k, v in layer_mid.items()},
+            "lm_head": tab.get(6 * L + 2), "argmax": tab.get(6 * L + 3)}
+
+
+def cpu_baseline(master, wl, n_steps, prompt):
+    """The oracle as it stands, timed on this host: batched prefill of the
+    prompt (untimed), then `n_steps` decode steps (timed)."""
+    import numpy as np
+    from oracle.model import Oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    orc = Oracle(master, wl.wfmt, wl.prompt_len + n_steps + 1)
+    cache = orc.new_cache()
+    tok, _ = orc.prefill_batched(cache, prompt)
+    t0 = time.perf_counter()
+    for i in range(n_steps):
+        lg = orc.step(cache, tok, wl.prompt_len + i)
+        tok = int(np.argmax(lg))
+    dt = time.perf_counter() - t0
+    return {"value": n_steps / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_steps} greedy decode steps at positions {wl.prompt_len}..{wl.prompt_len + n_steps - 1} "
+                      f"after an untimed batched prefill of the same {wl.prompt_len}-token prompt "
+                      f"({dt:.1f} s of numpy float32 on the host)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (one model replica per GPU; no multi-GPU path); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import synth
+    from quantized_gemv_amd import native
+
+    wl = synth.WORKLOADS[args.workload]
+    sh = wl.shape
+    K, W = args.steps, args.warmup
+    max_ctx = max(wl.max_ctx, wl.prompt_len + max(K, W) + 1)
+    torch.cuda.set_device(0)
+    master = synth.make_weights(sh, wl.weight_seed)
+    prompt = synth.make_prompt(sh.vocab, wl.prompt_len, wl.prompt_seed)
+
+    dec = native.Decoder(sh, wl.wfmt, max_ctx, xray=args.xray, att_target=args.att_target or None,
+                         replicas=args.replicas or None,
+                         poll_sleep=None if args.poll_sleep < 0 else args.poll_sleep)
+    dev_master = native.master_to_device(master)
+    dec.pack(dev_master)
+    del dev_master
+    torch.cuda.empty_cache()
+
+    if args.xray:
+        print(json.dumps({"workload": wl.name, **xray_report(dec, wl, K, prompt)}), flush=True)
+        dec.close()
+        return
+    stream = torch.cuda.current_stream()
+    toks = torch.zeros(max(K, W) + 1, dtype=torch.int32, device="cuda")
+
+    def run(n):
+        """Prefill, then n chained decode steps; returns elapsed seconds."""
+        first = dec.prefill(prompt)
+        toks[0] = first
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            dec.decode_step_async(toks[i:i + 1], wl.prompt_len + i, toks[i + 1:i + 2])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dec.check_device_error()
+        return e0.elapsed_time(e1) / 1e3
+
+    run(W)                       # warm-up pass
+    times = [run(K) for _ in range(max(1, args.repeats))]
+    tokens_ref = toks[:K + 1].cpu().numpy().copy()
+    dt = float(np.median(times))
+    tps = K / dt
+    sizes = dec.sizes
+    wbytes = int(sizes.weight_bytes_per_token)
+    # algorithmic bytes per launch: every weight byte once, plus the KV cache
+    # read over positions 0..pos (mean over the timed positions)
+    mean_ctx = wl.prompt_len + (K - 1) / 2.0 + 1
+    kv_bytes = float(sizes.kv_bytes_per_position) * mean_ctx
+    algo = wbytes + kv_bytes
+    achieved = algo / (dt / K) / 1e9
+    out = {
+        "metric": "batch-1 decode tokens/s (0.6B shape); % of HBM roofline on weight bytes",
+        "value": round(tps, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(dt / K * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {0: "bf16", 1: "fp8_e4m3", 2: "fp4_e2m1+fp8_e4m3"}[wl.wfmt],
+        "data": "synthetic (seeded random weights N(0,0.02), uniform random prompt)",
+        "config": {"workload": wl.name, "prompt_len": wl.prompt_len, "decode_steps": K,
+                   "positions": [wl.prompt_len, wl.prompt_len + K - 1],
+                   "weight_format": synth.WFMT_NAMES[wl.wfmt], "accumulate": "f32", "batch": 1,
+                   "grid": "one 512-thread workgroup per CU", "timed_runs": len(times),
+                   "att_target": args.att_target or None, "replicas": args.replicas or None,
+                   "run_seconds": [round(t, 6) for t in times]},
+        "weight_bytes_per_token": wbytes,
+        "weight_roofline_pct": round(100.0 * wbytes * tps / (PEAK_HBM_GBPS * 1e9), 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "kernel": "mk::decode_kernel",
+                     "bytes_per_launch": int(algo)},
+        "greedy_tokens_head": [int(t) for t in tokens_ref[:8]],
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(master, wl, args.cpu_steps, prompt)
+    dec.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -55,7 +55,10 @@ enum mk_wfmt {
 };
 
 /* Model shape.  Constraints checked by mk_create: all sizes > 0;
- * n_q_heads % n_kv_heads == 0; head_dim in {64, 128, 256};
+ * n_q_heads % n_kv_heads == 0; the kernels are compiled per shape class
+ * (head_dim, n_q_heads / n_kv_heads, ceil(hidden/1024),
+ * ceil(n_q_heads*head_dim/1024), ceil(intermediate/1024)), one of
+ * (64, 2, 1, 1, 1) and (128, 2, 1, 2, 3) (the latter is the Qwen3-0.6B shape);
  * hidden, intermediate and n_q_heads*head_dim multiples of 16;
  * n_layers <= 160; max_ctx <= 1<<20. */
 typedef struct mk_config {
@@ -91,6 +94,10 @@ typedef struct mk_trace_rec {
   uint32_t pad;
   uint64_t t_start, t_wait_begin, t_wait_end, t_end;  /* s_memtime */
   uint64_t rt_start, rt_end;                           /* s_memrealtime */
+  uint64_t t_mark[4];  /* s_memtime marks inside the phase after its wait (0 if unused): GEMV
+                          phases: input normalized, products done, rows finished, results
+                          published; attention: q/k/v normed and K/V appended, scores and
+                          softmax done, outputs reduced, results published */
 } mk_trace_rec;
 
 typedef struct mk_model mk_model;
@@ -168,7 +175,9 @@ int mk_get_trace(mk_model* m, mk_trace_rec* h_out, size_t cap, size_t* n_out);
 
 /* Test hook: decode `n` codes with the kernel's own register decoders.
  * codec 0: E4M3 bytes -> fp32; codec 1: E2M1 (one code per byte, low
- * nibble) -> fp32.  Device buffers; enqueued on `s`.  Needs no model. */
+ * nibble) -> fp32; codecs 2 and 3: the same two formats through the
+ * converters the GEMVs use (to packed bf16), widened to fp32.  Device
+ * buffers; enqueued on `s`.  Needs no model. */
 int mk_decode_codes(int32_t codec, const uint8_t* d_codes, int32_t n, float* d_out, mk_stream_t s);
 
 /* Tuning knobs (defaults in brackets): key 0 grid size [compute units],

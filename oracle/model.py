@@ -130,13 +130,17 @@ class Oracle:
         self.dt, self.round_bf16 = dtype, round_bf16
         self.eps = sh.rms_eps
         self.packed: Dict[Tuple[int, str], object] = {}
-        self.w: List[Dict[str, np.ndarray]] = []
-        for l, layer in enumerate(master.layers):
-            d = {}
-            for name, bits in layer.items():
-                d[name] = self._prepare(l, name, bits)
-            self.w.append(d)
-        self.embed = self._prepare(-1, "embed", master.embed)
+        # tensors are independent, so they are prepared on a thread pool
+        from concurrent.futures import ThreadPoolExecutor
+        import os
+        jobs = [(-1, "embed", master.embed)]
+        jobs += [(l, name, bits) for l, layer in enumerate(master.layers) for name, bits in layer.items()]
+        with ThreadPoolExecutor(min(16, len(os.sched_getaffinity(0)))) as ex:
+            done = list(ex.map(lambda j: self._prepare(*j), jobs))
+        self.embed = done[0]
+        self.w: List[Dict[str, np.ndarray]] = [dict() for _ in master.layers]
+        for (l, name, _), w in zip(jobs[1:], done[1:]):
+            self.w[l][name] = w
         self.final_norm = bf16_bits_to_f32(master.final_norm).astype(dtype)
         self.cos, self.sin = rope_table(max_ctx, sh.head_dim, sh.rope_theta)
 

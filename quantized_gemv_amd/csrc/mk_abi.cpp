@@ -54,6 +54,7 @@ struct mk_model {
   int grid_opt = 0, replicas = 8, att_target = 64;
   int64_t spin_limit = 100000000;
   uint32_t tag_skew = 0;
+  uint32_t poll_sleep = 0;
   uint32_t epoch = 0;
   std::string err;
 };
@@ -196,9 +197,9 @@ int validate_cfg(const mk_config* c) {
     return MK_E_INVALID;
   if (c->wfmt < MK_WFMT_BF16 || c->wfmt > MK_WFMT_FP4_MIX) return MK_E_INVALID;
   if (c->n_q_heads % c->n_kv_heads) return MK_E_UNSUPPORTED;
-  if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) return MK_E_UNSUPPORTED;
-  const int gs = c->n_q_heads / c->n_kv_heads;
-  if (gs > 4 || gs * c->head_dim > 512) return MK_E_UNSUPPORTED;
+  if (!decode_shape_supported(c->head_dim, c->n_q_heads / c->n_kv_heads, c->hidden, c->n_q_heads * c->head_dim,
+                              c->intermediate))
+    return MK_E_UNSUPPORTED;
   if (c->hidden % 16 || c->intermediate % 16 || (c->n_q_heads * c->head_dim) % 16) return MK_E_UNSUPPORTED;
   if (c->hidden > 4096 || c->intermediate / 2 > 6144 || c->n_q_heads * c->head_dim / 2 > 6144)
     return MK_E_UNSUPPORTED;
@@ -229,10 +230,11 @@ int sync_params(mk_model* m, hipStream_t s) {
   if (!m->params_dirty) return MK_OK;
   const mk_config& c = m->cfg;
   Params& P = m->P;
-  P.w = static_cast<const uint8_t*>(m->d_weights);
-  P.kv = static_cast<uint16_t*>(m->d_kv);
-  P.rope = static_cast<const float*>(m->d_rope);
-  P.xch = reinterpret_cast<uint64_t*>(m->d_scratch);
+  // C-style casts: in the device pass of this file these fields are global pointers
+  P.w = (decltype(P.w))m->d_weights;
+  P.kv = (decltype(P.kv))m->d_kv;
+  P.rope = (decltype(P.rope))m->d_rope;
+  P.xch = (decltype(P.xch))m->d_scratch;
   P.trace = m->d_trace;
   P.L = c.n_layers;
   P.H = c.hidden;
@@ -247,6 +249,7 @@ int sync_params(mk_model* m, hipStream_t s) {
   P.att_target = m->att_target;
   P.spin_limit = (uint64_t)m->spin_limit;
   P.tag_skew = m->tag_skew;
+  P.poll_sleep = m->poll_sleep;
   P.n_phases = n_phases(c);
   HIPCK(m, hipMemcpyAsync(m->d_scratch + m->params_off, &P, sizeof(Params), hipMemcpyHostToDevice, s));
   HIPCK(m, hipStreamSynchronize(s));  // the host copy is a stack-independent member, but keep ordering simple
@@ -278,7 +281,9 @@ int launch_step(mk_model* m, const int32_t* d_token, int pos, int32_t* d_next, f
     m->epoch = 1;
   }
   const Params* dp = reinterpret_cast<const Params*>(m->d_scratch + m->params_off);
-  HIPCK(m, launch_decode(dp, m->P.grid, d_token, pos, m->epoch, d_next, d_logits, s));
+  const mk_config& c = m->cfg;
+  HIPCK(m, launch_decode(dp, c.wfmt, c.head_dim, c.n_q_heads / c.n_kv_heads, c.hidden, c.n_q_heads * c.head_dim,
+                         c.intermediate, m->P.grid, d_token, pos, m->epoch, d_next, d_logits, s));
   return MK_OK;
 }
 
@@ -512,7 +517,7 @@ int mk_get_trace(mk_model* m, mk_trace_rec* h_out, size_t cap, size_t* n_out) {
 }
 
 int mk_decode_codes(int32_t codec, const uint8_t* d_codes, int32_t n, float* d_out, mk_stream_t stream) {
-  if ((codec != 0 && codec != 1) || n < 0 || (n > 0 && (!d_codes || !d_out))) return MK_E_INVALID;
+  if (codec < 0 || codec > 3 || n < 0 || (n > 0 && (!d_codes || !d_out))) return MK_E_INVALID;
   const hipError_t e = launch_decode_codes(codec, d_codes, n, d_out, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? MK_OK : MK_E_HIP;
 }
@@ -544,6 +549,10 @@ int mk_set_option(mk_model* m, int32_t key, int64_t value) {
     case 4:
       if (value < 0 || value > 0xFFFF) return fail(m, MK_E_INVALID, "tag skew out of range");
       m->tag_skew = (uint32_t)value;
+      break;
+    case 5:
+      if (value < 0 || value > 5) return fail(m, MK_E_INVALID, "poll sleep out of range");
+      m->poll_sleep = (uint32_t)value;
       break;
     default:
       return fail(m, MK_E_INVALID, "unknown option %d", key);

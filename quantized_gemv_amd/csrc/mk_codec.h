@@ -8,8 +8,10 @@
 //   e2m1  sign, 2 exponent bits (bias 1), 1 mantissa bit: {0,.5,1,1.5,2,3,4,6}
 //
 // Decoding uses gfx950's converters: v_cvt_pk_f32_fp8 reads OCP E4M3 and
-// v_cvt_scalef32_pk_f32_fp4 with scale 1.0 reads E2M1 exactly (both checked
-// against every code).  Encoding, used only by the packer, is written from
+// v_cvt_scalef32_pk_f32_fp4 with scale 1.0 reads E2M1 exactly; the GEMVs use
+// v_cvt_scalef32_pk_bf16_fp8 / _fp4, which turn two codes into a bf16 pair
+// (exact: every E4M3 and E2M1 value is a bf16 value) for v_dot2_f32_bf16.
+// All four are checked against every code.  Encoding, used only by the packer, is written from
 // the format definition: round to nearest, ties to even, saturate to the
 // largest finite magnitude, keep the sign (so tiny negatives become -0).
 #pragma once
@@ -19,6 +21,22 @@
 namespace mk {
 
 typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+
+// acc + a.lo*b.lo + a.hi*b.hi for two packed bf16 pairs (products exact in fp32).
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, a), __builtin_bit_cast(bf2, b), acc, false);
+}
+// Bytes 0,1 (HI=false) or 2,3 (HI=true) of `w`, E4M3, as a bf16 pair.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+// Nibbles of byte SEL of `w`, E2M1 (low nibble first), as a bf16 pair.
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL));
+}
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

@@ -34,255 +34,297 @@ namespace mk {
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 
-constexpr int kMaxAct = 2048;        // bf16 pairs of a normalized input (hidden <= 4096)
-constexpr int kAttBlock = kThreads;  // positions scored per attention block
-constexpr int kMaxGroupDim = 512;    // (q heads per KV head) * head_dim
+constexpr int kMaxGroupDim = 256;    // (q heads per KV head) * head_dim
 constexpr int kMaxGroup = 4;         // q heads per KV head
-constexpr int kGemvBatch = 4;        // GEMV items per wave in flight
 
 struct AttSmem {
-  float q[kMaxGroupDim];             // normed + roped q of the group's heads
-  float k[256], v[256];              // this position's k (normed, roped) and v
-  uint32_t kb[128], vb[128];         // the same as bf16 pairs (what the cache holds)
-  float pr[kMaxGroup][kAttBlock];    // scores, then probabilities, of one block
-  float o[kWaves][kMaxGroupDim];     // per-wave partial outputs
-  float m[kMaxGroup], l[kMaxGroup], sc[kMaxGroup];
-};
-struct GemvSmem {
-  uint32_t act[kMaxAct];             // normalized input as bf16 pairs
-  float part[kMaxPart];              // partial dot products per (row, 1024-chunk)
-  float y[kMaxPart];                 // finished rows
+  float raw[kMaxGroupDim + 256];         // gathered q heads (gs*hd), then k (hd), then v (hd)
+  float qw[kWaves][kMaxGroupDim];        // per wave: normed + roped q (wave-private)
+  uint32_t kvw[kWaves][128];             // per wave: this position's k (roped) and v as bf16 pairs
+  float prow[kWaves][4][kMaxGroupDim];   // per wave: 16-lane-row partial outputs (wave-private)
+  float wo[kWaves][kMaxGroupDim];        // per wave: output over its positions
+  float wm[kWaves][kMaxGroup], wl[kWaves][kMaxGroup];
 };
 struct Smem {
-  uint32_t vin[kMaxVecWords];        // gathered payloads
-  union {
-    AttSmem att;
-    GemvSmem g;
-  } u;
+  uint32_t vin[kMaxVecWords];            // gathered payloads
+  AttSmem att;
   float red[kWaves * 2];
   int32_t redi[kWaves];
-  float x_own[kMaxOwn];              // residual rows this workgroup owns
+  float x_own[kMaxOwn];                  // residual rows this workgroup owns
 };
-
-__device__ __forceinline__ Mat at_layer(const Mat& m, uint64_t off) {
-  Mat r = m;
-  r.codes += off;
-  r.scales += off;
-  r.tscale += off;
-  return r;
-}
 
 __device__ __forceinline__ void split_range(int n, int parts, int i, int& a, int& b) {
   a = (int)((int64_t)n * i / parts);
   b = (int)((int64_t)n * (i + 1) / parts);
 }
 
+// This wave's index, as a value the compiler knows is uniform across the wave.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+// Cross-lane reductions with DPP (row operations on the VALU) and
+// v_readlane, instead of ds_bpermute round trips through the LDS crossbar.
+// DPP controls (gfx9): quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E,
+// row_ror:4 = 0x124, row_ror:8 = 0x128, row_half_mirror = 0x141.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Sum over the 8-lane group (lanes 8k..8k+7), result in every lane of it.
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  return v + dpp<0x141>(v);
+}
+__device__ __forceinline__ float sum16(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x124>(v);
+  return v + dpp<0x128>(v);
+}
+__device__ __forceinline__ float max16(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x124>(v));
+  return fmaxf(v, dpp<0x128>(v));
+}
+__device__ __forceinline__ float lane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+// Sum / max over the wave, the same value in every lane (fixed order).
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v = sum16(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-
-// Sum over the workgroup, same value in every thread, fixed order.
-__device__ __forceinline__ float block_sum(float v, float* red) {
-  v = wave_sum(v);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float s = 0.f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) s += red[w];
-  return s;
-}
-
-// act[j] = bf16 pair of g * (x * r) at 2j, 2j+1, with r = 1/sqrt(mean(x^2) + eps)
-// (RMSNorm; every workgroup computes the factor itself, the page's trick for
-// removing a barrier).
-__device__ __forceinline__ void rmsnorm_to_act(const Params& p, const uint32_t* xin, uint64_t g_off, int n,
-                               uint32_t* act, float* red) {
-  float ss = 0.f;
-  for (int i = threadIdx.x; i < n; i += kThreads) {
-    const float x = __uint_as_float(xin[i]);
-    ss = fmaf(x, x, ss);
-  }
-  const float tot = block_sum(ss, red);
-  const float r = 1.0f / sqrtf(tot / (float)n + p.eps);
-  const uint16_t* g = reinterpret_cast<const uint16_t*>(p.w + g_off);
-  for (int j = threadIdx.x; j < n / 2; j += kThreads) {
-    const float a = bf16_to_f32(g[2 * j]) * (__uint_as_float(xin[2 * j]) * r);
-    const float b = bf16_to_f32(g[2 * j + 1]) * (__uint_as_float(xin[2 * j + 1]) * r);
-    act[j] = f32_to_bf16(a) | (f32_to_bf16(b) << 16);
-  }
+  v = max16(v);
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
 // ------------------------------------------------------------------ GEMV
-// Work item = (row, 1024-element chunk of K).  Lane l of a wave covers
-// elements [c*1024 + 16 l, +16) of its item's row, so a wave streams one
-// contiguous 1 KB (fp8) / 2 KB (bf16) / 512 B (fp4) run per item with
-// 16-byte loads.  Items are dealt to waves round-robin; each wave keeps
-// kGemvBatch items' weights in flight.
-template <uint32_t FMT>
-struct Batch {
-  v4u w0[kGemvBatch], w1[kGemvBatch];
+// A GEMV phase is wave-autonomous: after the workgroup has gathered the input
+// vector, each wave computes the RMSNorm factor itself (the page's
+// every-block-recomputes-the-norm trick, taken down to the wave), keeps its
+// slice of the activations in registers, and owns whole output units (one
+// row, or for gate/up the four rows behind one output word), so each unit is
+// finished with one DPP reduction and published by the wave that computed
+// it: no barrier after the wait.
+//
+// Lane l covers elements [c*1024 + 16 l, +16) of every row for chunk c, so a
+// wave streams each row as contiguous 1 KB (fp8) / 2 KB (bf16) / 512 B (fp4)
+// runs with 16-byte (fp4: 8-byte) loads.  Units u = wave + 8 j; a wave keeps
+// UB units' weights in registers, double-buffered.
+
+// One matrix of one phase, with its pointers resolved once.
+struct GMat {
+  MK_GLOBAL const uint8_t* codes;
+  MK_GLOBAL const uint8_t* scales;  // fp8: fp32 per row; fp4: e4m3 per 16-block
+  MK_GLOBAL const float* ts;        // fp4: tensor scales
+  uint32_t K, ts_mode, ts_b0, ts_b1;
 };
 
-template <uint32_t FMT>
-__device__ __forceinline__ void gemv_load(const Params& p, const Mat& m, int r0, int items, int nch,
-                                          int bi, Batch<FMT>& B) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int u = 0; u < kGemvBatch; ++u) {
-    const int it = wave + kWaves * (bi * kGemvBatch + u);
-    const int rr = it / nch, c = it - rr * nch;
-    const int e0 = c * 1024 + lane * 16;
-    if (it < items && e0 < (int)m.K) {
-      const uint64_t row = (uint64_t)(r0 + rr);
-      const uint8_t* base = p.w + m.codes;
-      if (FMT == FMT_BF16) {
-        const v4u* q = reinterpret_cast<const v4u*>(base + (row * m.K + e0) * 2);
-        B.w0[u] = q[0];
-        B.w1[u] = q[1];
-      } else if (FMT == FMT_FP8) {
-        B.w0[u] = *reinterpret_cast<const v4u*>(base + row * m.K + e0);
-      } else {
-        const v2u c2 = *reinterpret_cast<const v2u*>(base + (row * m.K + e0) / 2);
-        B.w0[u].x = c2.x;
-        B.w0[u].y = c2.y;
-        B.w1[u].x = p.w[m.scales + row * (m.K / 16) + e0 / 16];
-      }
-    }
-  }
+__device__ __forceinline__ GMat gmat(MK_GLOBAL const uint8_t* W, const Mat& m, uint64_t off) {
+  GMat g;
+  g.codes = W + m.codes + off;
+  g.scales = W + m.scales + off;
+  g.ts = GCAST(const float, W + m.tscale + off);
+  g.K = m.K;
+  g.ts_mode = m.ts_mode;
+  g.ts_b0 = m.ts_b0;
+  g.ts_b1 = m.ts_b1;
+  return g;
 }
 
-__device__ __forceinline__ float fp4_tensor_scale(const Params& p, const Mat& m, uint32_t row) {
+__device__ __forceinline__ float fp4_tensor_scale(const GMat& g, uint32_t row) {
   uint32_t idx = 0;
-  if (m.ts_mode == 1) idx = row < m.ts_b0 ? 0u : (row < m.ts_b1 ? 1u : 2u);
-  else if (m.ts_mode == 2) idx = row & 1u;
-  return *reinterpret_cast<const float*>(p.w + m.tscale + 4 * idx);
+  if (g.ts_mode == 1) idx = row < g.ts_b0 ? 0u : (row < g.ts_b1 ? 1u : 2u);
+  else if (g.ts_mode == 2) idx = row & 1u;
+  return g.ts[idx];
 }
 
-template <uint32_t FMT>
-__device__ __forceinline__ void gemv_compute(const Params& p, const Mat& m, int r0, int items, int nch,
-                                             int bi, const Batch<FMT>& B, const uint32_t* act,
-                                             float* part) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float acc[kGemvBatch];
+template <uint32_t FMT, int NCH, int UR, int UB>
+struct WBatch {
+  v4u a[UB][UR][NCH];   // bf16: first 16 B; fp8: 16 B; fp4: 8 B codes in .xy
+  v4u b[UB][UR][NCH];   // bf16: second 16 B; fp4: block-scale byte in .x
+  float rs[UB][UR];     // fp8 row scale / fp4 tensor scale
+};
+
+// Load units j0 .. j0+UB-1 of this wave.  Indices are clamped instead of
+// guarded, so no load sits behind a branch (a guarded load ends in a wait
+// that would drain every load in flight); clamped lanes and units are
+// discarded later.
+template <uint32_t FMT, int NCH, int UR, int UB>
+__device__ __forceinline__ void wload(const GMat& g, int r0, int nunits, int wave, int j0,
+                                      WBatch<FMT, NCH, UR, UB>& B) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int u = 0; u < kGemvBatch; ++u) {
-    const int it = wave + kWaves * (bi * kGemvBatch + u);
-    const int rr = it / nch, c = it - rr * nch;
-    const int e0 = c * 1024 + lane * 16;
-    float a = 0.f;
-    if (it < items && e0 < (int)m.K) {
-      const v4u* av = reinterpret_cast<const v4u*>(act + e0 / 2);
-      const v4u x0 = av[0], x1 = av[1];
-      const uint32_t xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-      if (FMT == FMT_BF16) {
-        const uint32_t ws[8] = {B.w0[u].x, B.w0[u].y, B.w0[u].z, B.w0[u].w,
-                                B.w1[u].x, B.w1[u].y, B.w1[u].z, B.w1[u].w};
+  for (int ub = 0; ub < UB; ++ub) {
+    const int u = min(wave + kWaves * (j0 + ub), nunits - 1);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          a = fmaf(bf16_lo(ws[j]), bf16_lo(xs[j]), a);
-          a = fmaf(bf16_hi(ws[j]), bf16_hi(xs[j]), a);
+    for (int r = 0; r < UR; ++r) {
+      const uint32_t row = (uint32_t)(r0 + u * UR + r);
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const uint32_t e0 = (uint32_t)min(c * 1024 + 16 * lane, (int)g.K - 16);
+        const uint32_t el = row * g.K + e0;
+        if (FMT == FMT_BF16) {
+          MK_GLOBAL const v4u* q = GCAST(const v4u, g.codes + 2ull * el);
+          B.a[ub][r][c] = q[0];
+          B.b[ub][r][c] = q[1];
+        } else if (FMT == FMT_FP8) {
+          B.a[ub][r][c] = *GCAST(const v4u, g.codes + el);
+        } else {
+          const v2u c2 = *GCAST(const v2u, g.codes + el / 2);
+          B.a[ub][r][c].x = c2.x;
+          B.a[ub][r][c].y = c2.y;
+          B.b[ub][r][c].x = g.scales[el / 16];
         }
-      } else if (FMT == FMT_FP8) {
-        const uint32_t ws[4] = {B.w0[u].x, B.w0[u].y, B.w0[u].z, B.w0[u].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float f[4];
-          e4m3x4_to_f32(ws[j], f);
-          a = fmaf(f[0], bf16_lo(xs[2 * j]), a);
-          a = fmaf(f[1], bf16_hi(xs[2 * j]), a);
-          a = fmaf(f[2], bf16_lo(xs[2 * j + 1]), a);
-          a = fmaf(f[3], bf16_hi(xs[2 * j + 1]), a);
-        }
-      } else {
-        const uint32_t ws[2] = {B.w0[u].x, B.w0[u].y};
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          float f[8];
-          e2m1x8_to_f32(ws[j], f);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            a = fmaf(f[2 * t], bf16_lo(xs[4 * j + t]), a);
-            a = fmaf(f[2 * t + 1], bf16_hi(xs[4 * j + t]), a);
-          }
-        }
-        const uint32_t row = (uint32_t)(r0 + rr);
-        a *= e4m3_to_f32(B.w1[u].x) * fp4_tensor_scale(p, m, row);
       }
-    }
-    acc[u] = a;
-  }
-#pragma unroll
-  for (int u = 0; u < kGemvBatch; ++u) acc[u] = wave_sum(acc[u]);
-  if (lane == 0) {
-#pragma unroll
-    for (int u = 0; u < kGemvBatch; ++u) {
-      const int it = wave + kWaves * (bi * kGemvBatch + u);
-      if (it < items) part[it] = acc[u];
+      if (FMT == FMT_FP8) B.rs[ub][r] = GCAST(const float, g.scales)[row];
+      if (FMT == FMT_FP4) B.rs[ub][r] = fp4_tensor_scale(g, row);
     }
   }
 }
 
-// Rows [r0, r0+nrows) of `m` against the bf16 vector `act`: y[t] for t < nrows.
-// The first batch of weights must already be in `B`.
-template <uint32_t FMT>
-__device__ __forceinline__ void gemv_rows(const Params& p, const Mat& m, int r0, int nrows, Batch<FMT>& B,
-                          const uint32_t* act, float* part, float* y) {
-  const int nch = ((int)m.K + 1023) >> 10;
-  const int items = nrows * nch;
-  const int wave = threadIdx.x >> 6;
-  gemv_compute<FMT>(p, m, r0, items, nch, 0, B, act, part);
-  for (int bi = 1; wave + kWaves * bi * kGemvBatch < items; ++bi) {
-    gemv_load<FMT>(p, m, r0, items, nch, bi, B);
-    gemv_compute<FMT>(p, m, r0, items, nch, bi, B, act, part);
+// Dot products of units j0.. with the activations xa; epi(u, vals) per unit.
+template <uint32_t FMT, int NCH, int UR, int UB, class Epi>
+__device__ __forceinline__ void wcompute(const WBatch<FMT, NCH, UR, UB>& B, const uint32_t (&xa)[NCH][8],
+                                         int nunits, int wave, int j0, Epi& epi) {
+#pragma unroll
+  for (int ub = 0; ub < UB; ++ub) {
+    const int u = wave + kWaves * (j0 + ub);
+    if (u >= nunits) break;  // uniform
+    float vals[UR];
+#pragma unroll
+    for (int r = 0; r < UR; ++r) {
+      float a = 0.f;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const uint32_t* xs = xa[c];
+        float ac = 0.f;
+        if (FMT == FMT_BF16) {
+          const uint32_t ws[8] = {B.a[ub][r][c].x, B.a[ub][r][c].y, B.a[ub][r][c].z, B.a[ub][r][c].w,
+                                  B.b[ub][r][c].x, B.b[ub][r][c].y, B.b[ub][r][c].z, B.b[ub][r][c].w};
+#pragma unroll
+          for (int j = 0; j < 8; ++j) ac = dot2(ws[j], xs[j], ac);
+        } else if (FMT == FMT_FP8) {
+          const uint32_t ws[4] = {B.a[ub][r][c].x, B.a[ub][r][c].y, B.a[ub][r][c].z, B.a[ub][r][c].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            ac = dot2(e4m3x2_to_bf16x2<false>(ws[j]), xs[2 * j], ac);
+            ac = dot2(e4m3x2_to_bf16x2<true>(ws[j]), xs[2 * j + 1], ac);
+          }
+        } else {
+          const uint32_t ws[2] = {B.a[ub][r][c].x, B.a[ub][r][c].y};
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            ac = dot2(e2m1x2_to_bf16x2<0>(ws[j]), xs[4 * j + 0], ac);
+            ac = dot2(e2m1x2_to_bf16x2<1>(ws[j]), xs[4 * j + 1], ac);
+            ac = dot2(e2m1x2_to_bf16x2<2>(ws[j]), xs[4 * j + 2], ac);
+            ac = dot2(e2m1x2_to_bf16x2<3>(ws[j]), xs[4 * j + 3], ac);
+          }
+          ac *= e4m3_to_f32(B.b[ub][r][c].x);   // the lane's chunk is one 16-block
+        }
+        a += ac;
+      }
+      a = wave_sum(a);
+      if (FMT != FMT_BF16) a *= B.rs[ub][r];
+      vals[r] = a;
+    }
+    epi(u, vals);
   }
-  __syncthreads();
-  for (int t = threadIdx.x; t < nrows; t += kThreads) {
-    float s = 0.f;
-    for (int c = 0; c < nch; ++c) s += part[t * nch + c];
-    if (FMT == FMT_FP8) s *= *reinterpret_cast<const float*>(p.w + m.scales + 4ull * (uint64_t)(r0 + t));
-    y[t] = s;
-  }
-  __syncthreads();
 }
 
-// A GEMV phase: prefetch the first batch of weights, wait for the input
-// vector, optionally RMSNorm it, and compute the workgroup's rows into y.
-template <uint32_t FMT>
-__device__ __forceinline__ bool gemv_phase_t(const Params& p, Smem& s, const Mat& m, int r0, int nrows,
-                             const uint64_t* src, int nwords, uint32_t tag, uint64_t norm_g,
-                             XrayClock& xc) {
-  Batch<FMT> B;
-  const int nch = ((int)m.K + 1023) >> 10;
-  if (nrows > 0) gemv_load<FMT>(p, m, r0, nrows * nch, nch, 0, B);
+// A GEMV phase: gains and the first weight batch are loaded before the wait
+// for the input vector; then the wave's units are computed in double-buffered
+// batches.  NORM: the input is the fp32 residual and is RMSNormed (gains
+// `gain`) and rounded to bf16; otherwise it is already bf16 pairs.
+template <uint32_t FMT, int NCH, int UR, int UB, bool NORM, class Epi>
+__device__ __forceinline__ bool gemv_phase(const Params& p, Smem& s, const GMat& g, int r0, int nunits,
+                                           MK_GLOBAL const uint64_t* src, int nwords, uint32_t tag,
+                                           MK_GLOBAL const uint32_t* gain, XrayClock& xc, Epi epi) {
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int nj = nunits > wave ? (nunits - wave + kWaves - 1) / kWaves : 0;  // units of this wave
+  uint32_t gn[NCH][8];
+  if (NORM) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int e0 = min(c * 1024 + 16 * lane, (int)g.K - 16);
+      MK_GLOBAL const v4u* gp = GCAST(const v4u, gain + e0 / 2);
+      const v4u g0 = gp[0], g1 = gp[1];
+      gn[c][0] = g0.x; gn[c][1] = g0.y; gn[c][2] = g0.z; gn[c][3] = g0.w;
+      gn[c][4] = g1.x; gn[c][5] = g1.y; gn[c][6] = g1.z; gn[c][7] = g1.w;
+    }
+  }
+  WBatch<FMT, NCH, UR, UB> B0, B1;
+  if (nj > 0) wload(g, r0, nunits, wave, 0, B0);
+  // Compiler memory barrier: keeps the loads above issued before the wait.
+  // Without it they may legally sink to their first use after the wait (the
+  // wait touches only LDS and atomics the weights cannot alias), and every
+  // phase would pay the weight latency after its input arrives.  It reads no
+  // register, so it adds no wait of its own.
+  asm volatile("" ::: "memory");
   XR_WAIT_BEGIN(xc);
   const bool ok = gather(src, nwords, tag, s.vin, p);
   if (__syncthreads_or(!ok)) return false;
   XR_WAIT_END(xc);
-  if (nrows <= 0) return true;
+  if (nj <= 0) return true;
   XR_ACTIVE(xc);
-  const uint32_t* act = s.vin;
-  if (norm_g) {
-    rmsnorm_to_act(p, s.vin, norm_g, (int)m.K, s.u.g.act, s.red);
-    __syncthreads();
-    act = s.u.g.act;
+  uint32_t xa[NCH][8];
+  if (NORM) {
+    float x[NCH][16];
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int e0 = c * 1024 + 16 * lane;
+      const bool in = e0 < (int)g.K;
+      const v4u* xp = reinterpret_cast<const v4u*>(s.vin + min(e0, (int)g.K - 16));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const v4u w = xp[q];
+        x[c][4 * q + 0] = in ? __uint_as_float(w.x) : 0.f;
+        x[c][4 * q + 1] = in ? __uint_as_float(w.y) : 0.f;
+        x[c][4 * q + 2] = in ? __uint_as_float(w.z) : 0.f;
+        x[c][4 * q + 3] = in ? __uint_as_float(w.w) : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ss = fmaf(x[c][i], x[c][i], ss);
+    }
+    const float r = 1.0f / sqrtf(wave_sum(ss) / (float)g.K + p.eps);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float lo = bf16_lo(gn[c][j]) * (x[c][2 * j] * r);
+        const float hi = bf16_hi(gn[c][j]) * (x[c][2 * j + 1] * r);
+        xa[c][j] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+      }
+  } else {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int e0 = c * 1024 + 16 * lane;
+      const bool in = e0 < (int)g.K;
+      const v4u* xp = reinterpret_cast<const v4u*>(s.vin + min(e0, (int)g.K - 16) / 2);
+      const v4u w0 = xp[0], w1 = xp[1];
+      xa[c][0] = in ? w0.x : 0u; xa[c][1] = in ? w0.y : 0u; xa[c][2] = in ? w0.z : 0u; xa[c][3] = in ? w0.w : 0u;
+      xa[c][4] = in ? w1.x : 0u; xa[c][5] = in ? w1.y : 0u; xa[c][6] = in ? w1.z : 0u; xa[c][7] = in ? w1.w : 0u;
+    }
   }
-  gemv_rows<FMT>(p, m, r0, nrows, B, act, s.u.g.part, s.u.g.y);
+  XR_MARK(xc, 0);
+  // the scheduling barriers keep each next batch's loads ahead of the current
+  // batch's arithmetic (under register pressure the scheduler would otherwise
+  // sink them and serialize the stream)
+  for (int jb = 0; jb < nj; jb += 2 * UB) {
+    if (jb + UB < nj) wload(g, r0, nunits, wave, jb + UB, B1);
+    __builtin_amdgcn_sched_barrier(0);
+    wcompute(B0, xa, nunits, wave, jb, epi);
+    if (jb + UB >= nj) break;
+    if (jb + 2 * UB < nj) wload(g, r0, nunits, wave, jb + 2 * UB, B0);
+    __builtin_amdgcn_sched_barrier(0);
+    wcompute(B1, xa, nunits, wave, jb + UB, epi);
+  }
+  XR_MARK(xc, 1);
   return true;
-}
-
-__device__ __forceinline__ bool gemv_phase(const Params& p, Smem& s, const Mat& m, int r0, int nrows, const uint64_t* src,
-                           int nwords, uint32_t tag, uint64_t norm_g, XrayClock& xc) {
-  if (m.fmt == FMT_FP8) return gemv_phase_t<FMT_FP8>(p, s, m, r0, nrows, src, nwords, tag, norm_g, xc);
-  if (m.fmt == FMT_FP4) return gemv_phase_t<FMT_FP4>(p, s, m, r0, nrows, src, nwords, tag, norm_g, xc);
-  return gemv_phase_t<FMT_BF16>(p, s, m, r0, nrows, src, nwords, tag, norm_g, xc);
 }
 
 // ------------------------------------------------------------- attention
@@ -296,226 +338,258 @@ __device__ __forceinline__ void att_split(const Params& p, int n, int& ns, int& 
   ns = (n + span - 1) / span;
 }
 
-// RMSNorm (gain g, head_dim hd) then RoPE at `pos` of one head vector held in
-// LDS, by one wave.  Rotate-half pairs (i, i + hd/2).
-__device__ __forceinline__ void head_norm_rope(const Params& p, float* v, uint64_t g_off, int pos) {
-  const int lane = threadIdx.x & 63, hd = p.hd;
-  float ss = 0.f;
-  for (int d = lane; d < hd; d += 64) ss = fmaf(v[d], v[d], ss);
-  ss = wave_sum(ss);
-  const float r = 1.0f / sqrtf(ss / (float)hd + p.eps);
-  const uint16_t* g = reinterpret_cast<const uint16_t*>(p.w + g_off);
-  const float* cs = p.rope + (size_t)pos * hd;  // [hd/2][2]
-  const int half = hd / 2;
-  for (int i = lane; i < half; i += 64) {
-    const float a = bf16_to_f32(g[i]) * (v[i] * r);
-    const float b = bf16_to_f32(g[i + half]) * (v[i + half] * r);
-    const float c = cs[2 * i], sn = cs[2 * i + 1];
-    v[i] = a * c - b * sn;
-    v[i + half] = b * c + a * sn;
-  }
-}
-
-// One unit = (KV head g, position split): scores of the group's q heads over
-// the split's positions with an online softmax, producing either the final
-// output (one split) or (max, sum, unnormalized output) for the merge.
-__device__ __forceinline__ bool attention_unit(const Params& p, Smem& s, int l, int g, int sidx, int ns, int span, int pos,
-                               uint32_t epoch) {
-  AttSmem& A = s.u.att;
-  const int hd = p.hd, gs = p.nq / p.nkv, nq = p.nq, nkv = p.nkv;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// One unit = (KV head g, position split [j0, j1)) on one workgroup.  Eight
+// threads share a position (HD/8 dims each); wave w takes positions
+// jb + 8w .. jb + 8w + 7 of every 64-position pass, so a wave reads eight
+// consecutive cache rows as one coalesced run.  The rows of positions before
+// `pos` are already in the cache, so the first pass is loaded before waiting
+// for this step's q/k/v and each later pass while the previous one is used.
+// Each wave norms and ropes q and k itself (in wave-private LDS) and keeps its
+// own online softmax over its positions; one barrier at the end merges the
+// eight waves.  The result is the final output (one split) or (max, sum,
+// unnormalized output) for the merge phase.
+template <int HD, int GS>
+__device__ __forceinline__ bool attention_unit_t(const Params& p, Smem& s, int l, int g, int sidx, int ns,
+                                                 int span, int pos, uint32_t epoch, XrayClock& xc) {
+  constexpr int TPP = 8;              // threads per position
+  constexpr int DPT = HD / TPP;       // dims per thread
+  constexpr int WPT = DPT / 2;        // bf16 pairs per thread
+  constexpr int PPP = kThreads / TPP; // positions per pass
+  constexpr int NOUT = GS * HD;       // outputs of the unit
+  static_assert(NOUT <= kMaxGroupDim && HD <= 128, "attention shape");
+  AttSmem& A = s.att;
+  const int nq = p.nq, nkv = p.nkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int pl = lane >> 3, c = lane & 7;
   const int j0 = sidx * span, j1 = min(j0 + span, pos + 1);
   const int par = l & 1;
-  const uint32_t tag_qkv = make_tag(epoch, 6 * l + 2);
-  const uint64_t* qkv = p.xch + p.x.qkv + (uint64_t)par * p.x.par_qkv +
-                        (uint64_t)(blockIdx.x % p.R) * p.x.rep_qkv;
-  bool ok = gather(qkv + (uint64_t)g * gs * hd, gs * hd, tag_qkv, reinterpret_cast<uint32_t*>(A.q), p);
-  ok = ok && gather(qkv + (uint64_t)(nq + g) * hd, hd, tag_qkv, reinterpret_cast<uint32_t*>(A.k), p);
-  ok = ok && gather(qkv + (uint64_t)(nq + nkv + g) * hd, hd, tag_qkv, reinterpret_cast<uint32_t*>(A.v), p);
-  if (__syncthreads_or(!ok)) return false;
+  const size_t plane = (size_t)p.max_ctx * HD;
+  MK_GLOBAL uint32_t* kc = GCAST(uint32_t, p.kv + ((size_t)(l * 2 + 0) * nkv + g) * plane);
+  MK_GLOBAL uint32_t* vc = GCAST(uint32_t, p.kv + ((size_t)(l * 2 + 1) * nkv + g) * plane);
 
+  uint32_t kr[WPT], vr[WPT], kn[WPT], vn[WPT];
+  // Clamped loads (no guarded loads); positions past the split, and `pos`
+  // itself (not yet in the cache: substituted later), become exact zeros so
+  // they add nothing, whatever the cache memory held.
+  auto load_kv = [&](int jb, uint32_t* kk, uint32_t* vv) {
+    const int jr = jb + wave * 8 + pl;
+    const int j = min(jr, j1 - 1);
+    const bool use = jr < j1 && jr != pos;
+    MK_GLOBAL const v4u* kp = GCAST(const v4u, kc + (size_t)j * (HD / 2) + c * WPT);
+    MK_GLOBAL const v4u* vp = GCAST(const v4u, vc + (size_t)j * (HD / 2) + c * WPT);
+#pragma unroll
+    for (int w = 0; w < WPT / 4; ++w) {
+      const v4u a = kp[w], b = vp[w];
+      kk[4 * w] = use ? a.x : 0u; kk[4 * w + 1] = use ? a.y : 0u;
+      kk[4 * w + 2] = use ? a.z : 0u; kk[4 * w + 3] = use ? a.w : 0u;
+      vv[4 * w] = use ? b.x : 0u; vv[4 * w + 1] = use ? b.y : 0u;
+      vv[4 * w + 2] = use ? b.z : 0u; vv[4 * w + 3] = use ? b.w : 0u;
+    }
+  };
+  load_kv(j0, kr, vr);
+  // q/k-norm gains and this position's RoPE pair (lane i < HD/2 owns pair i)
   const Layer& L0 = p.layer0;
   const uint64_t loff = (uint64_t)l * p.layer_stride;
-  if (wave < gs) head_norm_rope(p, A.q + wave * hd, L0.q_norm + loff, pos);
-  else if (wave == gs) head_norm_rope(p, A.k, L0.k_norm + loff, pos);
-  __syncthreads();
-  for (int t = threadIdx.x; t < hd / 2; t += kThreads) {
-    A.kb[t] = f32_to_bf16(A.k[2 * t]) | (f32_to_bf16(A.k[2 * t + 1]) << 16);
-    A.vb[t] = f32_to_bf16(A.v[2 * t]) | (f32_to_bf16(A.v[2 * t + 1]) << 16);
-  }
-  __syncthreads();
-  const size_t plane = (size_t)p.max_ctx * hd;  // bf16 elements per (layer, k|v, head)
-  uint32_t* kc = reinterpret_cast<uint32_t*>(p.kv + ((size_t)(l * 2 + 0) * nkv + g) * plane);
-  uint32_t* vc = reinterpret_cast<uint32_t*>(p.kv + ((size_t)(l * 2 + 1) * nkv + g) * plane);
-  if (j0 <= pos && pos < j1) {
-    for (int t = threadIdx.x; t < hd / 2; t += kThreads) {
-      kc[(size_t)pos * (hd / 2) + t] = A.kb[t];
-      vc[(size_t)pos * (hd / 2) + t] = A.vb[t];
-    }
-  }
-  // bf16 k/v of this position, as the cache holds them
-  for (int t = threadIdx.x; t < hd / 2; t += kThreads) {
-    A.k[2 * t] = bf16_lo(A.kb[t]);
-    A.k[2 * t + 1] = bf16_hi(A.kb[t]);
-    A.v[2 * t] = bf16_lo(A.vb[t]);
-    A.v[2 * t + 1] = bf16_hi(A.vb[t]);
-  }
-  if (threadIdx.x < kMaxGroup) {
-    A.m[threadIdx.x] = -INFINITY;
-    A.l[threadIdx.x] = 0.f;
-  }
-  const int dpl = hd / 64;  // dims per lane in the PV product (1, 2 or 4)
-  float o[kMaxGroup][4];
-#pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) o[h][k] = 0.f;
-  const float rs = sqrtf((float)hd);
-  __syncthreads();
+  const int li = min(lane, HD / 2 - 1);
+  MK_GLOBAL const uint16_t* gq = GCAST(const uint16_t, p.w + L0.q_norm + loff);
+  MK_GLOBAL const uint16_t* gk = GCAST(const uint16_t, p.w + L0.k_norm + loff);
+  const float gq_lo = bf16_to_f32(gq[li]), gq_hi = bf16_to_f32(gq[li + HD / 2]);
+  const float gk_lo = bf16_to_f32(gk[li]), gk_hi = bf16_to_f32(gk[li + HD / 2]);
+  MK_GLOBAL const float* cs = p.rope + ((size_t)pos * (HD / 2) + li) * 2;
+  const float rc = cs[0], rsn = cs[1];
+  asm volatile("" ::: "memory");  // keep the K/V, gain and RoPE loads ahead of the wait
 
-  for (int jb = j0; jb < j1; jb += kAttBlock) {
-    const int nb = min(kAttBlock, j1 - jb);
-    // scores: one position per thread
-    if ((int)threadIdx.x < nb) {
-      const int j = jb + threadIdx.x;
-      float dot[kMaxGroup] = {0.f, 0.f, 0.f, 0.f};
-      if (j == pos) {
-        for (int d = 0; d < hd; ++d) {
+  // this step's q, k, v of the group, in one gather
+  const uint32_t tag_qkv = make_tag(epoch, 6 * l + 2);
+  MK_GLOBAL const uint64_t* qkv = p.xch + p.x.qkv + (uint64_t)par * p.x.par_qkv + (uint64_t)(blockIdx.x % p.R) * p.x.rep_qkv;
+  const int qo = g * NOUT, ko = (nq + g) * HD, vo = (nq + nkv + g) * HD;
+  XR_WAIT_BEGIN(xc);
+  const bool ok = gather_map(qkv, NOUT + 2 * HD, tag_qkv, reinterpret_cast<uint32_t*>(A.raw), p,
+                             [=](int i) { return i < NOUT ? qo + i : (i < NOUT + HD ? ko + i - NOUT : vo + i - NOUT - HD); });
+  if (__syncthreads_or(!ok)) return false;
+  XR_WAIT_END(xc);
+
+  // every wave: RMSNorm + RoPE of the q heads and k (lane i < HD/2: pair i)
+  const bool pair_lane = lane < HD / 2;
+  float* qw = A.qw[wave];
+  uint32_t* kvw = A.kvw[wave];
 #pragma unroll
-          for (int h = 0; h < kMaxGroup; ++h)
-            if (h < gs) dot[h] = fmaf(A.q[h * hd + d], A.k[d], dot[h]);
-        }
-      } else {
-        const v4u* kr = reinterpret_cast<const v4u*>(kc + (size_t)j * (hd / 2));
-        for (int c = 0; c < hd / 8; ++c) {
-          const v4u w = kr[c];
-          const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int d = c * 8 + 2 * e;
-            const float k0 = bf16_lo(ws[e]), k1 = bf16_hi(ws[e]);
-#pragma unroll
-            for (int h = 0; h < kMaxGroup; ++h) {
-              if (h < gs) {
-                dot[h] = fmaf(A.q[h * hd + d], k0, dot[h]);
-                dot[h] = fmaf(A.q[h * hd + d + 1], k1, dot[h]);
-              }
-            }
-          }
-        }
+  for (int h = 0; h <= GS; ++h) {
+    const float* src = A.raw + h * HD;
+    const float xa = pair_lane ? src[li] : 0.f, xb = pair_lane ? src[li + HD / 2] : 0.f;
+    const float r = 1.0f / sqrtf(wave_sum(xa * xa + xb * xb) / (float)HD + p.eps);
+    const float glo = h < GS ? gq_lo : gk_lo, ghi = h < GS ? gq_hi : gk_hi;
+    const float a = glo * (xa * r), b = ghi * (xb * r);
+    const float ra = a * rc - b * rsn, rb = b * rc + a * rsn;
+    if (h < GS) {
+      if (pair_lane) {
+        qw[h * HD + li] = ra;
+        qw[h * HD + li + HD / 2] = rb;
       }
-#pragma unroll
-      for (int h = 0; h < kMaxGroup; ++h)
-        if (h < gs) A.pr[h][threadIdx.x] = dot[h] / rs;
+    } else if (pair_lane) {
+      // bf16 k as the cache holds it: pairs (2t, 2t+1) are packed below
+      A.prow[wave][0][li] = ra;
+      A.prow[wave][0][li + HD / 2] = rb;
     }
-    __syncthreads();
-    // block max and new running max, one wave per head
-    if (wave < gs) {
-      float mx = -INFINITY;
-      for (int t = lane; t < nb; t += 64) mx = fmaxf(mx, A.pr[wave][t]);
-      mx = wave_max(mx);
-      if (lane == 0) {
-        const float mn = fmaxf(A.m[wave], mx);
-        A.sc[wave] = expf(A.m[wave] - mn);
-        A.m[wave] = mn;
-      }
-    }
-    __syncthreads();
-    if ((int)threadIdx.x < nb)
-      for (int h = 0; h < gs; ++h) A.pr[h][threadIdx.x] = expf(A.pr[h][threadIdx.x] - A.m[h]);
-    __syncthreads();
-    if (wave < gs) {
-      float sm = 0.f;
-      for (int t = lane; t < nb; t += 64) sm += A.pr[wave][t];
-      sm = wave_sum(sm);
-      if (lane == 0) A.l[wave] = A.l[wave] * A.sc[wave] + sm;
-    }
-    // PV: wave w takes positions w, w+8, ...; lane owns dims [lane*dpl, +dpl)
-#pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h) {
-      const float scl = h < gs ? A.sc[h] : 0.f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) o[h][k] *= scl;
-    }
-    for (int t = wave; t < nb; t += kWaves) {
-      const int j = jb + t;
-      float vv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (j == pos) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          if (k < dpl) vv[k] = A.v[lane * dpl + k];
-      } else {
-        const uint16_t* vr = reinterpret_cast<const uint16_t*>(vc) + (size_t)j * hd + lane * dpl;
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          if (k < dpl) vv[k] = bf16_to_f32(vr[k]);
-      }
-#pragma unroll
-      for (int h = 0; h < kMaxGroup; ++h) {
-        if (h < gs) {
-          const float pj = A.pr[h][t];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) o[h][k] = fmaf(pj, vv[k], o[h][k]);
-        }
-      }
-    }
-    __syncthreads();
   }
+  __builtin_amdgcn_wave_barrier();
+  if (lane < HD / 2) {
+    const float* kf = A.prow[wave][0];
+    kvw[lane] = f32_to_bf16(kf[2 * lane]) | (f32_to_bf16(kf[2 * lane + 1]) << 16);
+    const float* vf = A.raw + (GS + 1) * HD;
+    kvw[HD / 2 + lane] = f32_to_bf16(vf[2 * lane]) | (f32_to_bf16(vf[2 * lane + 1]) << 16);
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (wave == 0 && j0 <= pos && pos < j1 && lane < HD / 2) {
+    kc[(size_t)pos * (HD / 2) + lane] = kvw[lane];
+    vc[(size_t)pos * (HD / 2) + lane] = kvw[HD / 2 + lane];
+  }
+  // q pre-scaled by log2(e)/sqrt(HD): scores come out in log2 units, so every
+  // exponential below is one v_exp_f32 (exp2); the unit's max is kept in the
+  // same units for the merge
+  const float kq = 1.4426950408889634f / sqrtf((float)HD);
+  float qr[GS][DPT];
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h)
+  for (int h = 0; h < GS; ++h)
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (h < gs && k < dpl) A.o[wave][h * hd + lane * dpl + k] = o[h][k];
+    for (int e = 0; e < DPT; ++e) qr[h][e] = qw[h * HD + c * DPT + e] * kq;
+  XR_MARK(xc, 0);
+
+  float acc[GS][DPT];
+  float mrun[GS], lrun[GS];
+#pragma unroll
+  for (int h = 0; h < GS; ++h) {
+    mrun[h] = -INFINITY;
+    lrun[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) acc[h][e] = 0.f;
+  }
+  for (int jb = j0; jb < j1; jb += PPP) {
+    const bool more = jb + PPP < j1;
+    if (more) load_kv(jb + PPP, kn, vn);
+    const int j = jb + wave * 8 + pl;
+    const bool act = j < j1;
+    if (act && j == pos) {
+#pragma unroll
+      for (int w = 0; w < WPT; ++w) {
+        kr[w] = kvw[c * WPT + w];
+        vr[w] = kvw[HD / 2 + c * WPT + w];
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < GS; ++h) {
+      float d = 0.f;
+#pragma unroll
+      for (int w = 0; w < WPT; ++w) {
+        d = fmaf(qr[h][2 * w], bf16_lo(kr[w]), d);
+        d = fmaf(qr[h][2 * w + 1], bf16_hi(kr[w]), d);
+      }
+      const float sc = act ? sum8(d) : -INFINITY;
+      const float mn = fmaxf(mrun[h], wave_max(sc));
+      if (mn == -INFINITY) continue;   // no position of this wave yet (uniform)
+      const float scale = __builtin_amdgcn_exp2f(mrun[h] - mn);
+      const float pr = act ? __builtin_amdgcn_exp2f(sc - mn) : 0.f;
+      mrun[h] = mn;
+      lrun[h] = lrun[h] * scale + wave_sum(c == 0 ? pr : 0.f);
+#pragma unroll
+      for (int w = 0; w < WPT; ++w) {
+        acc[h][2 * w] = fmaf(pr, bf16_lo(vr[w]), acc[h][2 * w] * scale);
+        acc[h][2 * w + 1] = fmaf(pr, bf16_hi(vr[w]), acc[h][2 * w + 1] * scale);
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int w = 0; w < WPT; ++w) {
+        kr[w] = kn[w];
+        vr[w] = vn[w];
+      }
+    }
+  }
+  // this wave's output: sum over its 8 positions (lanes with the same c):
+  // the two 8-lane halves of each 16-lane row with one DPP step, then the
+  // four rows through wave-private LDS
+#pragma unroll
+  for (int h = 0; h < GS; ++h)
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) acc[h][e] += dpp<0x128>(acc[h][e]);
+  if ((lane & 8) == 0) {
+#pragma unroll
+    for (int h = 0; h < GS; ++h)
+#pragma unroll
+      for (int e = 0; e < DPT; ++e) A.prow[wave][lane >> 4][h * HD + c * DPT + e] = acc[h][e];
+  }
+  __builtin_amdgcn_wave_barrier();
+  for (int t = lane; t < NOUT; t += 64)
+    A.wo[wave][t] = (A.prow[wave][0][t] + A.prow[wave][1][t]) + (A.prow[wave][2][t] + A.prow[wave][3][t]);
+  if (lane < GS) {
+    float mh = mrun[0], lh = lrun[0];
+#pragma unroll
+    for (int h = 1; h < GS; ++h)
+      if (lane == h) {
+        mh = mrun[h];
+        lh = lrun[h];
+      }
+    A.wm[wave][lane] = mh;
+    A.wl[wave][lane] = lh;
+  }
+  XR_MARK(xc, 1);
   __syncthreads();
-  // combine waves in a fixed order
-  for (int t = threadIdx.x; t < gs * hd; t += kThreads) {
-    float acc = 0.f;
-    for (int w = 0; w < kWaves; ++w) acc += A.o[w][t];
-    A.o[0][t] = acc;
-  }
-  __syncthreads();
-  if (ns == 1) {
-    const uint32_t tag = make_tag(epoch, 6 * l + 3);
-    uint64_t* ob = p.xch + p.x.o + (uint64_t)par * p.x.par_o;
-    for (int t = threadIdx.x; t < gs * hd / 2; t += kThreads) {
-      const int h = (2 * t) / hd;
-      const float inv = 1.0f / A.l[h];
-      const uint32_t w = f32_to_bf16(A.o[0][2 * t] * inv) | (f32_to_bf16(A.o[0][2 * t + 1] * inv) << 16);
-      publish(ob, p.x.rep_o, p.R, g * gs * hd / 2 + t, w, tag);
+  // merge the eight waves (fixed order)
+  const uint32_t tag = make_tag(epoch, 6 * l + 3);
+  for (int t = tid; t < NOUT; t += kThreads) {
+    const int h = t / HD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, A.wm[w][h]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float e = A.wm[w][h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(A.wm[w][h] - M);
+      L = fmaf(A.wl[w][h], e, L);
+      O = fmaf(A.wo[w][t], e, O);
     }
-  } else {
-    const uint32_t tag = make_tag(epoch, 6 * l + 3);
-    uint64_t* pb = p.xch + p.x.part + (uint64_t)par * p.x.par_part;
-    for (int t = threadIdx.x; t < gs * (hd + 2); t += kThreads) {
-      const int h = t / (hd + 2), k = t - h * (hd + 2);
-      const float v = k == 0 ? A.m[h] : (k == 1 ? A.l[h] : A.o[0][h * hd + k - 2]);
-      const uint64_t idx = ((uint64_t)(g * gs + h) * p.ns_max + sidx) * (hd + 2) + k;
-      st_word(pb + idx, ((uint64_t)__float_as_uint(v) << 32) | tag);
+    if (ns == 1) {
+      // final output: pairs of consecutive dims form one bf16-pair word
+      const float o = O / L;
+      const float o1 = __shfl_xor(o, 1);
+      if ((t & 1) == 0) {
+        MK_GLOBAL uint64_t* ob = p.xch + p.x.o + (uint64_t)par * p.x.par_o;
+        publish(ob, p.x.rep_o, p.R, (g * NOUT + t) / 2, f32_to_bf16(o) | (f32_to_bf16(o1) << 16), tag);
+      }
+    } else {
+      MK_GLOBAL uint64_t* pb = p.xch + p.x.part + (uint64_t)par * p.x.par_part;
+      const uint64_t base = ((uint64_t)(g * GS + h) * p.ns_max + sidx) * (HD + 2);
+      st_word(pb + base + 2 + (t - h * HD), ((uint64_t)__float_as_uint(O) << 32) | tag);
+      if (t - h * HD == 0) {
+        st_word(pb + base, ((uint64_t)__float_as_uint(M) << 32) | tag);
+        st_word(pb + base + 1, ((uint64_t)__float_as_uint(L) << 32) | tag);
+      }
     }
   }
+  XR_MARK(xc, 2);
   return true;
 }
 
-// Merge the splits of q head h: M = max m_s, L = sum l_s e^(m_s-M),
-// o = sum o_s e^(m_s-M) / L.
+// Merge the splits of q head h (maxima in log2 units): M = max m_s,
+// L = sum l_s 2^(m_s-M), o = sum o_s 2^(m_s-M) / L.
 __device__ __forceinline__ bool merge_unit(const Params& p, Smem& s, int l, int h, int ns, uint32_t epoch) {
   const int hd = p.hd, par = l & 1;
   const uint32_t tag = make_tag(epoch, 6 * l + 3);
-  const uint64_t* pb = p.xch + p.x.part + (uint64_t)par * p.x.par_part + (uint64_t)h * p.ns_max * (hd + 2);
+  MK_GLOBAL const uint64_t* pb = p.xch + p.x.part + (uint64_t)par * p.x.par_part + (uint64_t)h * p.ns_max * (hd + 2);
   const bool ok = gather(pb, ns * (hd + 2), tag, s.vin, p);
   if (__syncthreads_or(!ok)) return false;
   float M = -INFINITY;
   for (int k = 0; k < ns; ++k) M = fmaxf(M, __uint_as_float(s.vin[k * (hd + 2)]));
   float L = 0.f;
   for (int k = 0; k < ns; ++k)
-    L += __uint_as_float(s.vin[k * (hd + 2) + 1]) * expf(__uint_as_float(s.vin[k * (hd + 2)]) - M);
+    L += __uint_as_float(s.vin[k * (hd + 2) + 1]) * __builtin_amdgcn_exp2f(__uint_as_float(s.vin[k * (hd + 2)]) - M);
   const float inv = 1.0f / L;
   const uint32_t tag_o = make_tag(epoch, 6 * l + 4);
-  uint64_t* ob = p.xch + p.x.o + (uint64_t)par * p.x.par_o;
+  MK_GLOBAL uint64_t* ob = p.xch + p.x.o + (uint64_t)par * p.x.par_o;
   for (int t = threadIdx.x; t < hd / 2; t += kThreads) {
     float a = 0.f, b = 0.f;
     for (int k = 0; k < ns; ++k) {
-      const float e = expf(__uint_as_float(s.vin[k * (hd + 2)]) - M);
+      const float e = __builtin_amdgcn_exp2f(__uint_as_float(s.vin[k * (hd + 2)]) - M);
       a = fmaf(__uint_as_float(s.vin[k * (hd + 2) + 2 + 2 * t]), e, a);
       b = fmaf(__uint_as_float(s.vin[k * (hd + 2) + 3 + 2 * t]), e, b);
     }
@@ -526,12 +600,21 @@ __device__ __forceinline__ bool merge_unit(const Params& p, Smem& s, int l, int 
 }
 
 // ----------------------------------------------------------------- kernel
+// One instantiation per (weight format, head_dim, q heads per KV head,
+// 1024-chunks of hidden, of n_q_heads*head_dim and of intermediate): the
+// formats, the attention shape and every per-lane register array size are
+// compile-time constants.
+template <int WF, int HD, int GS, int NH, int NQ, int NI>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const Params* __restrict__ pp,
                                                               const int32_t* d_token, int pos, uint32_t epoch,
                                                               int32_t* d_next, float* d_logits) {
   __shared__ Smem s;
   const Params& p = *pp;
+  MK_GLOBAL const uint8_t* const W = p.w;  // held in registers for the whole step
+  constexpr uint32_t F_LIN = WF == 0 ? FMT_BF16 : (WF == 1 ? FMT_FP8 : FMT_FP4);  // q, k, v, o, gate, up
+  constexpr uint32_t F_8 = WF == 0 ? FMT_BF16 : FMT_FP8;                          // down, embed / LM head
   const int G = p.grid, wg = blockIdx.x;
+  const int lane = threadIdx.x & 63;
   XrayClock xc;
   const int token = __hip_atomic_load(const_cast<int32_t*>(d_token), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (token < 0 || token >= p.V) {
@@ -542,26 +625,29 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const Params* __res
     return;
   }
   if (wg == 0 && threadIdx.x == 0) *d_next = -1;  // overwritten on success
-  const int H = p.H, hd = p.hd;
+  const int H = p.H, hd = p.hd, R = p.R;
   const int nqkv = (p.nq + 2 * p.nkv) * hd;
   int oa, ob;
   split_range(H, G, wg, oa, ob);
   const int nown = ob - oa;
-  const int rep = wg % p.R;
+  const int rep = wg % R;
+  // publish by lanes 0..R-1, one replica each
+  auto put = [&](MK_GLOBAL uint64_t* base, uint64_t rep_stride, int i, uint32_t payload, uint32_t tag) {
+    if (lane < R) st_word(base + (uint64_t)lane * rep_stride + i, ((uint64_t)payload << 32) | tag);
+  };
 
   // ---- embedding: this workgroup's residual rows
   XR_BEGIN(xc);
   {
     const uint32_t tag = make_tag(epoch, 1);
-    uint64_t* xd = p.xch + p.x.x_d + 1 * p.x.par_x;  // parity of layer -1
+    MK_GLOBAL uint64_t* xd = p.xch + p.x.x_d + 1 * p.x.par_x;  // parity of layer -1
     for (int i = threadIdx.x; i < nown; i += kThreads) {
       const uint64_t e = (uint64_t)token * H + oa + i;
       float v;
-      if (p.embed.fmt == FMT_BF16) v = bf16_to_f32(reinterpret_cast<const uint16_t*>(p.w + p.embed.codes)[e]);
-      else v = e4m3_to_f32(p.w[p.embed.codes + e]) *
-               reinterpret_cast<const float*>(p.w + p.embed.scales)[token];
+      if (F_8 == FMT_BF16) v = bf16_to_f32(GCAST(const uint16_t, W + p.embed.codes)[e]);
+      else v = e4m3_to_f32(W[p.embed.codes + e]) * GCAST(const float, W + p.embed.scales)[token];
       s.x_own[i] = v;
-      publish(xd, p.x.rep_x, p.R, oa + i, __float_as_uint(v), tag);
+      publish(xd, p.x.rep_x, R, oa + i, __float_as_uint(v), tag);
     }
   }
   XR_END(xc, p, 1);
@@ -576,15 +662,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const Params* __res
     // ---- QKV
     {
       XR_BEGIN(xc);
-      const Mat m = at_layer(L0.qkv, loff);
       int ra, rb;
       split_range(nqkv, G, wg, ra, rb);
-      const uint64_t* src = p.xch + p.x.x_d + (uint64_t)((l + 1) & 1) * p.x.par_x + (uint64_t)rep * p.x.rep_x;
-      if (!gemv_phase(p, s, m, ra, rb - ra, src, H, make_tag(epoch, 6 * l + 1), L0.in_norm + loff, xc)) return;
+      MK_GLOBAL const uint64_t* src = p.xch + p.x.x_d + (uint64_t)((l + 1) & 1) * p.x.par_x + (uint64_t)rep * p.x.rep_x;
+      MK_GLOBAL uint64_t* dst = p.xch + p.x.qkv + (uint64_t)par * p.x.par_qkv;
       const uint32_t tag = make_tag(epoch, 6 * l + 2);
-      uint64_t* dst = p.xch + p.x.qkv + (uint64_t)par * p.x.par_qkv;
-      for (int t = threadIdx.x; t < rb - ra; t += kThreads)
-        publish(dst, p.x.rep_qkv, p.R, ra + t, __float_as_uint(s.u.g.y[t]), tag);
+      auto epi = [&](int u, const float* v) { put(dst, p.x.rep_qkv, ra + u, __float_as_uint(v[0]), tag); };
+      if (!gemv_phase<F_LIN, NH, 1, 2, true>(p, s, gmat(W, L0.qkv, loff), ra, rb - ra, src, H,
+                                            make_tag(epoch, 6 * l + 1), GCAST(const uint32_t, W + L0.in_norm + loff),
+                                            xc, epi))
+        return;
+      XR_MARK(xc, 3);
       XR_END(xc, p, 6 * l + 2);
     }
     // ---- attention
@@ -592,7 +680,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const Params* __res
       XR_BEGIN(xc);
       for (int u = wg; u < p.nkv * ns; u += G) {
         XR_ACTIVE(xc);
-        if (!attention_unit(p, s, l, u / ns, u % ns, ns, span, pos, epoch)) return;
+        if (!attention_unit_t<HD, GS>(p, s, l, u / ns, u % ns, ns, span, pos, epoch, xc)) return;
         __syncthreads();
       }
       XR_END(xc, p, 6 * l + 3);
@@ -612,49 +700,55 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const Params* __res
     // ---- O-projection + residual
     {
       XR_BEGIN(xc);
-      const Mat m = at_layer(L0.o, loff);
-      const uint64_t* src = p.xch + p.x.o + (uint64_t)par * p.x.par_o + (uint64_t)rep * p.x.rep_o;
-      const uint32_t tag_in = make_tag(epoch, ns > 1 ? 6 * l + 4 : 6 * l + 3);
-      if (!gemv_phase(p, s, m, oa, nown, src, p.nq * hd / 2, tag_in, 0, xc)) return;
+      MK_GLOBAL const uint64_t* src = p.xch + p.x.o + (uint64_t)par * p.x.par_o + (uint64_t)rep * p.x.rep_o;
+      MK_GLOBAL uint64_t* dst = p.xch + p.x.x_o + (uint64_t)par * p.x.par_x;
       const uint32_t tag = make_tag(epoch, 6 * l + 5);
-      uint64_t* dst = p.xch + p.x.x_o + (uint64_t)par * p.x.par_x;
-      for (int t = threadIdx.x; t < nown; t += kThreads) {
-        s.x_own[t] += s.u.g.y[t];
-        publish(dst, p.x.rep_x, p.R, oa + t, __float_as_uint(s.x_own[t]), tag);
-      }
+      auto epi = [&](int u, const float* v) {
+        const float x = s.x_own[u] + v[0];
+        s.x_own[u] = x;  // this row belongs to this wave only
+        put(dst, p.x.rep_x, oa + u, __float_as_uint(x), tag);
+      };
+      if (!gemv_phase<F_LIN, NQ, 1, 1, false>(p, s, gmat(W, L0.o, loff), oa, nown, src, p.nq * hd / 2,
+                                             make_tag(epoch, ns > 1 ? 6 * l + 4 : 6 * l + 3), nullptr, xc, epi))
+        return;
+      XR_MARK(xc, 3);
       XR_END(xc, p, 6 * l + 5);
     }
-    // ---- gate/up + SwiGLU
+    // ---- gate/up + SwiGLU: a unit is the four rows behind one output word
     {
       XR_BEGIN(xc);
-      const Mat m = at_layer(L0.gu, loff);
       int pa, pb;
       split_range(p.I / 2, G, wg, pa, pb);
-      const uint64_t* src = p.xch + p.x.x_o + (uint64_t)par * p.x.par_x + (uint64_t)rep * p.x.rep_x;
-      if (!gemv_phase(p, s, m, 4 * pa, 4 * (pb - pa), src, H, make_tag(epoch, 6 * l + 5), L0.post_norm + loff, xc))
-        return;
+      MK_GLOBAL const uint64_t* src = p.xch + p.x.x_o + (uint64_t)par * p.x.par_x + (uint64_t)rep * p.x.rep_x;
+      MK_GLOBAL uint64_t* dst = p.xch + p.x.h + (uint64_t)par * p.x.par_h;
       const uint32_t tag = make_tag(epoch, 6 * l + 6);
-      uint64_t* dst = p.xch + p.x.h + (uint64_t)par * p.x.par_h;
-      for (int t = threadIdx.x; t < pb - pa; t += kThreads) {
-        const float* y = s.u.g.y + 4 * t;
+      auto epi = [&](int u, const float* y) {
         const float h0 = (y[0] / (1.0f + expf(-y[0]))) * y[1];
         const float h1 = (y[2] / (1.0f + expf(-y[2]))) * y[3];
-        publish(dst, p.x.rep_h, p.R, pa + t, f32_to_bf16(h0) | (f32_to_bf16(h1) << 16), tag);
-      }
+        put(dst, p.x.rep_h, pa + u, f32_to_bf16(h0) | (f32_to_bf16(h1) << 16), tag);
+      };
+      if (!gemv_phase<F_LIN, NH, 4, 1, true>(p, s, gmat(W, L0.gu, loff), 4 * pa, pb - pa, src, H,
+                                            make_tag(epoch, 6 * l + 5), GCAST(const uint32_t, W + L0.post_norm + loff),
+                                            xc, epi))
+        return;
+      XR_MARK(xc, 3);
       XR_END(xc, p, 6 * l + 6);
     }
     // ---- down + residual
     {
       XR_BEGIN(xc);
-      const Mat m = at_layer(L0.down, loff);
-      const uint64_t* src = p.xch + p.x.h + (uint64_t)par * p.x.par_h + (uint64_t)rep * p.x.rep_h;
-      if (!gemv_phase(p, s, m, oa, nown, src, p.I / 2, make_tag(epoch, 6 * l + 6), 0, xc)) return;
+      MK_GLOBAL const uint64_t* src = p.xch + p.x.h + (uint64_t)par * p.x.par_h + (uint64_t)rep * p.x.rep_h;
+      MK_GLOBAL uint64_t* dst = p.xch + p.x.x_d + (uint64_t)par * p.x.par_x;
       const uint32_t tag = make_tag(epoch, 6 * l + 7);
-      uint64_t* dst = p.xch + p.x.x_d + (uint64_t)par * p.x.par_x;
-      for (int t = threadIdx.x; t < nown; t += kThreads) {
-        s.x_own[t] += s.u.g.y[t];
-        publish(dst, p.x.rep_x, p.R, oa + t, __float_as_uint(s.x_own[t]), tag);
-      }
+      auto epi = [&](int u, const float* v) {
+        const float x = s.x_own[u] + v[0];
+        s.x_own[u] = x;
+        put(dst, p.x.rep_x, oa + u, __float_as_uint(x), tag);
+      };
+      if (!gemv_phase<F_8, NI, 1, 1, false>(p, s, gmat(W, L0.down, loff), oa, nown, src, p.I / 2,
+                                           make_tag(epoch, 6 * l + 6), nullptr, xc, epi))
+        return;
+      XR_MARK(xc, 3);
       XR_END(xc, p, 6 * l + 7);
     }
   }
@@ -665,41 +759,37 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const Params* __res
     XR_BEGIN(xc);
     int va, vb;
     split_range(p.V, G, wg, va, vb);
-    const uint64_t* src = p.xch + p.x.x_d + (uint64_t)((p.L - 1) & 1) * p.x.par_x + (uint64_t)rep * p.x.rep_x;
-    if (!gemv_phase(p, s, p.embed, va, vb - va, src, H, make_tag(epoch, 6 * p.L + 1), p.final_norm, xc)) return;
+    MK_GLOBAL const uint64_t* src = p.xch + p.x.x_d + (uint64_t)((p.L - 1) & 1) * p.x.par_x + (uint64_t)rep * p.x.rep_x;
     float best = -INFINITY;
     int bidx = 0x7FFFFFFF;
-    for (int t = threadIdx.x; t < vb - va; t += kThreads) {
-      const float v = s.u.g.y[t];
-      if (d_logits) d_logits[va + t] = v;
-      if (v > best) {  // rows ascend within a thread, so the first maximum is kept
-        best = v;
-        bidx = va + t;
+    auto epi = [&](int u, const float* v) {
+      if (d_logits && lane == 0) d_logits[va + u] = v[0];
+      if (v[0] > best) {  // a wave's rows ascend, so the first maximum is kept
+        best = v[0];
+        bidx = va + u;
       }
-    }
+    };
+    constexpr int UBH = F_8 == FMT_BF16 ? 4 : 8;
+    if (!gemv_phase<F_8, NH, 1, UBH, true>(p, s, gmat(W, p.embed, 0), va, vb - va, src, H,
+                                          make_tag(epoch, 6 * p.L + 1), GCAST(const uint32_t, W + p.final_norm), xc,
+                                          epi))
+      return;
     // workgroup argmax: largest value, then smallest index
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(best, o);
-      const int oi = __shfl_xor(bidx, o);
-      if (ov > best || (ov == best && oi < bidx)) {
-        best = ov;
-        bidx = oi;
-      }
-    }
-    if ((threadIdx.x & 63) == 0) {
-      s.red[threadIdx.x >> 6] = best;
-      s.redi[threadIdx.x >> 6] = bidx;
+    if (lane == 0) {
+      s.red[wave_id()] = best;
+      s.redi[wave_id()] = bidx;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
+      best = s.red[0];
+      bidx = s.redi[0];
       for (int w = 1; w < kWaves; ++w)
         if (s.red[w] > best || (s.red[w] == best && s.redi[w] < bidx)) {
           best = s.red[w];
           bidx = s.redi[w];
         }
       const uint32_t tag = make_tag(epoch, ph_head);
-      uint64_t* a = p.xch + p.x.arg + 2ull * wg;
+      MK_GLOBAL uint64_t* a = p.xch + p.x.arg + 2ull * wg;
       st_word(a, ((uint64_t)__float_as_uint(best) << 32) | tag);
       st_word(a + 1, ((uint64_t)(uint32_t)bidx << 32) | tag);
     }
@@ -713,37 +803,24 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const Params* __res
     const bool ok = gather(p.xch + p.x.arg, 2 * G, make_tag(epoch, ph_head), s.vin, p);
     if (__syncthreads_or(!ok)) return;
     XR_WAIT_END(xc);
-    float best = -INFINITY;
-    int bidx = 0x7FFFFFFF;
-    for (int t = threadIdx.x; t < G; t += kThreads) {
-      const float v = __uint_as_float(s.vin[2 * t]);
-      const int i = (int)s.vin[2 * t + 1];
-      if (v > best || (v == best && i < bidx)) {
-        best = v;
-        bidx = i;
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(best, o);
-      const int oi = __shfl_xor(bidx, o);
-      if (ov > best || (ov == best && oi < bidx)) {
-        best = ov;
-        bidx = oi;
-      }
-    }
-    if ((threadIdx.x & 63) == 0) {
-      s.red[threadIdx.x >> 6] = best;
-      s.redi[threadIdx.x >> 6] = bidx;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      for (int w = 1; w < kWaves; ++w)
-        if (s.red[w] > best || (s.red[w] == best && s.redi[w] < bidx)) {
-          best = s.red[w];
-          bidx = s.redi[w];
+    if (threadIdx.x < 64) {
+      float best = -INFINITY;
+      int bidx = 0x7FFFFFFF;
+      for (int t = lane; t < G; t += 64) {
+        const float v = __uint_as_float(s.vin[2 * t]);
+        const int i = (int)s.vin[2 * t + 1];
+        if (v > best || (v == best && i < bidx)) {
+          best = v;
+          bidx = i;
         }
-      *d_next = bidx;
+      }
+      const float m = wave_max(best);
+      const int cand = best == m ? bidx : 0x7FFFFFFF;
+      // smallest index among the lanes holding the maximum
+      int mi = cand;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) mi = min(mi, __shfl_xor(mi, o));
+      if (lane == 0) *d_next = mi;
     }
     XR_END(xc, p, ph_head + 1);
   }
@@ -846,21 +923,52 @@ __global__ void rope_kernel(float* out, int max_ctx, int hd, double theta) {
 __global__ void decode_codes_kernel(int codec, const uint8_t* in, int n, float* out) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
+  const uint32_t b = in[i];
   if (codec == 0) {
-    out[i] = e4m3_to_f32(in[i]);
-  } else {
+    out[i] = e4m3_to_f32(b);
+  } else if (codec == 1) {
     float f[8];
-    e2m1x8_to_f32((uint32_t)(in[i] & 0xF), f);
+    e2m1x8_to_f32(b & 0xFu, f);
     out[i] = f[0];
+  } else if (codec == 2) {   // E4M3 -> bf16 converter (the GEMV path), byte in position 2
+    out[i] = bf16_lo(e4m3x2_to_bf16x2<true>(b << 16));
+  } else {                   // E2M1 -> bf16 converter (the GEMV path), nibble in the high half of byte 1
+    out[i] = bf16_hi(e2m1x2_to_bf16x2<1>((b & 0xFu) << 12));
   }
 }
 
 // ------------------------------------------------------- launch wrappers
-hipError_t launch_decode(const Params* d_params, int grid, const int32_t* d_token, int pos, uint32_t epoch,
-                         int32_t* d_next, float* d_logits, hipStream_t s) {
+// Compiled shape classes: (head_dim, q heads per KV head, 1024-chunks of
+// hidden, of n_q_heads*head_dim, of intermediate); three weight formats each.
+// The tiny test decoder and the Qwen3-0.6B shape.
+#define MK_SHAPES(X) X(64, 2, 1, 1, 1) X(128, 2, 1, 2, 3)
+
+static int cdiv1024(int n) { return (n + 1023) / 1024; }
+
+bool decode_shape_supported(int hd, int gs, int hidden, int qdim, int inter) {
+  const int nh = cdiv1024(hidden), nqd = cdiv1024(qdim), ni = cdiv1024(inter);
+#define MK_CASE(H_, G_, A_, B_, C_) if (hd == H_ && gs == G_ && nh == A_ && nqd == B_ && ni == C_) return true;
+  MK_SHAPES(MK_CASE)
+#undef MK_CASE
+  return false;
+}
+
+hipError_t launch_decode(const Params* d_params, int wfmt, int hd, int gs, int hidden, int qdim, int inter, int grid,
+                         const int32_t* d_token, int pos, uint32_t epoch, int32_t* d_next, float* d_logits,
+                         hipStream_t s) {
+  const void* fn = nullptr;
+  const int nh = cdiv1024(hidden), nqd = cdiv1024(qdim), ni = cdiv1024(inter);
+#define MK_CASE(H_, G_, A_, B_, C_)                                                                             \
+  if (hd == H_ && gs == G_ && nh == A_ && nqd == B_ && ni == C_) {                                              \
+    fn = wfmt == 0 ? reinterpret_cast<const void*>(decode_kernel<0, H_, G_, A_, B_, C_>)                        \
+                   : (wfmt == 1 ? reinterpret_cast<const void*>(decode_kernel<1, H_, G_, A_, B_, C_>)           \
+                                : reinterpret_cast<const void*>(decode_kernel<2, H_, G_, A_, B_, C_>));         \
+  }
+  MK_SHAPES(MK_CASE)
+#undef MK_CASE
+  if (!fn) return hipErrorInvalidValue;
   void* args[] = {&d_params, &d_token, &pos, &epoch, &d_next, &d_logits};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(decode_kernel), dim3(grid), dim3(kThreads),
-                                    args, 0, s);
+  return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
 }
 
 hipError_t launch_pack_bf16(const uint16_t* src, int N, int K, uint16_t* dst, int row_off, int row_step,

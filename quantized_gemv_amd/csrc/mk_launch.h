@@ -7,8 +7,10 @@
 
 namespace mk {
 // `d_params` points to a Params copy in device memory that stays unchanged while the kernel runs.
-hipError_t launch_decode(const Params* d_params, int grid, const int32_t* d_token, int pos, uint32_t epoch,
-                         int32_t* d_next, float* d_logits, hipStream_t s);
+hipError_t launch_decode(const Params* d_params, int wfmt, int hd, int gs, int hidden, int qdim, int inter, int grid,
+                         const int32_t* d_token, int pos, uint32_t epoch, int32_t* d_next, float* d_logits,
+                         hipStream_t s);
+bool decode_shape_supported(int hd, int gs, int hidden, int qdim, int inter);
 hipError_t launch_pack_bf16(const uint16_t* src, int N, int K, uint16_t* dst, int row_off, int row_step,
                             hipStream_t s);
 hipError_t launch_pack_fp8(const uint16_t* src, int N, int K, uint8_t* codes, float* scales, int row_off,

@@ -2,6 +2,17 @@
 #pragma once
 #include <stdint.h>
 
+// Device code sees the buffers through address-space-1 (global) pointers, so
+// the compiler emits global_* instead of flat_* accesses: flat loads count
+// against the LDS counter too, and waiting on LDS would then also drain the
+// weight prefetch.  The host pass sees plain pointers of the same size.
+#if defined(__HIP_DEVICE_COMPILE__)
+#define MK_GLOBAL __attribute__((address_space(1)))
+#else
+#define MK_GLOBAL
+#endif
+#define GCAST(T, ptr) reinterpret_cast<MK_GLOBAL T*>(ptr)
+
 namespace mk {
 
 enum : uint32_t { FMT_BF16 = 0, FMT_FP8 = 1, FMT_FP4 = 2 };
@@ -49,11 +60,11 @@ struct Xch {
 };
 
 struct Params {
-  const uint8_t* w;       // weight arena
-  uint16_t* kv;           // [L][2][nkv][max_ctx][hd] bf16
-  const float* rope;      // [max_ctx][hd/2][2] cos, sin
-  uint64_t* xch;          // scratch
-  void* trace;            // mk_trace_rec records, or null
+  MK_GLOBAL const uint8_t* w;   // weight arena
+  MK_GLOBAL uint16_t* kv;       // [L][2][nkv][max_ctx][hd] bf16
+  MK_GLOBAL const float* rope;  // [max_ctx][hd/2][2] cos, sin
+  MK_GLOBAL uint64_t* xch;      // scratch
+  void* trace;                  // mk_trace_rec records, or null
   int L, H, nq, nkv, hd, I, V, max_ctx;
   float eps;
   Mat embed;
@@ -64,6 +75,7 @@ struct Params {
   int grid, R, att_target, ns_max;
   uint64_t spin_limit;    // s_memrealtime ticks
   uint32_t tag_skew;      // test hook: added to every expected tag (non-zero makes every wait time out)
+  uint32_t poll_sleep;    // s_sleep units (64 clocks each) between polls of a word that is not ready
   int n_phases;           // phase ids per step (trace stride per workgroup)
 };
 

@@ -18,6 +18,7 @@ namespace mk {
 struct XrayClock {
 #ifdef MK_XRAY
   uint64_t t_start, t_wb, t_we, rt_start;
+  uint64_t mark[4];
   uint32_t active;
 #endif
 };
@@ -29,12 +30,14 @@ struct XrayClock {
       (xc).t_start = __builtin_amdgcn_s_memtime();                \
       (xc).rt_start = __builtin_amdgcn_s_memrealtime();           \
       (xc).t_wb = (xc).t_we = (xc).t_start;                       \
+      (xc).mark[0] = (xc).mark[1] = (xc).mark[2] = (xc).mark[3] = 0; \
       (xc).active = 0;                                            \
     }                                                             \
   } while (0)
 #define XR_WAIT_BEGIN(xc) do { if (threadIdx.x == 0) (xc).t_wb = __builtin_amdgcn_s_memtime(); } while (0)
 #define XR_WAIT_END(xc) do { if (threadIdx.x == 0) (xc).t_we = __builtin_amdgcn_s_memtime(); } while (0)
 #define XR_ACTIVE(xc) do { if (threadIdx.x == 0) (xc).active = 1; } while (0)
+#define XR_MARK(xc, k) do { if (threadIdx.x == 0) (xc).mark[k] = __builtin_amdgcn_s_memtime(); } while (0)
 #define XR_END(xc, p, ph_id)                                                          \
   do {                                                                                \
     if (threadIdx.x == 0 && (p).trace) {                                              \
@@ -51,6 +54,7 @@ struct XrayClock {
       r.t_end = __builtin_amdgcn_s_memtime();                                         \
       r.rt_start = (xc).rt_start;                                                     \
       r.rt_end = __builtin_amdgcn_s_memrealtime();                                    \
+      for (int k_ = 0; k_ < 4; ++k_) r.t_mark[k_] = (xc).mark[k_];                     \
       static_cast<mk_trace_rec*>((p).trace)[(size_t)blockIdx.x * (p).n_phases + (ph_id)] = r; \
     }                                                                                 \
   } while (0)
@@ -59,6 +63,7 @@ struct XrayClock {
 #define XR_WAIT_BEGIN(xc) do { } while (0)
 #define XR_WAIT_END(xc) do { } while (0)
 #define XR_ACTIVE(xc) do { } while (0)
+#define XR_MARK(xc, k) do { } while (0)
 #define XR_END(xc, p, phase) do { } while (0)
 #endif
 

@@ -18,7 +18,7 @@ from .build import lib_path
 MK_OK, MK_E_INVALID, MK_E_UNSUPPORTED, MK_E_STATE, MK_E_HIP, MK_E_TIMEOUT = 0, -1, -2, -3, -4, -5
 BF16, FP8_ROW, FP4_MIX = 0, 1, 2
 MATRICES = {"q": 0, "k": 1, "v": 2, "o": 3, "gate": 4, "up": 5, "down": 6, "embed": 7}
-OPT_GRID, OPT_REPLICAS, OPT_ATT_TARGET, OPT_SPIN_LIMIT, OPT_TAG_SKEW = 0, 1, 2, 3, 4
+OPT_GRID, OPT_REPLICAS, OPT_ATT_TARGET, OPT_SPIN_LIMIT, OPT_TAG_SKEW, OPT_POLL_SLEEP = 0, 1, 2, 3, 4, 5
 
 
 class MkError(RuntimeError):
@@ -44,12 +44,13 @@ class mk_trace_rec(ctypes.Structure):
                 ("xcc", ctypes.c_uint32), ("active", ctypes.c_uint32), ("pad", ctypes.c_uint32),
                 ("t_start", ctypes.c_uint64), ("t_wait_begin", ctypes.c_uint64),
                 ("t_wait_end", ctypes.c_uint64), ("t_end", ctypes.c_uint64),
-                ("rt_start", ctypes.c_uint64), ("rt_end", ctypes.c_uint64)]
+                ("rt_start", ctypes.c_uint64), ("rt_end", ctypes.c_uint64),
+                ("t_mark", ctypes.c_uint64 * 4)]
 
 
 TRACE_DTYPE = np.dtype([(n, np.uint32) for n in ("phase", "wg", "hw_id", "xcc", "active", "pad")] +
                        [(n, np.uint64) for n in ("t_start", "t_wait_begin", "t_wait_end", "t_end",
-                                                 "rt_start", "rt_end")])
+                                                 "rt_start", "rt_end")] + [("t_mark", np.uint64, (4,))])
 
 _LIBS: Dict[bool, ctypes.CDLL] = {}
 _VP = ctypes.c_void_p
@@ -107,7 +108,7 @@ class Decoder:
 
     def __init__(self, shape, wfmt: int, max_ctx: int, xray: bool = False, grid: int = 0,
                  replicas: Optional[int] = None, att_target: Optional[int] = None,
-                 spin_limit: Optional[int] = None):
+                 spin_limit: Optional[int] = None, poll_sleep: Optional[int] = None):
         import torch
         self.lib = load(xray)
         self.shape, self.wfmt, self.max_ctx = shape, wfmt, max_ctx
@@ -123,6 +124,8 @@ class Decoder:
             self._check(self.lib.mk_set_option(self.h, OPT_ATT_TARGET, att_target))
         if spin_limit is not None:
             self._check(self.lib.mk_set_option(self.h, OPT_SPIN_LIMIT, spin_limit))
+        if poll_sleep is not None:
+            self._check(self.lib.mk_set_option(self.h, OPT_POLL_SLEEP, poll_sleep))
         self.sizes = mk_sizes()
         self._check(self.lib.mk_query_sizes(self.h, ctypes.byref(self.sizes)))
         dev = torch.device("cuda", torch.cuda.current_device())

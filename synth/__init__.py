@@ -23,6 +23,7 @@ Recipe (one bf16 master per shape; the quantized configs quantize it):
 from __future__ import annotations
 
 import dataclasses
+import os
 from typing import Dict, List
 
 import numpy as np
@@ -117,22 +118,29 @@ class MasterWeights:
 
 def make_weights(shape: Shape, seed: int = 0, zero_linears: bool = False) -> MasterWeights:
     """Draw the bf16 master for `shape`.  `zero_linears` zeroes every layer
-    linear (q, k, v, o, gate, up, down), a degenerate case used by tests."""
-    idx = 0
-    embed = _draw(seed, idx, (shape.vocab, shape.hidden), False)
-    idx += 1
+    linear (q, k, v, o, gate, up, down), a degenerate case used by tests.
+    Tensors are drawn in parallel; each has its own generator, so the result
+    does not depend on the order."""
+    from concurrent.futures import ThreadPoolExecutor
     shapes = shape.tensor_shapes()
+    jobs = [(0, (shape.vocab, shape.hidden), False)]
+    for l in range(shape.n_layers):
+        for j, name in enumerate(LAYER_TENSORS):
+            jobs.append((1 + 11 * l + j, shapes[name], name in NORM_TENSORS))
+    jobs.append((1 + 11 * shape.n_layers, (shape.hidden,), True))
+    workers = min(16, len(os.sched_getaffinity(0)))
+    with ThreadPoolExecutor(workers) as ex:
+        out = list(ex.map(lambda j: _draw(seed, *j), jobs))
+    embed, final_norm = out[0], out[-1]
     layers = []
-    for _ in range(shape.n_layers):
+    for l in range(shape.n_layers):
         layer = {}
-        for name in LAYER_TENSORS:
-            t = _draw(seed, idx, shapes[name], name in NORM_TENSORS)
+        for j, name in enumerate(LAYER_TENSORS):
+            t = out[1 + 11 * l + j]
             if zero_linears and name not in NORM_TENSORS:
                 t[...] = 0
             layer[name] = t
-            idx += 1
         layers.append(layer)
-    final_norm = _draw(seed, idx, (shape.hidden,), True)
     return MasterWeights(shape, embed, layers, final_norm)
 
 

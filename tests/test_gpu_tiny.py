@@ -57,6 +57,14 @@ def test_codec_tables(native):
     native.decode_codes(1, c16, o16)
     assert np.array_equal(o16.cpu().numpy().view(np.uint32),
                           e2m1_decode(np.arange(16, dtype=np.uint8)).view(np.uint32))
+    # the converters the GEMVs use (to packed bf16)
+    native.decode_codes(2, codes, out)
+    got = out.cpu().numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[fin].view(np.uint32), ref[fin].view(np.uint32))
+    native.decode_codes(3, c16, o16)
+    assert np.array_equal(o16.cpu().numpy().view(np.uint32),
+                          e2m1_decode(np.arange(16, dtype=np.uint8)).view(np.uint32))
 
 
 @pytest.mark.parametrize("wfmt", FORMATS)

@@ -30,16 +30,15 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=12)
     ap.add_argument("--repeats", type=int, default=5, help="timed runs; the median is reported")
-    ap.add_argument("--att-target", type=int, default=0, help="attention positions per unit (0: library default)")
-    ap.add_argument("--replicas", type=int, default=0, help="exchange replicas (0: library default)")
-    ap.add_argument("--poll-sleep", type=int, default=-1, help="poll back-off level (-1: library default)")
+    ap.add_argument("--poll-sleep", type=int, default=-1, help="poll back-off 0/1 (-1: library default)")
+    ap.add_argument("--xray-dump", default="", help="with --xray: also save the raw records (.npy)")
     ap.add_argument("--xray", action="store_true",
                     help="X-ray build: print the per-phase budget of the step at position P + K/2 "
                          "instead of the headline line")
     return ap.parse_args()
 
 
-def xray_report(dec, wl, K, prompt):
+def xray_report(dec, wl, K, prompt, dump=""):
     """Run the X-ray build to position P + K/2 and report that step's budget."""
     import torch
     from quantized_gemv_amd import xray
@@ -51,14 +50,17 @@ def xray_report(dec, wl, K, prompt):
     torch.cuda.synchronize()
     dec.check_device_error()
     rec = dec.trace()
+    if dump:
+        import numpy as np
+        np.save(dump, rec)
     b = xray.budget(rec, wl.shape.n_layers)
     tab = xray.phase_table(rec, wl.shape.n_layers)
     L = wl.shape.n_layers
-    layer_mid = {t["name"]: t for ph, t in tab.items() if (ph - 2) // 6 == L // 2 and 2 <= ph < 6 * L + 2}
-    return {"xray_position": pos + K // 2 - 1, "budget": b,
-            "middle_layer_phases": {k: {kk: round(vv, 1) if isinstance(vv, float) else vv for kk, vv in v.items()}
-                                    for k, v in layer_mid.items()},
-            "lm_head": tab.get(6 * L + 2), "argmax": tab.get(6 * L + 3)}
+    rnd = lambda d: {k: round(v, 1) if isinstance(v, float) else v for k, v in d.items()}
+    layer_mid = {t["name"]: rnd(t) for ph, t in tab.items() if 2 <= ph < 6 * L + 2 and (ph - 2) // 6 == L // 2}
+    return {"xray_position": pos + K // 2 - 1, "budget": b, "middle_layer_phases": layer_mid,
+            "embed": rnd(tab.get(1, {})), "lm_head": rnd(tab.get(6 * L + 2, {})),
+            "argmax": rnd(tab.get(6 * L + 3, {}))}
 
 
 def cpu_baseline(master, wl, n_steps, prompt):
@@ -105,8 +107,7 @@ def main():
     master = synth.make_weights(sh, wl.weight_seed)
     prompt = synth.make_prompt(sh.vocab, wl.prompt_len, wl.prompt_seed)
 
-    dec = native.Decoder(sh, wl.wfmt, max_ctx, xray=args.xray, att_target=args.att_target or None,
-                         replicas=args.replicas or None,
+    dec = native.Decoder(sh, wl.wfmt, max_ctx, xray=args.xray,
                          poll_sleep=None if args.poll_sleep < 0 else args.poll_sleep)
     dev_master = native.master_to_device(master)
     dec.pack(dev_master)
@@ -114,7 +115,7 @@ def main():
     torch.cuda.empty_cache()
 
     if args.xray:
-        print(json.dumps({"workload": wl.name, **xray_report(dec, wl, K, prompt)}), flush=True)
+        print(json.dumps({"workload": wl.name, **xray_report(dec, wl, K, prompt, args.xray_dump)}), flush=True)
         dec.close()
         return
     stream = torch.cuda.current_stream()
@@ -164,8 +165,8 @@ def main():
         "config": {"workload": wl.name, "prompt_len": wl.prompt_len, "decode_steps": K,
                    "positions": [wl.prompt_len, wl.prompt_len + K - 1],
                    "weight_format": synth.WFMT_NAMES[wl.wfmt], "accumulate": "f32", "batch": 1,
-                   "grid": "one 512-thread workgroup per CU", "timed_runs": len(times),
-                   "att_target": args.att_target or None, "replicas": args.replicas or None,
+                   "grid": "one workgroup per CU: 1 courier + 7 compute waves; attention on one "
+                           "workgroup per KV head", "timed_runs": len(times),
                    "run_seconds": [round(t, 6) for t in times]},
         "weight_bytes_per_token": wbytes,
         "weight_roofline_pct": round(100.0 * wbytes * tps / (PEAK_HBM_GBPS * 1e9), 2),

@@ -59,8 +59,11 @@ enum mk_wfmt {
  * (head_dim, n_q_heads / n_kv_heads, ceil(hidden/1024),
  * ceil(n_q_heads*head_dim/1024), ceil(intermediate/1024)), one of
  * (64, 2, 1, 1, 1) and (128, 2, 1, 2, 3) (the latter is the Qwen3-0.6B shape);
- * hidden, intermediate and n_q_heads*head_dim multiples of 16;
- * n_layers <= 160; max_ctx <= 1<<20. */
+ * hidden a multiple of 128; intermediate and n_q_heads*head_dim multiples
+ * of 16; n_layers <= 170; max_ctx <= 1<<20.  mk_bind further needs a grid
+ * with more workgroups than KV heads whose work table fits the kernel's
+ * per-wave limits (the default grid, one workgroup per compute unit of an
+ * MI355X, does). */
 typedef struct mk_config {
   int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, intermediate, vocab, max_ctx;
   float rope_theta;   /* RoPE base (Qwen3: 1e6) */
@@ -81,23 +84,24 @@ typedef struct mk_sizes {
   size_t kv_bytes_per_position;   /* KV bytes one step reads per cached position */
 } mk_sizes;
 
-/* One X-ray record: one workgroup, one phase of one step.  Times are
- * s_memtime ticks (the shader clock counter) except rt_*, which are
- * s_memrealtime ticks (a 100 MHz constant-rate counter shared by all XCDs). */
+/* One X-ray record: one workgroup, one phase of one step.  Every time is an
+ * s_memrealtime tick (a 100 MHz counter common to all XCDs).  Phases: 1
+ * embedding; 2+6l+{0..5} layer l QKV, attention, (unused), O, gate/up, down;
+ * 2+6L final norm + LM head; 3+6L argmax reduce.  A phase's input is
+ * gathered by the workgroup's courier wave: t_start (gather began), t_ready
+ * (every word present), t_handoff (input in LDS for the compute waves).  The
+ * compute waves record t_seen (the first of them past its wait) and t_done
+ * (the last of them done with its outputs).  t_mark: attention [0] scores and
+ * outputs of every wave done, [1] outputs published. */
 typedef struct mk_trace_rec {
-  uint32_t phase;      /* phase id: 1 embed; 2+6l+{0..5} layer l QKV, attention, merge, O,
-                          gate/up, down; 2+6L final norm + LM head; 3+6L argmax reduce */
+  uint32_t phase;      /* phase id (above) */
   uint32_t wg;         /* workgroup index */
   uint32_t hw_id;      /* HW_ID register (CU, SE, SIMD, wave slot) */
   uint32_t xcc;        /* XCC_ID register (which XCD) */
   uint32_t active;     /* 1 if this workgroup had work in the phase */
   uint32_t pad;
-  uint64_t t_start, t_wait_begin, t_wait_end, t_end;  /* s_memtime */
-  uint64_t rt_start, rt_end;                           /* s_memrealtime */
-  uint64_t t_mark[4];  /* s_memtime marks inside the phase after its wait (0 if unused): GEMV
-                          phases: input normalized, products done, rows finished, results
-                          published; attention: q/k/v normed and K/V appended, scores and
-                          softmax done, outputs reduced, results published */
+  uint64_t t_start, t_ready, t_handoff, t_seen, t_done;
+  uint64_t t_mark[3];
 } mk_trace_rec;
 
 typedef struct mk_model mk_model;
@@ -181,12 +185,13 @@ int mk_get_trace(mk_model* m, mk_trace_rec* h_out, size_t cap, size_t* n_out);
 int mk_decode_codes(int32_t codec, const uint8_t* d_codes, int32_t n, float* d_out, mk_stream_t s);
 
 /* Tuning knobs (defaults in brackets): key 0 grid size [compute units],
- * key 1 exchange replicas [8], key 2 attention positions per unit [64],
- * key 3 spin bound in 100 MHz ticks [100000000 = 1 s], key 4 test hook
- * [0]: a non-zero value shifts every tag the kernel waits for, so no wait
- * can be satisfied and each one ends at the spin bound (used to test the
- * MK_E_TIMEOUT path without hanging).  Keys 0 and 1 must be set before
- * mk_bind.  Errors: MK_E_INVALID, MK_E_STATE. */
+ * set before mk_bind; key 3 spin bound in 100 MHz ticks [100000000 = 1 s];
+ * key 4 test hook [0]: a non-zero value shifts every tag the kernel waits
+ * for, so no wait can be satisfied and each one ends at the spin bound (used
+ * to test the MK_E_TIMEOUT path without hanging); key 5 poll back-off
+ * between exchange poll rounds, 0..16 units of about 512 clocks [0].  Keys
+ * 1 and 2 are reserved.
+ * Errors: MK_E_INVALID (unknown key, value out of range), MK_E_STATE. */
 int mk_set_option(mk_model* m, int32_t key, int64_t value);
 
 /* 1 if the library was built with the X-ray stamps, else 0. */

@@ -51,8 +51,9 @@ struct mk_model {
   void* d_trace = nullptr;
   bool bound = false, packed = false, params_dirty = true;
   int device = -1, cus = 0;
-  int grid_opt = 0, replicas = 8, att_target = 64;
+  int grid_opt = 0;
   int64_t spin_limit = 100000000;
+  std::vector<int32_t> sched;   // the work table (host copy)
   uint32_t tag_skew = 0;
   uint32_t poll_sleep = 0;
   uint32_t epoch = 0;
@@ -138,49 +139,123 @@ void layout_weights(mk_model* m) {
   m->algo_bytes = algo;
 }
 
-// Lay out the scratch buffer: exchange words, the params copy, token slots.
+// Lay out the scratch buffer: per-layer exchange vectors, argmax words, the
+// error word, the zero page, the work table, the params copy, token slots.
 void layout_scratch(mk_model* m, int grid, bool for_sizing = true) {
   const mk_config& c = m->cfg;
-  Params& P = m->P;
-  Xch& X = P.x;
-  const int R = m->replicas;
-  const uint64_t H = c.hidden, hd = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads;
-  const uint64_t pad = 32;  // words between replicas, so copies start on different lines
-  uint64_t w = 0;
-  auto vec = [&](uint64_t& base, uint64_t& rep, uint64_t& par, uint64_t n) {
-    rep = n + pad;
-    par = rep * R;
-    base = w;
-    w += 2 * par;
-  };
-  uint64_t dummy_rep = 0;
-  vec(X.x_d, X.rep_x, X.par_x, H);
-  uint64_t rep2 = 0, par2 = 0;
-  vec(X.x_o, rep2, par2, H);  // same shape as x_d: same strides
-  vec(X.qkv, X.rep_qkv, X.par_qkv, (nq + 2 * nkv) * hd);
-  vec(X.o, X.rep_o, X.par_o, nq * hd / 2);
-  vec(X.h, X.rep_h, X.par_h, (uint64_t)c.intermediate / 2);
-  (void)dummy_rep;
-  int ns_max = grid / (int)nkv;
-  const int cap = kMaxVecWords / (int)(hd + 2);
-  if (ns_max > cap) ns_max = cap;
-  if (ns_max < 1) ns_max = 1;
-  P.ns_max = ns_max;
-  X.part = w;
-  X.par_part = nq * (uint64_t)ns_max * (hd + 2);
-  w += 2 * X.par_part;
-  X.arg = w;
-  w += 2ull * grid;
-  X.err = w;
-  w += 1;
-  X.amax = w;
-  w += 1;
+  Xch& X = m->P.x;
+  const uint64_t H = c.hidden, hd = c.head_dim, nq = c.n_q_heads, nkv = c.n_kv_heads, I = c.intermediate;
+  auto al = [](uint64_t w) { return (w + 15) / 16 * 16; };   // 128-byte boundaries
+  X.base = 0;
+  uint64_t lw = 0;
+  const uint64_t sizes[kTypes] = {(nq + 2 * nkv) * hd, 0, nq * hd / 2, H, I / 2, H};
+  for (int t = 0; t < kTypes; ++t) {
+    X.off[t] = lw;
+    lw = al(lw + sizes[t]);
+  }
+  X.layer_words = lw;
+  uint64_t w = lw * (uint64_t)c.n_layers;
+  X.arg = al(w);
+  w = X.arg + 2ull * grid;
+  X.err = al(w);
+  X.amax = X.err + 1;
+  w = X.amax + 1;
+  X.sched = (w + 31) / 32 * 32;                 // 256-byte boundary
+  w = X.sched;
+  w += (uint64_t)grid * kWaves * kSchedInts / 2;
   w = (w + 31) / 32 * 32;
   X.words = w;
   m->params_off = align_up(w * 8);
   m->tok_off = align_up(m->params_off + sizeof(Params));
   m->scratch_bytes = align_up(m->tok_off + 4ull * ((size_t)c.max_ctx + 4));
   if (for_sizing) m->scratch_reported = m->scratch_bytes;
+}
+
+// The work table: which workgroup runs which KV head's attention, and which
+// rows of each matrix every compute wave owns.  Returns an error message, or
+// nullptr.
+//  * Attention: KV head g on workgroup g, which the hardware places on XCD
+//    g % 8 (workgroups are dealt to the XCDs round robin).
+//  * Every matrix is split into contiguous blocks of rows, one block per
+//    workgroup, so one workgroup's output words share cache lines only with
+//    each other (words of many producers in one line make every exchange
+//    slower); inside a block the rows go to the compute waves in turn.
+//  * QKV: the q, k and v rows of head g go to the other workgroups of the
+//    same XCD, so the attention workgroup gathers them from its own L2.
+//  * O, gate/up (units of four rows = one output word), down: over the
+//    workgroups without attention; each matrix starts at a different wave
+//    so every wave gets a similar share.
+const char* build_sched(const mk_config& c, int grid, std::vector<int32_t>& tab) {
+  const int nkv = c.n_kv_heads, hd = c.head_dim, nq = c.n_q_heads, gs = nq / nkv;
+  const int H = c.hidden, I = c.intermediate;
+  const int nA = nkv;
+  if (grid < nA + 1) return "grid too small for one attention workgroup per KV head";
+  tab.assign((size_t)grid * kWaves * kSchedInts, -1);
+  auto hdr = [&](int wg, int i) -> int32_t& { return tab[(size_t)wg * kWaves * kSchedInts + i]; };
+  auto unit = [&](int wg, int cw, int i) -> int32_t& {
+    return tab[(size_t)wg * kWaves * kSchedInts + (size_t)(cw + 1) * kSchedInts + i];
+  };
+  auto add = [&](int wg, int cw, int off, int maxu, int row) -> bool {
+    for (int k = 0; k < maxu; ++k)
+      if (unit(wg, cw, off + k) < 0) {
+        unit(wg, cw, off + k) = row;
+        return true;
+      }
+    return false;
+  };
+  // units [0, n) of `rows` in contiguous blocks over `wgs`, waves in turn from `w0`
+  auto deal = [&](const std::vector<int>& rows, const std::vector<int>& wgs, int w0, int slot, int maxu) -> bool {
+    const size_t n = rows.size(), C = wgs.size();
+    for (size_t i = 0; i < C; ++i) {
+      const size_t a = n * i / C, b = n * (i + 1) / C;
+      for (size_t u = a; u < b; ++u)
+        if (!add(wgs[i], (int)((w0 + (u - a)) % kCW), slot, maxu, rows[u])) return false;
+    }
+    return true;
+  };
+  for (int wg = 0; wg < grid; ++wg) hdr(wg, S_ATT) = wg < nA ? wg : -1;
+  // QKV, per XCD slot
+  for (int sl = 0; sl < 8; ++sl) {
+    std::vector<int> wgs;
+    for (int wg = sl; wg < grid; wg += 8)
+      if (wg >= nA) wgs.push_back(wg);
+    std::vector<int> rows;
+    for (int g = sl; g < nkv; g += 8) {
+      for (int i = 0; i < gs * hd; ++i) rows.push_back(g * gs * hd + i);
+      for (int i = 0; i < hd; ++i) rows.push_back((nq + g) * hd + i);
+      for (int i = 0; i < hd; ++i) rows.push_back((nq + nkv + g) * hd + i);
+    }
+    if (rows.empty()) continue;
+    if (wgs.empty()) return "no workgroup on an XCD that holds a KV head";
+    if (!deal(rows, wgs, 0, S_QKV, kMaxQKV)) return "too many QKV rows per wave for this grid";
+  }
+  // O, gate/up, down
+  std::vector<int> gw;
+  for (int wg = nA; wg < grid; ++wg) gw.push_back(wg);
+  std::vector<int> rh(H), ri(I / 2);
+  for (int i = 0; i < H; ++i) rh[i] = i;
+  for (int i = 0; i < I / 2; ++i) ri[i] = i;
+  if (!deal(rh, gw, 0, S_O, kMaxO)) return "too many O rows per wave for this grid";
+  if (!deal(ri, gw, 0, S_GU, kMaxGU)) return "too many gate/up units per wave for this grid";
+  if (!deal(rh, gw, 3, S_D, kMaxD)) return "too many down rows per wave for this grid";
+  // per-workgroup inputs, in the courier's order: xd, qkv, o, xo, h
+  for (int wg = 0; wg < grid; ++wg) {
+    bool q = false, o = false, gu = false, d = false;
+    for (int cw = 0; cw < kCW; ++cw) {
+      q |= unit(wg, cw, S_QKV) >= 0;
+      o |= unit(wg, cw, S_O) >= 0;
+      gu |= unit(wg, cw, S_GU) >= 0;
+      d |= unit(wg, cw, S_D) >= 0;
+    }
+    const bool att = hdr(wg, S_ATT) >= 0;
+    const bool need[5] = {q || o, att, o, gu || d, d};
+    const int slot[5] = {S_IXD, S_IQKV, S_IO, S_IXO, S_IH};
+    int n = 0;
+    for (int i = 0; i < 5; ++i) hdr(wg, slot[i]) = need[i] ? n++ : -1;
+    hdr(wg, S_NIN) = n;
+    hdr(wg, S_FLAGS) = (need[0] ? 1 : 0) | (o ? 2 : 0) | (need[3] ? 4 : 0) | (d ? 8 : 0);
+  }
+  return nullptr;
 }
 
 int n_phases(const mk_config& c) { return 6 * c.n_layers + 4; }
@@ -200,27 +275,20 @@ int validate_cfg(const mk_config* c) {
   if (!decode_shape_supported(c->head_dim, c->n_q_heads / c->n_kv_heads, c->hidden, c->n_q_heads * c->head_dim,
                               c->intermediate))
     return MK_E_UNSUPPORTED;
-  if (c->hidden % 16 || c->intermediate % 16 || (c->n_q_heads * c->head_dim) % 16) return MK_E_UNSUPPORTED;
+  if (c->hidden % 128 || c->intermediate % 16 || (c->n_q_heads * c->head_dim) % 16) return MK_E_UNSUPPORTED;
   if (c->hidden > 4096 || c->intermediate / 2 > 6144 || c->n_q_heads * c->head_dim / 2 > 6144)
     return MK_E_UNSUPPORTED;
-  if (c->n_layers > 160 || c->max_ctx > (1 << 20)) return MK_E_UNSUPPORTED;
+  if (c->n_layers > kMaxLayers || c->max_ctx > (1 << 20)) return MK_E_UNSUPPORTED;
   return MK_OK;
 }
 
-// Per-workgroup capacities of the kernel (LDS arrays) for a given grid.
+// Grids the kernel handles: at most kMaxGrid workgroups and a work table
+// within the per-wave unit limits.
 int check_grid(mk_model* m, int grid) {
-  const mk_config& c = m->cfg;
-  auto cdiv = [](long a, long b) { return (a + b - 1) / b; };
-  const long G = grid, nch_h = cdiv(c.hidden, 1024);
-  const long nqkv = (long)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim;
   if (grid < 1) return fail(m, MK_E_INVALID, "grid must be positive");
-  if (cdiv(c.hidden, G) > kMaxOwn) return fail(m, MK_E_UNSUPPORTED, "grid %d too small for hidden %d", grid, c.hidden);
-  const long items[5] = {cdiv(nqkv, G) * nch_h, cdiv(c.hidden, G) * cdiv((long)c.n_q_heads * c.head_dim, 1024),
-                         4 * cdiv(c.intermediate / 2, G) * nch_h, cdiv(c.hidden, G) * cdiv(c.intermediate, 1024),
-                         cdiv(c.vocab, G) * nch_h};
-  for (long it : items)
-    if (it > kMaxPart) return fail(m, MK_E_UNSUPPORTED, "grid %d leaves %ld GEMV items per workgroup", grid, it);
-  if (2 * G > kMaxVecWords) return fail(m, MK_E_UNSUPPORTED, "grid %d too large", grid);
+  std::vector<int32_t> tab;
+  const char* why = build_sched(m->cfg, grid, tab);
+  if (why) return fail(m, MK_E_UNSUPPORTED, "grid %d: %s", grid, why);
   return MK_OK;
 }
 
@@ -232,6 +300,7 @@ int sync_params(mk_model* m, hipStream_t s) {
   Params& P = m->P;
   // C-style casts: in the device pass of this file these fields are global pointers
   P.w = (decltype(P.w))m->d_weights;
+  P.w_bytes = (uint32_t)m->weights_bytes;
   P.kv = (decltype(P.kv))m->d_kv;
   P.rope = (decltype(P.rope))m->d_rope;
   P.xch = (decltype(P.xch))m->d_scratch;
@@ -245,8 +314,6 @@ int sync_params(mk_model* m, hipStream_t s) {
   P.V = c.vocab;
   P.max_ctx = c.max_ctx;
   P.eps = c.rms_eps;
-  P.R = m->replicas;
-  P.att_target = m->att_target;
   P.spin_limit = (uint64_t)m->spin_limit;
   P.tag_skew = m->tag_skew;
   P.poll_sleep = m->poll_sleep;
@@ -277,7 +344,7 @@ int launch_step(mk_model* m, const int32_t* d_token, int pos, int32_t* d_next, f
   if (rc) return rc;
   m->epoch = (m->epoch + 1) & kEpochMask;
   if (m->epoch == 0) {  // tags would repeat: clear the exchange words and restart
-    HIPCK(m, hipMemsetAsync(m->d_scratch, 0, 8 * m->P.x.words, s));
+    HIPCK(m, hipMemsetAsync(m->d_scratch, 0, 8 * m->P.x.err, s));
     m->epoch = 1;
   }
   const Params* dp = reinterpret_cast<const Params*>(m->d_scratch + m->params_off);
@@ -307,6 +374,10 @@ int mk_create(const mk_config* cfg, mk_model** out) {
   }
   layout_weights(m);
   layout_scratch(m, sizing_grid(m));
+  if (m->weights_bytes > kMaxBuffer || 8 * m->P.x.words > kMaxBuffer) {
+    delete m;
+    return MK_E_UNSUPPORTED;   // the kernels address weights and scratch with 32-bit offsets
+  }
   *out = m;
   return MK_OK;
 }
@@ -354,7 +425,11 @@ int mk_bind(mk_model* m, void* d_weights, void* d_kv, void* d_rope, void* d_scra
   m->bound = true;
   m->params_dirty = true;
   m->epoch = 0;
+  const char* why = build_sched(m->cfg, grid, m->sched);
+  if (why) return fail(m, MK_E_UNSUPPORTED, "grid %d: %s", grid, why);
   HIPCK(m, hipMemsetAsync(d_scratch, 0, m->scratch_bytes, s));
+  HIPCK(m, hipMemcpyAsync(m->d_scratch + 8 * m->P.x.sched, m->sched.data(), m->sched.size() * sizeof(int32_t),
+                          hipMemcpyHostToDevice, s));
   return sync_params(m, s);
 }
 
@@ -532,16 +607,6 @@ int mk_set_option(mk_model* m, int32_t key, int64_t value) {
       m->grid_opt = (int)value;
       layout_scratch(m, sizing_grid(m));
       break;
-    case 1:
-      if (value < 1 || value > 64) return fail(m, MK_E_INVALID, "replicas %lld out of range", (long long)value);
-      if (m->bound) return fail(m, MK_E_STATE, "set replicas before mk_bind");
-      m->replicas = (int)value;
-      layout_scratch(m, sizing_grid(m));
-      break;
-    case 2:
-      if (value < 1 || value > (1 << 20)) return fail(m, MK_E_INVALID, "attention target out of range");
-      m->att_target = (int)value;
-      break;
     case 3:
       if (value < 0) return fail(m, MK_E_INVALID, "spin limit must be >= 0");
       m->spin_limit = value;
@@ -551,7 +616,7 @@ int mk_set_option(mk_model* m, int32_t key, int64_t value) {
       m->tag_skew = (uint32_t)value;
       break;
     case 5:
-      if (value < 0 || value > 5) return fail(m, MK_E_INVALID, "poll sleep out of range");
+      if (value < 0 || value > 16) return fail(m, MK_E_INVALID, "poll back-off out of range");
       m->poll_sleep = (uint32_t)value;
       break;
     default:

@@ -1,0 +1,1123 @@
+// gfx950 persistent batch-1 decode kernel.
+//
+// One launch computes one greedy decode step of a Qwen3-style decoder (the
+// model of the monolith project page, "Upstream facts"): embedding lookup,
+// then per layer RMSNorm -> fused QKV GEMV -> q/k RMSNorm + RoPE + KV append
+// -> GQA attention -> O-projection + residual -> RMSNorm -> gate/up GEMV +
+// SwiGLU -> down GEMV + residual, then the final RMSNorm, the tied LM-head
+// GEMV and the argmax, so one launch yields one token (the page's "fold the LM
+// head and argmax into the megakernel").
+//
+// Launch: cooperative, one workgroup of eight waves per compute unit.  Wave 0
+// of every workgroup is its courier (mk_sync.h): it gathers each input
+// vector the workgroup needs from the exchange words, normalises it where the
+// consumer wants that (every workgroup recomputes the RMSNorm factor itself,
+// the page's trick, so no phase waits for a reduction), and hands it over in
+// LDS.  Waves 1..7 compute.  A host-built table gives each compute wave its
+// rows of every matrix; the wave keeps those rows' weights in registers and
+// loads the next layer's rows of a matrix right after it has used this
+// layer's, so about one layer of weights per compute unit is always in
+// flight and weight streaming never waits for the dependency chain.
+// Attention runs on dedicated workgroups, one per KV head, placed on the XCD
+// whose workgroups compute that head's q/k/v rows; each keeps the cached K/V
+// rows of its head in registers, loaded one layer ahead.
+//
+// Weights are dequantized in registers (FP8 and FP4 through the gfx950
+// converters) and every product accumulates in fp32 (the page's W8A16
+// scheme; the pages' contract also asks for each weight byte to be read once
+// per token).  No MFMA: these are matrix-vector products, bound by HBM
+// bandwidth.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "mk.h"
+#include "mk_codec.h"
+#include "mk_launch.h"
+#include "mk_shared.h"
+#include "mk_sync.h"
+#include "mk_xray.h"
+
+namespace mk {
+
+// This wave's index, as a value the compiler knows is uniform across the wave.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+
+// Cross-lane reductions with DPP (row operations on the VALU) and
+// v_readlane.  DPP controls (gfx9): quad_perm [1,0,3,2] = 0xB1,
+// [2,3,0,1] = 0x4E, row_ror:4 = 0x124, row_ror:8 = 0x128,
+// row_half_mirror = 0x141.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Sum over each 8-lane group, result in every lane of it.
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  return v + dpp<0x141>(v);
+}
+__device__ __forceinline__ float sum16(float v) {
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x124>(v);
+  return v + dpp<0x128>(v);
+}
+__device__ __forceinline__ float max16(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x124>(v));
+  return fmaxf(v, dpp<0x128>(v));
+}
+__device__ __forceinline__ float lane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+// Sum / max over the wave, the same value in every lane (fixed order).
+__device__ __forceinline__ float wave_sum(float v) {
+  v = sum16(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = max16(v);
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) { return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16); }
+
+// ------------------------------------------------------------------ LDS
+template <int HD, int GS, int NH, int NQ, int NI>
+struct Smem {
+  // every array starts on a 16-byte boundary: the compute waves read them
+  // with 16-byte LDS loads
+  alignas(16) float xd_raw[NH * 1024];   // residual entering the layer (fp32)
+  alignas(16) uint32_t o_in[NQ * 512];   // attention output, bf16 pairs (O input)
+  alignas(16) float xo_raw[NH * 1024];   // residual after O (fp32)
+  alignas(16) uint32_t h_in[NI * 512];   // SwiGLU output, bf16 pairs (down input)
+  // attention workgroups
+  alignas(16) float qraw[(GS + 2) * HD]; // gathered q heads, k, v of the KV head
+  alignas(16) float q[GS * HD];          // normed, roped, pre-scaled q heads
+  alignas(16) float kf[HD];              // roped k before rounding
+  alignas(16) uint32_t kp[HD / 2];       // this position's k, bf16 pairs
+  alignas(16) uint32_t vp[HD / 2];       // this position's v, bf16 pairs
+  alignas(16) float part[kCW][4][GS * HD];  // per wave and 16-lane row: unnormalised outputs
+  alignas(16) float wm[kCW][GS];         // per wave: running max (log2 units)
+  alignas(16) float wl[kCW][GS];         // per wave: running sum
+  alignas(16) float sp[GS];              // this position's scores (log2 units)
+  // argmax
+  alignas(16) float best[kCW];
+  alignas(16) int32_t bidx[kCW];
+  float r_xd, r_xo;                      // 1/rms of xd_raw and xo_raw
+  uint32_t seq;                          // inputs handed over by the courier (kAbort: abort)
+  XR_FIELD
+};
+
+// ------------------------------------------------------------------ GEMV
+// Lane l covers elements [c*1024 + 16 l, +16) of a row for chunk c, so a
+// wave streams each row as contiguous 2 KB (bf16) / 1 KB (fp8) / 512 B (fp4)
+// runs with 16-byte (fp4: 8-byte) loads.
+
+// Weights are read through a buffer resource over the arena.  An absent
+// unit reads at kOOB (zeros, no memory traffic), so every wave issues the
+// same loads in the same order (the compiler's wait counts stay exact) and
+// the results are never used.
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+struct GMat {
+  uint32_t codes, scales, ts;       // byte offsets in the arena
+  uint32_t K, ts_mode, ts_b0, ts_b1;
+};
+
+__device__ __forceinline__ GMat gmat(const Mat& m, uint64_t off) {
+  GMat g;
+  g.codes = (uint32_t)(m.codes + off);
+  g.scales = (uint32_t)(m.scales + off);
+  g.ts = (uint32_t)(m.tscale + off);
+  g.K = m.K;
+  g.ts_mode = m.ts_mode;
+  g.ts_b0 = m.ts_b0;
+  g.ts_b1 = m.ts_b1;
+  return g;
+}
+
+template <uint32_t FMT, int NCH>
+struct WRow {
+  v4u a[NCH];   // bf16: bytes 0..15 of the lane's 32; fp8: 16 bytes; fp4: 8 bytes of codes in .xy
+  v4u b[NCH];   // bf16: bytes 16..31; fp4: the 16-block's E4M3 scale in .x
+  float s;      // fp8 row scale / fp4 tensor scale
+};
+
+// Load one row's per-lane weights (row < 0: an absent unit, zeros).
+template <uint32_t FMT, int NCH>
+__device__ __forceinline__ void wrow_load(__amdgpu_buffer_rsrc_t rw, const GMat& g, int row, WRow<FMT, NCH>& w) {
+  const int lane = lane_id();
+  const bool have = row >= 0;
+  const uint32_t r = have ? (uint32_t)row : 0u;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const uint32_t e0 = (uint32_t)min(c * 1024 + 16 * lane, (int)g.K - 16);
+    const uint32_t el = r * g.K + e0;
+    if (FMT == FMT_BF16) {
+      const uint32_t o = have ? g.codes + 2 * el : kOOB;
+      w.a[c] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rw, o, 0, 0));
+      w.b[c] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rw, o + 16, 0, 0));
+    } else if (FMT == FMT_FP8) {
+      w.a[c] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rw, have ? g.codes + el : kOOB, 0, 0));
+    } else {
+      const v2u c2 = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(rw, have ? g.codes + el / 2 : kOOB, 0, 0));
+      w.a[c].x = c2.x;
+      w.a[c].y = c2.y;
+      w.b[c].x = __builtin_amdgcn_raw_buffer_load_b8(rw, have ? g.scales + el / 16 : kOOB, 0, 0);
+    }
+  }
+  if (FMT == FMT_FP8)
+    w.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, have ? g.scales + 4 * r : kOOB, 0, 0));
+  if (FMT == FMT_FP4) {
+    uint32_t idx = 0;
+    if (g.ts_mode == 1) idx = r < g.ts_b0 ? 0u : (r < g.ts_b1 ? 1u : 2u);
+    else if (g.ts_mode == 2) idx = r & 1u;
+    w.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, have ? g.ts + 4 * idx : kOOB, 0, 0));
+  }
+}
+
+// The lane's part of one row's dot product with the activations xa.
+template <uint32_t FMT, int NCH>
+__device__ __forceinline__ float wrow_partial(const WRow<FMT, NCH>& w, const uint32_t (&xa)[NCH][8]) {
+  float a = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const uint32_t* xs = xa[c];
+    float ac = 0.f;
+    if (FMT == FMT_BF16) {
+      const uint32_t ws[8] = {w.a[c].x, w.a[c].y, w.a[c].z, w.a[c].w, w.b[c].x, w.b[c].y, w.b[c].z, w.b[c].w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ac = dot2(ws[j], xs[j], ac);
+    } else if (FMT == FMT_FP8) {
+      const uint32_t ws[4] = {w.a[c].x, w.a[c].y, w.a[c].z, w.a[c].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ac = dot2(e4m3x2_to_bf16x2<false>(ws[j]), xs[2 * j], ac);
+        ac = dot2(e4m3x2_to_bf16x2<true>(ws[j]), xs[2 * j + 1], ac);
+      }
+    } else {
+      const uint32_t ws[2] = {w.a[c].x, w.a[c].y};
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        ac = dot2(e2m1x2_to_bf16x2<0>(ws[j]), xs[4 * j + 0], ac);
+        ac = dot2(e2m1x2_to_bf16x2<1>(ws[j]), xs[4 * j + 1], ac);
+        ac = dot2(e2m1x2_to_bf16x2<2>(ws[j]), xs[4 * j + 2], ac);
+        ac = dot2(e2m1x2_to_bf16x2<3>(ws[j]), xs[4 * j + 3], ac);
+      }
+      ac *= e4m3_to_f32(w.b[c].x & 0xFFu);   // the lane's chunk is one 16-block
+    }
+    a += ac;
+  }
+  return a;
+}
+
+template <uint32_t FMT, int NCH>
+__device__ __forceinline__ float wrow_dot(const WRow<FMT, NCH>& w, const uint32_t (&xa)[NCH][8]) {
+  float a = wave_sum(wrow_partial(w, xa));
+  if (FMT != FMT_BF16) a *= w.s;
+  return a;
+}
+
+// The lane's activations (bf16 pairs) of a K-element input held in LDS:
+// pairs [512 c + 8 l, +8); lanes past K read zeros.
+template <int NCH>
+__device__ __forceinline__ void load_act(const uint32_t* src, int K, uint32_t (&xa)[NCH][8]) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int e0 = c * 1024 + 16 * lane;
+    const bool in = e0 < K;
+    const v4u* xp = reinterpret_cast<const v4u*>(src + min(e0, K - 16) / 2);
+    const v4u w0 = xp[0], w1 = xp[1];
+    xa[c][0] = in ? w0.x : 0u; xa[c][1] = in ? w0.y : 0u; xa[c][2] = in ? w0.z : 0u; xa[c][3] = in ? w0.w : 0u;
+    xa[c][4] = in ? w1.x : 0u; xa[c][5] = in ? w1.y : 0u; xa[c][6] = in ? w1.z : 0u; xa[c][7] = in ? w1.w : 0u;
+  }
+}
+
+// ------------------------------------------------------------- courier
+// A residual vector for LDS: pairs j = l + 64k of x (fp32 bits in lo/hi) go
+// to x_raw, and 1/sqrt(mean(x^2) + eps) to *r.  The compute waves apply the
+// gains and round to bf16 themselves, each for its own slice.  Pairs past
+// H/2 hold don't-care values and are masked.
+template <int MAXK>
+__device__ __forceinline__ void raw_to_lds(const Params& p, const uint32_t (&lo)[MAXK], const uint32_t (&hi)[MAXK],
+                                           int H, float* x_raw, float* r) {
+  const int lane = lane_id();
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < MAXK; ++k) {
+    const int j = lane + 64 * k;
+    if (j < H / 2) {
+      const float a = __uint_as_float(lo[k]), b = __uint_as_float(hi[k]);
+      ss = fmaf(a, a, ss);
+      ss = fmaf(b, b, ss);
+      *reinterpret_cast<v2u*>(x_raw + 2 * j) = v2u{lo[k], hi[k]};
+    }
+  }
+  const float rr = 1.0f / sqrtf(wave_sum(ss) / (float)H + p.eps);
+  if (lane == 0) *r = rr;
+}
+
+// Compute waves: the lane's slice of bf16(g * x * r) (RMSNorm with gains g,
+// bf16 pairs in gw) from the raw vector in LDS; lanes past K read zeros.
+template <int NCH>
+__device__ __forceinline__ void norm_act(const float* x_raw, float r, const uint32_t (&gw)[NCH][8], int K,
+                                         uint32_t (&xa)[NCH][8]) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int e0 = c * 1024 + 16 * lane;
+    const bool in = e0 < K;
+    const float4* xp = reinterpret_cast<const float4*>(x_raw + min(e0, K - 16));
+    float x[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = xp[q];
+      x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      xa[c][j] = in ? pack_bf16(bf16_lo(gw[c][j]) * (x[2 * j] * r), bf16_hi(gw[c][j]) * (x[2 * j + 1] * r)) : 0u;
+  }
+}
+
+// The lane's gains (bf16 pairs) for norm_act, from the weight arena (have =
+// false: kOOB, zeros).
+template <int NCH>
+__device__ __forceinline__ void gain_load(__amdgpu_buffer_rsrc_t rw, uint32_t off, int K, bool have,
+                                          uint32_t (&gw)[NCH][8]) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const uint32_t o = have ? off + 2u * (uint32_t)min(c * 1024 + 16 * lane, K - 16) : kOOB;
+    const v4u a = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rw, o, 0, 0));
+    const v4u b = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rw, o + 16, 0, 0));
+    gw[c][0] = a.x; gw[c][1] = a.y; gw[c][2] = a.z; gw[c][3] = a.w;
+    gw[c][4] = b.x; gw[c][5] = b.y; gw[c][6] = b.z; gw[c][7] = b.w;
+  }
+}
+
+template <int WF, int HD, int GS, int NH, int NQ, int NI>
+struct Kern {
+  static constexpr uint32_t F_LIN = WF == 0 ? FMT_BF16 : (WF == 1 ? FMT_FP8 : FMT_FP4);  // q, k, v, o, gate, up
+  static constexpr uint32_t F_8 = WF == 0 ? FMT_BF16 : FMT_FP8;                          // down, embed / LM head
+  static constexpr int KX = NH * 8;            // courier pairs per lane: residual vectors
+  static constexpr int KO = NQ * 4;            // attention output (bf16 pairs)
+  static constexpr int KH = NI * 4;            // SwiGLU output (bf16 pairs)
+  static constexpr int KA = ((GS + 2) * HD / 2 + 63) / 64;   // q/k/v of one KV head
+  static constexpr int KG = 16;                // argmax words of up to 1024 workgroups
+  static constexpr int DPL = HD / 8;           // attention: dims per lane (8 lanes per position)
+  static constexpr int WPL = DPL / 2;          // bf16 pairs per lane
+  static constexpr int PPW = 8;                // positions per wave per pass
+  static constexpr int PPP = PPW * kCW;        // positions per pass
+  static constexpr int MP = 7;                 // passes held in registers
+  static constexpr int NOUT = GS * HD;         // outputs of one attention workgroup
+  typedef Smem<HD, GS, NH, NQ, NI> S;
+
+  // ------------------------------------------------------------ courier
+  // The inputs this workgroup needs, in order, for every layer; then the
+  // final residual for the LM head; workgroup 0 then reduces the argmax.
+  static __device__ bool courier(const Params& p, S& s, const int* hdr, int token, int pos, uint32_t epoch,
+                                 int32_t* d_next) {
+    MK_GLOBAL const uint8_t* const W = p.w;
+    const int lane = lane_id();
+    const int H = p.H, L = p.L;
+    const int flags = hdr[S_FLAGS], att = hdr[S_ATT];
+    const __amdgpu_buffer_rsrc_t rs = xch_rsrc(p);
+    const Layer& L0 = p.layer0;
+    uint32_t seq = 0;
+    uint32_t lo[KX], hi[KX];
+    // ---- embedding -> the residual of layer 0
+    if (flags & 1) {
+      XR_PUT(s, 1, XR_START);
+#pragma unroll
+      for (int k = 0; k < KX; ++k) {
+        const int j = min(lane + 64 * k, H / 2 - 1);
+        const uint64_t e = (uint64_t)token * H + 2 * j;
+        if (F_8 == FMT_BF16) {
+          const uint32_t w = *GCAST(const uint32_t, W + p.embed.codes + 2 * e);
+          lo[k] = __float_as_uint(bf16_lo(w));
+          hi[k] = __float_as_uint(bf16_hi(w));
+        } else {
+          const uint32_t w = *GCAST(const uint16_t, W + p.embed.codes + e);
+          const float sc = GCAST(const float, W + p.embed.scales)[token];
+          lo[k] = __float_as_uint(e4m3_to_f32(w & 0xFFu) * sc);
+          hi[k] = __float_as_uint(e4m3_to_f32(w >> 8) * sc);
+        }
+      }
+      raw_to_lds<KX>(p, lo, hi, H, s.xd_raw, &s.r_xd);
+      hand_over(&s.seq, ++seq);
+      XR_PUT(s, 1, XR_HANDOFF);
+    }
+    for (int l = 0; l < L; ++l) {
+      const uint64_t loff = (uint64_t)l * p.layer_stride;
+      const int ph = 2 + 6 * l;
+      // ---- residual entering layer l (layer 0: the embedding above)
+      if ((flags & 1) && l > 0) {
+        XR_PUT(s, ph + 0, XR_START);
+        const uint32_t base = (uint32_t)(xvec(p, l - 1, V_XD) - p.xch);
+        if (!gather_pairs<KX>(p, rs, H / 2, make_tag(epoch, vec_id(l - 1, V_XD)), lo, hi,
+                              [=](int j) { return base + 2u * j; }))
+          return abort(s);
+        XR_PUT(s, ph + 0, XR_READY);
+        raw_to_lds<KX>(p, lo, hi, H, s.xd_raw, &s.r_xd);
+        hand_over(&s.seq, ++seq);
+        XR_PUT(s, ph + 0, XR_HANDOFF);
+      }
+      if (att < 0) lds_barrier();   // the compute waves' QKV stores are out; their weight burst follows
+      // ---- q, k, v of KV head `att`: q/k RMSNorm, RoPE, KV append
+      if (att >= 0) {
+        XR_PUT(s, ph + 1, XR_START);
+        if (!attention_input(p, s, l, att, pos, epoch, rs)) return abort(s);
+        hand_over(&s.seq, ++seq);
+        XR_PUT(s, ph + 1, XR_HANDOFF);
+        lds_barrier();   // every compute wave has written its partial outputs
+        lds_barrier();   // and merged them: the LDS arrays may be reused
+      }
+      // ---- attention output
+      if (flags & 2) {
+        XR_PUT(s, ph + 3, XR_START);
+        uint32_t ol[KO], oh[KO];
+        const uint32_t base = (uint32_t)(xvec(p, l, V_O) - p.xch);
+        if (!gather_pairs<KO>(p, rs, p.nq * HD / 4, make_tag(epoch, vec_id(l, V_O)), ol, oh,
+                              [=](int j) { return base + 2u * j; }))
+          return abort(s);
+        XR_PUT(s, ph + 3, XR_READY);
+#pragma unroll
+        for (int k = 0; k < KO; ++k) {
+          const int j = lane + 64 * k;
+          if (j < p.nq * HD / 4) *reinterpret_cast<v2u*>(s.o_in + 2 * j) = v2u{ol[k], oh[k]};
+        }
+        hand_over(&s.seq, ++seq);
+        XR_PUT(s, ph + 3, XR_HANDOFF);
+      }
+      // ---- residual after O
+      if (flags & 4) {
+        XR_PUT(s, ph + 4, XR_START);
+        const uint32_t base = (uint32_t)(xvec(p, l, V_XO) - p.xch);
+        if (!gather_pairs<KX>(p, rs, H / 2, make_tag(epoch, vec_id(l, V_XO)), lo, hi,
+                              [=](int j) { return base + 2u * j; }))
+          return abort(s);
+        XR_PUT(s, ph + 4, XR_READY);
+        raw_to_lds<KX>(p, lo, hi, H, s.xo_raw, &s.r_xo);
+        hand_over(&s.seq, ++seq);
+        XR_PUT(s, ph + 4, XR_HANDOFF);
+      }
+      // ---- SwiGLU output
+      if (flags & 8) {
+        XR_PUT(s, ph + 5, XR_START);
+        uint32_t hl[KH], hh[KH];
+        const uint32_t base = (uint32_t)(xvec(p, l, V_H) - p.xch);
+        if (!gather_pairs<KH>(p, rs, p.I / 4, make_tag(epoch, vec_id(l, V_H)), hl, hh,
+                              [=](int j) { return base + 2u * j; }))
+          return abort(s);
+        XR_PUT(s, ph + 5, XR_READY);
+#pragma unroll
+        for (int k = 0; k < KH; ++k) {
+          const int j = lane + 64 * k;
+          if (j < p.I / 4) *reinterpret_cast<v2u*>(s.h_in + 2 * j) = v2u{hl[k], hh[k]};
+        }
+        hand_over(&s.seq, ++seq);
+        XR_PUT(s, ph + 5, XR_HANDOFF);
+      }
+    }
+    // ---- final residual -> final RMSNorm (LM-head input)
+    const int ph_head = 2 + 6 * L;
+    {
+      XR_PUT(s, ph_head, XR_START);
+      const uint32_t base = (uint32_t)(xvec(p, L - 1, V_XD) - p.xch);
+      if (!gather_pairs<KX>(p, rs, H / 2, make_tag(epoch, vec_id(L - 1, V_XD)), lo, hi,
+                            [=](int j) { return base + 2u * j; }))
+        return abort(s);
+      XR_PUT(s, ph_head, XR_READY);
+      raw_to_lds<KX>(p, lo, hi, H, s.xd_raw, &s.r_xd);
+      hand_over(&s.seq, ++seq);
+      XR_PUT(s, ph_head, XR_HANDOFF);
+    }
+    lds_barrier();   // the compute waves' argmax candidates are in LDS
+    // ---- workgroup 0: reduce every workgroup's (value, index)
+    if (blockIdx.x == 0) {
+      XR_PUT(s, ph_head + 1, XR_START);
+      uint32_t vl[KG], il[KG];
+      const uint32_t base = (uint32_t)p.x.arg;
+      if (!gather_pairs<KG>(p, rs, p.grid, make_tag(epoch, vec_id(L, 0)), vl, il,
+                            [=](int j) { return base + 2u * j; }))
+        return false;
+      XR_PUT(s, ph_head + 1, XR_READY);
+      float best = -INFINITY;
+      int bidx = 0x7FFFFFFF;
+#pragma unroll
+      for (int k = 0; k < KG; ++k) {
+        const int j = lane + 64 * k;
+        if (j < p.grid) {
+          const float v = __uint_as_float(vl[k]);
+          const int i = (int)il[k];
+          if (v > best || (v == best && i < bidx)) {
+            best = v;
+            bidx = i;
+          }
+        }
+      }
+      const float m = wave_max(best);
+      int mi = best == m ? bidx : 0x7FFFFFFF;   // smallest index among the lanes holding the maximum
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) mi = min(mi, __shfl_xor(mi, o));
+      if (lane == 0) *d_next = mi;
+      XR_PUT(s, ph_head + 1, XR_HANDOFF);
+    }
+    return true;
+  }
+
+  static __device__ bool abort(S& s) {
+    hand_over(&s.seq, kAbort);
+    return false;
+  }
+
+  // Gather q (GS heads), k and v of KV head g, apply q/k RMSNorm and RoPE,
+  // append bf16 k and v to the cache at `pos`, and leave q (pre-scaled so
+  // that scores come out in log2 units), k and v in LDS.
+  static __device__ bool attention_input(const Params& p, S& s, int l, int g, int pos, uint32_t epoch,
+                                         __amdgpu_buffer_rsrc_t rs) {
+    MK_GLOBAL const uint8_t* const W = p.w;
+    const int lane = lane_id();
+    const int nq = p.nq, nkv = p.nkv;
+    const uint64_t loff = (uint64_t)l * p.layer_stride;
+    const Layer& L0 = p.layer0;
+    // gains and this position's RoPE pair (lane i < HD/2 owns pair i), loaded ahead of the gather
+    const int li = min(lane, HD / 2 - 1);
+    MK_GLOBAL const uint16_t* gq = GCAST(const uint16_t, W + L0.q_norm + loff);
+    MK_GLOBAL const uint16_t* gk = GCAST(const uint16_t, W + L0.k_norm + loff);
+    const float gq_lo = bf16_to_f32(gq[li]), gq_hi = bf16_to_f32(gq[li + HD / 2]);
+    const float gk_lo = bf16_to_f32(gk[li]), gk_hi = bf16_to_f32(gk[li + HD / 2]);
+    MK_GLOBAL const float* cs = p.rope + ((size_t)pos * (HD / 2) + li) * 2;
+    const float rc = cs[0], rsn = cs[1];
+    const uint32_t base = (uint32_t)(xvec(p, l, V_QKV) - p.xch);
+    const uint32_t qo = base + (uint32_t)(g * NOUT), ko = base + (uint32_t)((nq + g) * HD),
+                   vo = base + (uint32_t)((nq + nkv + g) * HD);
+    uint32_t lo[KA], hi[KA];
+    if (!gather_pairs<KA>(p, rs, (GS + 2) * HD / 2, make_tag(epoch, vec_id(l, V_QKV)), lo, hi, [=](int j) {
+          const int w = 2 * j;
+          return w < NOUT ? qo + w : (w < NOUT + HD ? ko + (w - NOUT) : vo + (w - NOUT - HD));
+        }))
+      return false;
+    XR_PUT(s, 2 + 6 * l + 1, XR_READY);
+#pragma unroll
+    for (int k = 0; k < KA; ++k) {
+      const int j = lane + 64 * k;
+      if (j < (GS + 2) * HD / 2) *reinterpret_cast<v2u*>(s.qraw + 2 * j) = v2u{lo[k], hi[k]};
+    }
+    lds_drain();
+    const bool pl = lane < HD / 2;
+    const float kq = 1.4426950408889634f / sqrtf((float)HD);
+#pragma unroll
+    for (int h = 0; h <= GS; ++h) {
+      const float* src = s.qraw + h * HD;
+      const float xa = pl ? src[li] : 0.f, xb = pl ? src[li + HD / 2] : 0.f;
+      const float r = 1.0f / sqrtf(wave_sum(xa * xa + xb * xb) / (float)HD + p.eps);
+      const float glo = h < GS ? gq_lo : gk_lo, ghi = h < GS ? gq_hi : gk_hi;
+      const float a = glo * (xa * r), b = ghi * (xb * r);
+      const float ra = a * rc - b * rsn, rb = b * rc + a * rsn;
+      if (pl) {
+        if (h < GS) {
+          s.q[h * HD + li] = ra * kq;
+          s.q[h * HD + li + HD / 2] = rb * kq;
+        } else {
+          s.kf[li] = ra;
+          s.kf[li + HD / 2] = rb;
+        }
+      }
+    }
+    lds_drain();
+    if (lane < HD / 2) {
+      const uint32_t kw = pack_bf16(s.kf[2 * lane], s.kf[2 * lane + 1]);
+      const float* vf = s.qraw + (GS + 1) * HD;
+      const uint32_t vw = pack_bf16(vf[2 * lane], vf[2 * lane + 1]);
+      s.kp[lane] = kw;
+      s.vp[lane] = vw;
+      const size_t plane = (size_t)p.max_ctx * HD;
+      MK_GLOBAL uint32_t* kc = GCAST(uint32_t, p.kv + ((size_t)(l * 2 + 0) * nkv + g) * plane);
+      MK_GLOBAL uint32_t* vc = GCAST(uint32_t, p.kv + ((size_t)(l * 2 + 1) * nkv + g) * plane);
+      kc[(size_t)pos * (HD / 2) + lane] = kw;
+      vc[(size_t)pos * (HD / 2) + lane] = vw;
+    }
+    lds_drain();
+    // scores of this position (its k as the cache holds it, bf16)
+    {
+      const uint32_t kw = lane < HD / 2 ? s.kp[lane] : 0u;
+#pragma unroll
+      for (int h = 0; h < GS; ++h) {
+        const float d = lane < HD / 2 ? s.q[h * HD + 2 * lane] * bf16_lo(kw) + s.q[h * HD + 2 * lane + 1] * bf16_hi(kw)
+                                      : 0.f;
+        const float sc = wave_sum(d);
+        if (lane == 0) s.sp[h] = sc;
+      }
+    }
+    return true;
+  }
+
+  // --------------------------------------------------- GEMV compute waves
+  // Every branch below depends on wave-uniform values only and holds no
+  // global load, and a wave's stores go through buffer offsets (kOOB drops
+  // them) instead of branches, so all paths through a layer issue the same
+  // vector-memory operations and the compiler's vmcnt waits for each
+  // matrix's rows count exactly the loads issued after them.  An abort is
+  // not an early exit (that would add a path to the loop latch with fewer
+  // loads and make every wait conservative): the remaining phases run on
+  // whatever LDS holds and store nothing.
+  //
+  // Weight loads go out in one burst per layer, right after the wave's QKV
+  // rows are published: the O, gate/up and down rows of this layer and the
+  // QKV rows of the next.  While the attention workgroups work, nothing is
+  // exchanged, so the burst drains then; the later exchanges of the layer
+  // travel through an idle memory system.  An exchange word that waits
+  // behind a full HBM queue takes several microseconds instead of well
+  // under one.
+  struct GemvW {
+    WRow<F_LIN, NH> q[kMaxQKV];
+    WRow<F_LIN, NQ> o[kMaxO];
+    WRow<F_LIN, NH> gu[kMaxGU][4];
+    WRow<F_8, NI> d[kMaxD];
+    uint32_t gin[NH][8];     // input-norm gains of the QKV rows' layer (lane slice)
+    uint32_t gpost[NH][8];   // post-attention-norm gains (gate/up input)
+  };
+
+  static __device__ __forceinline__ void load_layer_qkv(const Params& p, __amdgpu_buffer_rsrc_t rw, const int* u,
+                                                        int l, GemvW& w) {
+    const uint64_t lo = (uint64_t)l * p.layer_stride;
+    const GMat g = gmat(p.layer0.qkv, lo);
+#pragma unroll
+    for (int k = 0; k < kMaxQKV; ++k) wrow_load(rw, g, u[S_QKV + k], w.q[k]);
+    gain_load<NH>(rw, (uint32_t)(p.layer0.in_norm + lo), p.H, u[S_QKV] >= 0, w.gin);
+  }
+  static __device__ __forceinline__ void load_layer_rest(const Params& p, __amdgpu_buffer_rsrc_t rw, const int* u,
+                                                         int l, GemvW& w) {
+    const uint64_t lo = (uint64_t)l * p.layer_stride;
+    const GMat go = gmat(p.layer0.o, lo);
+#pragma unroll
+    for (int k = 0; k < kMaxO; ++k) wrow_load(rw, go, u[S_O + k], w.o[k]);
+    const GMat gg = gmat(p.layer0.gu, lo);
+#pragma unroll
+    for (int k = 0; k < kMaxGU; ++k)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) wrow_load(rw, gg, u[S_GU + k] >= 0 ? 4 * u[S_GU + k] + r : -1, w.gu[k][r]);
+    gain_load<NH>(rw, (uint32_t)(p.layer0.post_norm + lo), p.H, u[S_GU] >= 0, w.gpost);
+    const GMat gd = gmat(p.layer0.down, lo);
+#pragma unroll
+    for (int k = 0; k < kMaxD; ++k) wrow_load(rw, gd, u[S_D + k], w.d[k]);
+  }
+
+  // One layer of a GEMV compute wave.  NEXT: the burst also loads the next
+  // layer's QKV rows.
+  template <bool NEXT>
+  static __device__ __forceinline__ bool gemv_layer(const Params& p, S& s, int l, const int* hdr, const int* u,
+                                                    GemvW& w, uint32_t epoch, __amdgpu_buffer_rsrc_t rw,
+                                                    __amdgpu_buffer_rsrc_t rx, bool ok) {
+    const bool l0 = lane_id() == 0;
+    const int H = p.H, nin = hdr[S_NIN];
+    const uint32_t sbase = (uint32_t)(l * nin) + 1u;
+    const int ph = 2 + 6 * l;
+    // ---- QKV
+    {
+      if (u[S_QKV] >= 0) {
+        ok = ok && wait_seq(p, &s.seq, sbase + hdr[S_IXD]);
+        XR_MIN(s, ph + 0, XR_SEEN);
+      }
+      uint32_t xa[NH][8];
+      norm_act<NH>(s.xd_raw, s.r_xd, w.gin, H, xa);
+#ifdef MK_XRAY
+      {  // X-ray: when this wave's QKV rows are all in registers
+        uint32_t z = 0;
+#pragma unroll
+        for (int k = 0; k < kMaxQKV; ++k) z ^= w.q[k].a[NH - 1].w ^ w.q[k].b[NH - 1].w;
+        asm volatile("" ::"v"(z));
+        if (u[S_QKV] >= 0) XR_MAX(s, ph + 0, XR_M0);
+      }
+#endif
+      const uint32_t base = xword(p, l, V_QKV), tag = make_tag(epoch, vec_id(l, V_QKV));
+#pragma unroll
+      for (int k = 0; k < kMaxQKV; ++k) {
+        const int r = u[S_QKV + k];
+        const float v = wrow_dot(w.q[k], xa);
+        st_xword(rx, ok && r >= 0 && l0 ? 8u * (base + r) : kOOB, __float_as_uint(v), tag);
+      }
+      if (u[S_QKV] >= 0) XR_MAX(s, ph + 0, XR_DONE);
+    }
+    // ---- the layer's weight burst, once every wave of the workgroup has
+    // issued its QKV stores (the courier joins this barrier after handing
+    // over the layer's input): a burst queued ahead of another wave's stores
+    // would delay the attention workgroups' input by the burst's issue time
+    lds_barrier();
+    load_layer_rest(p, rw, u, l, w);
+    if (NEXT) load_layer_qkv(p, rw, u, l + 1, w);
+    // ---- O-projection + residual
+    {
+      if (u[S_O] >= 0) {
+        ok = ok && wait_seq(p, &s.seq, sbase + hdr[S_IO]);
+        XR_MIN(s, ph + 3, XR_SEEN);
+      }
+      uint32_t xa[NQ][8];
+      load_act<NQ>(s.o_in, p.nq * HD, xa);
+      const uint32_t base = xword(p, l, V_XO), tag = make_tag(epoch, vec_id(l, V_XO));
+#pragma unroll
+      for (int k = 0; k < kMaxO; ++k) {
+        const int r = u[S_O + k];
+        const float v = s.xd_raw[max(r, 0)] + wrow_dot(w.o[k], xa);
+        st_xword(rx, ok && r >= 0 && l0 ? 8u * (base + r) : kOOB, __float_as_uint(v), tag);
+      }
+      if (u[S_O] >= 0) XR_MAX(s, ph + 3, XR_DONE);
+    }
+    // ---- gate/up + SwiGLU: a unit is the four rows behind one output word
+    {
+      if (u[S_GU] >= 0) {
+        ok = ok && wait_seq(p, &s.seq, sbase + hdr[S_IXO]);
+        XR_MIN(s, ph + 4, XR_SEEN);
+      }
+      uint32_t xa[NH][8];
+      norm_act<NH>(s.xo_raw, s.r_xo, w.gpost, H, xa);
+      const uint32_t base = xword(p, l, V_H), tag = make_tag(epoch, vec_id(l, V_H));
+#pragma unroll
+      for (int k = 0; k < kMaxGU; ++k) {
+        const int t = u[S_GU + k];
+        float y[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[r] = wrow_partial(w.gu[k][r], xa);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          y[r] = wave_sum(y[r]);
+          if (F_LIN != FMT_BF16) y[r] *= w.gu[k][r].s;
+        }
+        const float h0 = silu(y[0]) * y[1], h1 = silu(y[2]) * y[3];
+        st_xword(rx, ok && t >= 0 && l0 ? 8u * (base + t) : kOOB, pack_bf16(h0, h1), tag);
+      }
+      if (u[S_GU] >= 0) XR_MAX(s, ph + 4, XR_DONE);
+    }
+    // ---- down + residual
+    {
+      if (u[S_D] >= 0) {
+        ok = ok && wait_seq(p, &s.seq, sbase + hdr[S_IH]);
+        XR_MIN(s, ph + 5, XR_SEEN);
+      }
+      uint32_t xa[NI][8];
+      load_act<NI>(s.h_in, p.I, xa);
+      const uint32_t base = xword(p, l, V_XD), tag = make_tag(epoch, vec_id(l, V_XD));
+#pragma unroll
+      for (int k = 0; k < kMaxD; ++k) {
+        const int r = u[S_D + k];
+        const float v = s.xo_raw[max(r, 0)] + wrow_dot(w.d[k], xa);
+        st_xword(rx, ok && r >= 0 && l0 ? 8u * (base + r) : kOOB, __float_as_uint(v), tag);
+      }
+      if (u[S_D] >= 0) XR_MAX(s, ph + 5, XR_DONE);
+    }
+    return ok;
+  }
+
+  static __device__ __forceinline__ bool gemv_waves(const Params& p, S& s, const int* hdr, const int* u,
+                                                    uint32_t epoch, __amdgpu_buffer_rsrc_t rw,
+                                                    __amdgpu_buffer_rsrc_t rx) {
+    GemvW w;
+    load_layer_qkv(p, rw, u, 0, w);
+    bool ok = true;
+    for (int l = 0; l + 1 < p.L; ++l) ok = gemv_layer<true>(p, s, l, hdr, u, w, epoch, rw, rx, ok);
+    return gemv_layer<false>(p, s, p.L - 1, hdr, u, w, epoch, rw, rx, ok);
+  }
+
+  // ---------------------------------------------- attention compute waves
+  // Wave cw takes positions 8 cw .. 8 cw + 7 of every 56-position pass, one
+  // position per 8 lanes (lane c of the 8 holds dims [c*HD/8, +HD/8)), so a
+  // wave reads eight consecutive cache rows as one coalesced run.  The first
+  // MP passes are loaded a layer ahead; longer contexts stream the rest.
+  struct KVRegs {
+    v4u k[MP][WPL / 4];
+    v4u v[MP][WPL / 4];
+  };
+
+  static __device__ __forceinline__ void kv_load_pass(const Params& p, int l, int g, int pass, int pos, int cw,
+                                                      v4u (&kk)[WPL / 4], v4u (&vv)[WPL / 4]) {
+    const int lane = lane_id();
+    const int j = pass * PPP + cw * PPW + (lane >> 3);
+    // positions >= pos are not (yet) in the cache: read a written row instead (weight 0 at use)
+    const int jc = max(min(j, pos - 1), 0);
+    const size_t plane = (size_t)p.max_ctx * HD;
+    MK_GLOBAL const v4u* kp = GCAST(const v4u, p.kv + ((size_t)(l * 2 + 0) * p.nkv + g) * plane +
+                                                   (size_t)jc * HD + (lane & 7) * DPL);
+    MK_GLOBAL const v4u* vp = GCAST(const v4u, p.kv + ((size_t)(l * 2 + 1) * p.nkv + g) * plane +
+                                                   (size_t)jc * HD + (lane & 7) * DPL);
+#pragma unroll
+    for (int i = 0; i < WPL / 4; ++i) {
+      kk[i] = kp[i];
+      vv[i] = vp[i];
+    }
+  }
+  static __device__ __forceinline__ void kv_prefetch(const Params& p, int l, int g, int pos, int cw, KVRegs& kv) {
+#pragma unroll
+    for (int t = 0; t < MP; ++t) kv_load_pass(p, l, g, t, pos, cw, kv.k[t], kv.v[t]);
+  }
+
+  // Scores of one pass (both q heads) for the lanes' position j; -inf past pos.
+  static __device__ __forceinline__ void att_scores(const S& s, const v4u (&kk)[WPL / 4], bool act, float (&sc)[GS]) {
+    const int c = lane_id() & 7;
+    asm volatile("" ::: "memory");   // re-read q from LDS for every pass (keeps it out of registers)
+#pragma unroll
+    for (int h = 0; h < GS; ++h) {
+      const float4* qp = reinterpret_cast<const float4*>(s.q + h * HD + c * DPL);
+      float d = 0.f;
+#pragma unroll
+      for (int i = 0; i < WPL / 4; ++i) {
+        const float4 q0 = qp[2 * i], q1 = qp[2 * i + 1];
+        const v4u kw = kk[i];
+        d = fmaf(q0.x, bf16_lo(kw.x), d);
+        d = fmaf(q0.y, bf16_hi(kw.x), d);
+        d = fmaf(q0.z, bf16_lo(kw.y), d);
+        d = fmaf(q0.w, bf16_hi(kw.y), d);
+        d = fmaf(q1.x, bf16_lo(kw.z), d);
+        d = fmaf(q1.y, bf16_hi(kw.z), d);
+        d = fmaf(q1.z, bf16_lo(kw.w), d);
+        d = fmaf(q1.w, bf16_hi(kw.w), d);
+      }
+      d = sum8(d);
+      sc[h] = act ? d : -INFINITY;
+    }
+  }
+  // acc += p * v for one pass.  Lanes past `pos` carry p = 0 and a row the
+  // cache holds (finite), so they add nothing.
+  static __device__ __forceinline__ void att_accum(const v4u (&vv)[WPL / 4], const float (&pr)[GS],
+                                                   float (&acc)[GS][DPL]) {
+#pragma unroll
+    for (int i = 0; i < WPL / 4; ++i) {
+      const uint32_t w4[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int h = 0; h < GS; ++h) {
+          acc[h][8 * i + 2 * q] = fmaf(pr[h], bf16_lo(w4[q]), acc[h][8 * i + 2 * q]);
+          acc[h][8 * i + 2 * q + 1] = fmaf(pr[h], bf16_hi(w4[q]), acc[h][8 * i + 2 * q + 1]);
+        }
+    }
+  }
+  // Online softmax step: fold a new maximum candidate into (m, lsum, acc).
+  static __device__ __forceinline__ void att_rescale(float bm, float& m, float& lsum, float (&acc)[DPL]) {
+    const float mn = fmaxf(m, wave_max(bm));
+    const float scale = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+    m = mn;
+    lsum *= scale;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[e] *= scale;
+  }
+
+  // Positions 0..pos-1 come from the cache (registers); position `pos`
+  // itself (its k and v were produced in this step) enters at the merge.
+  template <bool NEXT>
+  static __device__ __forceinline__ bool att_layer(const Params& p, S& s, int l, int g, int pos, int cw, KVRegs& kv,
+                                                   uint32_t epoch, __amdgpu_buffer_rsrc_t rx, bool ok) {
+    const int lane = lane_id();
+    const int c = lane & 7;
+    const int ph = 2 + 6 * l;
+    ok = ok && wait_seq(p, &s.seq, (uint32_t)l + 1u);
+    XR_MIN(s, ph + 1, XR_SEEN);
+    float acc[GS][DPL], m[GS], lsum[GS];
+#pragma unroll
+    for (int h = 0; h < GS; ++h) {
+      m[h] = -INFINITY;
+      lsum[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
+    }
+    const int npass = (pos + PPP - 1) / PPP;   // passes covering the cached positions 0..pos-1
+#ifdef MK_XRAY
+    {  // X-ray: when the prefetched rows are all in registers
+      uint32_t z = 0;
+#pragma unroll
+      for (int t = 0; t < MP; ++t) z ^= kv.k[t][0].x ^ kv.v[t][WPL / 4 - 1].w;
+      asm volatile("" ::"v"(z));   // wait until they have arrived
+      XR_MAX(s, ph + 1, XR_M0 + 1);
+    }
+#endif
+    // ---- the passes held in registers (loaded a layer ahead)
+    if (npass > 0) {
+      float sc[MP][GS];
+#pragma unroll
+      for (int t = 0; t < MP; ++t) {
+#pragma unroll
+        for (int h = 0; h < GS; ++h) sc[t][h] = -INFINITY;
+        if (t < npass) {
+          const int j = t * PPP + cw * PPW + (lane >> 3);
+          att_scores(s, kv.k[t], j < pos, sc[t]);
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < GS; ++h) {
+        float bm = sc[0][h];
+#pragma unroll
+        for (int t = 1; t < MP; ++t) bm = fmaxf(bm, sc[t][h]);
+        att_rescale(bm, m[h], lsum[h], acc[h]);
+      }
+#pragma unroll
+      for (int t = 0; t < MP; ++t) {
+        if (t < npass) {
+          float pr[GS];
+#pragma unroll
+          for (int h = 0; h < GS; ++h) {
+            // sc = -inf past pos (and m may still be -inf in a wave with no position yet)
+            pr[h] = sc[t][h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[t][h] - m[h]);
+            lsum[h] += pr[h];
+          }
+          att_accum(kv.v[t], pr, acc);
+        }
+      }
+    }
+    // ---- longer contexts: the remaining passes stream through two buffers
+    if (npass > MP) {
+      v4u k0[WPL / 4], v0[WPL / 4], k1[WPL / 4], v1[WPL / 4];
+      kv_load_pass(p, l, g, MP, pos, cw, k0, v0);
+      for (int t = MP; t < npass; t += 2) {
+        kv_load_pass(p, l, g, t + 1, pos, cw, k1, v1);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          v4u(&kk)[WPL / 4] = half ? k1 : k0;
+          v4u(&vv)[WPL / 4] = half ? v1 : v0;
+          const int j = (t + half) * PPP + cw * PPW + (lane >> 3);
+          float sc[GS], pr[GS];
+          att_scores(s, kk, j < pos, sc);
+#pragma unroll
+          for (int h = 0; h < GS; ++h) {
+            att_rescale(sc[h], m[h], lsum[h], acc[h]);
+            pr[h] = sc[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[h] - m[h]);
+            lsum[h] += pr[h];
+          }
+          att_accum(vv, pr, acc);
+          if (half == 0) kv_load_pass(p, l, g, t + 2, pos, cw, k0, v0);
+        }
+      }
+    }
+    // this wave's outputs: the two 8-lane halves of each 16-lane row with one
+    // DPP step, then the four rows go to LDS
+#pragma unroll
+    for (int h = 0; h < GS; ++h)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[h][e] += dpp<0x128>(acc[h][e]);
+    if ((lane & 8) == 0) {
+#pragma unroll
+      for (int h = 0; h < GS; ++h)
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) s.part[cw][lane >> 4][h * HD + c * DPL + e] = acc[h][e];
+    }
+#pragma unroll
+    for (int h = 0; h < GS; ++h) {
+      const float lt = wave_sum(c == 0 ? lsum[h] : 0.f);
+      if (lane == 0) {
+        s.wm[cw][h] = m[h];
+        s.wl[cw][h] = lt;
+      }
+    }
+    XR_MAX(s, ph + 1, XR_M0);
+    lds_barrier();
+    // merge the seven waves (fixed order); thread t < NOUT owns output t
+    const int t = cw * 64 + lane;
+    const int tc = min(t, NOUT - 1);
+    const int h = tc / HD;
+    const float sp = s.sp[h];
+    float M = sp;
+#pragma unroll
+    for (int w = 0; w < kCW; ++w) M = fmaxf(M, s.wm[w][h]);
+    const uint32_t vpw = s.vp[(tc % HD) / 2];
+    const float ec = __builtin_amdgcn_exp2f(sp - M);
+    float Lt = ec, O = ec * ((tc & 1) ? bf16_hi(vpw) : bf16_lo(vpw));
+#pragma unroll
+    for (int w = 0; w < kCW; ++w) {
+      const float e = s.wm[w][h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s.wm[w][h] - M);
+      Lt = fmaf(s.wl[w][h], e, Lt);
+      O = fmaf((s.part[w][0][tc] + s.part[w][1][tc]) + (s.part[w][2][tc] + s.part[w][3][tc]), e, O);
+    }
+    const float o = O / Lt;
+    const float o1 = dpp<0xB1>(o);   // the neighbouring output (t ^ 1)
+    st_xword(rx, ok && t < NOUT && (t & 1) == 0 ? 8u * (xword(p, l, V_O) + (g * NOUT + t) / 2) : kOOB,
+             pack_bf16(o, o1), make_tag(epoch, vec_id(l, V_O)));
+    XR_MAX(s, ph + 1, XR_DONE);
+    lds_barrier();
+    if (NEXT) kv_prefetch(p, l + 1, g, pos, cw, kv);
+    return ok;
+  }
+
+  static __device__ __forceinline__ bool att_waves(const Params& p, S& s, int g, int pos, int cw, uint32_t epoch,
+                                                   __amdgpu_buffer_rsrc_t rx) {
+    KVRegs kv;
+    kv_prefetch(p, 0, g, pos, cw, kv);
+    bool ok = true;
+    for (int l = 0; l + 1 < p.L; ++l) ok = att_layer<true>(p, s, l, g, pos, cw, kv, epoch, rx, ok);
+    return att_layer<false>(p, s, p.L - 1, g, pos, cw, kv, epoch, rx, ok);
+  }
+
+  // ------------------------------------------------------------ LM head
+  // Rows [va, vb) of this workgroup; compute wave cw takes va + cw + 7k, in
+  // double-buffered batches of UB rows.  Returns the wave's best (value,
+  // smallest index).  Rows past the wave's last are clamped to it and their
+  // results dropped (no branch around a load or a store).
+  static constexpr int UBH = F_8 == FMT_BF16 ? 4 : 8;
+  static __device__ __forceinline__ bool lm_head(const Params& p, S& s, const int* hdr, int cw, float* d_logits,
+                                                 __amdgpu_buffer_rsrc_t rw, bool ok, float& best, int& bidx) {
+    const bool l0 = lane_id() == 0;
+    const int G = p.grid, wg = blockIdx.x;
+    const int va = (int)((int64_t)p.V * wg / G), vb = (int)((int64_t)p.V * (wg + 1) / G);
+    const int n = vb > va + cw ? (vb - va - cw + kCW - 1) / kCW : 0;   // rows of this wave
+    const GMat g = gmat(p.embed, 0);
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(d_logits, d_logits ? 4u * (uint32_t)p.V : 0u);
+    auto row = [&](int k) { return n > 0 ? va + cw + kCW * min(k, n - 1) : -1; };
+    WRow<F_8, NH> B0[UBH], B1[UBH];
+#pragma unroll
+    for (int b = 0; b < UBH; ++b) wrow_load(rw, g, row(b), B0[b]);
+    asm volatile("" ::: "memory");
+    uint32_t gf[NH][8];
+    gain_load<NH>(rw, (uint32_t)p.final_norm, p.H, true, gf);
+    ok = ok && wait_seq(p, &s.seq, (uint32_t)(p.L * hdr[S_NIN]) + 1u);
+    XR_MIN(s, 2 + 6 * p.L, XR_SEEN);
+    uint32_t xa[NH][8];
+    norm_act<NH>(s.xd_raw, s.r_xd, gf, p.H, xa);
+    best = -INFINITY;
+    bidx = 0x7FFFFFFF;
+    auto use = [&](const WRow<F_8, NH>(&B)[UBH], int k0) {
+#pragma unroll
+      for (int b = 0; b < UBH; ++b) {
+        const float v = wrow_dot(B[b], xa);
+        const bool in = k0 + b < n;
+        const int r = va + cw + kCW * (k0 + b);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rl, in && l0 ? 4u * (uint32_t)r : kOOB, 0, 0);
+        const bool take = in && v > best;   // a wave's rows ascend, so the first maximum is kept
+        best = take ? v : best;
+        bidx = take ? r : bidx;
+      }
+    };
+    // the scheduling barriers keep each next batch's loads ahead of the
+    // current batch's arithmetic
+    for (int k0 = 0; k0 < n; k0 += 2 * UBH) {
+#pragma unroll
+      for (int b = 0; b < UBH; ++b) wrow_load(rw, g, row(k0 + UBH + b), B1[b]);
+      __builtin_amdgcn_sched_barrier(0);
+      use(B0, k0);
+#pragma unroll
+      for (int b = 0; b < UBH; ++b) wrow_load(rw, g, row(k0 + 2 * UBH + b), B0[b]);
+      __builtin_amdgcn_sched_barrier(0);
+      use(B1, k0 + UBH);
+    }
+    XR_MAX(s, 2 + 6 * p.L, XR_DONE);
+    return ok;
+  }
+
+  // -------------------------------------------------------------- kernel
+  static __device__ void run(const Params& p, S& s, const int32_t* d_token, int pos, uint32_t epoch, int32_t* d_next,
+                             float* d_logits) {
+    const int wave = wave_id(), lane = lane_id();
+    const int wg = blockIdx.x;
+    if (threadIdx.x == 0) s.seq = 0;
+    XR_INIT(s);
+    const int token = *d_token;
+    if (token < 0 || token >= p.V) {
+      if (wg == 0 && threadIdx.x == 0) {
+        raise_error(p, ERR_TOKEN);
+        *d_next = -1;
+      }
+      return;
+    }
+    if (wg == 0 && threadIdx.x == 0) *d_next = -1;  // overwritten on success
+    // this workgroup's row of the work table, as wave-uniform values
+    MK_GLOBAL const int* tab = GCAST(const int, p.xch + p.x.sched) + (size_t)wg * kSchedInts * kWaves;
+    int hdr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) hdr[i] = __builtin_amdgcn_readfirstlane(tab[i]);
+    lds_barrier();   // seq and the X-ray records are initialised
+    const __amdgpu_buffer_rsrc_t rx = xch_rsrc(p);
+    if (wave == 0) {
+      if (!courier(p, s, hdr, token, pos, epoch, d_next)) return;
+    } else {
+      const int cw = wave - 1;
+      int u[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) u[i] = __builtin_amdgcn_readfirstlane(tab[kSchedInts * wave + i]);
+      const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w, p.w_bytes);
+      bool ok = hdr[S_ATT] >= 0 ? att_waves(p, s, hdr[S_ATT], pos, cw, epoch, rx)
+                                : gemv_waves(p, s, hdr, u, epoch, rw, rx);
+      float best;
+      int bidx;
+      ok = lm_head(p, s, hdr, cw, d_logits, rw, ok, best, bidx);
+      if (lane == 0) {
+        s.best[cw] = best;
+        s.bidx[cw] = bidx;
+      }
+      lds_barrier();
+      if (cw == 0) {
+        // workgroup argmax: largest value, then smallest index
+        float b = s.best[0];
+        int bi = s.bidx[0];
+#pragma unroll
+        for (int w = 1; w < kCW; ++w)
+          if (s.best[w] > b || (s.best[w] == b && s.bidx[w] < bi)) {
+            b = s.best[w];
+            bi = s.bidx[w];
+          }
+        const uint32_t tag = make_tag(epoch, vec_id(p.L, 0));
+        const uint32_t off = 8u * (uint32_t)(p.x.arg + 2ull * wg);
+        st_xword(rx, ok && lane == 0 ? off : kOOB, __float_as_uint(b), tag);
+        st_xword(rx, ok && lane == 0 ? off + 8u : kOOB, (uint32_t)bi, tag);
+      }
+    }
+#ifdef MK_XRAY
+    __syncthreads();
+    XR_DUMP(s, p);
+#endif
+  }
+};
+
+// One instantiation per (weight format, head_dim, q heads per KV head,
+// 1024-chunks of hidden, of n_q_heads*head_dim and of intermediate): the
+// formats, the attention shape and every per-lane register array size are
+// compile-time constants.
+template <int WF, int HD, int GS, int NH, int NQ, int NI>
+__global__ __launch_bounds__(kThreads, 1) void decode_kernel(const Params* __restrict__ pp, const int32_t* d_token,
+                                                             int pos, uint32_t epoch, int32_t* d_next,
+                                                             float* d_logits) {
+  __shared__ Smem<HD, GS, NH, NQ, NI> s;
+  Kern<WF, HD, GS, NH, NQ, NI>::run(*pp, s, d_token, pos, epoch, d_next, d_logits);
+}
+
+// ------------------------------------------------------- launch wrappers
+// Compiled shape classes: (head_dim, q heads per KV head, 1024-chunks of
+// hidden, of n_q_heads*head_dim, of intermediate); three weight formats each.
+// The tiny test decoder and the Qwen3-0.6B shape.
+#define MK_SHAPES(X) X(64, 2, 1, 1, 1) X(128, 2, 1, 2, 3)
+
+static int cdiv1024(int n) { return (n + 1023) / 1024; }
+
+bool decode_shape_supported(int hd, int gs, int hidden, int qdim, int inter) {
+  const int nh = cdiv1024(hidden), nqd = cdiv1024(qdim), ni = cdiv1024(inter);
+#define MK_CASE(H_, G_, A_, B_, C_) if (hd == H_ && gs == G_ && nh == A_ && nqd == B_ && ni == C_) return true;
+  MK_SHAPES(MK_CASE)
+#undef MK_CASE
+  return false;
+}
+
+hipError_t launch_decode(const Params* d_params, int wfmt, int hd, int gs, int hidden, int qdim, int inter, int grid,
+                         const int32_t* d_token, int pos, uint32_t epoch, int32_t* d_next, float* d_logits,
+                         hipStream_t s) {
+  const void* fn = nullptr;
+  const int nh = cdiv1024(hidden), nqd = cdiv1024(qdim), ni = cdiv1024(inter);
+#define MK_CASE(H_, G_, A_, B_, C_)                                                                             \
+  if (hd == H_ && gs == G_ && nh == A_ && nqd == B_ && ni == C_) {                                              \
+    fn = wfmt == 0 ? reinterpret_cast<const void*>(decode_kernel<0, H_, G_, A_, B_, C_>)                        \
+                   : (wfmt == 1 ? reinterpret_cast<const void*>(decode_kernel<1, H_, G_, A_, B_, C_>)           \
+                                : reinterpret_cast<const void*>(decode_kernel<2, H_, G_, A_, B_, C_>));         \
+  }
+  MK_SHAPES(MK_CASE)
+#undef MK_CASE
+  if (!fn) return hipErrorInvalidValue;
+  void* args[] = {&d_params, &d_token, &pos, &epoch, &d_next, &d_logits};
+  return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
+}
+
+}  // namespace mk

@@ -17,13 +17,29 @@ namespace mk {
 
 enum : uint32_t { FMT_BF16 = 0, FMT_FP8 = 1, FMT_FP4 = 2 };
 
-constexpr int kThreads = 512;            // threads per workgroup (8 wave64s)
-constexpr int kWaves = kThreads / 64;
-constexpr int kMaxOwn = 64;              // residual rows one workgroup may own
-constexpr int kMaxVecWords = 6144;       // words one gather may bring into LDS
-constexpr int kMaxPart = 2048;           // GEMV (row, 1024-chunk) items per workgroup per phase
-constexpr int kPhaseBits = 10;           // low bits of an exchange tag hold the phase id
+// A decode workgroup is one courier wave (wave 0) and seven compute waves.
+// The courier alone polls the exchange words in global memory; it gathers
+// each input vector into LDS and hands it over with an LDS sequence counter.
+// The compute waves hold their rows' weights in registers, a full layer
+// ahead, and never wait on global memory for anything but their own weights.
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kCW = kWaves - 1;              // compute waves (wave ids 1..7)
+constexpr int kPhaseBits = 10;               // low bits of an exchange tag hold the vector id
 constexpr uint32_t kEpochMask = (1u << (32 - kPhaseBits)) - 1;
+constexpr int kTypes = 6;                    // exchange vectors per layer (see below)
+constexpr int kMaxLayers = (int)((1u << kPhaseBits) - 4) / kTypes;   // 170
+
+// Weights and exchange words are read and written through buffer resources
+// (32-bit offsets).  kOOB is an offset past the end of every such buffer: a
+// load there returns zeros and a store there is dropped, without touching
+// memory, which lets a wave skip a row or a store without a branch.
+constexpr uint32_t kOOB = 0x7FFFFFF0u;
+constexpr uint64_t kMaxBuffer = 0x7FFF0000ull;   // largest buffer read that way
+
+// Units per compute wave and phase (the host checks its schedule against these).
+constexpr int kMaxQKV = 3, kMaxO = 1, kMaxGU = 1, kMaxD = 1;
+constexpr int kSchedInts = 32;               // ints per workgroup header and per compute wave
 
 // One packed matrix in the weight arena (byte offsets from the arena base).
 //  bf16: codes = N*K uint16.  fp8: codes = N*K bytes, scales = N fp32.
@@ -44,23 +60,35 @@ struct Layer {
   uint64_t in_norm, post_norm, q_norm, k_norm;
 };
 
-// Exchange buffers in scratch, in 64-bit words.  Every word is
-// (payload << 32) | tag, written and read with agent-scope atomic stores and
-// loads.  Buffers a consumer set reads are replicated R times; layer-indexed
-// buffers alternate between two parities.
+// Exchange vectors of layer l (word offsets inside the layer's block).  Each
+// word is (payload << 32) | tag with tag = (epoch << kPhaseBits) | vector id,
+// vector id = 2 + kTypes*l + type; the argmax words of the step use id
+// 2 + kTypes*L.
+enum : int { V_QKV = 0, V_ATT = 1, V_O = 2, V_XO = 3, V_H = 4, V_XD = 5 };
 struct Xch {
-  uint64_t x_d, x_o, qkv, o, h;   // replicated vectors: base word offsets
-  uint64_t rep_x, rep_qkv, rep_o, rep_h;  // stride between replicas (words)
-  uint64_t par_x, par_qkv, par_o, par_h;  // stride between parities (words)
-  uint64_t part, par_part;        // split-attention partials [ns_max][nq][hd+2]
-  uint64_t arg;                   // argmax slots [grid][2]
-  uint64_t err;                   // error word (uint32 in a 64-bit slot)
-  uint64_t amax;                  // packing scratch: tensor abs-max (uint32 bits)
-  uint64_t words;                 // total words
+  uint64_t base;              // word offset of layer 0's block
+  uint64_t layer_words;       // words per layer block
+  uint64_t off[kTypes];       // offset of each vector in a block
+  uint64_t arg;               // argmax words [grid][2] (value, index)
+  uint64_t err;               // error word (uint32 in a 64-bit slot)
+  uint64_t amax;              // packing scratch: tensor abs-max (uint32 bits)
+  uint64_t sched;             // the work table (int32)
+  uint64_t words;             // total words
 };
+
+// Per-workgroup header of the work table (ints).
+enum : int {
+  S_FLAGS = 0,      // bit 0: gathers xd (QKV or O units), 1: o, 2: xo (gate/up or down), 3: h
+  S_ATT = 1,        // KV head whose attention this workgroup runs, or -1
+  S_NIN = 2,        // inputs the courier gathers per layer
+  S_IXD = 3, S_IQKV = 4, S_IO = 5, S_IXO = 6, S_IH = 7,   // input index in the layer, or -1
+};
+// Per compute wave: units of each phase (-1 = none), at these offsets.
+enum : int { S_QKV = 0, S_O = 4, S_GU = 8, S_D = 12 };
 
 struct Params {
   MK_GLOBAL const uint8_t* w;   // weight arena
+  uint32_t w_bytes;             // its size (read through a buffer resource: below 2 GB)
   MK_GLOBAL uint16_t* kv;       // [L][2][nkv][max_ctx][hd] bf16
   MK_GLOBAL const float* rope;  // [max_ctx][hd/2][2] cos, sin
   MK_GLOBAL uint64_t* xch;      // scratch
@@ -72,11 +100,11 @@ struct Params {
   uint64_t layer_stride;  // bytes between consecutive layers' matrices
   uint64_t final_norm;
   Xch x;
-  int grid, R, att_target, ns_max;
+  int grid;
   uint64_t spin_limit;    // s_memrealtime ticks
   uint32_t tag_skew;      // test hook: added to every expected tag (non-zero makes every wait time out)
-  uint32_t poll_sleep;    // s_sleep units (64 clocks each) between polls of a word that is not ready
-  int n_phases;           // phase ids per step (trace stride per workgroup)
+  uint32_t poll_sleep;    // s_sleep units between courier poll rounds
+  int n_phases;           // trace phases per step (trace stride per workgroup)
 };
 
 }  // namespace mk

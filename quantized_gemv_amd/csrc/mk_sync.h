@@ -1,27 +1,31 @@
-// Inter-workgroup exchange for the persistent decode kernel.
+// Inter-workgroup exchange and the courier / compute hand-off inside a
+// workgroup, for the persistent decode kernel.
 //
-// The monolith page ("Design decisions", sync experiments) replaces grid-wide
-// barriers by per-tile counters with release/acquire ordering, so that a
+// The monolith page ("Design decisions", the sync experiments) replaces
+// grid-wide barriers by per-tile counters with release/acquire ordering, so a
 // consumer waits only for the tiles it reads.  On gfx950 the eight XCDs have
 // separate L2 caches, and an agent-scope release/acquire pair costs an L2
-// write-back plus an L2 invalidate.  Measured on MI355X, counters with those
-// fences take 16-21 us per all-to-all round of 256 workgroups, against
-// 2.2-5 us for the scheme used here:
+// write-back plus an L2 invalidate (the invalidate would also drop the
+// prefetched weights).  Here instead every produced value travels in its own
+// 64-bit word, (payload << 32) | tag, stored with an agent-scope relaxed
+// atomic store (coherent across XCDs without cache maintenance).  The tag is
+// (epoch << 10) | vector id, unique per launch and vector, so a word that
+// carries the expected tag holds that producer's value: flag and data are one
+// atomic object and no fence is needed.
 //
-//   * every produced value travels in its own 64-bit word,
-//     (payload << 32) | tag, written with an agent-scope relaxed atomic
-//     store and read with an agent-scope relaxed atomic load (the compiler
-//     emits sc1 accesses, coherent across XCDs without cache maintenance);
-//   * the tag is (epoch << 10) | phase, unique per launch and phase, so a
-//     consumer that reads a word carrying the expected tag holds that
-//     producer's value: the flag and the data are one atomic object, and no
-//     fence is needed;
-//   * producers write R replicas of each word and consumer workgroup b reads
-//     replica b % R, which spreads the consumers' polling over memory
-//     channels instead of one hot spot.
+// gfx9 retires a wave's vector memory operations in order under one counter
+// (vmcnt), so a poll issued behind a weight prefetch would return only after
+// the prefetch.  Only the courier wave of a workgroup polls; it keeps no
+// weight loads in flight.  It reads two words per lane per 16-byte load
+// (each 8-byte half is one producer's atomic store and carries its own tag),
+// re-polls only what is missing, and once a vector is complete it writes the
+// payloads (normalised where the consumer wants that) into LDS and bumps the
+// workgroup's LDS sequence counter.  Compute waves wait on that counter with
+// LDS reads, which count against lgkmcnt, not vmcnt.
 //
-// Each wait is bounded: past `spin_limit` s_memrealtime ticks, or once any
-// workgroup has recorded an error, the wait gives up and the kernel exits.
+// Each courier wait is bounded: past `spin_limit` s_memrealtime ticks, or once
+// any workgroup has recorded an error, it gives up and raises the abort value
+// in the sequence counter, which ends the compute waves' waits.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -31,16 +35,19 @@
 namespace mk {
 
 enum : uint32_t { ERR_TIMEOUT = 1u, ERR_TOKEN = 2u };
+constexpr uint32_t kAbort = 0xFFFFFFFFu;
 
-__device__ __forceinline__ uint64_t ld_word(MK_GLOBAL const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ void st_word(MK_GLOBAL uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint32_t make_tag(uint32_t epoch, uint32_t phase) {
-  return (epoch << kPhaseBits) | phase;
+__device__ __forceinline__ void put_word(MK_GLOBAL uint64_t* p, uint32_t payload, uint32_t tag) {
+  st_word(p, ((uint64_t)payload << 32) | tag);
 }
+__device__ __forceinline__ uint32_t make_tag(uint32_t epoch, uint32_t id) { return (epoch << kPhaseBits) | id; }
+__device__ __forceinline__ uint32_t vec_id(int l, int type) { return (uint32_t)(2 + kTypes * l + type); }
 
 __device__ __forceinline__ MK_GLOBAL uint32_t* err_word(const Params& p) {
   return GCAST(uint32_t, p.xch + p.x.err);
@@ -49,93 +56,120 @@ __device__ __forceinline__ void raise_error(const Params& p, uint32_t code) {
   __hip_atomic_fetch_or(err_word(p), code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Write word i of a replicated vector: one copy per replica.
-__device__ __forceinline__ void publish(MK_GLOBAL uint64_t* base, uint64_t rep_stride, int R, int i,
-                                        uint32_t payload, uint32_t tag) {
-  const uint64_t v = ((uint64_t)payload << 32) | tag;
-  for (int r = 0; r < R; ++r) st_word(base + (uint64_t)r * rep_stride + i, v);
+// Exchange vector `type` of layer l: pointer, and word offset in the scratch buffer.
+__device__ __forceinline__ MK_GLOBAL uint64_t* xvec(const Params& p, int l, int type) {
+  return p.xch + p.x.base + (uint64_t)l * p.x.layer_words + p.x.off[type];
+}
+__device__ __forceinline__ uint32_t xword(const Params& p, int l, int type) {
+  return (uint32_t)(p.x.base + (uint64_t)l * p.x.layer_words + p.x.off[type]);
 }
 
-// Poll one word until its tag matches; false on timeout or a recorded error.
-__device__ __forceinline__ bool wait_word(MK_GLOBAL const uint64_t* src, uint32_t tag, uint64_t& v,
-                                          const Params& p, uint64_t t0) {
-  uint32_t n = 0;
-  while ((uint32_t)v != tag) {
-    // back off between polls: polling traffic goes to the memory side and
-    // slows every other access there
-    switch (p.poll_sleep) {
-      case 0: break;
-      case 1: __builtin_amdgcn_s_sleep(1); break;
-      case 2: __builtin_amdgcn_s_sleep(2); break;
-      case 3: __builtin_amdgcn_s_sleep(4); break;
-      case 4: __builtin_amdgcn_s_sleep(8); break;
-      default: __builtin_amdgcn_s_sleep(16); break;
-    }
-    if ((++n & 63u) == 0) {
-      if (__builtin_amdgcn_s_memrealtime() - t0 > p.spin_limit) {
-        raise_error(p, ERR_TIMEOUT);
-        return false;
-      }
-      if (__hip_atomic_load(err_word(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return false;
-    }
-    v = ld_word(src);
-  }
-  return true;
+// Wait until this wave's LDS accesses have completed, without waiting for
+// its global loads (s_waitcnt lgkmcnt(0); vmcnt and expcnt at their maxima),
+// and keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_drain() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ uint32_t lds_ld(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_st(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// All threads of the workgroup read words [0, n) of `src` (one replica),
-// waiting for each to carry `tag`, and store the payloads to dst[0, n).
-// Returns this thread's success; callers combine it across the workgroup.
-__device__ __forceinline__ bool gather(MK_GLOBAL const uint64_t* src, int n, uint32_t tag, uint32_t* dst,
-                                       const Params& p) {
-  constexpr int B = 4;  // words in flight per thread per pass
+// Workgroup barrier that waits only for LDS (the waves may keep global loads
+// in flight across it).
+__device__ __forceinline__ void lds_barrier() {
+  lds_drain();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Compute waves: wait until the courier has handed over `want` inputs.
+// Returns false if the courier aborted, or (a safety net: the courier's own
+// waits are bounded) after `spin_limit` ticks.
+__device__ __forceinline__ bool wait_seq(const Params& p, const uint32_t* seq, uint32_t want) {
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-  tag += p.tag_skew;
-  bool ok = true;
-  for (int base = 0; base < n; base += kThreads * B) {
-    uint64_t v[B];
-#pragma unroll
-    for (int k = 0; k < B; ++k) {  // unconditional (clamped) loads: no branch, no early wait
-      const int i = base + (int)threadIdx.x + k * kThreads;
-      v[k] = ld_word(src + min(i, n - 1));
+  while (true) {
+    const uint32_t s = __builtin_amdgcn_readfirstlane(lds_ld(seq));
+    if (s >= want) return s != kAbort;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > p.spin_limit) {
+      if ((threadIdx.x & 63) == 0) raise_error(p, ERR_TIMEOUT);
+      return false;
     }
-#pragma unroll
-    for (int k = 0; k < B; ++k) {
-      const int i = base + (int)threadIdx.x + k * kThreads;
-      if (i < n && ok) {
-        ok = wait_word(src + i, tag, v[k], p, t0);
-        dst[i] = (uint32_t)(v[k] >> 32);
-      }
-    }
+    __builtin_amdgcn_s_sleep(1);
   }
-  return ok;
 }
 
-// The same for words base[idx(i)], i in [0, n), stored to dst[i].
-template <class F>
-__device__ __forceinline__ bool gather_map(MK_GLOBAL const uint64_t* base, int n, uint32_t tag, uint32_t* dst,
-                                           const Params& p, F idx) {
-  constexpr int B = 4;
-  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+// Courier: publish one more input (LDS writes first, then the counter).
+__device__ __forceinline__ void hand_over(uint32_t* seq, uint32_t value) {
+  lds_drain();
+  if ((threadIdx.x & 63) == 0) lds_st(seq, value);
+  lds_drain();
+}
+
+// 16-byte load of two consecutive exchange words with device-scope
+// coherence (sc1), through a buffer resource over the scratch buffer.
+__device__ __forceinline__ v4u ld_pair(__amdgpu_buffer_rsrc_t r, uint32_t word) {
+  return __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(r, word * 8u, 0, 16));
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t xch_rsrc(const Params& p) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p.xch, (short)0, (int)(p.x.words * 8), 0x00020000);
+}
+
+// Store one exchange word, device-scope coherent (sc1), through the scratch
+// buffer resource.  A byte offset past the buffer (see kOOB) drops the
+// store, which lets a wave skip a store without a branch.
+__device__ __forceinline__ void st_xword(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint32_t payload,
+                                         uint32_t tag) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, v2u{tag, payload}), r, byte_off, 0, 16);
+}
+
+// Courier gather: `npairs` pairs of words; pair j is at word src(j) (even,
+// the two words consecutive).  Lane l owns pairs l + 64k, k < MAXK; their
+// payloads land in lo[k] (word 2j) and hi[k] (word 2j+1).  Each round issues
+// every missing pair's load before waiting, so one round costs one memory
+// latency.  Returns false on timeout or when another workgroup has failed.
+template <int MAXK, class F>
+__device__ __forceinline__ bool gather_pairs(const Params& p, __amdgpu_buffer_rsrc_t r, int npairs, uint32_t tag,
+                                             uint32_t (&lo)[MAXK], uint32_t (&hi)[MAXK], F src) {
+  const int lane = threadIdx.x & 63;
   tag += p.tag_skew;
-  bool ok = true;
-  for (int b0 = 0; b0 < n; b0 += kThreads * B) {
-    uint64_t v[B];
+  uint32_t pend = 0;
+  v4u v[MAXK];
 #pragma unroll
-    for (int k = 0; k < B; ++k) {
-      const int i = b0 + (int)threadIdx.x + k * kThreads;
-      v[k] = ld_word(base + idx(min(i, n - 1)));
-    }
-#pragma unroll
-    for (int k = 0; k < B; ++k) {
-      const int i = b0 + (int)threadIdx.x + k * kThreads;
-      if (i < n && ok) {
-        ok = wait_word(base + idx(i), tag, v[k], p, t0);
-        dst[i] = (uint32_t)(v[k] >> 32);
-      }
-    }
+  for (int k = 0; k < MAXK; ++k) {
+    const int j = lane + 64 * k;
+    if (j < npairs) pend |= 1u << k;
+    v[k] = ld_pair(r, src(min(j, npairs - 1)));   // clamped: no load behind a branch
   }
-  return ok;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  uint32_t rounds = 0;
+  while (true) {
+#pragma unroll
+    for (int k = 0; k < MAXK; ++k) {
+      if (v[k].x == tag && v[k].z == tag) pend &= ~(1u << k);
+      lo[k] = v[k].y;
+      hi[k] = v[k].w;
+    }
+    if (__builtin_amdgcn_ballot_w64(pend != 0) == 0) return true;
+    ++rounds;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > p.spin_limit) {
+      raise_error(p, ERR_TIMEOUT);
+      return false;
+    }
+    if ((rounds & 63u) == 0 &&
+        __hip_atomic_load(err_word(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+      return false;
+    for (uint32_t z = 0; z < p.poll_sleep; ++z) __builtin_amdgcn_s_sleep(8);   // back-off: ~512 clocks each
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int k = 0; k < MAXK; ++k)
+      if ((pend >> k) & 1u) v[k] = ld_pair(r, src(lane + 64 * k));
+  }
 }
 
 }  // namespace mk

@@ -18,7 +18,7 @@ from .build import lib_path
 MK_OK, MK_E_INVALID, MK_E_UNSUPPORTED, MK_E_STATE, MK_E_HIP, MK_E_TIMEOUT = 0, -1, -2, -3, -4, -5
 BF16, FP8_ROW, FP4_MIX = 0, 1, 2
 MATRICES = {"q": 0, "k": 1, "v": 2, "o": 3, "gate": 4, "up": 5, "down": 6, "embed": 7}
-OPT_GRID, OPT_REPLICAS, OPT_ATT_TARGET, OPT_SPIN_LIMIT, OPT_TAG_SKEW, OPT_POLL_SLEEP = 0, 1, 2, 3, 4, 5
+OPT_GRID, OPT_SPIN_LIMIT, OPT_TAG_SKEW, OPT_POLL_SLEEP = 0, 3, 4, 5
 
 
 class MkError(RuntimeError):
@@ -49,8 +49,8 @@ class mk_trace_rec(ctypes.Structure):
 
 
 TRACE_DTYPE = np.dtype([(n, np.uint32) for n in ("phase", "wg", "hw_id", "xcc", "active", "pad")] +
-                       [(n, np.uint64) for n in ("t_start", "t_wait_begin", "t_wait_end", "t_end",
-                                                 "rt_start", "rt_end")] + [("t_mark", np.uint64, (4,))])
+                       [(n, np.uint64) for n in ("t_start", "t_ready", "t_handoff", "t_seen", "t_done")] +
+                       [("t_mark", np.uint64, (3,))])
 
 _LIBS: Dict[bool, ctypes.CDLL] = {}
 _VP = ctypes.c_void_p
@@ -107,7 +107,6 @@ class Decoder:
     """One model handle with its device buffers (allocated through torch)."""
 
     def __init__(self, shape, wfmt: int, max_ctx: int, xray: bool = False, grid: int = 0,
-                 replicas: Optional[int] = None, att_target: Optional[int] = None,
                  spin_limit: Optional[int] = None, poll_sleep: Optional[int] = None):
         import torch
         self.lib = load(xray)
@@ -118,10 +117,6 @@ class Decoder:
         self.h = h
         if grid:
             self._check(self.lib.mk_set_option(self.h, OPT_GRID, grid))
-        if replicas:
-            self._check(self.lib.mk_set_option(self.h, OPT_REPLICAS, replicas))
-        if att_target:
-            self._check(self.lib.mk_set_option(self.h, OPT_ATT_TARGET, att_target))
         if spin_limit is not None:
             self._check(self.lib.mk_set_option(self.h, OPT_SPIN_LIMIT, spin_limit))
         if poll_sleep is not None:

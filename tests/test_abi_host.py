@@ -104,8 +104,10 @@ def test_calls_out_of_order_and_bad_arguments(lib):
     # options
     assert lib.mk_set_option(h, 99, 0) == native.MK_E_INVALID
     assert lib.mk_set_option(h, native.OPT_GRID, -1) == native.MK_E_INVALID
-    assert lib.mk_set_option(h, native.OPT_REPLICAS, 0) == native.MK_E_INVALID
-    assert lib.mk_set_option(h, native.OPT_ATT_TARGET, 64) == native.MK_OK
+    assert lib.mk_set_option(h, 1, 0) == native.MK_E_INVALID          # reserved keys
+    assert lib.mk_set_option(h, 2, 64) == native.MK_E_INVALID
+    assert lib.mk_set_option(h, native.OPT_POLL_SLEEP, 17) == native.MK_E_INVALID
+    assert lib.mk_set_option(h, native.OPT_SPIN_LIMIT, 1000) == native.MK_OK
     assert lib.mk_last_error(h)
     n_out = ctypes.c_size_t(7)
     assert lib.mk_get_trace(h, None, 0, ctypes.byref(n_out)) == native.MK_OK and n_out.value == 0

@@ -180,8 +180,10 @@ int mk_get_trace(mk_model* m, mk_trace_rec* h_out, size_t cap, size_t* n_out);
 /* Test hook: decode `n` codes with the kernel's own register decoders.
  * codec 0: E4M3 bytes -> fp32; codec 1: E2M1 (one code per byte, low
  * nibble) -> fp32; codecs 2 and 3: the same two formats through the
- * converters the GEMVs use (to packed bf16), widened to fp32.  Device
- * buffers; enqueued on `s`.  Needs no model. */
+ * converters the GEMVs use (to packed bf16), widened to fp32; codec 4:
+ * `d_codes` holds n fp32 values, rounded to bf16 the way the kernel packs
+ * activations and widened back.  Device buffers; enqueued on `s`.  Needs no
+ * model. */
 int mk_decode_codes(int32_t codec, const uint8_t* d_codes, int32_t n, float* d_out, mk_stream_t s);
 
 /* Tuning knobs (defaults in brackets): key 0 grid size [compute units],

@@ -592,7 +592,7 @@ int mk_get_trace(mk_model* m, mk_trace_rec* h_out, size_t cap, size_t* n_out) {
 }
 
 int mk_decode_codes(int32_t codec, const uint8_t* d_codes, int32_t n, float* d_out, mk_stream_t stream) {
-  if (codec < 0 || codec > 3 || n < 0 || (n > 0 && (!d_codes || !d_out))) return MK_E_INVALID;
+  if (codec < 0 || codec > 4 || n < 0 || (n > 0 && (!d_codes || !d_out))) return MK_E_INVALID;
   const hipError_t e = launch_decode_codes(codec, d_codes, n, d_out, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? MK_OK : MK_E_HIP;
 }

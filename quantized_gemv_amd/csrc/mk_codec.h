@@ -48,6 +48,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two fp32 -> one bf16 pair (lo in bits 0..15), round to nearest even, with
+// gfx950's v_cvt_pk_bf16_f32 (checked against the bit formula above).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  typedef float f2v __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v){lo, hi}, bf2));
+}
+
 // Four e4m3 bytes of `w` -> four floats.
 __device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float* o) {
   f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);

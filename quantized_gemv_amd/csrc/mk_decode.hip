@@ -84,7 +84,6 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) { return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16); }
 
 // ------------------------------------------------------------------ LDS
 template <int HD, int GS, int NH, int NQ, int NI>
@@ -105,6 +104,8 @@ struct Smem {
   alignas(16) float wm[kCW][GS];         // per wave: running max (log2 units)
   alignas(16) float wl[kCW][GS];         // per wave: running sum
   alignas(16) float sp[GS];              // this position's scores (log2 units)
+  alignas(16) float gq[HD], gk[HD];      // q/k-norm gains of the layer
+  alignas(16) float rc[HD / 2], rs[HD / 2];   // this position's RoPE cos, sin
   // argmax
   alignas(16) float best[kCW];
   alignas(16) int32_t bidx[kCW];
@@ -379,6 +380,7 @@ struct Kern {
         if (!attention_input(p, s, l, att, pos, epoch, rs)) return abort(s);
         hand_over(&s.seq, ++seq);
         XR_PUT(s, ph + 1, XR_HANDOFF);
+        lds_barrier();   // q, k and v are normed, roped and appended
         lds_barrier();   // every compute wave has written its partial outputs
         lds_barrier();   // and merged them: the LDS arrays may be reused
       }
@@ -481,9 +483,9 @@ struct Kern {
     return false;
   }
 
-  // Gather q (GS heads), k and v of KV head g, apply q/k RMSNorm and RoPE,
-  // append bf16 k and v to the cache at `pos`, and leave q (pre-scaled so
-  // that scores come out in log2 units), k and v in LDS.
+  // Gather q (GS heads), k and v of KV head g into LDS, with this layer's
+  // q/k-norm gains and this position's RoPE pairs (loaded ahead of the
+  // gather); the compute waves norm, rope and append them (att_prepare).
   static __device__ bool attention_input(const Params& p, S& s, int l, int g, int pos, uint32_t epoch,
                                          __amdgpu_buffer_rsrc_t rs) {
     MK_GLOBAL const uint8_t* const W = p.w;
@@ -491,7 +493,6 @@ struct Kern {
     const int nq = p.nq, nkv = p.nkv;
     const uint64_t loff = (uint64_t)l * p.layer_stride;
     const Layer& L0 = p.layer0;
-    // gains and this position's RoPE pair (lane i < HD/2 owns pair i), loaded ahead of the gather
     const int li = min(lane, HD / 2 - 1);
     MK_GLOBAL const uint16_t* gq = GCAST(const uint16_t, W + L0.q_norm + loff);
     MK_GLOBAL const uint16_t* gk = GCAST(const uint16_t, W + L0.k_norm + loff);
@@ -514,53 +515,79 @@ struct Kern {
       const int j = lane + 64 * k;
       if (j < (GS + 2) * HD / 2) *reinterpret_cast<v2u*>(s.qraw + 2 * j) = v2u{lo[k], hi[k]};
     }
-    lds_drain();
+    if (lane < HD / 2) {
+      s.gq[lane] = gq_lo;
+      s.gq[lane + HD / 2] = gq_hi;
+      s.gk[lane] = gk_lo;
+      s.gk[lane + HD / 2] = gk_hi;
+      s.rc[lane] = rc;
+      s.rs[lane] = rsn;
+    }
+    return true;
+  }
+
+  // Compute wave cw of an attention workgroup, once the raw q/k/v are in
+  // LDS: waves 0..GS-1 RMSNorm and rope q head cw (pre-scaled by
+  // log2(e)/sqrt(HD), so scores come out in log2 units); wave GS does k
+  // (rounded to bf16 as the cache holds it) and wave GS+1 rounds v; both
+  // append to the cache at `pos`.  Lane i < HD/2 owns the RoPE pair
+  // (i, i + HD/2).
+  static __device__ __forceinline__ void att_prepare(const Params& p, S& s, int l, int g, int pos, int cw, bool ok) {
+    const int lane = lane_id();
     const bool pl = lane < HD / 2;
-    const float kq = 1.4426950408889634f / sqrtf((float)HD);
-#pragma unroll
-    for (int h = 0; h <= GS; ++h) {
-      const float* src = s.qraw + h * HD;
+    const int li = min(lane, HD / 2 - 1);
+    if (cw <= GS) {
+      const float* src = s.qraw + cw * HD;
       const float xa = pl ? src[li] : 0.f, xb = pl ? src[li + HD / 2] : 0.f;
       const float r = 1.0f / sqrtf(wave_sum(xa * xa + xb * xb) / (float)HD + p.eps);
-      const float glo = h < GS ? gq_lo : gk_lo, ghi = h < GS ? gq_hi : gk_hi;
-      const float a = glo * (xa * r), b = ghi * (xb * r);
-      const float ra = a * rc - b * rsn, rb = b * rc + a * rsn;
-      if (pl) {
-        if (h < GS) {
-          s.q[h * HD + li] = ra * kq;
-          s.q[h * HD + li + HD / 2] = rb * kq;
-        } else {
+      const float* gg = cw < GS ? s.gq : s.gk;
+      const float a = gg[li] * (xa * r), b = gg[li + HD / 2] * (xb * r);
+      const float c = s.rc[li], sn = s.rs[li];
+      const float ra = a * c - b * sn, rb = b * c + a * sn;
+      if (cw < GS) {
+        const float kq = 1.4426950408889634f / sqrtf((float)HD);
+        if (pl) {
+          s.q[cw * HD + li] = ra * kq;
+          s.q[cw * HD + li + HD / 2] = rb * kq;
+        }
+      } else {
+        if (pl) {
           s.kf[li] = ra;
           s.kf[li + HD / 2] = rb;
         }
+        lds_drain();
+        if (pl) {
+          const uint32_t kw = pack_bf16(s.kf[2 * lane], s.kf[2 * lane + 1]);
+          s.kp[lane] = kw;
+          const size_t plane = (size_t)p.max_ctx * HD;
+          MK_GLOBAL uint32_t* kc = GCAST(uint32_t, p.kv + ((size_t)(l * 2 + 0) * p.nkv + g) * plane);
+          if (ok) kc[(size_t)pos * (HD / 2) + lane] = kw;   // an aborted step leaves the cache alone
+        }
+      }
+    } else if (cw == GS + 1) {
+      if (pl) {
+        const float* vf = s.qraw + (GS + 1) * HD;
+        const uint32_t vw = pack_bf16(vf[2 * lane], vf[2 * lane + 1]);
+        s.vp[lane] = vw;
+        const size_t plane = (size_t)p.max_ctx * HD;
+        MK_GLOBAL uint32_t* vc = GCAST(uint32_t, p.kv + ((size_t)(l * 2 + 1) * p.nkv + g) * plane);
+        if (ok) vc[(size_t)pos * (HD / 2) + lane] = vw;
       }
     }
-    lds_drain();
-    if (lane < HD / 2) {
-      const uint32_t kw = pack_bf16(s.kf[2 * lane], s.kf[2 * lane + 1]);
-      const float* vf = s.qraw + (GS + 1) * HD;
-      const uint32_t vw = pack_bf16(vf[2 * lane], vf[2 * lane + 1]);
-      s.kp[lane] = kw;
-      s.vp[lane] = vw;
-      const size_t plane = (size_t)p.max_ctx * HD;
-      MK_GLOBAL uint32_t* kc = GCAST(uint32_t, p.kv + ((size_t)(l * 2 + 0) * nkv + g) * plane);
-      MK_GLOBAL uint32_t* vc = GCAST(uint32_t, p.kv + ((size_t)(l * 2 + 1) * nkv + g) * plane);
-      kc[(size_t)pos * (HD / 2) + lane] = kw;
-      vc[(size_t)pos * (HD / 2) + lane] = vw;
-    }
-    lds_drain();
-    // scores of this position (its k as the cache holds it, bf16)
-    {
-      const uint32_t kw = lane < HD / 2 ? s.kp[lane] : 0u;
+  }
+
+  // Scores of the current position for every q head (its k as the cache
+  // holds it, bf16), into s.sp; one wave, after att_prepare.
+  static __device__ __forceinline__ void att_current_scores(S& s) {
+    const int lane = lane_id();
+    const uint32_t kw = lane < HD / 2 ? s.kp[lane] : 0u;
 #pragma unroll
-      for (int h = 0; h < GS; ++h) {
-        const float d = lane < HD / 2 ? s.q[h * HD + 2 * lane] * bf16_lo(kw) + s.q[h * HD + 2 * lane + 1] * bf16_hi(kw)
-                                      : 0.f;
-        const float sc = wave_sum(d);
-        if (lane == 0) s.sp[h] = sc;
-      }
+    for (int h = 0; h < GS; ++h) {
+      const float d =
+          lane < HD / 2 ? s.q[h * HD + 2 * lane] * bf16_lo(kw) + s.q[h * HD + 2 * lane + 1] * bf16_hi(kw) : 0.f;
+      const float sc = wave_sum(d);
+      if (lane == 0) s.sp[h] = sc;
     }
-    return true;
   }
 
   // --------------------------------------------------- GEMV compute waves
@@ -630,6 +657,7 @@ struct Kern {
         ok = ok && wait_seq(p, &s.seq, sbase + hdr[S_IXD]);
         XR_MIN(s, ph + 0, XR_SEEN);
       }
+      if (u[S_QKV] >= 0) {
       uint32_t xa[NH][8];
       norm_act<NH>(s.xd_raw, s.r_xd, w.gin, H, xa);
 #ifdef MK_XRAY
@@ -648,7 +676,8 @@ struct Kern {
         const float v = wrow_dot(w.q[k], xa);
         st_xword(rx, ok && r >= 0 && l0 ? 8u * (base + r) : kOOB, __float_as_uint(v), tag);
       }
-      if (u[S_QKV] >= 0) XR_MAX(s, ph + 0, XR_DONE);
+      XR_MAX(s, ph + 0, XR_DONE);
+      }
     }
     // ---- the layer's weight burst, once every wave of the workgroup has
     // issued its QKV stores (the courier joins this barrier after handing
@@ -663,6 +692,7 @@ struct Kern {
         ok = ok && wait_seq(p, &s.seq, sbase + hdr[S_IO]);
         XR_MIN(s, ph + 3, XR_SEEN);
       }
+      if (u[S_O] >= 0) {
       uint32_t xa[NQ][8];
       load_act<NQ>(s.o_in, p.nq * HD, xa);
       const uint32_t base = xword(p, l, V_XO), tag = make_tag(epoch, vec_id(l, V_XO));
@@ -672,7 +702,8 @@ struct Kern {
         const float v = s.xd_raw[max(r, 0)] + wrow_dot(w.o[k], xa);
         st_xword(rx, ok && r >= 0 && l0 ? 8u * (base + r) : kOOB, __float_as_uint(v), tag);
       }
-      if (u[S_O] >= 0) XR_MAX(s, ph + 3, XR_DONE);
+      XR_MAX(s, ph + 3, XR_DONE);
+      }
     }
     // ---- gate/up + SwiGLU: a unit is the four rows behind one output word
     {
@@ -680,6 +711,7 @@ struct Kern {
         ok = ok && wait_seq(p, &s.seq, sbase + hdr[S_IXO]);
         XR_MIN(s, ph + 4, XR_SEEN);
       }
+      if (u[S_GU] >= 0) {
       uint32_t xa[NH][8];
       norm_act<NH>(s.xo_raw, s.r_xo, w.gpost, H, xa);
       const uint32_t base = xword(p, l, V_H), tag = make_tag(epoch, vec_id(l, V_H));
@@ -697,7 +729,8 @@ struct Kern {
         const float h0 = silu(y[0]) * y[1], h1 = silu(y[2]) * y[3];
         st_xword(rx, ok && t >= 0 && l0 ? 8u * (base + t) : kOOB, pack_bf16(h0, h1), tag);
       }
-      if (u[S_GU] >= 0) XR_MAX(s, ph + 4, XR_DONE);
+      XR_MAX(s, ph + 4, XR_DONE);
+      }
     }
     // ---- down + residual
     {
@@ -705,6 +738,7 @@ struct Kern {
         ok = ok && wait_seq(p, &s.seq, sbase + hdr[S_IH]);
         XR_MIN(s, ph + 5, XR_SEEN);
       }
+      if (u[S_D] >= 0) {
       uint32_t xa[NI][8];
       load_act<NI>(s.h_in, p.I, xa);
       const uint32_t base = xword(p, l, V_XD), tag = make_tag(epoch, vec_id(l, V_XD));
@@ -714,7 +748,8 @@ struct Kern {
         const float v = s.xo_raw[max(r, 0)] + wrow_dot(w.d[k], xa);
         st_xword(rx, ok && r >= 0 && l0 ? 8u * (base + r) : kOOB, __float_as_uint(v), tag);
       }
-      if (u[S_D] >= 0) XR_MAX(s, ph + 5, XR_DONE);
+      XR_MAX(s, ph + 5, XR_DONE);
+      }
     }
     return ok;
   }
@@ -822,6 +857,9 @@ struct Kern {
     const int ph = 2 + 6 * l;
     ok = ok && wait_seq(p, &s.seq, (uint32_t)l + 1u);
     XR_MIN(s, ph + 1, XR_SEEN);
+    att_prepare(p, s, l, g, pos, cw, ok);
+    lds_barrier();
+    if (cw == 0) att_current_scores(s);   // read in the merge, after the next barrier
     float acc[GS][DPL], m[GS], lsum[GS];
 #pragma unroll
     for (int h = 0; h < GS; ++h) {

@@ -126,6 +126,16 @@ __global__ void decode_codes_kernel(int codec, const uint8_t* in, int n, float* 
   }
 }
 
+// fp32 -> bf16 as the decode kernel packs activations (pairs), widened back.
+__global__ void round_bf16_kernel(const float* in, int n, float* out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (2 * i >= n) return;
+  const float a = in[2 * i], b = 2 * i + 1 < n ? in[2 * i + 1] : 0.f;
+  const uint32_t w = pack_bf16(a, b);
+  out[2 * i] = bf16_lo(w);
+  if (2 * i + 1 < n) out[2 * i + 1] = bf16_hi(w);
+}
+
 // ------------------------------------------------------- launch wrappers
 hipError_t launch_pack_bf16(const uint16_t* src, int N, int K, uint16_t* dst, int row_off, int row_step,
                             hipStream_t s) {
@@ -158,6 +168,11 @@ hipError_t launch_rope(float* out, int max_ctx, int hd, double theta, hipStream_
 
 hipError_t launch_decode_codes(int codec, const uint8_t* in, int n, float* out, hipStream_t s) {
   if (n <= 0) return hipSuccess;
+  if (codec == 4) {
+    hipLaunchKernelGGL(round_bf16_kernel, dim3((n / 2 + 256) / 256), dim3(256), 0, s,
+                       reinterpret_cast<const float*>(in), n, out);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(decode_codes_kernel, dim3((n + 255) / 256), dim3(256), 0, s, codec, in, n, out);
   return hipGetLastError();
 }

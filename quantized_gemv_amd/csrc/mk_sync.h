@@ -91,15 +91,17 @@ __device__ __forceinline__ void lds_barrier() {
 // Returns false if the courier aborted, or (a safety net: the courier's own
 // waits are bounded) after `spin_limit` ticks.
 __device__ __forceinline__ bool wait_seq(const Params& p, const uint32_t* seq, uint32_t want) {
+  uint32_t s = __builtin_amdgcn_readfirstlane(lds_ld(seq));
+  if (s >= want) return s != kAbort;
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-  while (true) {
-    const uint32_t s = __builtin_amdgcn_readfirstlane(lds_ld(seq));
+  for (uint32_t n = 1;; ++n) {
+    __builtin_amdgcn_s_sleep(1);
+    s = __builtin_amdgcn_readfirstlane(lds_ld(seq));
     if (s >= want) return s != kAbort;
-    if (__builtin_amdgcn_s_memrealtime() - t0 > p.spin_limit) {
+    if ((n & 255u) == 0 && __builtin_amdgcn_s_memrealtime() - t0 > p.spin_limit) {
       if ((threadIdx.x & 63) == 0) raise_error(p, ERR_TIMEOUT);
       return false;
     }
-    __builtin_amdgcn_s_sleep(1);
   }
 }
 

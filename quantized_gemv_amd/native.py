@@ -217,9 +217,20 @@ def _tensor_format(wfmt: int, name: str) -> str:
 
 
 def decode_codes(codec: int, d_codes, d_out) -> None:
-    """Decode codes with the kernel's register decoders (0: E4M3, 1: E2M1)."""
+    """Decode codes with the kernel's register decoders (0: E4M3, 1: E2M1;
+    2, 3: the same through the GEMV converters; 4: fp32 values rounded to
+    bf16 the way the kernel packs activations)."""
     L = load()
     rc = L.mk_decode_codes(codec, d_codes.data_ptr(), d_codes.numel(), d_out.data_ptr(), _stream())
+    if rc < 0:
+        raise MkError(rc, L.mk_status_str(rc).decode())
+
+
+def round_bf16(d_in, d_out) -> None:
+    """Round fp32 device values to bf16 the way the decode kernel packs
+    activations (codec hook 4), widened back to fp32 in `d_out`."""
+    L = load()
+    rc = L.mk_decode_codes(4, d_in.data_ptr(), d_in.numel(), d_out.data_ptr(), _stream())
     if rc < 0:
         raise MkError(rc, L.mk_status_str(rc).decode())
 

@@ -67,6 +67,26 @@ def test_codec_tables(native):
                           e2m1_decode(np.arange(16, dtype=np.uint8)).view(np.uint32))
 
 
+def test_bf16_activation_rounding(native):
+    """The kernel's activation packing (gfx950 v_cvt_pk_bf16_f32) rounds
+    fp32 to bf16 exactly as the oracle's round-to-nearest-even bit formula:
+    random values over many binades, exact bf16 values, and every kind of
+    tie (halfway values with even and odd bf16 neighbours)."""
+    from oracle.codecs import bf16_round
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal(1 << 16) * np.exp2(rng.integers(-40, 40, 1 << 16))).astype(np.float32)
+    b = x.view(np.uint32) & np.uint32(0xFFFF0000)
+    ties = (b | np.uint32(0x8000)).view(np.float32)                   # exactly halfway
+    near = (b | np.uint32(0x7FFF)).view(np.float32)                   # just below halfway
+    above = (b | np.uint32(0x8001)).view(np.float32)                  # just above halfway
+    vals = np.concatenate([x, b.view(np.float32), ties, near, above, np.float32([0.0, -0.0, 1.0, -1.0])])
+    d_in = torch.from_numpy(vals).cuda()
+    d_out = torch.empty_like(d_in)
+    native.round_bf16(d_in, d_out)
+    got = d_out.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), bf16_round(vals).view(np.uint32))
+
+
 @pytest.mark.parametrize("wfmt", FORMATS)
 def test_packed_bytes_bit_exact(native, master, wfmt):
     """G1: the GPU packer's canonical bytes equal the oracle quantizer's."""

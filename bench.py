@@ -28,10 +28,14 @@ def parse():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="qwen3_0p6b_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-steps", type=int, default=12)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the oracle baseline")
     ap.add_argument("--repeats", type=int, default=5, help="timed runs; the median is reported")
     ap.add_argument("--poll-sleep", type=int, default=-1, help="poll back-off 0/1 (-1: library default)")
+    ap.add_argument("--launch", type=int, default=-1, help="0 cooperative, 1 plain launch (-1: library default, plain when the grid fits at once)")
     ap.add_argument("--xray-dump", default="", help="with --xray: also save the raw records (.npy)")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="before decoding, run a plain device copy of this many MiB three times (the "
+                         "known-size reference for scaling HBM traffic counters under rocprofv3 --pmc)")
     ap.add_argument("--xray", action="store_true",
                     help="X-ray build: print the per-phase budget of the step at position P + K/2 "
                          "instead of the headline line")
@@ -63,9 +67,41 @@ def xray_report(dec, wl, K, prompt, dump=""):
             "argmax": rnd(tab.get(6 * L + 3, {}))}
 
 
-def cpu_baseline(master, wl, n_steps, prompt):
-    """The oracle as it stands, timed on this host: batched prefill of the
-    prompt (untimed), then `n_steps` decode steps (timed)."""
+def kernel_source_hash() -> str:
+    """sha256 over the decode kernel's sources: traffic counters taken from
+    another version of the kernel are not reported."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_gemv_amd", "csrc")
+    for name in ("mk_decode.hip", "mk_sync.h", "mk_shared.h", "mk_codec.h", "mk_xray.h"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode launch from profiles/decode_kernel_traffic.json
+    (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by the same counter's
+    reading for a plain copy of known size), or None when absent or taken on
+    another version of the kernel."""
+    path = os.path.join(ROOT, "profiles", "decode_kernel_traffic.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = d.get("workloads", {}).get(workload)
+    if not e or d.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return int(e["fetch_bytes_per_launch"] + e["write_bytes_per_launch"])
+
+
+def cpu_baseline(master, wl, n_steps, prompt, budget_s):
+    """The oracle as it stands, timed on this host over a bounded sample of
+    the timed workload: after an untimed batched prefill of the prompt, the
+    decode steps at positions P..P+n_steps-1 (a second pass over the same
+    positions if time is left), stopping once `budget_s` seconds of timed
+    decoding have been spent."""
     import numpy as np
     from oracle.model import Oracle
     try:
@@ -74,17 +110,25 @@ def cpu_baseline(master, wl, n_steps, prompt):
     except Exception:
         threads = len(os.sched_getaffinity(0))
     orc = Oracle(master, wl.wfmt, wl.prompt_len + n_steps + 1)
-    cache = orc.new_cache()
-    tok, _ = orc.prefill_batched(cache, prompt)
-    t0 = time.perf_counter()
-    for i in range(n_steps):
-        lg = orc.step(cache, tok, wl.prompt_len + i)
-        tok = int(np.argmax(lg))
-    dt = time.perf_counter() - t0
-    return {"value": n_steps / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n_steps} greedy decode steps at positions {wl.prompt_len}..{wl.prompt_len + n_steps - 1} "
-                      f"after an untimed batched prefill of the same {wl.prompt_len}-token prompt "
-                      f"({dt:.1f} s of numpy float32 on the host)"}
+    done, spent, last = 0, 0.0, wl.prompt_len
+    for _ in range(2):
+        cache = orc.new_cache()
+        tok, _ = orc.prefill_batched(cache, prompt)
+        for i in range(n_steps):
+            t0 = time.perf_counter()
+            lg = orc.step(cache, tok, wl.prompt_len + i)
+            tok = int(np.argmax(lg))
+            spent += time.perf_counter() - t0
+            done += 1
+            last = max(last, wl.prompt_len + i)
+            if spent >= budget_s:
+                break
+        if spent >= budget_s:
+            break
+    return {"value": done / spent, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} greedy decode steps at positions {wl.prompt_len}..{last} (the timed positions, "
+                      f"in up to two passes, each after an untimed batched prefill of the same "
+                      f"{wl.prompt_len}-token prompt); {spent:.1f} s of numpy float32 on the host"}
 
 
 def main():
@@ -108,12 +152,21 @@ def main():
     prompt = synth.make_prompt(sh.vocab, wl.prompt_len, wl.prompt_seed)
 
     dec = native.Decoder(sh, wl.wfmt, max_ctx, xray=args.xray,
-                         poll_sleep=None if args.poll_sleep < 0 else args.poll_sleep)
+                         poll_sleep=None if args.poll_sleep < 0 else args.poll_sleep,
+                         launch_mode=None if args.launch < 0 else args.launch)
     dev_master = native.master_to_device(master)
     dec.pack(dev_master)
     del dev_master
     torch.cuda.empty_cache()
 
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.mul(a, 1.0, out=b)   # reads and writes n*4 bytes
+        torch.cuda.synchronize()
+        del a, b
     if args.xray:
         print(json.dumps({"workload": wl.name, **xray_report(dec, wl, K, prompt, args.xray_dump)}), flush=True)
         dec.close()
@@ -171,13 +224,13 @@ def main():
         "weight_bytes_per_token": wbytes,
         "weight_roofline_pct": round(100.0 * wbytes * tps / (PEAK_HBM_GBPS * 1e9), 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(wl.name),
                      "kernel": "mk::decode_kernel",
                      "bytes_per_launch": int(algo)},
         "greedy_tokens_head": [int(t) for t in tokens_ref[:8]],
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(master, wl, args.cpu_steps, prompt)
+        out["cpu_baseline"] = cpu_baseline(master, wl, K, prompt, args.cpu_seconds)
     dec.close()
     print(json.dumps(out), flush=True)
 

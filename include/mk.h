@@ -177,6 +177,19 @@ int mk_check_device_error(mk_model* m, mk_stream_t s);
  * smaller than the number available. */
 int mk_get_trace(mk_model* m, mk_trace_rec* h_out, size_t cap, size_t* n_out);
 
+/* Test hook: copy back one activation vector of the last decode step, as
+ * one phase handed it to the next (the step's per-layer intermediates, for
+ * op-by-op parity).  vec: 0 the q, k and v GEMV outputs before the q/k norms
+ * ((nq + 2*nkv)*hd floats: the q heads, then the k heads, then the v heads);
+ * 1 the attention output ((nq*hd), bf16 values, q-head order); 2 the residual
+ * stream after the O-projection (hidden); 3 the SwiGLU output silu(gate)*up
+ * (intermediate, bf16 values); 4 the residual stream after the down
+ * projection (hidden).  `h_out` is host memory for exactly `n` floats, and n
+ * must be the vector's length.  Every word must carry the last step's tag
+ * (MK_E_STATE if no step ran, or a word was not written by it).  Waits for
+ * the device.  Errors: MK_E_INVALID, MK_E_STATE, MK_E_HIP. */
+int mk_read_exchange(mk_model* m, int32_t layer, int32_t vec, float* h_out, size_t n);
+
 /* Test hook: decode `n` codes with the kernel's own register decoders.
  * codec 0: E4M3 bytes -> fp32; codec 1: E2M1 (one code per byte, low
  * nibble) -> fp32; codecs 2 and 3: the same two formats through the
@@ -191,8 +204,15 @@ int mk_decode_codes(int32_t codec, const uint8_t* d_codes, int32_t n, float* d_o
  * key 4 test hook [0]: a non-zero value shifts every tag the kernel waits
  * for, so no wait can be satisfied and each one ends at the spin bound (used
  * to test the MK_E_TIMEOUT path without hanging); key 5 poll back-off
- * between exchange poll rounds, 0..16 units of about 512 clocks [0].  Keys
- * 1 and 2 are reserved.
+ * between exchange poll rounds, 0..16 units of about 512 clocks [0]; key 6
+ * launch mode [-1]: 0 launches each step cooperatively (the runtime checks
+ * that the grid is resident at once; on MI355X this adds about 20 us between
+ * consecutive steps), 1 with a plain launch, allowed only when mk_bind found
+ * that the device holds the whole grid at once, -1 plain when it does, else
+ * cooperative.  The kernel's waits assume that every workgroup runs: should
+ * another process hold compute units during a plain launch, they end at the
+ * spin bound with MK_E_TIMEOUT instead of hanging.
+ * Keys 1 and 2 are reserved.
  * Errors: MK_E_INVALID (unknown key, value out of range), MK_E_STATE. */
 int mk_set_option(mk_model* m, int32_t key, int64_t value);
 

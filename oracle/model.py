@@ -50,6 +50,21 @@ def tensor_format(wfmt: int, name: str) -> str:
 
 
 # ------------------------------------------------------------ primitives
+def quantize_tensor(bits: np.ndarray, fmt: str):
+    """Store one bf16 master tensor in `fmt` ("bf16", "fp8" or "fp4") and
+    return (the packed form, its float32 dequantization).  FP8 scales are per
+    row, so rows of a tensor may be quantized on their own; FP4 needs the
+    whole tensor (its tensor scale)."""
+    w = bf16_bits_to_f32(bits)
+    if fmt == "fp8":
+        p = quant_fp8_row(w)
+        return p, p.dequant()
+    if fmt == "fp4":
+        p = quant_fp4(w)
+        return p, p.dequant()
+    return bits, w
+
+
 def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float, dt=np.float32) -> np.ndarray:
     """g * (x / sqrt(mean(x^2) + eps)) along the last axis."""
     x = x.astype(dt)
@@ -145,18 +160,8 @@ class Oracle:
         self.cos, self.sin = rope_table(max_ctx, sh.head_dim, sh.rope_theta)
 
     def _prepare(self, layer: int, name: str, bits: np.ndarray) -> np.ndarray:
-        w = bf16_bits_to_f32(bits)
-        fmt = tensor_format(self.wfmt, name)
-        if fmt == "fp8":
-            p = quant_fp8_row(w)
-            self.packed[(layer, name)] = p
-            w = p.dequant()
-        elif fmt == "fp4":
-            p = quant_fp4(w)
-            self.packed[(layer, name)] = p
-            w = p.dequant()
-        else:
-            self.packed[(layer, name)] = bits
+        p, w = quantize_tensor(bits, tensor_format(self.wfmt, name))
+        self.packed[(layer, name)] = p
         return w.astype(self.dt)
 
     def _r(self, x: np.ndarray) -> np.ndarray:
@@ -170,9 +175,14 @@ class Oracle:
         z = np.zeros((sh.n_layers, sh.n_kv_heads, self.max_ctx, sh.head_dim), dtype=self.dt)
         return KVCache(z, z.copy())
 
-    def step(self, cache: KVCache, token: int, pos: int) -> np.ndarray:
+    def step(self, cache: KVCache, token: int, pos: int, trace: Optional[dict] = None) -> np.ndarray:
         """One decode step at position `pos`; writes K/V at `pos` and returns
-        float logits over the vocabulary."""
+        float logits over the vocabulary.  With `trace`, also records each
+        layer's intermediates under (layer, name): "qkv" the q, k, v GEMV
+        outputs (concatenated, before the q/k norms), "attn" the attention
+        output as the O-projection reads it, "x_o" the residual after the
+        O-projection, "h" the SwiGLU output, "x_d" the residual after the
+        down projection."""
         sh, dt = self.shape, self.dt
         if not (0 <= pos < self.max_ctx) or not (0 <= token < sh.vocab):
             raise ValueError("token or position out of range")
@@ -184,17 +194,24 @@ class Oracle:
             q = (w["q"] @ xn).astype(dt).reshape(nq, hd)
             k = (w["k"] @ xn).astype(dt).reshape(nkv, hd)
             v = (w["v"] @ xn).astype(dt).reshape(nkv, hd)
+            if trace is not None:
+                trace[(l, "qkv")] = np.concatenate([q.reshape(-1), k.reshape(-1), v.reshape(-1)])
             q = apply_rope(rmsnorm(q, w["q_norm"], self.eps, dt), cos, sin, dt)
             k = apply_rope(rmsnorm(k, w["k_norm"], self.eps, dt), cos, sin, dt)
             cache.k[l, :, pos] = self._r(k)
             cache.v[l, :, pos] = self._r(v)
             o = gqa_attention(q, cache.k[l, :, :pos + 1], cache.v[l, :, :pos + 1], dt)
-            x = (x + (w["o"] @ self._r(o.reshape(-1))).astype(dt)).astype(dt)
+            o = self._r(o.reshape(-1))
+            x = (x + (w["o"] @ o).astype(dt)).astype(dt)
             xn2 = self._r(rmsnorm(x, w["post_norm"], self.eps, dt))
             g = (w["gate"] @ xn2).astype(dt)
             u = (w["up"] @ xn2).astype(dt)
             h = self._r(silu(g, dt) * u)
+            if trace is not None:
+                trace[(l, "attn")], trace[(l, "x_o")], trace[(l, "h")] = o, x.copy(), h
             x = (x + (w["down"] @ h).astype(dt)).astype(dt)
+            if trace is not None:
+                trace[(l, "x_d")] = x.copy()
         xf = self._r(rmsnorm(x, self.final_norm, self.eps, dt))
         return (self.embed @ xf).astype(dt)
 

@@ -56,6 +56,8 @@ struct mk_model {
   std::vector<int32_t> sched;   // the work table (host copy)
   uint32_t tag_skew = 0;
   uint32_t poll_sleep = 0;
+  int launch_mode = -1;         // 0 cooperative, 1 plain launch of a grid that fits at once, -1 choose
+  int coresident = 0;           // decode workgroups the device holds at once (set by mk_bind)
   uint32_t epoch = 0;
   std::string err;
 };
@@ -349,8 +351,12 @@ int launch_step(mk_model* m, const int32_t* d_token, int pos, int32_t* d_next, f
   }
   const Params* dp = reinterpret_cast<const Params*>(m->d_scratch + m->params_off);
   const mk_config& c = m->cfg;
+  const bool coop = m->launch_mode == 0 || (m->launch_mode < 0 && m->P.grid > m->coresident);
+  if (!coop && m->P.grid > m->coresident)
+    return fail(m, MK_E_UNSUPPORTED, "plain launch: grid %d exceeds the %d workgroups the device holds at once",
+                m->P.grid, m->coresident);
   HIPCK(m, launch_decode(dp, c.wfmt, c.head_dim, c.n_q_heads / c.n_kv_heads, c.hidden, c.n_q_heads * c.head_dim,
-                         c.intermediate, m->P.grid, d_token, pos, m->epoch, d_next, d_logits, s));
+                         c.intermediate, m->P.grid, coop, d_token, pos, m->epoch, d_next, d_logits, s));
   return MK_OK;
 }
 
@@ -415,6 +421,13 @@ int mk_bind(mk_model* m, void* d_weights, void* d_kv, void* d_rope, void* d_scra
   if (grid > kMaxGrid) return fail(m, MK_E_UNSUPPORTED, "grid %d above %d", grid, kMaxGrid);
   const int gc = check_grid(m, grid);
   if (gc) return gc;
+  {
+    const mk_config& c = m->cfg;
+    int per_cu = 0;
+    HIPCK(m, decode_coresident(c.wfmt, c.head_dim, c.n_q_heads / c.n_kv_heads, c.hidden, c.n_q_heads * c.head_dim,
+                               c.intermediate, &per_cu));
+    m->coresident = per_cu * m->cus;
+  }
   layout_scratch(m, grid, false);  // never larger than the size reported for sizing_grid()
   m->P.grid = grid;
   m->d_weights = d_weights;
@@ -591,6 +604,39 @@ int mk_get_trace(mk_model* m, mk_trace_rec* h_out, size_t cap, size_t* n_out) {
   return MK_OK;
 }
 
+int mk_read_exchange(mk_model* m, int32_t layer, int32_t vec, float* h_out, size_t n) {
+  if (!m) return MK_E_INVALID;
+  const mk_config& c = m->cfg;
+  if (layer < 0 || layer >= c.n_layers) return fail(m, MK_E_INVALID, "mk_read_exchange: bad layer");
+  static const int kType[5] = {V_QKV, V_O, V_XO, V_H, V_XD};
+  static const bool kPairs[5] = {false, true, false, true, false};
+  if (vec < 0 || vec > 4) return fail(m, MK_E_INVALID, "mk_read_exchange: bad vector");
+  const size_t len = vec == 0 ? (size_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim
+                   : vec == 1 ? (size_t)c.n_q_heads * c.head_dim
+                   : vec == 3 ? (size_t)c.intermediate : (size_t)c.hidden;
+  if (!h_out || n != len) return fail(m, MK_E_INVALID, "mk_read_exchange: need %zu outputs", len);
+  if (!m->bound || m->epoch == 0) return fail(m, MK_E_STATE, "mk_read_exchange before any decode step");
+  const size_t words = kPairs[vec] ? len / 2 : len;
+  std::vector<uint64_t> w(words);
+  const Xch& X = m->P.x;
+  const uint64_t first = X.base + (uint64_t)layer * X.layer_words + X.off[kType[vec]];
+  HIPCK(m, hipMemcpy(w.data(), m->d_scratch + 8 * first, 8 * words, hipMemcpyDeviceToHost));
+  const uint32_t tag = (m->epoch << kPhaseBits) | (uint32_t)(2 + kTypes * layer + kType[vec]);
+  for (size_t i = 0; i < words; ++i) {
+    if ((uint32_t)w[i] != tag)
+      return fail(m, MK_E_STATE, "mk_read_exchange: word %zu was not written by the last step", i);
+    const uint32_t pay = (uint32_t)(w[i] >> 32);
+    if (kPairs[vec]) {
+      const uint32_t lo = pay << 16, hi = pay & 0xFFFF0000u;
+      memcpy(&h_out[2 * i], &lo, 4);
+      memcpy(&h_out[2 * i + 1], &hi, 4);
+    } else {
+      memcpy(&h_out[i], &pay, 4);
+    }
+  }
+  return MK_OK;
+}
+
 int mk_decode_codes(int32_t codec, const uint8_t* d_codes, int32_t n, float* d_out, mk_stream_t stream) {
   if (codec < 0 || codec > 4 || n < 0 || (n > 0 && (!d_codes || !d_out))) return MK_E_INVALID;
   const hipError_t e = launch_decode_codes(codec, d_codes, n, d_out, reinterpret_cast<hipStream_t>(stream));
@@ -618,6 +664,10 @@ int mk_set_option(mk_model* m, int32_t key, int64_t value) {
     case 5:
       if (value < 0 || value > 16) return fail(m, MK_E_INVALID, "poll back-off out of range");
       m->poll_sleep = (uint32_t)value;
+      break;
+    case 6:
+      if (value < -1 || value > 1) return fail(m, MK_E_INVALID, "launch mode must be -1, 0 or 1");
+      m->launch_mode = (int)value;
       break;
     default:
       return fail(m, MK_E_INVALID, "unknown option %d", key);

@@ -1140,9 +1140,7 @@ bool decode_shape_supported(int hd, int gs, int hidden, int qdim, int inter) {
   return false;
 }
 
-hipError_t launch_decode(const Params* d_params, int wfmt, int hd, int gs, int hidden, int qdim, int inter, int grid,
-                         const int32_t* d_token, int pos, uint32_t epoch, int32_t* d_next, float* d_logits,
-                         hipStream_t s) {
+static const void* decode_fn(int wfmt, int hd, int gs, int hidden, int qdim, int inter) {
   const void* fn = nullptr;
   const int nh = cdiv1024(hidden), nqd = cdiv1024(qdim), ni = cdiv1024(inter);
 #define MK_CASE(H_, G_, A_, B_, C_)                                                                             \
@@ -1153,9 +1151,23 @@ hipError_t launch_decode(const Params* d_params, int wfmt, int hd, int gs, int h
   }
   MK_SHAPES(MK_CASE)
 #undef MK_CASE
+  return fn;
+}
+
+hipError_t decode_coresident(int wfmt, int hd, int gs, int hidden, int qdim, int inter, int* per_cu) {
+  const void* fn = decode_fn(wfmt, hd, gs, hidden, qdim, inter);
+  if (!fn) return hipErrorInvalidValue;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, fn, kThreads, 0);
+}
+
+hipError_t launch_decode(const Params* d_params, int wfmt, int hd, int gs, int hidden, int qdim, int inter, int grid,
+                         bool cooperative, const int32_t* d_token, int pos, uint32_t epoch, int32_t* d_next,
+                         float* d_logits, hipStream_t s) {
+  const void* fn = decode_fn(wfmt, hd, gs, hidden, qdim, inter);
   if (!fn) return hipErrorInvalidValue;
   void* args[] = {&d_params, &d_token, &pos, &epoch, &d_next, &d_logits};
-  return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
+  if (cooperative) return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
+  return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
 }
 
 }  // namespace mk

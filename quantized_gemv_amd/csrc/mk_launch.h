@@ -1,4 +1,4 @@
-// Host-side entry points into mk_kernels.hip (used by the C-ABI layer).
+// Host-side entry points into the kernel sources (used by the C-ABI layer).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -7,9 +7,14 @@
 
 namespace mk {
 // `d_params` points to a Params copy in device memory that stays unchanged while the kernel runs.
+// `cooperative`: hipLaunchCooperativeKernel (the runtime guarantees that the
+// whole grid is resident) or a plain launch (the caller has checked with
+// decode_coresident() that the grid fits the device at once).
 hipError_t launch_decode(const Params* d_params, int wfmt, int hd, int gs, int hidden, int qdim, int inter, int grid,
-                         const int32_t* d_token, int pos, uint32_t epoch, int32_t* d_next, float* d_logits,
-                         hipStream_t s);
+                         bool cooperative, const int32_t* d_token, int pos, uint32_t epoch, int32_t* d_next,
+                         float* d_logits, hipStream_t s);
+// Workgroups of the decode kernel that one compute unit holds at once.
+hipError_t decode_coresident(int wfmt, int hd, int gs, int hidden, int qdim, int inter, int* per_cu);
 bool decode_shape_supported(int hd, int gs, int hidden, int qdim, int inter);
 hipError_t launch_pack_bf16(const uint16_t* src, int N, int K, uint16_t* dst, int row_off, int row_step,
                             hipStream_t s);

@@ -18,7 +18,10 @@ from .build import lib_path
 MK_OK, MK_E_INVALID, MK_E_UNSUPPORTED, MK_E_STATE, MK_E_HIP, MK_E_TIMEOUT = 0, -1, -2, -3, -4, -5
 BF16, FP8_ROW, FP4_MIX = 0, 1, 2
 MATRICES = {"q": 0, "k": 1, "v": 2, "o": 3, "gate": 4, "up": 5, "down": 6, "embed": 7}
-OPT_GRID, OPT_SPIN_LIMIT, OPT_TAG_SKEW, OPT_POLL_SLEEP = 0, 3, 4, 5
+# mk_read_exchange vectors: q/k/v GEMV outputs, attention output, residual after O, SwiGLU output,
+# residual after down
+EXCHANGE = {"qkv": 0, "attn": 1, "x_o": 2, "h": 3, "x_d": 4}
+OPT_GRID, OPT_SPIN_LIMIT, OPT_TAG_SKEW, OPT_POLL_SLEEP, OPT_LAUNCH_MODE = 0, 3, 4, 5, 6
 
 
 class MkError(RuntimeError):
@@ -73,6 +76,8 @@ def load(xray: bool = False) -> ctypes.CDLL:
         "mk_pack_weights": (ctypes.c_int, [_VP, P(_VP), ctypes.c_int32, _VP]),
         "mk_read_packed": (ctypes.c_int, [_VP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP,
                                           P(ctypes.c_float)]),
+        "mk_read_exchange": (ctypes.c_int, [_VP, ctypes.c_int32, ctypes.c_int32, P(ctypes.c_float),
+                                            ctypes.c_size_t]),
         "mk_prefill": (ctypes.c_int32, [_VP, P(ctypes.c_int32), ctypes.c_int32, _VP]),
         "mk_decode_step": (ctypes.c_int32, [_VP, ctypes.c_int32, ctypes.c_int32, _VP]),
         "mk_decode_step_async": (ctypes.c_int, [_VP, _VP, ctypes.c_int32, _VP, _VP, _VP]),
@@ -107,7 +112,8 @@ class Decoder:
     """One model handle with its device buffers (allocated through torch)."""
 
     def __init__(self, shape, wfmt: int, max_ctx: int, xray: bool = False, grid: int = 0,
-                 spin_limit: Optional[int] = None, poll_sleep: Optional[int] = None):
+                 spin_limit: Optional[int] = None, poll_sleep: Optional[int] = None,
+                 launch_mode: Optional[int] = None):
         import torch
         self.lib = load(xray)
         self.shape, self.wfmt, self.max_ctx = shape, wfmt, max_ctx
@@ -121,6 +127,8 @@ class Decoder:
             self._check(self.lib.mk_set_option(self.h, OPT_SPIN_LIMIT, spin_limit))
         if poll_sleep is not None:
             self._check(self.lib.mk_set_option(self.h, OPT_POLL_SLEEP, poll_sleep))
+        if launch_mode is not None:
+            self._check(self.lib.mk_set_option(self.h, OPT_LAUNCH_MODE, launch_mode))
         self.sizes = mk_sizes()
         self._check(self.lib.mk_query_sizes(self.h, ctypes.byref(self.sizes)))
         dev = torch.device("cuda", torch.cuda.current_device())
@@ -172,6 +180,16 @@ class Decoder:
                                             scales.ctypes.data, bscales.ctypes.data, ctypes.byref(ts)))
         return codes, (scales if fmt == "fp8" else None), (bscales if fmt == "fp4" else None), \
             (np.float32(ts.value) if fmt == "fp4" else None)
+
+    def read_exchange(self, layer: int, vec: str) -> np.ndarray:
+        """The last step's activation `vec` of `layer` (see EXCHANGE)."""
+        sh = self.shape
+        n = {"qkv": (sh.n_q_heads + 2 * sh.n_kv_heads) * sh.head_dim, "attn": sh.n_q_heads * sh.head_dim,
+             "x_o": sh.hidden, "h": sh.intermediate, "x_d": sh.hidden}[vec]
+        out = np.empty(n, np.float32)
+        self._check(self.lib.mk_read_exchange(self.h, layer, EXCHANGE[vec],
+                                              out.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), n))
+        return out
 
     def prefill(self, tokens: Sequence[int]) -> int:
         arr = (ctypes.c_int32 * len(tokens))(*[int(t) for t in tokens])

@@ -38,7 +38,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("mk_create", "mk_query_sizes", "mk_bind", "mk_pack_weights", "mk_prefill", "mk_decode_step",
-              "mk_decode_step_async", "mk_get_trace", "mk_read_packed", "mk_destroy"):
+              "mk_decode_step_async", "mk_get_trace", "mk_read_packed", "mk_read_exchange", "mk_destroy"):
         assert n in names
 
 
@@ -101,12 +101,20 @@ def test_calls_out_of_order_and_bad_arguments(lib):
     assert lib.mk_read_packed(h, 0, 0, ctypes.c_void_p(256), None, None, None) == native.MK_E_STATE
     assert lib.mk_read_packed(h, 0, 9, ctypes.c_void_p(256), None, None, None) == native.MK_E_INVALID
     assert lib.mk_read_packed(h, 5, 0, ctypes.c_void_p(256), None, None, None) == native.MK_E_INVALID
+    buf = (ctypes.c_float * synth.TINY.hidden)()
+    assert lib.mk_read_exchange(h, 0, 2, buf, synth.TINY.hidden) == native.MK_E_STATE     # no step yet
+    assert lib.mk_read_exchange(h, 0, 5, buf, synth.TINY.hidden) == native.MK_E_INVALID   # bad vector
+    assert lib.mk_read_exchange(h, 2, 2, buf, synth.TINY.hidden) == native.MK_E_INVALID   # bad layer
+    assert lib.mk_read_exchange(h, 0, 2, buf, 7) == native.MK_E_INVALID                   # wrong length
     # options
     assert lib.mk_set_option(h, 99, 0) == native.MK_E_INVALID
     assert lib.mk_set_option(h, native.OPT_GRID, -1) == native.MK_E_INVALID
     assert lib.mk_set_option(h, 1, 0) == native.MK_E_INVALID          # reserved keys
     assert lib.mk_set_option(h, 2, 64) == native.MK_E_INVALID
     assert lib.mk_set_option(h, native.OPT_POLL_SLEEP, 17) == native.MK_E_INVALID
+    assert lib.mk_set_option(h, native.OPT_LAUNCH_MODE, 2) == native.MK_E_INVALID
+    assert lib.mk_set_option(h, native.OPT_LAUNCH_MODE, -2) == native.MK_E_INVALID
+    assert lib.mk_set_option(h, native.OPT_LAUNCH_MODE, 1) == native.MK_OK
     assert lib.mk_set_option(h, native.OPT_SPIN_LIMIT, 1000) == native.MK_OK
     assert lib.mk_last_error(h)
     n_out = ctypes.c_size_t(7)

@@ -1,0 +1,183 @@
+"""Op-by-op GPU parity through the C-ABI.
+
+After a decode step, every phase's output is read back (mk_read_exchange and
+the caller-owned KV cache) and recomputed by tests/opcheck.py with the
+oracle's functions from the GPU's own input to that phase (tolerances there).
+
+Tiny decoder: every layer and every output.  Qwen3-0.6B shape, launched as
+the benchmark launches it (one workgroup per compute unit): a sample of
+layers and of output rows, at the benchmark's first timed position and at
+positions whose attention streams cache passes beyond the ones held in
+registers.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle.model import Oracle, argmax_lowest
+from opcheck import Weights, check_step
+
+pytestmark = pytest.mark.gpu
+
+FORMATS = [synth.BF16, synth.FP8_ROW, synth.FP4_MIX]
+
+
+@pytest.fixture(scope="module")
+def native():
+    from quantized_gemv_amd import native as n
+    assert torch.cuda.is_available()
+    return n
+
+
+class GpuStep:
+    """The intermediates of the decoder's last step, for check_step."""
+
+    def __init__(self, dec, sh):
+        self.dec, self.sh = dec, sh
+
+    def read_exchange(self, layer, vec):
+        return self.dec.read_exchange(layer, vec)
+
+    def kv_bits(self):
+        sh, d = self.sh, self.dec
+        raw = d.kv[: sh.n_layers * 2 * sh.n_kv_heads * d.max_ctx * sh.head_dim * 2].cpu().numpy()
+        return raw.view(np.uint16).reshape(sh.n_layers, 2, sh.n_kv_heads, d.max_ctx, sh.head_dim)
+
+
+def _step(dec, sh, token, pos):
+    tok = torch.tensor([token, 0], dtype=torch.int32, device="cuda")
+    lg = torch.zeros(sh.vocab, dtype=torch.float32, device="cuda")
+    dec.decode_step_async(tok[0:1], pos, tok[1:2], lg)
+    torch.cuda.synchronize()
+    dec.check_device_error()
+    logits = lg.cpu().numpy()
+    assert int(tok[1].item()) == argmax_lowest(logits)
+    return logits
+
+
+def _decoder(native, shape, master, wfmt, max_ctx):
+    d = native.Decoder(shape, wfmt, max_ctx)
+    d.pack(native.master_to_device(master))
+    return d
+
+
+# ------------------------------------------------------------------ tiny
+@pytest.fixture(scope="module")
+def tiny_master():
+    return synth.make_weights(synth.TINY, 0)
+
+
+@pytest.mark.parametrize("wfmt", FORMATS)
+def test_ops_tiny_every_output(native, tiny_master, wfmt):
+    """All layers, all outputs, at position 39 (after a 39-token prefill)."""
+    sh = synth.TINY
+    toks = synth.make_prompt(sh.vocab, 40, 11)
+    d = _decoder(native, sh, tiny_master, wfmt, 64)
+    d.prefill(toks[:39])
+    logits = _step(d, sh, int(toks[39]), 39)
+    check_step(GpuStep(d, sh), Weights(tiny_master, wfmt), sh, int(toks[39]), 39, logits, range(sh.n_layers),
+               np.random.default_rng(0))
+    d.close()
+
+
+def test_ops_tiny_streamed_attention(native, tiny_master):
+    """Positions 400 and 470: one and two cache passes stream after the
+    seven held in registers."""
+    sh = synth.TINY
+    toks = synth.make_prompt(sh.vocab, 471, 12)
+    d = _decoder(native, sh, tiny_master, synth.BF16, 480)
+    W = Weights(tiny_master, synth.BF16)
+    d.prefill(toks[:400])
+    logits = _step(d, sh, int(toks[400]), 400)
+    check_step(GpuStep(d, sh), W, sh, int(toks[400]), 400, logits, range(sh.n_layers), np.random.default_rng(0))
+    for pos in range(401, 470):
+        _step(d, sh, int(toks[pos]), pos)
+    logits = _step(d, sh, int(toks[470]), 470)
+    check_step(GpuStep(d, sh), W, sh, int(toks[470]), 470, logits, range(sh.n_layers), np.random.default_rng(0))
+    d.close()
+
+
+def test_exchange_needs_a_step(native, tiny_master):
+    d = _decoder(native, synth.TINY, tiny_master, synth.BF16, 64)
+    with pytest.raises(native.MkError):
+        d.read_exchange(0, "x_o")
+    d.close()
+
+
+# ------------------------------------------------------------ Qwen3-0.6B
+@pytest.fixture(scope="module")
+def q_master():
+    return synth.make_weights(synth.QWEN3_0P6B, 0)
+
+
+Q_LAYERS = (0, 1, 14, 27)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("wfmt", FORMATS)
+def test_ops_qwen3_0p6b_sampled(native, q_master, wfmt):
+    """The benchmark's workload and launch: the 128-token prompt, then the
+    first timed step (position 128); layers 0, 1, 14, 27 and the LM head,
+    160 sampled rows of every matrix (plus the first, the last and the
+    argmax row)."""
+    sh = synth.QWEN3_0P6B
+    wl = {synth.BF16: "qwen3_0p6b_bf16", synth.FP8_ROW: "qwen3_0p6b_fp8",
+          synth.FP4_MIX: "qwen3_0p6b_fp4mix"}[wfmt]
+    prompt = synth.make_prompt(sh.vocab, 128, synth.WORKLOADS[wl].prompt_seed)
+    d = _decoder(native, sh, q_master, wfmt, 512)
+    first = d.prefill(prompt)
+    logits = _step(d, sh, first, 128)
+    check_step(GpuStep(d, sh), Weights(q_master, wfmt), sh, first, 128, logits, Q_LAYERS, np.random.default_rng(1),
+               n_sample=160)
+    d.close()
+
+
+@pytest.mark.timeout(900)
+def test_ops_qwen3_0p6b_streamed_attention(native, q_master):
+    """Positions 400 and 460 (one and two streamed cache passes), bf16."""
+    sh = synth.QWEN3_0P6B
+    toks = synth.make_prompt(sh.vocab, 461, 13)
+    d = _decoder(native, sh, q_master, synth.BF16, 512)
+    W = Weights(q_master, synth.BF16)
+    d.prefill(toks[:400])
+    logits = _step(d, sh, int(toks[400]), 400)
+    check_step(GpuStep(d, sh), W, sh, int(toks[400]), 400, logits, Q_LAYERS, np.random.default_rng(2), n_sample=96)
+    for pos in range(401, 460):
+        _step(d, sh, int(toks[pos]), pos)
+    logits = _step(d, sh, int(toks[460]), 460)
+    check_step(GpuStep(d, sh), W, sh, int(toks[460]), 460, logits, Q_LAYERS, np.random.default_rng(3), n_sample=96)
+    d.close()
+
+
+@pytest.mark.timeout(900)
+def test_end_to_end_qwen3_0p6b_bf16(native, q_master):
+    """Whole-step parity at the benchmark's size: after the benchmark's
+    prompt, 4 teacher-forced steps (positions 128..131) against the full
+    oracle: logits within relative L2 1e-2, and the fused argmax equal to
+    the oracle's where the oracle's top-2 gap is at least 1e-3 (else a valid
+    argmax within 1e-2 of the oracle's maximum)."""
+    sh = synth.QWEN3_0P6B
+    wl = synth.WORKLOADS["qwen3_0p6b_bf16"]
+    prompt = synth.make_prompt(sh.vocab, wl.prompt_len, wl.prompt_seed)
+    orc = Oracle(q_master, synth.BF16, 160)
+    cache = orc.new_cache()
+    want, last = orc.prefill_batched(cache, prompt)
+    d = _decoder(native, sh, q_master, synth.BF16, 160)
+    got = d.prefill(prompt)
+    top2 = np.sort(last)[-2:]
+    if top2[1] - top2[0] >= 1e-3:
+        assert got == want
+    forced = synth.make_prompt(sh.vocab, 4, 21)
+    for i, t in enumerate(forced):
+        pos = wl.prompt_len + i
+        logits = _step(d, sh, int(t), pos)
+        ref = orc.step(cache, int(t), pos)
+        assert np.linalg.norm(logits - ref) / np.linalg.norm(ref) <= 1e-2, pos
+        g = argmax_lowest(logits)
+        top2 = np.sort(ref)[-2:]
+        if top2[1] - top2[0] >= 1e-3:
+            assert g == argmax_lowest(ref), pos
+        else:
+            assert ref[g] >= ref.max() - 1e-2, pos
+    d.close()

@@ -32,6 +32,11 @@ def parse():
     ap.add_argument("--repeats", type=int, default=5, help="timed runs; the median is reported")
     ap.add_argument("--poll-sleep", type=int, default=-1, help="poll back-off 0/1 (-1: library default)")
     ap.add_argument("--launch", type=int, default=-1, help="0 cooperative, 1 plain launch (-1: library default, plain when the grid fits at once)")
+    ap.add_argument("--prompt-len", type=int, default=0,
+                    help="position sweep: prompt length in place of the workload's (the line then names "
+                         "the workload '<name>@<prompt_len>')")
+    ap.add_argument("--split-chunk", type=int, default=-1,
+                    help="split attention: cached positions per workgroup (0 off, -1 library default)")
     ap.add_argument("--xray-dump", default="", help="with --xray: also save the raw records (.npy)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="before decoding, run a plain device copy of this many MiB three times (the "
@@ -144,6 +149,10 @@ def main():
     from quantized_gemv_amd import native
 
     wl = synth.WORKLOADS[args.workload]
+    if args.prompt_len > 0:
+        import dataclasses
+        wl = dataclasses.replace(wl, name=f"{wl.name}@{args.prompt_len}", prompt_len=args.prompt_len,
+                                 max_ctx=args.prompt_len + args.steps + 8)
     sh = wl.shape
     K, W = args.steps, args.warmup
     max_ctx = max(wl.max_ctx, wl.prompt_len + max(K, W) + 1)
@@ -153,7 +162,8 @@ def main():
 
     dec = native.Decoder(sh, wl.wfmt, max_ctx, xray=args.xray,
                          poll_sleep=None if args.poll_sleep < 0 else args.poll_sleep,
-                         launch_mode=None if args.launch < 0 else args.launch)
+                         launch_mode=None if args.launch < 0 else args.launch,
+                         split_chunk=None if args.split_chunk < 0 else args.split_chunk)
     dev_master = native.master_to_device(master)
     dec.pack(dev_master)
     del dev_master
@@ -219,7 +229,8 @@ def main():
                    "positions": [wl.prompt_len, wl.prompt_len + K - 1],
                    "weight_format": synth.WFMT_NAMES[wl.wfmt], "accumulate": "f32", "batch": 1,
                    "grid": "one workgroup per CU: 1 courier + 7 compute waves; attention on one "
-                           "workgroup per KV head", "timed_runs": len(times),
+                           "workgroup per KV head, split over the workgroups of its XCD from 448 "
+                           "cached positions on", "timed_runs": len(times),
                    "run_seconds": [round(t, 6) for t in times]},
         "weight_bytes_per_token": wbytes,
         "weight_roofline_pct": round(100.0 * wbytes * tps / (PEAK_HBM_GBPS * 1e9), 2),

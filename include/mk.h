@@ -211,7 +211,14 @@ int mk_decode_codes(int32_t codec, const uint8_t* d_codes, int32_t n, float* d_o
  * that the device holds the whole grid at once, -1 plain when it does, else
  * cooperative.  The kernel's waits assume that every workgroup runs: should
  * another process hold compute units during a plain launch, they end at the
- * spin bound with MK_E_TIMEOUT instead of hanging.
+ * spin bound with MK_E_TIMEOUT instead of hanging.  Keys 7 and 8, split
+ * attention [64, 448]: with key 7 = c > 0, a step at a position pos at or
+ * past key 8 spreads KV head g's cached positions over its home workgroup and
+ * ns = min(helpers, pos / c) helper workgroups on the same XCD (helpers = the
+ * GEMV workgroups there, at most 32 per head), each taking an equal slice;
+ * the home merges their partial (maximum, sum, output) triples with the
+ * log-sum-exp rule.  c = 0 turns it off.  (On MI355X at the 0.6B shape the
+ * split path is faster from about 450 cached positions on.)
  * Keys 1 and 2 are reserved.
  * Errors: MK_E_INVALID (unknown key, value out of range), MK_E_STATE. */
 int mk_set_option(mk_model* m, int32_t key, int64_t value);

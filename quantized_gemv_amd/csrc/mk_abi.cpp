@@ -5,6 +5,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <new>
 #include <string>
@@ -57,6 +58,9 @@ struct mk_model {
   uint32_t tag_skew = 0;
   uint32_t poll_sleep = 0;
   int launch_mode = -1;         // 0 cooperative, 1 plain launch of a grid that fits at once, -1 choose
+  int split_chunk = 64;         // split attention: cached positions per participant (0: off)
+  int split_from = 448;         // split attention from this position on
+  int split_n = 0;              // helpers per KV head in the work table
   int coresident = 0;           // decode workgroups the device holds at once (set by mk_bind)
   uint32_t epoch = 0;
   std::string err;
@@ -143,6 +147,13 @@ void layout_weights(mk_model* m) {
 
 // Lay out the scratch buffer: per-layer exchange vectors, argmax words, the
 // error word, the zero page, the work table, the params copy, token slots.
+// Words of one split-attention partial: the outputs of the KV head's q heads,
+// their maxima and sums, padded to 128 bytes.
+uint64_t split_pw(const mk_config& c) {
+  const uint64_t gs = c.n_q_heads / c.n_kv_heads;
+  return (gs * c.head_dim + 2 * gs + 15) / 16 * 16;
+}
+
 void layout_scratch(mk_model* m, int grid, bool for_sizing = true) {
   const mk_config& c = m->cfg;
   Xch& X = m->P.x;
@@ -150,7 +161,8 @@ void layout_scratch(mk_model* m, int grid, bool for_sizing = true) {
   auto al = [](uint64_t w) { return (w + 15) / 16 * 16; };   // 128-byte boundaries
   X.base = 0;
   uint64_t lw = 0;
-  const uint64_t sizes[kTypes] = {(nq + 2 * nkv) * hd, 0, nq * hd / 2, H, I / 2, H};
+  const uint64_t pw = split_pw(c);
+  const uint64_t sizes[kTypes] = {(nq + 2 * nkv) * hd, nkv * (uint64_t)kMaxSplit * pw, nq * hd / 2, H, I / 2, H};
   for (int t = 0; t < kTypes; ++t) {
     X.off[t] = lw;
     lw = al(lw + sizes[t]);
@@ -187,7 +199,7 @@ void layout_scratch(mk_model* m, int grid, bool for_sizing = true) {
 //  * O, gate/up (units of four rows = one output word), down: over the
 //    workgroups without attention; each matrix starts at a different wave
 //    so every wave gets a similar share.
-const char* build_sched(const mk_config& c, int grid, std::vector<int32_t>& tab) {
+const char* build_sched(const mk_config& c, int grid, std::vector<int32_t>& tab, int* split_n = nullptr) {
   const int nkv = c.n_kv_heads, hd = c.head_dim, nq = c.n_q_heads, gs = nq / nkv;
   const int H = c.hidden, I = c.intermediate;
   const int nA = nkv;
@@ -240,7 +252,28 @@ const char* build_sched(const mk_config& c, int grid, std::vector<int32_t>& tab)
   if (!deal(rh, gw, 0, S_O, kMaxO)) return "too many O rows per wave for this grid";
   if (!deal(ri, gw, 0, S_GU, kMaxGU)) return "too many gate/up units per wave for this grid";
   if (!deal(rh, gw, 3, S_D, kMaxD)) return "too many down rows per wave for this grid";
-  // per-workgroup inputs, in the courier's order: xd, qkv, o, xo, h
+  // split attention: the GEMV workgroups of an XCD that holds KV heads help
+  // those heads (in turn), up to the partials the home holds in LDS
+  const int cap = kMaxSplit;
+  std::vector<int> helpers(nkv, 0);
+  for (int sl = 0; sl < 8; ++sl) {
+    std::vector<int> heads;
+    for (int g = sl; g < nkv; g += 8) heads.push_back(g);
+    if (heads.empty()) continue;
+    int idx = 0;
+    for (int wg = sl; wg < grid; wg += 8) {
+      if (wg < nA) continue;
+      const int g = heads[idx % heads.size()], i = idx / (int)heads.size() + 1;
+      ++idx;
+      if (i > cap) continue;
+      hdr(wg, S_SPLIT) = g;
+      hdr(wg, S_SPLIT_IDX) = i;
+      helpers[g] = std::max(helpers[g], i);
+    }
+  }
+  if (split_n) *split_n = *std::min_element(helpers.begin(), helpers.end());
+  // per-workgroup inputs, in the courier's order: xd, qkv, o, xo, h (with
+  // split attention: xd, qkv, the helped head's q, o, xo, h)
   for (int wg = 0; wg < grid; ++wg) {
     bool q = false, o = false, gu = false, d = false;
     for (int cw = 0; cw < kCW; ++cw) {
@@ -255,6 +288,12 @@ const char* build_sched(const mk_config& c, int grid, std::vector<int32_t>& tab)
     int n = 0;
     for (int i = 0; i < 5; ++i) hdr(wg, slot[i]) = need[i] ? n++ : -1;
     hdr(wg, S_NIN) = n;
+    n = need[0] + need[1];
+    hdr(wg, S_IQS_L) = hdr(wg, S_SPLIT) >= 0 ? n++ : -1;
+    hdr(wg, S_IO_L) = need[2] ? n++ : -1;
+    hdr(wg, S_IXO_L) = need[3] ? n++ : -1;
+    hdr(wg, S_IH_L) = need[4] ? n++ : -1;
+    hdr(wg, S_NIN_L) = n;
     hdr(wg, S_FLAGS) = (need[0] ? 1 : 0) | (o ? 2 : 0) | (need[3] ? 4 : 0) | (d ? 8 : 0);
   }
   return nullptr;
@@ -320,6 +359,8 @@ int sync_params(mk_model* m, hipStream_t s) {
   P.tag_skew = m->tag_skew;
   P.poll_sleep = m->poll_sleep;
   P.n_phases = n_phases(c);
+  P.split_max = kMaxSplit;
+  P.split_pw = (int)split_pw(c);
   HIPCK(m, hipMemcpyAsync(m->d_scratch + m->params_off, &P, sizeof(Params), hipMemcpyHostToDevice, s));
   HIPCK(m, hipStreamSynchronize(s));  // the host copy is a stack-independent member, but keep ordering simple
   m->params_dirty = false;
@@ -352,11 +393,12 @@ int launch_step(mk_model* m, const int32_t* d_token, int pos, int32_t* d_next, f
   const Params* dp = reinterpret_cast<const Params*>(m->d_scratch + m->params_off);
   const mk_config& c = m->cfg;
   const bool coop = m->launch_mode == 0 || (m->launch_mode < 0 && m->P.grid > m->coresident);
+  const int ns = m->split_chunk > 0 && pos >= m->split_from ? std::min(m->split_n, pos / m->split_chunk) : 0;
   if (!coop && m->P.grid > m->coresident)
     return fail(m, MK_E_UNSUPPORTED, "plain launch: grid %d exceeds the %d workgroups the device holds at once",
                 m->P.grid, m->coresident);
   HIPCK(m, launch_decode(dp, c.wfmt, c.head_dim, c.n_q_heads / c.n_kv_heads, c.hidden, c.n_q_heads * c.head_dim,
-                         c.intermediate, m->P.grid, coop, d_token, pos, m->epoch, d_next, d_logits, s));
+                         c.intermediate, m->P.grid, coop, d_token, pos, ns, m->epoch, d_next, d_logits, s));
   return MK_OK;
 }
 
@@ -438,7 +480,7 @@ int mk_bind(mk_model* m, void* d_weights, void* d_kv, void* d_rope, void* d_scra
   m->bound = true;
   m->params_dirty = true;
   m->epoch = 0;
-  const char* why = build_sched(m->cfg, grid, m->sched);
+  const char* why = build_sched(m->cfg, grid, m->sched, &m->split_n);
   if (why) return fail(m, MK_E_UNSUPPORTED, "grid %d: %s", grid, why);
   HIPCK(m, hipMemsetAsync(d_scratch, 0, m->scratch_bytes, s));
   HIPCK(m, hipMemcpyAsync(m->d_scratch + 8 * m->P.x.sched, m->sched.data(), m->sched.size() * sizeof(int32_t),
@@ -668,6 +710,14 @@ int mk_set_option(mk_model* m, int32_t key, int64_t value) {
     case 6:
       if (value < -1 || value > 1) return fail(m, MK_E_INVALID, "launch mode must be -1, 0 or 1");
       m->launch_mode = (int)value;
+      break;
+    case 7:
+      if (value < 0 || value > (1 << 20)) return fail(m, MK_E_INVALID, "split chunk out of range");
+      m->split_chunk = (int)value;
+      break;
+    case 8:
+      if (value < 0 || value > (1 << 20)) return fail(m, MK_E_INVALID, "split start position out of range");
+      m->split_from = (int)value;
       break;
     default:
       return fail(m, MK_E_INVALID, "unknown option %d", key);

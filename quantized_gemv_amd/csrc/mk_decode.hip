@@ -106,6 +106,9 @@ struct Smem {
   alignas(16) float sp[GS];              // this position's scores (log2 units)
   alignas(16) float gq[HD], gk[HD];      // q/k-norm gains of the layer
   alignas(16) float rc[HD / 2], rs[HD / 2];   // this position's RoPE cos, sin
+  // split attention, home workgroup: the helpers' partials (outputs, then the
+  // per-head maxima and sums)
+  alignas(16) float spart[kMaxSplit][GS * HD + 2 * GS];
   // argmax
   alignas(16) float best[kCW];
   alignas(16) int32_t bidx[kCW];
@@ -306,7 +309,10 @@ __device__ __forceinline__ void gain_load(__amdgpu_buffer_rsrc_t rw, uint32_t of
   }
 }
 
-template <int WF, int HD, int GS, int NH, int NQ, int NI>
+// LONG: the split-attention variant (for long contexts): every GEMV
+// workgroup on a KV head's XCD also takes a slice of that head's cached
+// positions, and the head's home workgroup merges the slices.
+template <int WF, int HD, int GS, int NH, int NQ, int NI, bool LONG>
 struct Kern {
   static constexpr uint32_t F_LIN = WF == 0 ? FMT_BF16 : (WF == 1 ? FMT_FP8 : FMT_FP4);  // q, k, v, o, gate, up
   static constexpr uint32_t F_8 = WF == 0 ? FMT_BF16 : FMT_FP8;                          // down, embed / LM head
@@ -319,15 +325,20 @@ struct Kern {
   static constexpr int WPL = DPL / 2;          // bf16 pairs per lane
   static constexpr int PPW = 8;                // positions per wave per pass
   static constexpr int PPP = PPW * kCW;        // positions per pass
-  static constexpr int MP = 7;                 // passes held in registers
+  // passes the home holds in registers (the split variant keeps fewer: its
+  // home also gathers and merges the helpers' partials)
+  static constexpr int MP = LONG ? 5 : 7;
   static constexpr int NOUT = GS * HD;         // outputs of one attention workgroup
+  static constexpr int PP = (NOUT + 2 * GS) / 2;   // word pairs of one helper partial
+  static constexpr int KP = kSplitGatherK;     // helper-partial pairs per lane and round of the home's gather
+  static_assert(NOUT <= kCW * 64, "one merge thread per attention output");
   typedef Smem<HD, GS, NH, NQ, NI> S;
 
   // ------------------------------------------------------------ courier
   // The inputs this workgroup needs, in order, for every layer; then the
   // final residual for the LM head; workgroup 0 then reduces the argmax.
-  static __device__ bool courier(const Params& p, S& s, const int* hdr, int token, int pos, uint32_t epoch,
-                                 int32_t* d_next) {
+  static __device__ bool courier(const Params& p, S& s, const int* hdr, int token, int pos, int ns,
+                                 uint32_t epoch, int32_t* d_next) {
     MK_GLOBAL const uint8_t* const W = p.w;
     const int lane = lane_id();
     const int H = p.H, L = p.L;
@@ -377,12 +388,26 @@ struct Kern {
       // ---- q, k, v of KV head `att`: q/k RMSNorm, RoPE, KV append
       if (att >= 0) {
         XR_PUT(s, ph + 1, XR_START);
-        if (!attention_input(p, s, l, att, pos, epoch, rs)) return abort(s);
+        if (!attention_input<true>(p, s, l, att, pos, epoch, rs)) return abort(s);
         hand_over(&s.seq, ++seq);
         XR_PUT(s, ph + 1, XR_HANDOFF);
         lds_barrier();   // q, k and v are normed, roped and appended
         lds_barrier();   // every compute wave has written its partial outputs
+        if (LONG && ns > 0) lds_barrier();   // the helpers' partials are in LDS
         lds_barrier();   // and merged them: the LDS arrays may be reused
+      }
+      // ---- split attention helper: q of KV head hdr[S_SPLIT]
+      if (LONG && hdr[S_SPLIT] >= 0) {
+        if (hdr[S_SPLIT_IDX] <= ns) {
+          XR_PUT(s, ph + 1, XR_START);
+          if (!attention_input<false>(p, s, l, hdr[S_SPLIT], pos, epoch, rs)) return abort(s);
+          hand_over(&s.seq, ++seq);
+          XR_PUT(s, ph + 1, XR_HANDOFF);
+          lds_barrier();   // q is normed and roped
+          lds_barrier();   // every compute wave has written its partial outputs
+        } else {
+          hand_over(&s.seq, ++seq);   // no slice this step; keeps the input numbering
+        }
       }
       // ---- attention output
       if (flags & 2) {
@@ -486,6 +511,8 @@ struct Kern {
   // Gather q (GS heads), k and v of KV head g into LDS, with this layer's
   // q/k-norm gains and this position's RoPE pairs (loaded ahead of the
   // gather); the compute waves norm, rope and append them (att_prepare).
+  // Without KV (a split-attention helper): q only, with the q-norm gains.
+  template <bool KV>
   static __device__ bool attention_input(const Params& p, S& s, int l, int g, int pos, uint32_t epoch,
                                          __amdgpu_buffer_rsrc_t rs) {
     MK_GLOBAL const uint8_t* const W = p.w;
@@ -503,17 +530,19 @@ struct Kern {
     const uint32_t base = (uint32_t)(xvec(p, l, V_QKV) - p.xch);
     const uint32_t qo = base + (uint32_t)(g * NOUT), ko = base + (uint32_t)((nq + g) * HD),
                    vo = base + (uint32_t)((nq + nkv + g) * HD);
-    uint32_t lo[KA], hi[KA];
-    if (!gather_pairs<KA>(p, rs, (GS + 2) * HD / 2, make_tag(epoch, vec_id(l, V_QKV)), lo, hi, [=](int j) {
+    constexpr int NP = KV ? (GS + 2) * HD / 2 : NOUT / 2;   // pairs gathered
+    constexpr int K = (NP + 63) / 64;
+    uint32_t lo[K], hi[K];
+    if (!gather_pairs<K>(p, rs, NP, make_tag(epoch, vec_id(l, V_QKV)), lo, hi, [=](int j) {
           const int w = 2 * j;
           return w < NOUT ? qo + w : (w < NOUT + HD ? ko + (w - NOUT) : vo + (w - NOUT - HD));
         }))
       return false;
     XR_PUT(s, 2 + 6 * l + 1, XR_READY);
 #pragma unroll
-    for (int k = 0; k < KA; ++k) {
+    for (int k = 0; k < K; ++k) {
       const int j = lane + 64 * k;
-      if (j < (GS + 2) * HD / 2) *reinterpret_cast<v2u*>(s.qraw + 2 * j) = v2u{lo[k], hi[k]};
+      if (j < NP) *reinterpret_cast<v2u*>(s.qraw + 2 * j) = v2u{lo[k], hi[k]};
     }
     if (lane < HD / 2) {
       s.gq[lane] = gq_lo;
@@ -532,11 +561,13 @@ struct Kern {
   // (rounded to bf16 as the cache holds it) and wave GS+1 rounds v; both
   // append to the cache at `pos`.  Lane i < HD/2 owns the RoPE pair
   // (i, i + HD/2).
+  // Without KV (a split-attention helper): the q heads only.
+  template <bool KV>
   static __device__ __forceinline__ void att_prepare(const Params& p, S& s, int l, int g, int pos, int cw, bool ok) {
     const int lane = lane_id();
     const bool pl = lane < HD / 2;
     const int li = min(lane, HD / 2 - 1);
-    if (cw <= GS) {
+    if (cw < GS || (KV && cw == GS)) {
       const float* src = s.qraw + cw * HD;
       const float xa = pl ? src[li] : 0.f, xb = pl ? src[li + HD / 2] : 0.f;
       const float r = 1.0f / sqrtf(wave_sum(xa * xa + xb * xb) / (float)HD + p.eps);
@@ -564,7 +595,7 @@ struct Kern {
           if (ok) kc[(size_t)pos * (HD / 2) + lane] = kw;   // an aborted step leaves the cache alone
         }
       }
-    } else if (cw == GS + 1) {
+    } else if (KV && cw == GS + 1) {
       if (pl) {
         const float* vf = s.qraw + (GS + 1) * HD;
         const uint32_t vw = pack_bf16(vf[2 * lane], vf[2 * lane + 1]);
@@ -624,12 +655,15 @@ struct Kern {
     for (int k = 0; k < kMaxQKV; ++k) wrow_load(rw, g, u[S_QKV + k], w.q[k]);
     gain_load<NH>(rw, (uint32_t)(p.layer0.in_norm + lo), p.H, u[S_QKV] >= 0, w.gin);
   }
-  static __device__ __forceinline__ void load_layer_rest(const Params& p, __amdgpu_buffer_rsrc_t rw, const int* u,
-                                                         int l, GemvW& w) {
-    const uint64_t lo = (uint64_t)l * p.layer_stride;
-    const GMat go = gmat(p.layer0.o, lo);
+  static __device__ __forceinline__ void load_layer_o(const Params& p, __amdgpu_buffer_rsrc_t rw, const int* u,
+                                                      int l, GemvW& w) {
+    const GMat go = gmat(p.layer0.o, (uint64_t)l * p.layer_stride);
 #pragma unroll
     for (int k = 0; k < kMaxO; ++k) wrow_load(rw, go, u[S_O + k], w.o[k]);
+  }
+  static __device__ __forceinline__ void load_layer_mlp(const Params& p, __amdgpu_buffer_rsrc_t rw, const int* u,
+                                                        int l, GemvW& w) {
+    const uint64_t lo = (uint64_t)l * p.layer_stride;
     const GMat gg = gmat(p.layer0.gu, lo);
 #pragma unroll
     for (int k = 0; k < kMaxGU; ++k)
@@ -645,10 +679,12 @@ struct Kern {
   // layer's QKV rows.
   template <bool NEXT>
   static __device__ __forceinline__ bool gemv_layer(const Params& p, S& s, int l, const int* hdr, const int* u,
-                                                    GemvW& w, uint32_t epoch, __amdgpu_buffer_rsrc_t rw,
-                                                    __amdgpu_buffer_rsrc_t rx, bool ok) {
+                                                    GemvW& w, int pos, int ns, int cw, uint32_t epoch,
+                                                    __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rx, bool ok) {
     const bool l0 = lane_id() == 0;
-    const int H = p.H, nin = hdr[S_NIN];
+    const int H = p.H, nin = LONG ? hdr[S_NIN_L] : hdr[S_NIN];
+    const int i_o = LONG ? hdr[S_IO_L] : hdr[S_IO], i_xo = LONG ? hdr[S_IXO_L] : hdr[S_IXO];
+    const int i_h = LONG ? hdr[S_IH_L] : hdr[S_IH];
     const uint32_t sbase = (uint32_t)(l * nin) + 1u;
     const int ph = 2 + 6 * l;
     // ---- QKV
@@ -682,14 +718,25 @@ struct Kern {
     // ---- the layer's weight burst, once every wave of the workgroup has
     // issued its QKV stores (the courier joins this barrier after handing
     // over the layer's input): a burst queued ahead of another wave's stores
-    // would delay the attention workgroups' input by the burst's issue time
+    // would delay the attention workgroups' input by the burst's issue time.
+    // With split attention the burst is cut in two around this workgroup's
+    // attention slice, so that the slice has the registers of the gate/up,
+    // down and next QKV rows.
     lds_barrier();
-    load_layer_rest(p, rw, u, l, w);
-    if (NEXT) load_layer_qkv(p, rw, u, l + 1, w);
+    load_layer_o(p, rw, u, l, w);
+    if (!LONG) {
+      load_layer_mlp(p, rw, u, l, w);
+      if (NEXT) load_layer_qkv(p, rw, u, l + 1, w);
+    } else {
+      if (hdr[S_SPLIT] >= 0 && hdr[S_SPLIT_IDX] <= ns)
+        ok = att_help(p, s, l, hdr[S_SPLIT], hdr[S_SPLIT_IDX], pos, ns, cw, sbase + hdr[S_IQS_L], epoch, rx, ok);
+      load_layer_mlp(p, rw, u, l, w);
+      if (NEXT) load_layer_qkv(p, rw, u, l + 1, w);
+    }
     // ---- O-projection + residual
     {
       if (u[S_O] >= 0) {
-        ok = ok && wait_seq(p, &s.seq, sbase + hdr[S_IO]);
+        ok = ok && wait_seq(p, &s.seq, sbase + i_o);
         XR_MIN(s, ph + 3, XR_SEEN);
       }
       if (u[S_O] >= 0) {
@@ -708,7 +755,7 @@ struct Kern {
     // ---- gate/up + SwiGLU: a unit is the four rows behind one output word
     {
       if (u[S_GU] >= 0) {
-        ok = ok && wait_seq(p, &s.seq, sbase + hdr[S_IXO]);
+        ok = ok && wait_seq(p, &s.seq, sbase + i_xo);
         XR_MIN(s, ph + 4, XR_SEEN);
       }
       if (u[S_GU] >= 0) {
@@ -735,7 +782,7 @@ struct Kern {
     // ---- down + residual
     {
       if (u[S_D] >= 0) {
-        ok = ok && wait_seq(p, &s.seq, sbase + hdr[S_IH]);
+        ok = ok && wait_seq(p, &s.seq, sbase + i_h);
         XR_MIN(s, ph + 5, XR_SEEN);
       }
       if (u[S_D] >= 0) {
@@ -754,32 +801,34 @@ struct Kern {
     return ok;
   }
 
-  static __device__ __forceinline__ bool gemv_waves(const Params& p, S& s, const int* hdr, const int* u,
-                                                    uint32_t epoch, __amdgpu_buffer_rsrc_t rw,
+  static __device__ __forceinline__ bool gemv_waves(const Params& p, S& s, const int* hdr, const int* u, int pos,
+                                                    int ns, int cw, uint32_t epoch, __amdgpu_buffer_rsrc_t rw,
                                                     __amdgpu_buffer_rsrc_t rx) {
     GemvW w;
     load_layer_qkv(p, rw, u, 0, w);
     bool ok = true;
-    for (int l = 0; l + 1 < p.L; ++l) ok = gemv_layer<true>(p, s, l, hdr, u, w, epoch, rw, rx, ok);
-    return gemv_layer<false>(p, s, p.L - 1, hdr, u, w, epoch, rw, rx, ok);
+    for (int l = 0; l + 1 < p.L; ++l) ok = gemv_layer<true>(p, s, l, hdr, u, w, pos, ns, cw, epoch, rw, rx, ok);
+    return gemv_layer<false>(p, s, p.L - 1, hdr, u, w, pos, ns, cw, epoch, rw, rx, ok);
   }
 
   // ---------------------------------------------- attention compute waves
   // Wave cw takes positions 8 cw .. 8 cw + 7 of every 56-position pass, one
   // position per 8 lanes (lane c of the 8 holds dims [c*HD/8, +HD/8)), so a
-  // wave reads eight consecutive cache rows as one coalesced run.  The first
-  // MP passes are loaded a layer ahead; longer contexts stream the rest.
+  // wave reads eight consecutive cache rows as one coalesced run.  The home
+  // workgroup holds its first MP passes in registers, loaded a layer ahead;
+  // positions beyond, and the helpers' slices, stream through two buffers.
   struct KVRegs {
     v4u k[MP][WPL / 4];
     v4u v[MP][WPL / 4];
   };
 
-  static __device__ __forceinline__ void kv_load_pass(const Params& p, int l, int g, int pass, int pos, int cw,
-                                                      v4u (&kk)[WPL / 4], v4u (&vv)[WPL / 4]) {
+  // K and V rows of the pass starting at position j0 (this wave's eight
+  // positions); rows past `last` read row `last` instead (weight 0 at use).
+  static __device__ __forceinline__ void kv_load_at(const Params& p, int l, int g, int j0, int last, int cw,
+                                                    v4u (&kk)[WPL / 4], v4u (&vv)[WPL / 4]) {
     const int lane = lane_id();
-    const int j = pass * PPP + cw * PPW + (lane >> 3);
-    // positions >= pos are not (yet) in the cache: read a written row instead (weight 0 at use)
-    const int jc = max(min(j, pos - 1), 0);
+    const int j = j0 + cw * PPW + (lane >> 3);
+    const int jc = max(min(j, last), 0);
     const size_t plane = (size_t)p.max_ctx * HD;
     MK_GLOBAL const v4u* kp = GCAST(const v4u, p.kv + ((size_t)(l * 2 + 0) * p.nkv + g) * plane +
                                                    (size_t)jc * HD + (lane & 7) * DPL);
@@ -791,9 +840,10 @@ struct Kern {
       vv[i] = vp[i];
     }
   }
+  // the home's register passes cover positions 0 .. MP*PPP-1 of its slice
   static __device__ __forceinline__ void kv_prefetch(const Params& p, int l, int g, int pos, int cw, KVRegs& kv) {
 #pragma unroll
-    for (int t = 0; t < MP; ++t) kv_load_pass(p, l, g, t, pos, cw, kv.k[t], kv.v[t]);
+    for (int t = 0; t < MP; ++t) kv_load_at(p, l, g, t * PPP, pos - 1, cw, kv.k[t], kv.v[t]);
   }
 
   // Scores of one pass (both q heads) for the lanes' position j; -inf past pos.
@@ -821,8 +871,8 @@ struct Kern {
       sc[h] = act ? d : -INFINITY;
     }
   }
-  // acc += p * v for one pass.  Lanes past `pos` carry p = 0 and a row the
-  // cache holds (finite), so they add nothing.
+  // acc += p * v for one pass.  Lanes past the slice carry p = 0 and a row
+  // the cache holds (finite), so they add nothing.
   static __device__ __forceinline__ void att_accum(const v4u (&vv)[WPL / 4], const float (&pr)[GS],
                                                    float (&acc)[GS][DPL]) {
 #pragma unroll
@@ -846,97 +896,40 @@ struct Kern {
 #pragma unroll
     for (int e = 0; e < DPL; ++e) acc[e] *= scale;
   }
-
-  // Positions 0..pos-1 come from the cache (registers); position `pos`
-  // itself (its k and v were produced in this step) enters at the merge.
-  template <bool NEXT>
-  static __device__ __forceinline__ bool att_layer(const Params& p, S& s, int l, int g, int pos, int cw, KVRegs& kv,
-                                                   uint32_t epoch, __amdgpu_buffer_rsrc_t rx, bool ok) {
-    const int lane = lane_id();
-    const int c = lane & 7;
-    const int ph = 2 + 6 * l;
-    ok = ok && wait_seq(p, &s.seq, (uint32_t)l + 1u);
-    XR_MIN(s, ph + 1, XR_SEEN);
-    att_prepare(p, s, l, g, pos, cw, ok);
-    lds_barrier();
-    if (cw == 0) att_current_scores(s);   // read in the merge, after the next barrier
-    float acc[GS][DPL], m[GS], lsum[GS];
+  // One streamed pass (scores, rescale, accumulate) at position base j0.
+  static __device__ __forceinline__ void att_pass(const S& s, const v4u (&kk)[WPL / 4], const v4u (&vv)[WPL / 4],
+                                                  int j0, int b, int cw, float (&m)[GS], float (&lsum)[GS],
+                                                  float (&acc)[GS][DPL]) {
+    const int j = j0 + cw * PPW + (lane_id() >> 3);
+    float sc[GS], pr[GS];
+    att_scores(s, kk, j < b, sc);
 #pragma unroll
     for (int h = 0; h < GS; ++h) {
-      m[h] = -INFINITY;
-      lsum[h] = 0.f;
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
+      att_rescale(sc[h], m[h], lsum[h], acc[h]);
+      pr[h] = sc[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[h] - m[h]);
+      lsum[h] += pr[h];
     }
-    const int npass = (pos + PPP - 1) / PPP;   // passes covering the cached positions 0..pos-1
-#ifdef MK_XRAY
-    {  // X-ray: when the prefetched rows are all in registers
-      uint32_t z = 0;
-#pragma unroll
-      for (int t = 0; t < MP; ++t) z ^= kv.k[t][0].x ^ kv.v[t][WPL / 4 - 1].w;
-      asm volatile("" ::"v"(z));   // wait until they have arrived
-      XR_MAX(s, ph + 1, XR_M0 + 1);
+    att_accum(vv, pr, acc);
+  }
+  // Positions [a, b) of the cache in passes of PPP, two passes in flight.
+  static __device__ __forceinline__ void att_stream(const Params& p, const S& s, int l, int g, int a, int b, int cw,
+                                                    float (&m)[GS], float (&lsum)[GS], float (&acc)[GS][DPL]) {
+    if (b <= a) return;
+    v4u k0[WPL / 4], v0[WPL / 4], k1[WPL / 4], v1[WPL / 4];
+    kv_load_at(p, l, g, a, b - 1, cw, k0, v0);
+    for (int j0 = a; j0 < b; j0 += 2 * PPP) {
+      kv_load_at(p, l, g, j0 + PPP, b - 1, cw, k1, v1);
+      att_pass(s, k0, v0, j0, b, cw, m, lsum, acc);
+      kv_load_at(p, l, g, j0 + 2 * PPP, b - 1, cw, k0, v0);
+      att_pass(s, k1, v1, j0 + PPP, b, cw, m, lsum, acc);
     }
-#endif
-    // ---- the passes held in registers (loaded a layer ahead)
-    if (npass > 0) {
-      float sc[MP][GS];
-#pragma unroll
-      for (int t = 0; t < MP; ++t) {
-#pragma unroll
-        for (int h = 0; h < GS; ++h) sc[t][h] = -INFINITY;
-        if (t < npass) {
-          const int j = t * PPP + cw * PPW + (lane >> 3);
-          att_scores(s, kv.k[t], j < pos, sc[t]);
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < GS; ++h) {
-        float bm = sc[0][h];
-#pragma unroll
-        for (int t = 1; t < MP; ++t) bm = fmaxf(bm, sc[t][h]);
-        att_rescale(bm, m[h], lsum[h], acc[h]);
-      }
-#pragma unroll
-      for (int t = 0; t < MP; ++t) {
-        if (t < npass) {
-          float pr[GS];
-#pragma unroll
-          for (int h = 0; h < GS; ++h) {
-            // sc = -inf past pos (and m may still be -inf in a wave with no position yet)
-            pr[h] = sc[t][h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[t][h] - m[h]);
-            lsum[h] += pr[h];
-          }
-          att_accum(kv.v[t], pr, acc);
-        }
-      }
-    }
-    // ---- longer contexts: the remaining passes stream through two buffers
-    if (npass > MP) {
-      v4u k0[WPL / 4], v0[WPL / 4], k1[WPL / 4], v1[WPL / 4];
-      kv_load_pass(p, l, g, MP, pos, cw, k0, v0);
-      for (int t = MP; t < npass; t += 2) {
-        kv_load_pass(p, l, g, t + 1, pos, cw, k1, v1);
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          v4u(&kk)[WPL / 4] = half ? k1 : k0;
-          v4u(&vv)[WPL / 4] = half ? v1 : v0;
-          const int j = (t + half) * PPP + cw * PPW + (lane >> 3);
-          float sc[GS], pr[GS];
-          att_scores(s, kk, j < pos, sc);
-#pragma unroll
-          for (int h = 0; h < GS; ++h) {
-            att_rescale(sc[h], m[h], lsum[h], acc[h]);
-            pr[h] = sc[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[h] - m[h]);
-            lsum[h] += pr[h];
-          }
-          att_accum(vv, pr, acc);
-          if (half == 0) kv_load_pass(p, l, g, t + 2, pos, cw, k0, v0);
-        }
-      }
-    }
-    // this wave's outputs: the two 8-lane halves of each 16-lane row with one
-    // DPP step, then the four rows go to LDS
+  }
+  // This wave's outputs to LDS: the two 8-lane halves of each 16-lane row
+  // with one DPP step, then the four rows; the wave's max and sum.
+  static __device__ __forceinline__ void att_wave_part(S& s, int cw, const float (&m)[GS], const float (&lsum)[GS],
+                                                       float (&acc)[GS][DPL]) {
+    const int lane = lane_id();
+    const int c = lane & 7;
 #pragma unroll
     for (int h = 0; h < GS; ++h)
 #pragma unroll
@@ -955,9 +948,103 @@ struct Kern {
         s.wl[cw][h] = lt;
       }
     }
+  }
+  // weight of a partial with maximum mw under the common maximum M
+  static __device__ __forceinline__ float att_weight(float mw, float M) {
+    return mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+  }
+
+  // Home workgroup of KV head g.  Its slice is positions 0..P-1 of the cache
+  // (all of 0..pos-1 without helpers); position `pos` itself (its k and v were
+  // produced in this step) enters at the merge, with the helpers' partials.
+  template <bool NEXT>
+  static __device__ __forceinline__ bool att_layer(const Params& p, S& s, int l, int g, int pos, int ns, int cw,
+                                                   KVRegs& kv, uint32_t epoch, __amdgpu_buffer_rsrc_t rx, bool ok) {
+    const int lane = lane_id();
+    const int ph = 2 + 6 * l;
+    ok = ok && wait_seq(p, &s.seq, (uint32_t)l + 1u);
+    XR_MIN(s, ph + 1, XR_SEEN);
+    att_prepare<true>(p, s, l, g, pos, cw, ok);
+    lds_barrier();
+    if (cw == 0) att_current_scores(s);   // read in the merge, after the next barrier
+    float acc[GS][DPL], m[GS], lsum[GS];
+#pragma unroll
+    for (int h = 0; h < GS; ++h) {
+      m[h] = -INFINITY;
+      lsum[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
+    }
+    const int P = LONG && ns > 0 ? (pos + ns) / (ns + 1) : pos;   // the home's slice: slice 0
+    const int npass = (P + PPP - 1) / PPP;
+#ifdef MK_XRAY
+    {  // X-ray: when the prefetched rows are all in registers
+      uint32_t z = 0;
+#pragma unroll
+      for (int t = 0; t < MP; ++t) z ^= kv.k[t][0].x ^ kv.v[t][WPL / 4 - 1].w;
+      asm volatile("" ::"v"(z));   // wait until they have arrived
+      XR_MAX(s, ph + 1, XR_M0 + 1);
+    }
+#endif
+    // ---- the passes held in registers (loaded a layer ahead)
+    if (npass > 0) {
+      float sc[MP][GS];
+#pragma unroll
+      for (int t = 0; t < MP; ++t) {
+#pragma unroll
+        for (int h = 0; h < GS; ++h) sc[t][h] = -INFINITY;
+        if (t < npass) {
+          const int j = t * PPP + cw * PPW + (lane >> 3);
+          att_scores(s, kv.k[t], j < P, sc[t]);
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < GS; ++h) {
+        float bm = sc[0][h];
+#pragma unroll
+        for (int t = 1; t < MP; ++t) bm = fmaxf(bm, sc[t][h]);
+        att_rescale(bm, m[h], lsum[h], acc[h]);
+      }
+#pragma unroll
+      for (int t = 0; t < MP; ++t) {
+        if (t < npass) {
+          float pr[GS];
+#pragma unroll
+          for (int h = 0; h < GS; ++h) {
+            // sc = -inf past P (and m may still be -inf in a wave with no position yet)
+            pr[h] = sc[t][h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[t][h] - m[h]);
+            lsum[h] += pr[h];
+          }
+          att_accum(kv.v[t], pr, acc);
+        }
+      }
+    }
+    // ---- longer slices: the remaining passes stream
+    if (npass > MP) att_stream(p, s, l, g, MP * PPP, P, cw, m, lsum, acc);
+    att_wave_part(s, cw, m, lsum, acc);
     XR_MAX(s, ph + 1, XR_M0);
     lds_barrier();
-    // merge the seven waves (fixed order); thread t < NOUT owns output t
+    // ---- the helpers' partials (split attention): every compute wave
+    // gathers a share into LDS; nothing else of this workgroup is in flight
+    if (LONG && ns > 0) {
+      XR_MIN(s, ph + 2, XR_START);
+      const uint32_t pb = xword(p, l, V_ATT) + (uint32_t)(g * p.split_max * p.split_pw);
+      const int pw = p.split_pw;
+      const __amdgpu_buffer_rsrc_t rs = xch_rsrc(p);
+      // rounds of kCW * 64 * KP pairs (registers: one 16-byte load per pair in flight)
+      for (int r0 = 0; r0 < ns * PP; r0 += kCW * 64 * KP)
+        ok = ok && gather_pairs_to<KP>(
+                       p, rs, ns * PP, make_tag(epoch, vec_id(l, V_ATT)),
+                       [=](int j) { return pb + (uint32_t)((j / PP) * pw + 2 * (j % PP)); },
+                       [&](int j, uint32_t a, uint32_t b) {
+                         *reinterpret_cast<v2u*>(&s.spart[j / PP][2 * (j % PP)]) = v2u{a, b};
+                       },
+                       r0 + cw * 64, kCW * 64);
+      XR_MAX(s, ph + 2, XR_READY);
+      lds_barrier();
+    }
+    // merge the seven waves (fixed order), the helpers and the current
+    // position; thread t < NOUT owns output t
     const int t = cw * 64 + lane;
     const int tc = min(t, NOUT - 1);
     const int h = tc / HD;
@@ -965,15 +1052,23 @@ struct Kern {
     float M = sp;
 #pragma unroll
     for (int w = 0; w < kCW; ++w) M = fmaxf(M, s.wm[w][h]);
+    if (LONG)
+      for (int i = 0; i < ns; ++i) M = fmaxf(M, s.spart[i][NOUT + h]);
     const uint32_t vpw = s.vp[(tc % HD) / 2];
     const float ec = __builtin_amdgcn_exp2f(sp - M);
     float Lt = ec, O = ec * ((tc & 1) ? bf16_hi(vpw) : bf16_lo(vpw));
 #pragma unroll
     for (int w = 0; w < kCW; ++w) {
-      const float e = s.wm[w][h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s.wm[w][h] - M);
+      const float e = att_weight(s.wm[w][h], M);
       Lt = fmaf(s.wl[w][h], e, Lt);
       O = fmaf((s.part[w][0][tc] + s.part[w][1][tc]) + (s.part[w][2][tc] + s.part[w][3][tc]), e, O);
     }
+    if (LONG)
+      for (int i = 0; i < ns; ++i) {
+        const float e = att_weight(s.spart[i][NOUT + h], M);
+        Lt = fmaf(s.spart[i][NOUT + GS + h], e, Lt);
+        O = fmaf(s.spart[i][tc], e, O);
+      }
     const float o = O / Lt;
     const float o1 = dpp<0xB1>(o);   // the neighbouring output (t ^ 1)
     st_xword(rx, ok && t < NOUT && (t & 1) == 0 ? 8u * (xword(p, l, V_O) + (g * NOUT + t) / 2) : kOOB,
@@ -984,13 +1079,63 @@ struct Kern {
     return ok;
   }
 
-  static __device__ __forceinline__ bool att_waves(const Params& p, S& s, int g, int pos, int cw, uint32_t epoch,
-                                                   __amdgpu_buffer_rsrc_t rx) {
+  static __device__ __forceinline__ bool att_waves(const Params& p, S& s, int g, int pos, int ns, int cw,
+                                                   uint32_t epoch, __amdgpu_buffer_rsrc_t rx) {
     KVRegs kv;
     kv_prefetch(p, 0, g, pos, cw, kv);
     bool ok = true;
-    for (int l = 0; l + 1 < p.L; ++l) ok = att_layer<true>(p, s, l, g, pos, cw, kv, epoch, rx, ok);
-    return att_layer<false>(p, s, p.L - 1, g, pos, cw, kv, epoch, rx, ok);
+    for (int l = 0; l + 1 < p.L; ++l) ok = att_layer<true>(p, s, l, g, pos, ns, cw, kv, epoch, rx, ok);
+    return att_layer<false>(p, s, p.L - 1, g, pos, ns, cw, kv, epoch, rx, ok);
+  }
+
+  // Split-attention helper (a GEMV workgroup's compute waves, between their
+  // weight burst and the O-projection): slice i of KV head g's cached
+  // positions, merged over the waves and published as (unnormalised
+  // outputs, per-head maximum, per-head sum) for the head's home.
+  static __device__ __forceinline__ bool att_help(const Params& p, S& s, int l, int g, int i, int pos, int ns,
+                                                  int cw, uint32_t want, uint32_t epoch, __amdgpu_buffer_rsrc_t rx,
+                                                  bool ok) {
+    const int lane = lane_id();
+    const int ph = 2 + 6 * l;
+    ok = ok && wait_seq(p, &s.seq, want);
+    XR_MIN(s, ph + 1, XR_SEEN);
+    att_prepare<false>(p, s, l, g, pos, cw, ok);
+    lds_barrier();
+    const int chunk = (pos + ns) / (ns + 1);
+    const int a = min(pos, i * chunk), b = min(pos, a + chunk);
+    float acc[GS][DPL], m[GS], lsum[GS];
+#pragma unroll
+    for (int h = 0; h < GS; ++h) {
+      m[h] = -INFINITY;
+      lsum[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
+    }
+    att_stream(p, s, l, g, a, b, cw, m, lsum, acc);
+    att_wave_part(s, cw, m, lsum, acc);
+    lds_barrier();
+    const int t = cw * 64 + lane;
+    const int tc = min(t, NOUT - 1);
+    const int h = tc / HD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kCW; ++w) M = fmaxf(M, s.wm[w][h]);
+    float Lt = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < kCW; ++w) {
+      const float e = att_weight(s.wm[w][h], M);
+      Lt = fmaf(s.wl[w][h], e, Lt);
+      O = fmaf((s.part[w][0][tc] + s.part[w][1][tc]) + (s.part[w][2][tc] + s.part[w][3][tc]), e, O);
+    }
+    const uint32_t base = 8u * (xword(p, l, V_ATT) + (uint32_t)((g * p.split_max + i - 1) * p.split_pw));
+    const uint32_t tag = make_tag(epoch, vec_id(l, V_ATT));
+    const bool in = ok && t < NOUT;
+    st_xword(rx, in ? base + 8u * (uint32_t)t : kOOB, __float_as_uint(O), tag);
+    const bool first = in && (t % HD) == 0;   // one thread per head stores its maximum and sum
+    st_xword(rx, first ? base + 8u * (uint32_t)(NOUT + h) : kOOB, __float_as_uint(M), tag);
+    st_xword(rx, first ? base + 8u * (uint32_t)(NOUT + GS + h) : kOOB, __float_as_uint(Lt), tag);
+    XR_MAX(s, ph + 1, XR_DONE);
+    return ok;
   }
 
   // ------------------------------------------------------------ LM head
@@ -1014,7 +1159,7 @@ struct Kern {
     asm volatile("" ::: "memory");
     uint32_t gf[NH][8];
     gain_load<NH>(rw, (uint32_t)p.final_norm, p.H, true, gf);
-    ok = ok && wait_seq(p, &s.seq, (uint32_t)(p.L * hdr[S_NIN]) + 1u);
+    ok = ok && wait_seq(p, &s.seq, (uint32_t)(p.L * (LONG ? hdr[S_NIN_L] : hdr[S_NIN])) + 1u);
     XR_MIN(s, 2 + 6 * p.L, XR_SEEN);
     uint32_t xa[NH][8];
     norm_act<NH>(s.xd_raw, s.r_xd, gf, p.H, xa);
@@ -1049,8 +1194,8 @@ struct Kern {
   }
 
   // -------------------------------------------------------------- kernel
-  static __device__ void run(const Params& p, S& s, const int32_t* d_token, int pos, uint32_t epoch, int32_t* d_next,
-                             float* d_logits) {
+  static __device__ void run(const Params& p, S& s, const int32_t* d_token, int pos, int ns, uint32_t epoch,
+                             int32_t* d_next, float* d_logits) {
     const int wave = wave_id(), lane = lane_id();
     const int wg = blockIdx.x;
     if (threadIdx.x == 0) s.seq = 0;
@@ -1066,21 +1211,21 @@ struct Kern {
     if (wg == 0 && threadIdx.x == 0) *d_next = -1;  // overwritten on success
     // this workgroup's row of the work table, as wave-uniform values
     MK_GLOBAL const int* tab = GCAST(const int, p.xch + p.x.sched) + (size_t)wg * kSchedInts * kWaves;
-    int hdr[8];
+    int hdr[kHdrInts];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) hdr[i] = __builtin_amdgcn_readfirstlane(tab[i]);
+    for (int i = 0; i < kHdrInts; ++i) hdr[i] = __builtin_amdgcn_readfirstlane(tab[i]);
     lds_barrier();   // seq and the X-ray records are initialised
     const __amdgpu_buffer_rsrc_t rx = xch_rsrc(p);
     if (wave == 0) {
-      if (!courier(p, s, hdr, token, pos, epoch, d_next)) return;
+      if (!courier(p, s, hdr, token, pos, ns, epoch, d_next)) return;
     } else {
       const int cw = wave - 1;
       int u[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) u[i] = __builtin_amdgcn_readfirstlane(tab[kSchedInts * wave + i]);
       const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w, p.w_bytes);
-      bool ok = hdr[S_ATT] >= 0 ? att_waves(p, s, hdr[S_ATT], pos, cw, epoch, rx)
-                                : gemv_waves(p, s, hdr, u, epoch, rw, rx);
+      bool ok = hdr[S_ATT] >= 0 ? att_waves(p, s, hdr[S_ATT], pos, ns, cw, epoch, rx)
+                                : gemv_waves(p, s, hdr, u, pos, ns, cw, epoch, rw, rx);
       float best;
       int bidx;
       ok = lm_head(p, s, hdr, cw, d_logits, rw, ok, best, bidx);
@@ -1113,15 +1258,16 @@ struct Kern {
 };
 
 // One instantiation per (weight format, head_dim, q heads per KV head,
-// 1024-chunks of hidden, of n_q_heads*head_dim and of intermediate): the
-// formats, the attention shape and every per-lane register array size are
-// compile-time constants.
-template <int WF, int HD, int GS, int NH, int NQ, int NI>
+// 1024-chunks of hidden, of n_q_heads*head_dim and of intermediate, split
+// attention or not): the formats, the attention shape and every per-lane
+// register array size are compile-time constants.  `ns` is the number of
+// helpers per KV head in this step (0 without split attention).
+template <int WF, int HD, int GS, int NH, int NQ, int NI, bool LONG>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const Params* __restrict__ pp, const int32_t* d_token,
-                                                             int pos, uint32_t epoch, int32_t* d_next,
+                                                             int pos, int ns, uint32_t epoch, int32_t* d_next,
                                                              float* d_logits) {
   __shared__ Smem<HD, GS, NH, NQ, NI> s;
-  Kern<WF, HD, GS, NH, NQ, NI>::run(*pp, s, d_token, pos, epoch, d_next, d_logits);
+  Kern<WF, HD, GS, NH, NQ, NI, LONG>::run(*pp, s, d_token, pos, ns, epoch, d_next, d_logits);
 }
 
 // ------------------------------------------------------- launch wrappers
@@ -1140,32 +1286,41 @@ bool decode_shape_supported(int hd, int gs, int hidden, int qdim, int inter) {
   return false;
 }
 
-static const void* decode_fn(int wfmt, int hd, int gs, int hidden, int qdim, int inter) {
+static const void* decode_fn(int wfmt, int hd, int gs, int hidden, int qdim, int inter, bool split) {
   const void* fn = nullptr;
   const int nh = cdiv1024(hidden), nqd = cdiv1024(qdim), ni = cdiv1024(inter);
-#define MK_CASE(H_, G_, A_, B_, C_)                                                                             \
-  if (hd == H_ && gs == G_ && nh == A_ && nqd == B_ && ni == C_) {                                              \
-    fn = wfmt == 0 ? reinterpret_cast<const void*>(decode_kernel<0, H_, G_, A_, B_, C_>)                        \
-                   : (wfmt == 1 ? reinterpret_cast<const void*>(decode_kernel<1, H_, G_, A_, B_, C_>)           \
-                                : reinterpret_cast<const void*>(decode_kernel<2, H_, G_, A_, B_, C_>));         \
+#define MK_FN(W_, H_, G_, A_, B_, C_)                                                        \
+  (split ? reinterpret_cast<const void*>(decode_kernel<W_, H_, G_, A_, B_, C_, true>)         \
+         : reinterpret_cast<const void*>(decode_kernel<W_, H_, G_, A_, B_, C_, false>))
+#define MK_CASE(H_, G_, A_, B_, C_)                                                                 \
+  if (hd == H_ && gs == G_ && nh == A_ && nqd == B_ && ni == C_) {                                  \
+    fn = wfmt == 0 ? MK_FN(0, H_, G_, A_, B_, C_) : (wfmt == 1 ? MK_FN(1, H_, G_, A_, B_, C_)       \
+                                                               : MK_FN(2, H_, G_, A_, B_, C_));     \
   }
   MK_SHAPES(MK_CASE)
 #undef MK_CASE
+#undef MK_FN
   return fn;
 }
 
 hipError_t decode_coresident(int wfmt, int hd, int gs, int hidden, int qdim, int inter, int* per_cu) {
-  const void* fn = decode_fn(wfmt, hd, gs, hidden, qdim, inter);
-  if (!fn) return hipErrorInvalidValue;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, fn, kThreads, 0);
+  int n[2];
+  for (int v = 0; v < 2; ++v) {
+    const void* fn = decode_fn(wfmt, hd, gs, hidden, qdim, inter, v == 1);
+    if (!fn) return hipErrorInvalidValue;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[v], fn, kThreads, 0);
+    if (e != hipSuccess) return e;
+  }
+  *per_cu = n[0] < n[1] ? n[0] : n[1];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const Params* d_params, int wfmt, int hd, int gs, int hidden, int qdim, int inter, int grid,
-                         bool cooperative, const int32_t* d_token, int pos, uint32_t epoch, int32_t* d_next,
+                         bool cooperative, const int32_t* d_token, int pos, int ns, uint32_t epoch, int32_t* d_next,
                          float* d_logits, hipStream_t s) {
-  const void* fn = decode_fn(wfmt, hd, gs, hidden, qdim, inter);
+  const void* fn = decode_fn(wfmt, hd, gs, hidden, qdim, inter, ns > 0);
   if (!fn) return hipErrorInvalidValue;
-  void* args[] = {&d_params, &d_token, &pos, &epoch, &d_next, &d_logits};
+  void* args[] = {&d_params, &d_token, &pos, &ns, &epoch, &d_next, &d_logits};
   if (cooperative) return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
   return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
 }

@@ -63,7 +63,8 @@ struct Layer {
 // Exchange vectors of layer l (word offsets inside the layer's block).  Each
 // word is (payload << 32) | tag with tag = (epoch << kPhaseBits) | vector id,
 // vector id = 2 + kTypes*l + type; the argmax words of the step use id
-// 2 + kTypes*L.
+// 2 + kTypes*L.  V_ATT holds the split-attention partials:
+// [nkv][split_max][split_pw] words.
 enum : int { V_QKV = 0, V_ATT = 1, V_O = 2, V_XO = 3, V_H = 4, V_XD = 5 };
 struct Xch {
   uint64_t base;              // word offset of layer 0's block
@@ -79,10 +80,20 @@ struct Xch {
 // Per-workgroup header of the work table (ints).
 enum : int {
   S_FLAGS = 0,      // bit 0: gathers xd (QKV or O units), 1: o, 2: xo (gate/up or down), 3: h
-  S_ATT = 1,        // KV head whose attention this workgroup runs, or -1
+  S_ATT = 1,        // KV head whose attention this workgroup runs (its home workgroup), or -1
   S_NIN = 2,        // inputs the courier gathers per layer
   S_IXD = 3, S_IQKV = 4, S_IO = 5, S_IXO = 6, S_IH = 7,   // input index in the layer, or -1
+  // split attention (the kernel variant for long contexts): a GEMV workgroup
+  // also takes a slice of one KV head's cached positions, which adds the
+  // head's q to its inputs
+  S_SPLIT = 8,      // KV head whose positions this workgroup helps with, or -1
+  S_SPLIT_IDX = 9,  // its slice index among that head's helpers (1-based; the home takes slice 0)
+  S_NIN_L = 10,     // inputs per layer in the split variant
+  S_IQS_L = 11, S_IO_L = 12, S_IXO_L = 13, S_IH_L = 14,   // input indices in the split variant, or -1
+  kHdrInts = 16,
 };
+constexpr int kMaxSplit = 32;   // helpers per KV head (the home merges their partials in LDS)
+constexpr int kSplitGatherK = 5;    // partial word pairs per lane and round of the home's gather
 // Per compute wave: units of each phase (-1 = none), at these offsets.
 enum : int { S_QKV = 0, S_O = 4, S_GU = 8, S_D = 12 };
 
@@ -105,6 +116,8 @@ struct Params {
   uint32_t tag_skew;      // test hook: added to every expected tag (non-zero makes every wait time out)
   uint32_t poll_sleep;    // s_sleep units between courier poll rounds
   int n_phases;           // trace phases per step (trace stride per workgroup)
+  int split_max;          // helper slots per KV head in the partials vector
+  int split_pw;           // words per helper partial (outputs, maxima, sums; padded)
 };
 
 }  // namespace mk

@@ -130,21 +130,24 @@ __device__ __forceinline__ void st_xword(__amdgpu_buffer_rsrc_t r, uint32_t byte
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, v2u{tag, payload}), r, byte_off, 0, 16);
 }
 
-// Courier gather: `npairs` pairs of words; pair j is at word src(j) (even,
-// the two words consecutive).  Lane l owns pairs l + 64k, k < MAXK; their
-// payloads land in lo[k] (word 2j) and hi[k] (word 2j+1).  Each round issues
-// every missing pair's load before waiting, so one round costs one memory
-// latency.  Returns false on timeout or when another workgroup has failed.
+// Gather `npairs` (>= 1) pairs of words; pair j is at word src(j) (even,
+// the two words consecutive).  Lane l owns pairs j0 + l + jstep*k, k < MAXK;
+// their payloads land in lo[k] (word 2j) and hi[k] (word 2j+1).  Each round
+// issues every missing pair's load before waiting, so one round costs one
+// memory latency.  Returns false on timeout or when another workgroup has
+// failed.  The courier gathers with j0 = 0, jstep = 64; the waves of a
+// workgroup with no loads in flight may share a gather with other strides.
 template <int MAXK, class F>
 __device__ __forceinline__ bool gather_pairs(const Params& p, __amdgpu_buffer_rsrc_t r, int npairs, uint32_t tag,
-                                             uint32_t (&lo)[MAXK], uint32_t (&hi)[MAXK], F src) {
+                                             uint32_t (&lo)[MAXK], uint32_t (&hi)[MAXK], F src, int j0 = 0,
+                                             int jstep = 64) {
   const int lane = threadIdx.x & 63;
   tag += p.tag_skew;
   uint32_t pend = 0;
   v4u v[MAXK];
 #pragma unroll
   for (int k = 0; k < MAXK; ++k) {
-    const int j = lane + 64 * k;
+    const int j = j0 + lane + jstep * k;
     if (j < npairs) pend |= 1u << k;
     v[k] = ld_pair(r, src(min(j, npairs - 1)));   // clamped: no load behind a branch
   }
@@ -170,7 +173,49 @@ __device__ __forceinline__ bool gather_pairs(const Params& p, __amdgpu_buffer_rs
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int k = 0; k < MAXK; ++k)
-      if ((pend >> k) & 1u) v[k] = ld_pair(r, src(lane + 64 * k));
+      if ((pend >> k) & 1u) v[k] = ld_pair(r, src(j0 + lane + jstep * k));
+  }
+}
+
+// The same gather, but each pair's payloads are handed to put(j, lo, hi)
+// (an LDS write) as soon as the pair carries the tag, so a lane keeps only
+// its loads in flight in registers.
+template <int MAXK, class F, class G>
+__device__ __forceinline__ bool gather_pairs_to(const Params& p, __amdgpu_buffer_rsrc_t r, int npairs, uint32_t tag,
+                                                F src, G put, int j0, int jstep) {
+  const int lane = threadIdx.x & 63;
+  tag += p.tag_skew;
+  uint32_t pend = 0;
+  v4u v[MAXK];
+#pragma unroll
+  for (int k = 0; k < MAXK; ++k) {
+    const int j = j0 + lane + jstep * k;
+    if (j < npairs) pend |= 1u << k;
+    v[k] = ld_pair(r, src(min(j, npairs - 1)));
+  }
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  uint32_t rounds = 0;
+  while (true) {
+#pragma unroll
+    for (int k = 0; k < MAXK; ++k) {
+      if (((pend >> k) & 1u) && v[k].x == tag && v[k].z == tag) {
+        pend &= ~(1u << k);
+        put(j0 + lane + jstep * k, v[k].y, v[k].w);
+      }
+    }
+    if (__builtin_amdgcn_ballot_w64(pend != 0) == 0) return true;
+    ++rounds;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > p.spin_limit) {
+      raise_error(p, ERR_TIMEOUT);
+      return false;
+    }
+    if ((rounds & 63u) == 0 &&
+        __hip_atomic_load(err_word(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+      return false;
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int k = 0; k < MAXK; ++k)
+      if ((pend >> k) & 1u) v[k] = ld_pair(r, src(j0 + lane + jstep * k));
   }
 }
 

@@ -21,7 +21,8 @@ MATRICES = {"q": 0, "k": 1, "v": 2, "o": 3, "gate": 4, "up": 5, "down": 6, "embe
 # mk_read_exchange vectors: q/k/v GEMV outputs, attention output, residual after O, SwiGLU output,
 # residual after down
 EXCHANGE = {"qkv": 0, "attn": 1, "x_o": 2, "h": 3, "x_d": 4}
-OPT_GRID, OPT_SPIN_LIMIT, OPT_TAG_SKEW, OPT_POLL_SLEEP, OPT_LAUNCH_MODE = 0, 3, 4, 5, 6
+OPT_GRID, OPT_SPIN_LIMIT, OPT_TAG_SKEW, OPT_POLL_SLEEP, OPT_LAUNCH_MODE, OPT_SPLIT_CHUNK, OPT_SPLIT_FROM = \
+    0, 3, 4, 5, 6, 7, 8
 
 
 class MkError(RuntimeError):
@@ -113,7 +114,8 @@ class Decoder:
 
     def __init__(self, shape, wfmt: int, max_ctx: int, xray: bool = False, grid: int = 0,
                  spin_limit: Optional[int] = None, poll_sleep: Optional[int] = None,
-                 launch_mode: Optional[int] = None):
+                 launch_mode: Optional[int] = None, split_chunk: Optional[int] = None,
+                 split_from: Optional[int] = None):
         import torch
         self.lib = load(xray)
         self.shape, self.wfmt, self.max_ctx = shape, wfmt, max_ctx
@@ -129,6 +131,10 @@ class Decoder:
             self._check(self.lib.mk_set_option(self.h, OPT_POLL_SLEEP, poll_sleep))
         if launch_mode is not None:
             self._check(self.lib.mk_set_option(self.h, OPT_LAUNCH_MODE, launch_mode))
+        if split_chunk is not None:
+            self._check(self.lib.mk_set_option(self.h, OPT_SPLIT_CHUNK, split_chunk))
+        if split_from is not None:
+            self._check(self.lib.mk_set_option(self.h, OPT_SPLIT_FROM, split_from))
         self.sizes = mk_sizes()
         self._check(self.lib.mk_query_sizes(self.h, ctypes.byref(self.sizes)))
         dev = torch.device("cuda", torch.cuda.current_device())

@@ -56,8 +56,8 @@ def _step(dec, sh, token, pos):
     return logits
 
 
-def _decoder(native, shape, master, wfmt, max_ctx):
-    d = native.Decoder(shape, wfmt, max_ctx)
+def _decoder(native, shape, master, wfmt, max_ctx, **kw):
+    d = native.Decoder(shape, wfmt, max_ctx, **kw)
     d.pack(native.master_to_device(master))
     return d
 
@@ -82,11 +82,11 @@ def test_ops_tiny_every_output(native, tiny_master, wfmt):
 
 
 def test_ops_tiny_streamed_attention(native, tiny_master):
-    """Positions 400 and 470: one and two cache passes stream after the
-    seven held in registers."""
+    """Positions 400 and 470 without split attention: one and two cache
+    passes stream after the seven held in registers."""
     sh = synth.TINY
     toks = synth.make_prompt(sh.vocab, 471, 12)
-    d = _decoder(native, sh, tiny_master, synth.BF16, 480)
+    d = _decoder(native, sh, tiny_master, synth.BF16, 480, split_chunk=0)
     W = Weights(tiny_master, synth.BF16)
     d.prefill(toks[:400])
     logits = _step(d, sh, int(toks[400]), 400)
@@ -96,6 +96,43 @@ def test_ops_tiny_streamed_attention(native, tiny_master):
     logits = _step(d, sh, int(toks[470]), 470)
     check_step(GpuStep(d, sh), W, sh, int(toks[470]), 470, logits, range(sh.n_layers), np.random.default_rng(0))
     d.close()
+
+
+@pytest.mark.parametrize("wfmt,chunk,positions", [
+    (synth.BF16, 8, (39,)),             # 4 helpers per head, slices of 8
+    (synth.FP4_MIX, 5, (39,)),          # 7 helpers, one-wave slices
+    (synth.FP8_ROW, 16, (400, 470)),    # 25 and all 31 helpers, streamed home slice
+    (synth.BF16, 1, (470,)),            # every helper, slices of 15
+])
+def test_ops_tiny_split_attention(native, tiny_master, wfmt, chunk, positions):
+    """Split attention: the head's positions spread over its home and
+    helper workgroups, partials merged by the home; every output checked."""
+    sh = synth.TINY
+    n = max(positions) + 1
+    toks = synth.make_prompt(sh.vocab, n, 14)
+    d = _decoder(native, sh, tiny_master, wfmt, n + 8, split_chunk=chunk, split_from=0)
+    W = Weights(tiny_master, wfmt)
+    d.prefill(toks[:positions[0]])
+    for pos in range(positions[0], n):
+        logits = _step(d, sh, int(toks[pos]), pos)
+        if pos in positions:
+            check_step(GpuStep(d, sh), W, sh, int(toks[pos]), pos, logits, range(sh.n_layers),
+                       np.random.default_rng(pos))
+    d.close()
+
+
+def test_split_attention_deterministic(native, tiny_master):
+    """The split path's merge order is fixed: two runs, identical bits."""
+    sh = synth.TINY
+    toks = synth.make_prompt(sh.vocab, 120, 15)
+    outs = []
+    for _ in range(2):
+        d = _decoder(native, sh, tiny_master, synth.FP8_ROW, 128, split_chunk=4, split_from=0)
+        d.prefill(toks[:100])
+        got = [_step(d, sh, int(toks[pos]), pos).view(np.uint32).copy() for pos in range(100, 120)]
+        outs.append(np.array(got))
+        d.close()
+    assert np.array_equal(outs[0], outs[1])
 
 
 def test_exchange_needs_a_step(native, tiny_master):
@@ -135,10 +172,11 @@ def test_ops_qwen3_0p6b_sampled(native, q_master, wfmt):
 
 @pytest.mark.timeout(900)
 def test_ops_qwen3_0p6b_streamed_attention(native, q_master):
-    """Positions 400 and 460 (one and two streamed cache passes), bf16."""
+    """Positions 400 and 460 without split attention (one and two streamed
+    cache passes), bf16."""
     sh = synth.QWEN3_0P6B
     toks = synth.make_prompt(sh.vocab, 461, 13)
-    d = _decoder(native, sh, q_master, synth.BF16, 512)
+    d = _decoder(native, sh, q_master, synth.BF16, 512, split_chunk=0)
     W = Weights(q_master, synth.BF16)
     d.prefill(toks[:400])
     logits = _step(d, sh, int(toks[400]), 400)
@@ -147,6 +185,26 @@ def test_ops_qwen3_0p6b_streamed_attention(native, q_master):
         _step(d, sh, int(toks[pos]), pos)
     logits = _step(d, sh, int(toks[460]), 460)
     check_step(GpuStep(d, sh), W, sh, int(toks[460]), 460, logits, Q_LAYERS, np.random.default_rng(3), n_sample=96)
+    d.close()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("wfmt,chunk", [(synth.BF16, 16), (synth.FP8_ROW, 4)])
+def test_ops_qwen3_0p6b_split_attention(native, q_master, wfmt, chunk):
+    """Split attention at the 0.6B shape: position 128 after the benchmark's
+    prompt (8 or all 31 helpers per head) and position 460."""
+    sh = synth.QWEN3_0P6B
+    wl = synth.WORKLOADS["qwen3_0p6b_bf16"]
+    prompt = synth.make_prompt(sh.vocab, wl.prompt_len, wl.prompt_seed)
+    toks = np.concatenate([prompt, synth.make_prompt(sh.vocab, 340, 16)])
+    d = _decoder(native, sh, q_master, wfmt, 512, split_chunk=chunk, split_from=0)
+    W = Weights(q_master, wfmt)
+    d.prefill(prompt)
+    for pos in range(128, 461):
+        logits = _step(d, sh, int(toks[pos]), pos)
+        if pos in (128, 460):
+            check_step(GpuStep(d, sh), W, sh, int(toks[pos]), pos, logits, Q_LAYERS,
+                       np.random.default_rng(pos), n_sample=96)
     d.close()
 
 

@@ -37,6 +37,8 @@ def parse():
                          "the workload '<name>@<prompt_len>')")
     ap.add_argument("--split-chunk", type=int, default=-1,
                     help="split attention: cached positions per workgroup (0 off, -1 library default)")
+    ap.add_argument("--split-from", type=int, default=-1,
+                    help="split attention from this position on (-1: library default)")
     ap.add_argument("--xray-dump", default="", help="with --xray: also save the raw records (.npy)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="before decoding, run a plain device copy of this many MiB three times (the "
@@ -163,7 +165,8 @@ def main():
     dec = native.Decoder(sh, wl.wfmt, max_ctx, xray=args.xray,
                          poll_sleep=None if args.poll_sleep < 0 else args.poll_sleep,
                          launch_mode=None if args.launch < 0 else args.launch,
-                         split_chunk=None if args.split_chunk < 0 else args.split_chunk)
+                         split_chunk=None if args.split_chunk < 0 else args.split_chunk,
+                         split_from=None if args.split_from < 0 else args.split_from)
     dev_master = native.master_to_device(master)
     dec.pack(dev_master)
     del dev_master

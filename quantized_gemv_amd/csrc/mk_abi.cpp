@@ -162,7 +162,18 @@ void layout_scratch(mk_model* m, int grid, bool for_sizing = true) {
   X.base = 0;
   uint64_t lw = 0;
   const uint64_t pw = split_pw(c);
-  const uint64_t sizes[kTypes] = {(nq + 2 * nkv) * hd, nkv * (uint64_t)kMaxSplit * pw, nq * hd / 2, H, I / 2, H};
+  uint64_t sizes[kTypes] = {(nq + 2 * nkv) * hd, nkv * (uint64_t)kMaxSplit * pw, nq * hd / 2, H, I / 2, H};
+  // the residuals in the per-producer layout: the GEMV workgroups' blocks
+  // (even length) each start a 128-byte line
+  const uint32_t cg = (uint32_t)std::max(grid - (int)nkv, 1);
+  for (int t : {(int)V_XO, (int)V_XD}) {
+    const uint64_t np = sizes[t] / 2;
+    const uint32_t stride = (uint32_t)((2 * ((np + cg - 1) / cg) + 15) / 16 * 16);
+    X.pad_c[t] = cg;
+    X.pad_stride[t] = stride;
+    sizes[t] = (uint64_t)cg * stride;
+  }
+  for (int t : {(int)V_QKV, (int)V_ATT, (int)V_O, (int)V_H}) X.pad_c[t] = X.pad_stride[t] = 0;
   for (int t = 0; t < kTypes; ++t) {
     X.off[t] = lw;
     lw = al(lw + sizes[t]);
@@ -217,11 +228,14 @@ const char* build_sched(const mk_config& c, int grid, std::vector<int32_t>& tab,
       }
     return false;
   };
-  // units [0, n) of `rows` in contiguous blocks over `wgs`, waves in turn from `w0`
-  auto deal = [&](const std::vector<int>& rows, const std::vector<int>& wgs, int w0, int slot, int maxu) -> bool {
+  // units [0, n) of `rows` in contiguous blocks over `wgs`, waves in turn
+  // from `w0`; with `even`, the blocks have even bounds (the per-producer
+  // exchange layout deals word pairs)
+  auto deal = [&](const std::vector<int>& rows, const std::vector<int>& wgs, int w0, int slot, int maxu,
+                  bool even = false) -> bool {
     const size_t n = rows.size(), C = wgs.size();
     for (size_t i = 0; i < C; ++i) {
-      const size_t a = n * i / C, b = n * (i + 1) / C;
+      const size_t a = even ? 2 * (n / 2 * i / C) : n * i / C, b = even ? 2 * (n / 2 * (i + 1) / C) : n * (i + 1) / C;
       for (size_t u = a; u < b; ++u)
         if (!add(wgs[i], (int)((w0 + (u - a)) % kCW), slot, maxu, rows[u])) return false;
     }
@@ -249,9 +263,9 @@ const char* build_sched(const mk_config& c, int grid, std::vector<int32_t>& tab,
   std::vector<int> rh(H), ri(I / 2);
   for (int i = 0; i < H; ++i) rh[i] = i;
   for (int i = 0; i < I / 2; ++i) ri[i] = i;
-  if (!deal(rh, gw, 0, S_O, kMaxO)) return "too many O rows per wave for this grid";
+  if (!deal(rh, gw, 0, S_O, kMaxO, true)) return "too many O rows per wave for this grid";
   if (!deal(ri, gw, 0, S_GU, kMaxGU)) return "too many gate/up units per wave for this grid";
-  if (!deal(rh, gw, 3, S_D, kMaxD)) return "too many down rows per wave for this grid";
+  if (!deal(rh, gw, 3, S_D, kMaxD, true)) return "too many down rows per wave for this grid";
   // split attention: the GEMV workgroups of an XCD that holds KV heads help
   // those heads (in turn), up to the partials the home holds in LDS
   const int cap = kMaxSplit;
@@ -470,7 +484,10 @@ int mk_bind(mk_model* m, void* d_weights, void* d_kv, void* d_rope, void* d_scra
                                c.intermediate, &per_cu));
     m->coresident = per_cu * m->cus;
   }
-  layout_scratch(m, grid, false);  // never larger than the size reported for sizing_grid()
+  layout_scratch(m, grid, false);
+  if (m->scratch_bytes > m->scratch_reported)
+    return fail(m, MK_E_UNSUPPORTED, "grid %d needs %zu scratch bytes, more than the %zu reported", grid,
+                m->scratch_bytes, m->scratch_reported);
   m->P.grid = grid;
   m->d_weights = d_weights;
   m->d_kv = d_kv;
@@ -659,10 +676,13 @@ int mk_read_exchange(mk_model* m, int32_t layer, int32_t vec, float* h_out, size
   if (!h_out || n != len) return fail(m, MK_E_INVALID, "mk_read_exchange: need %zu outputs", len);
   if (!m->bound || m->epoch == 0) return fail(m, MK_E_STATE, "mk_read_exchange before any decode step");
   const size_t words = kPairs[vec] ? len / 2 : len;
-  std::vector<uint64_t> w(words);
   const Xch& X = m->P.x;
-  const uint64_t first = X.base + (uint64_t)layer * X.layer_words + X.off[kType[vec]];
-  HIPCK(m, hipMemcpy(w.data(), m->d_scratch + 8 * first, 8 * words, hipMemcpyDeviceToHost));
+  const int ty = kType[vec];
+  const size_t span = X.pad_c[ty] ? (size_t)X.pad_c[ty] * X.pad_stride[ty] : words;
+  std::vector<uint64_t> raw(span), w(words);
+  const uint64_t first = X.base + (uint64_t)layer * X.layer_words + X.off[ty];
+  HIPCK(m, hipMemcpy(raw.data(), m->d_scratch + 8 * first, 8 * span, hipMemcpyDeviceToHost));
+  for (size_t i = 0; i < words; ++i) w[i] = raw[xpad_word((uint32_t)i, (uint32_t)words, X.pad_c[ty], X.pad_stride[ty])];
   const uint32_t tag = (m->epoch << kPhaseBits) | (uint32_t)(2 + kTypes * layer + kType[vec]);
   for (size_t i = 0; i < words; ++i) {
     if ((uint32_t)w[i] != tag)

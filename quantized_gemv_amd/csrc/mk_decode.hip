@@ -369,15 +369,27 @@ struct Kern {
       hand_over(&s.seq, ++seq);
       XR_PUT(s, 1, XR_HANDOFF);
     }
+    // where the lane's pairs of the per-producer vectors sit (the same in every layer)
+    uint32_t mx[KX], mo[KX], mh[KH];
+#pragma unroll
+    for (int k = 0; k < KX; ++k) {
+      const uint32_t j = (uint32_t)min(lane + 64 * k, H / 2 - 1);
+      mx[k] = xpad_word(2 * j, H, p.x.pad_c[V_XD], p.x.pad_stride[V_XD]);
+      mo[k] = xpad_word(2 * j, H, p.x.pad_c[V_XO], p.x.pad_stride[V_XO]);
+    }
+#pragma unroll
+    for (int k = 0; k < KH; ++k) {
+      const uint32_t j = (uint32_t)min(lane + 64 * k, p.I / 4 - 1);
+      mh[k] = xpad_word(2 * j, p.I / 2, p.x.pad_c[V_H], p.x.pad_stride[V_H]);
+    }
     for (int l = 0; l < L; ++l) {
       const uint64_t loff = (uint64_t)l * p.layer_stride;
       const int ph = 2 + 6 * l;
       // ---- residual entering layer l (layer 0: the embedding above)
       if ((flags & 1) && l > 0) {
         XR_PUT(s, ph + 0, XR_START);
-        const uint32_t base = (uint32_t)(xvec(p, l - 1, V_XD) - p.xch);
-        if (!gather_pairs<KX>(p, rs, H / 2, make_tag(epoch, vec_id(l - 1, V_XD)), lo, hi,
-                              [=](int j) { return base + 2u * j; }))
+        if (!gather_pairs_at<KX>(p, rs, H / 2, make_tag(epoch, vec_id(l - 1, V_XD)), lo, hi, xword(p, l - 1, V_XD),
+                                 mx))
           return abort(s);
         XR_PUT(s, ph + 0, XR_READY);
         raw_to_lds<KX>(p, lo, hi, H, s.xd_raw, &s.r_xd);
@@ -429,9 +441,7 @@ struct Kern {
       // ---- residual after O
       if (flags & 4) {
         XR_PUT(s, ph + 4, XR_START);
-        const uint32_t base = (uint32_t)(xvec(p, l, V_XO) - p.xch);
-        if (!gather_pairs<KX>(p, rs, H / 2, make_tag(epoch, vec_id(l, V_XO)), lo, hi,
-                              [=](int j) { return base + 2u * j; }))
+        if (!gather_pairs_at<KX>(p, rs, H / 2, make_tag(epoch, vec_id(l, V_XO)), lo, hi, xword(p, l, V_XO), mo))
           return abort(s);
         XR_PUT(s, ph + 4, XR_READY);
         raw_to_lds<KX>(p, lo, hi, H, s.xo_raw, &s.r_xo);
@@ -442,9 +452,7 @@ struct Kern {
       if (flags & 8) {
         XR_PUT(s, ph + 5, XR_START);
         uint32_t hl[KH], hh[KH];
-        const uint32_t base = (uint32_t)(xvec(p, l, V_H) - p.xch);
-        if (!gather_pairs<KH>(p, rs, p.I / 4, make_tag(epoch, vec_id(l, V_H)), hl, hh,
-                              [=](int j) { return base + 2u * j; }))
+        if (!gather_pairs_at<KH>(p, rs, p.I / 4, make_tag(epoch, vec_id(l, V_H)), hl, hh, xword(p, l, V_H), mh))
           return abort(s);
         XR_PUT(s, ph + 5, XR_READY);
 #pragma unroll
@@ -460,9 +468,8 @@ struct Kern {
     const int ph_head = 2 + 6 * L;
     {
       XR_PUT(s, ph_head, XR_START);
-      const uint32_t base = (uint32_t)(xvec(p, L - 1, V_XD) - p.xch);
-      if (!gather_pairs<KX>(p, rs, H / 2, make_tag(epoch, vec_id(L - 1, V_XD)), lo, hi,
-                            [=](int j) { return base + 2u * j; }))
+      if (!gather_pairs_at<KX>(p, rs, H / 2, make_tag(epoch, vec_id(L - 1, V_XD)), lo, hi, xword(p, L - 1, V_XD),
+                               mx))
         return abort(s);
       XR_PUT(s, ph_head, XR_READY);
       raw_to_lds<KX>(p, lo, hi, H, s.xd_raw, &s.r_xd);
@@ -645,6 +652,7 @@ struct Kern {
     WRow<F_8, NI> d[kMaxD];
     uint32_t gin[NH][8];     // input-norm gains of the QKV rows' layer (lane slice)
     uint32_t gpost[NH][8];   // post-attention-norm gains (gate/up input)
+    uint32_t so[kMaxO], sg[kMaxGU], sd[kMaxD];   // output word of each O / gate-up / down unit
   };
 
   static __device__ __forceinline__ void load_layer_qkv(const Params& p, __amdgpu_buffer_rsrc_t rw, const int* u,
@@ -747,7 +755,7 @@ struct Kern {
       for (int k = 0; k < kMaxO; ++k) {
         const int r = u[S_O + k];
         const float v = s.xd_raw[max(r, 0)] + wrow_dot(w.o[k], xa);
-        st_xword(rx, ok && r >= 0 && l0 ? 8u * (base + r) : kOOB, __float_as_uint(v), tag);
+        st_xword(rx, ok && r >= 0 && l0 ? 8u * (base + w.so[k]) : kOOB, __float_as_uint(v), tag);
       }
       XR_MAX(s, ph + 3, XR_DONE);
       }
@@ -774,7 +782,7 @@ struct Kern {
           if (F_LIN != FMT_BF16) y[r] *= w.gu[k][r].s;
         }
         const float h0 = silu(y[0]) * y[1], h1 = silu(y[2]) * y[3];
-        st_xword(rx, ok && t >= 0 && l0 ? 8u * (base + t) : kOOB, pack_bf16(h0, h1), tag);
+        st_xword(rx, ok && t >= 0 && l0 ? 8u * (base + w.sg[k]) : kOOB, pack_bf16(h0, h1), tag);
       }
       XR_MAX(s, ph + 4, XR_DONE);
       }
@@ -793,7 +801,7 @@ struct Kern {
       for (int k = 0; k < kMaxD; ++k) {
         const int r = u[S_D + k];
         const float v = s.xo_raw[max(r, 0)] + wrow_dot(w.d[k], xa);
-        st_xword(rx, ok && r >= 0 && l0 ? 8u * (base + r) : kOOB, __float_as_uint(v), tag);
+        st_xword(rx, ok && r >= 0 && l0 ? 8u * (base + w.sd[k]) : kOOB, __float_as_uint(v), tag);
       }
       XR_MAX(s, ph + 5, XR_DONE);
       }
@@ -805,6 +813,15 @@ struct Kern {
                                                     int ns, int cw, uint32_t epoch, __amdgpu_buffer_rsrc_t rw,
                                                     __amdgpu_buffer_rsrc_t rx) {
     GemvW w;
+#pragma unroll
+    for (int k = 0; k < kMaxO; ++k)
+      w.so[k] = xpad_word((uint32_t)max(u[S_O + k], 0), p.H, p.x.pad_c[V_XO], p.x.pad_stride[V_XO]);
+#pragma unroll
+    for (int k = 0; k < kMaxGU; ++k)
+      w.sg[k] = xpad_word((uint32_t)max(u[S_GU + k], 0), p.I / 2, p.x.pad_c[V_H], p.x.pad_stride[V_H]);
+#pragma unroll
+    for (int k = 0; k < kMaxD; ++k)
+      w.sd[k] = xpad_word((uint32_t)max(u[S_D + k], 0), p.H, p.x.pad_c[V_XD], p.x.pad_stride[V_XD]);
     load_layer_qkv(p, rw, u, 0, w);
     bool ok = true;
     for (int l = 0; l + 1 < p.L; ++l) ok = gemv_layer<true>(p, s, l, hdr, u, w, pos, ns, cw, epoch, rw, rx, ok);
@@ -1140,10 +1157,12 @@ struct Kern {
 
   // ------------------------------------------------------------ LM head
   // Rows [va, vb) of this workgroup; compute wave cw takes va + cw + 7k, in
-  // double-buffered batches of UB rows.  Returns the wave's best (value,
+  // batches of UBH rows, NBH batches in flight (the first NBH go out before
+  // the wait for the final residual).  Returns the wave's best (value,
   // smallest index).  Rows past the wave's last are clamped to it and their
   // results dropped (no branch around a load or a store).
   static constexpr int UBH = F_8 == FMT_BF16 ? 4 : 8;
+  static constexpr int NBH = 4;
   static __device__ __forceinline__ bool lm_head(const Params& p, S& s, const int* hdr, int cw, float* d_logits,
                                                  __amdgpu_buffer_rsrc_t rw, bool ok, float& best, int& bidx) {
     const bool l0 = lane_id() == 0;
@@ -1153,9 +1172,11 @@ struct Kern {
     const GMat g = gmat(p.embed, 0);
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(d_logits, d_logits ? 4u * (uint32_t)p.V : 0u);
     auto row = [&](int k) { return n > 0 ? va + cw + kCW * min(k, n - 1) : -1; };
-    WRow<F_8, NH> B0[UBH], B1[UBH];
+    WRow<F_8, NH> B[NBH][UBH];
 #pragma unroll
-    for (int b = 0; b < UBH; ++b) wrow_load(rw, g, row(b), B0[b]);
+    for (int q = 0; q < NBH; ++q)
+#pragma unroll
+      for (int b = 0; b < UBH; ++b) wrow_load(rw, g, row(q * UBH + b), B[q][b]);
     asm volatile("" ::: "memory");
     uint32_t gf[NH][8];
     gain_load<NH>(rw, (uint32_t)p.final_norm, p.H, true, gf);
@@ -1165,10 +1186,10 @@ struct Kern {
     norm_act<NH>(s.xd_raw, s.r_xd, gf, p.H, xa);
     best = -INFINITY;
     bidx = 0x7FFFFFFF;
-    auto use = [&](const WRow<F_8, NH>(&B)[UBH], int k0) {
+    auto use = [&](const WRow<F_8, NH>(&Bq)[UBH], int k0) {
 #pragma unroll
       for (int b = 0; b < UBH; ++b) {
-        const float v = wrow_dot(B[b], xa);
+        const float v = wrow_dot(Bq[b], xa);
         const bool in = k0 + b < n;
         const int r = va + cw + kCW * (k0 + b);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rl, in && l0 ? 4u * (uint32_t)r : kOOB, 0, 0);
@@ -1177,17 +1198,16 @@ struct Kern {
         bidx = take ? r : bidx;
       }
     };
-    // the scheduling barriers keep each next batch's loads ahead of the
-    // current batch's arithmetic
-    for (int k0 = 0; k0 < n; k0 += 2 * UBH) {
+    // each batch is reloaded right after its use; the scheduling barriers
+    // keep the loads ahead of the next batch's arithmetic
+    for (int k0 = 0; k0 < n; k0 += NBH * UBH) {
 #pragma unroll
-      for (int b = 0; b < UBH; ++b) wrow_load(rw, g, row(k0 + UBH + b), B1[b]);
-      __builtin_amdgcn_sched_barrier(0);
-      use(B0, k0);
+      for (int q = 0; q < NBH; ++q) {
+        use(B[q], k0 + q * UBH);
 #pragma unroll
-      for (int b = 0; b < UBH; ++b) wrow_load(rw, g, row(k0 + 2 * UBH + b), B0[b]);
-      __builtin_amdgcn_sched_barrier(0);
-      use(B1, k0 + UBH);
+        for (int b = 0; b < UBH; ++b) wrow_load(rw, g, row(k0 + (q + NBH) * UBH + b), B[q][b]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     XR_MAX(s, 2 + 6 * p.L, XR_DONE);
     return ok;

@@ -1,5 +1,6 @@
 // Structures shared by the host launcher and the gfx950 kernels.
 #pragma once
+#include <hip/hip_runtime.h>
 #include <stdint.h>
 
 // Device code sees the buffers through address-space-1 (global) pointers, so
@@ -70,12 +71,25 @@ struct Xch {
   uint64_t base;              // word offset of layer 0's block
   uint64_t layer_words;       // words per layer block
   uint64_t off[kTypes];       // offset of each vector in a block
+  // Vectors written by many producers (the residuals after O and down) are
+  // laid out per producer: the vector's words are dealt
+  // in contiguous blocks of even length over pad_c producers, and block i
+  // starts a line of its own, at word i * pad_stride (0 = packed layout).
+  uint32_t pad_c[kTypes], pad_stride[kTypes];
   uint64_t arg;               // argmax words [grid][2] (value, index)
   uint64_t err;               // error word (uint32 in a 64-bit slot)
   uint64_t amax;              // packing scratch: tensor abs-max (uint32 bits)
   uint64_t sched;             // the work table (int32)
   uint64_t words;             // total words
 };
+
+// Word w of an n-word exchange vector in the per-producer layout (see Xch).
+__host__ __device__ inline uint32_t xpad_word(uint32_t w, uint32_t n, uint32_t c, uint32_t stride) {
+  if (c == 0) return w;
+  const uint32_t np = n / 2, j = w / 2;
+  const uint32_t i = ((j + 1) * c - 1) / np;   // the block holding pair j
+  return i * stride + 2 * (j - np * i / c) + (w & 1u);
+}
 
 // Per-workgroup header of the work table (ints).
 enum : int {

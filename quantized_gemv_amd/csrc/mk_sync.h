@@ -177,6 +177,49 @@ __device__ __forceinline__ bool gather_pairs(const Params& p, __amdgpu_buffer_rs
   }
 }
 
+// Courier gather of a vector in the per-producer layout: the lane's pair k
+// (pair lane + 64k of the vector, valid if below npairs) is at word
+// base + off[k]; off[] was computed once per launch (clamped for lanes past
+// the end).
+template <int MAXK>
+__device__ __forceinline__ bool gather_pairs_at(const Params& p, __amdgpu_buffer_rsrc_t r, int npairs, uint32_t tag,
+                                                uint32_t (&lo)[MAXK], uint32_t (&hi)[MAXK], uint32_t base,
+                                                const uint32_t (&off)[MAXK]) {
+  const int lane = threadIdx.x & 63;
+  tag += p.tag_skew;
+  uint32_t pend = 0;
+  v4u v[MAXK];
+#pragma unroll
+  for (int k = 0; k < MAXK; ++k) {
+    if (lane + 64 * k < npairs) pend |= 1u << k;
+    v[k] = ld_pair(r, base + off[k]);
+  }
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  uint32_t rounds = 0;
+  while (true) {
+#pragma unroll
+    for (int k = 0; k < MAXK; ++k) {
+      if (v[k].x == tag && v[k].z == tag) pend &= ~(1u << k);
+      lo[k] = v[k].y;
+      hi[k] = v[k].w;
+    }
+    if (__builtin_amdgcn_ballot_w64(pend != 0) == 0) return true;
+    ++rounds;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > p.spin_limit) {
+      raise_error(p, ERR_TIMEOUT);
+      return false;
+    }
+    if ((rounds & 63u) == 0 &&
+        __hip_atomic_load(err_word(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+      return false;
+    for (uint32_t z = 0; z < p.poll_sleep; ++z) __builtin_amdgcn_s_sleep(8);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int k = 0; k < MAXK; ++k)
+      if ((pend >> k) & 1u) v[k] = ld_pair(r, base + off[k]);
+  }
+}
+
 // The same gather, but each pair's payloads are handed to put(j, lo, hi)
 // (an LDS write) as soon as the pair carries the tag, so a lane keeps only
 // its loads in flight in registers.

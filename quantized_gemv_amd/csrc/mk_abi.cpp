@@ -163,17 +163,17 @@ void layout_scratch(mk_model* m, int grid, bool for_sizing = true) {
   uint64_t lw = 0;
   const uint64_t pw = split_pw(c);
   uint64_t sizes[kTypes] = {(nq + 2 * nkv) * hd, nkv * (uint64_t)kMaxSplit * pw, nq * hd / 2, H, I / 2, H};
-  // the residuals in the per-producer layout: the GEMV workgroups' blocks
-  // (even length) each start a 128-byte line
+  // the residuals and the SwiGLU output in the per-producer layout: the
+  // GEMV workgroups' blocks (even length) each start a 128-byte line
   const uint32_t cg = (uint32_t)std::max(grid - (int)nkv, 1);
-  for (int t : {(int)V_XO, (int)V_XD}) {
+  for (int t : {(int)V_XO, (int)V_H, (int)V_XD}) {
     const uint64_t np = sizes[t] / 2;
     const uint32_t stride = (uint32_t)((2 * ((np + cg - 1) / cg) + 15) / 16 * 16);
     X.pad_c[t] = cg;
     X.pad_stride[t] = stride;
     sizes[t] = (uint64_t)cg * stride;
   }
-  for (int t : {(int)V_QKV, (int)V_ATT, (int)V_O, (int)V_H}) X.pad_c[t] = X.pad_stride[t] = 0;
+  for (int t : {(int)V_QKV, (int)V_ATT, (int)V_O}) X.pad_c[t] = X.pad_stride[t] = 0;
   for (int t = 0; t < kTypes; ++t) {
     X.off[t] = lw;
     lw = al(lw + sizes[t]);
@@ -264,7 +264,7 @@ const char* build_sched(const mk_config& c, int grid, std::vector<int32_t>& tab,
   for (int i = 0; i < H; ++i) rh[i] = i;
   for (int i = 0; i < I / 2; ++i) ri[i] = i;
   if (!deal(rh, gw, 0, S_O, kMaxO, true)) return "too many O rows per wave for this grid";
-  if (!deal(ri, gw, 0, S_GU, kMaxGU)) return "too many gate/up units per wave for this grid";
+  if (!deal(ri, gw, 0, S_GU, kMaxGU, true)) return "too many gate/up units per wave for this grid";
   if (!deal(rh, gw, 3, S_D, kMaxD, true)) return "too many down rows per wave for this grid";
   // split attention: the GEMV workgroups of an XCD that holds KV heads help
   // those heads (in turn), up to the partials the home holds in LDS

@@ -773,6 +773,7 @@ struct Kern {
 #pragma unroll
       for (int k = 0; k < kMaxGU; ++k) {
         const int t = u[S_GU + k];
+        if (k > 0 && t < 0) break;   // wave-uniform, and no load inside the loop
         float y[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) y[r] = wrow_partial(w.gu[k][r], xa);

@@ -39,7 +39,7 @@ constexpr uint32_t kOOB = 0x7FFFFFF0u;
 constexpr uint64_t kMaxBuffer = 0x7FFF0000ull;   // largest buffer read that way
 
 // Units per compute wave and phase (the host checks its schedule against these).
-constexpr int kMaxQKV = 3, kMaxO = 1, kMaxGU = 1, kMaxD = 1;
+constexpr int kMaxQKV = 3, kMaxO = 1, kMaxGU = 2, kMaxD = 1;
 constexpr int kSchedInts = 32;               // ints per workgroup header and per compute wave
 
 // One packed matrix in the weight arena (byte offsets from the arena base).
@@ -71,8 +71,8 @@ struct Xch {
   uint64_t base;              // word offset of layer 0's block
   uint64_t layer_words;       // words per layer block
   uint64_t off[kTypes];       // offset of each vector in a block
-  // Vectors written by many producers (the residuals after O and down) are
-  // laid out per producer: the vector's words are dealt
+  // Vectors written by many producers (the residuals after O and down, the
+  // SwiGLU output) are laid out per producer: the vector's words are dealt
   // in contiguous blocks of even length over pad_c producers, and block i
   // starts a line of its own, at word i * pad_stride (0 = packed layout).
   uint32_t pad_c[kTypes], pad_stride[kTypes];

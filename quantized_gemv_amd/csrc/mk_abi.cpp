@@ -55,6 +55,7 @@ struct mk_model {
   int grid_opt = 0;
   int64_t spin_limit = 100000000;
   std::vector<int32_t> sched;   // the work table (host copy)
+  std::vector<int32_t> qkv_word;   // word of each q/k/v row in the per-producer layout
   uint32_t tag_skew = 0;
   uint32_t poll_sleep = 0;
   int launch_mode = -1;         // 0 cooperative, 1 plain launch of a grid that fits at once, -1 choose
@@ -154,6 +155,31 @@ uint64_t split_pw(const mk_config& c) {
   return (gs * c.head_dim + 2 * gs + 15) / 16 * 16;
 }
 
+// The per-producer layout of the q/k/v vector: XCD slot sl holds the rows
+// of KV heads g = sl, sl + 8, ... (each head's q rows, k rows, v rows), dealt
+// in even blocks over the slot's GEMV workgroups; block i of the slot starts
+// at word base + i * stride.
+struct QkvSlot {
+  uint64_t n = 0, c = 0, stride = 0, base = 0;
+};
+void qkv_slots(const mk_config& c, int grid, QkvSlot (&sl)[8], uint64_t* total) {
+  const int nkv = c.n_kv_heads, gs = c.n_q_heads / c.n_kv_heads, hd = c.head_dim;
+  uint64_t w = 0;
+  for (int t = 0; t < 8; ++t) {
+    QkvSlot q;
+    for (int g = t; g < nkv; g += 8) q.n += (uint64_t)(gs + 2) * hd;
+    for (int wg = t; wg < grid; wg += 8)
+      if (wg >= nkv) ++q.c;
+    if (q.n && q.c) {
+      q.stride = (2 * ((q.n / 2 + q.c - 1) / q.c) + 15) / 16 * 16;
+      q.base = w;
+      w += q.c * q.stride;
+    }
+    sl[t] = q;
+  }
+  *total = w;
+}
+
 void layout_scratch(mk_model* m, int grid, bool for_sizing = true) {
   const mk_config& c = m->cfg;
   Xch& X = m->P.x;
@@ -174,6 +200,10 @@ void layout_scratch(mk_model* m, int grid, bool for_sizing = true) {
     sizes[t] = (uint64_t)cg * stride;
   }
   for (int t : {(int)V_QKV, (int)V_ATT, (int)V_O}) X.pad_c[t] = X.pad_stride[t] = 0;
+  {
+    QkvSlot sl[8];
+    qkv_slots(c, grid, sl, &sizes[V_QKV]);
+  }
   for (int t = 0; t < kTypes; ++t) {
     X.off[t] = lw;
     lw = al(lw + sizes[t]);
@@ -188,6 +218,8 @@ void layout_scratch(mk_model* m, int grid, bool for_sizing = true) {
   X.sched = (w + 31) / 32 * 32;                 // 256-byte boundary
   w = X.sched;
   w += (uint64_t)grid * kWaves * kSchedInts / 2;
+  X.qmap = w;
+  w += (nkv * (uint64_t)(nq / nkv + 2) * hd / 2 + 1) / 2;
   w = (w + 31) / 32 * 32;
   X.words = w;
   m->params_off = align_up(w * 8);
@@ -210,7 +242,8 @@ void layout_scratch(mk_model* m, int grid, bool for_sizing = true) {
 //  * O, gate/up (units of four rows = one output word), down: over the
 //    workgroups without attention; each matrix starts at a different wave
 //    so every wave gets a similar share.
-const char* build_sched(const mk_config& c, int grid, std::vector<int32_t>& tab, int* split_n = nullptr) {
+const char* build_sched(const mk_config& c, int grid, std::vector<int32_t>& tab, int* split_n = nullptr,
+                        std::vector<int32_t>* qkv_word = nullptr) {
   const int nkv = c.n_kv_heads, hd = c.head_dim, nq = c.n_q_heads, gs = nq / nkv;
   const int H = c.hidden, I = c.intermediate;
   const int nA = nkv;
@@ -242,7 +275,15 @@ const char* build_sched(const mk_config& c, int grid, std::vector<int32_t>& tab,
     return true;
   };
   for (int wg = 0; wg < grid; ++wg) hdr(wg, S_ATT) = wg < nA ? wg : -1;
-  // QKV, per XCD slot
+  // QKV, per XCD slot, in the per-producer layout; the table after the
+  // workgroups' rows maps each KV head's q/k/v pairs to their words
+  QkvSlot qs[8];
+  uint64_t qtotal = 0;
+  qkv_slots(c, grid, qs, &qtotal);
+  const size_t np_head = (size_t)(gs + 2) * hd / 2;
+  tab.resize((size_t)grid * kWaves * kSchedInts + nkv * np_head, -1);
+  int32_t* qmap = tab.data() + (size_t)grid * kWaves * kSchedInts;
+  std::vector<int32_t> word((size_t)(nq + 2 * nkv) * hd, -1);
   for (int sl = 0; sl < 8; ++sl) {
     std::vector<int> wgs;
     for (int wg = sl; wg < grid; wg += 8)
@@ -255,8 +296,23 @@ const char* build_sched(const mk_config& c, int grid, std::vector<int32_t>& tab,
     }
     if (rows.empty()) continue;
     if (wgs.empty()) return "no workgroup on an XCD that holds a KV head";
-    if (!deal(rows, wgs, 0, S_QKV, kMaxQKV)) return "too many QKV rows per wave for this grid";
+    if (!deal(rows, wgs, 0, S_QKV, kMaxQKV, true)) return "too many QKV rows per wave for this grid";
+    const QkvSlot& q = qs[sl];
+    for (size_t u = 0; u < rows.size(); ++u)
+      word[rows[u]] = (int32_t)(q.base + xpad_word((uint32_t)u, (uint32_t)q.n, (uint32_t)q.c, (uint32_t)q.stride));
+    size_t hu = 0;   // the slot's heads in deal order
+    for (int g = sl; g < nkv; g += 8, hu += 2 * np_head)
+      for (size_t j = 0; j < np_head; ++j)
+        qmap[(size_t)g * np_head + j] = (int32_t)(q.base + xpad_word((uint32_t)(hu + 2 * j), (uint32_t)q.n,
+                                                                      (uint32_t)q.c, (uint32_t)q.stride));
   }
+  for (int wg = 0; wg < grid; ++wg)
+    for (int cw = 0; cw < kCW; ++cw)
+      for (int k = 0; k < kMaxQKV; ++k) {
+        const int r = unit(wg, cw, S_QKV + k);
+        unit(wg, cw, S_QKVW + k) = r >= 0 ? word[r] : -1;
+      }
+  if (qkv_word) *qkv_word = word;
   // O, gate/up, down
   std::vector<int> gw;
   for (int wg = nA; wg < grid; ++wg) gw.push_back(wg);
@@ -497,7 +553,7 @@ int mk_bind(mk_model* m, void* d_weights, void* d_kv, void* d_rope, void* d_scra
   m->bound = true;
   m->params_dirty = true;
   m->epoch = 0;
-  const char* why = build_sched(m->cfg, grid, m->sched, &m->split_n);
+  const char* why = build_sched(m->cfg, grid, m->sched, &m->split_n, &m->qkv_word);
   if (why) return fail(m, MK_E_UNSUPPORTED, "grid %d: %s", grid, why);
   HIPCK(m, hipMemsetAsync(d_scratch, 0, m->scratch_bytes, s));
   HIPCK(m, hipMemcpyAsync(m->d_scratch + 8 * m->P.x.sched, m->sched.data(), m->sched.size() * sizeof(int32_t),
@@ -678,11 +734,14 @@ int mk_read_exchange(mk_model* m, int32_t layer, int32_t vec, float* h_out, size
   const size_t words = kPairs[vec] ? len / 2 : len;
   const Xch& X = m->P.x;
   const int ty = kType[vec];
-  const size_t span = X.pad_c[ty] ? (size_t)X.pad_c[ty] * X.pad_stride[ty] : words;
+  const size_t span = ty == V_QKV ? (size_t)(X.off[V_QKV + 1] - X.off[V_QKV])
+                     : X.pad_c[ty] ? (size_t)X.pad_c[ty] * X.pad_stride[ty] : words;
   std::vector<uint64_t> raw(span), w(words);
   const uint64_t first = X.base + (uint64_t)layer * X.layer_words + X.off[ty];
   HIPCK(m, hipMemcpy(raw.data(), m->d_scratch + 8 * first, 8 * span, hipMemcpyDeviceToHost));
-  for (size_t i = 0; i < words; ++i) w[i] = raw[xpad_word((uint32_t)i, (uint32_t)words, X.pad_c[ty], X.pad_stride[ty])];
+  for (size_t i = 0; i < words; ++i)
+    w[i] = raw[ty == V_QKV ? (size_t)m->qkv_word[i]
+                           : xpad_word((uint32_t)i, (uint32_t)words, X.pad_c[ty], X.pad_stride[ty])];
   const uint32_t tag = (m->epoch << kPhaseBits) | (uint32_t)(2 + kTypes * layer + kType[vec]);
   for (size_t i = 0; i < words; ++i) {
     if ((uint32_t)w[i] != tag)

@@ -370,6 +370,9 @@ struct Kern {
       XR_PUT(s, 1, XR_HANDOFF);
     }
     // where the lane's pairs of the per-producer vectors sit (the same in every layer)
+    uint32_t qm[KA];
+    qkv_map(p, att >= 0 ? att : (LONG && hdr[S_SPLIT] >= 0 ? hdr[S_SPLIT] : 0),
+            att >= 0 ? (GS + 2) * HD / 2 : NOUT / 2, qm);
     uint32_t mx[KX], mo[KX], mh[KH];
 #pragma unroll
     for (int k = 0; k < KX; ++k) {
@@ -400,7 +403,7 @@ struct Kern {
       // ---- q, k, v of KV head `att`: q/k RMSNorm, RoPE, KV append
       if (att >= 0) {
         XR_PUT(s, ph + 1, XR_START);
-        if (!attention_input<true>(p, s, l, att, pos, epoch, rs)) return abort(s);
+        if (!attention_input<true>(p, s, l, att, pos, epoch, rs, qm)) return abort(s);
         hand_over(&s.seq, ++seq);
         XR_PUT(s, ph + 1, XR_HANDOFF);
         lds_barrier();   // q, k and v are normed, roped and appended
@@ -412,7 +415,7 @@ struct Kern {
       if (LONG && hdr[S_SPLIT] >= 0) {
         if (hdr[S_SPLIT_IDX] <= ns) {
           XR_PUT(s, ph + 1, XR_START);
-          if (!attention_input<false>(p, s, l, hdr[S_SPLIT], pos, epoch, rs)) return abort(s);
+          if (!attention_input<false>(p, s, l, hdr[S_SPLIT], pos, epoch, rs, qm)) return abort(s);
           hand_over(&s.seq, ++seq);
           XR_PUT(s, ph + 1, XR_HANDOFF);
           lds_barrier();   // q is normed and roped
@@ -515,13 +518,23 @@ struct Kern {
     return false;
   }
 
+  // The word offsets (in the q/k/v vector) of the lane's pairs of KV head
+  // g's q, k and v rows, from the map in the work table (read once per
+  // launch; pairs past the first np repeat the last one).
+  static __device__ __forceinline__ void qkv_map(const Params& p, int g, int np, uint32_t (&qm)[KA]) {
+    MK_GLOBAL const int* m = GCAST(const int, p.xch + p.x.qmap) + (size_t)g * ((GS + 2) * HD / 2);
+#pragma unroll
+    for (int k = 0; k < KA; ++k) qm[k] = (uint32_t)m[min(lane_id() + 64 * k, np - 1)];
+  }
+
   // Gather q (GS heads), k and v of KV head g into LDS, with this layer's
   // q/k-norm gains and this position's RoPE pairs (loaded ahead of the
   // gather); the compute waves norm, rope and append them (att_prepare).
   // Without KV (a split-attention helper): q only, with the q-norm gains.
+  // qm: the word offsets of the lane's pairs (see qkv_map).
   template <bool KV>
   static __device__ bool attention_input(const Params& p, S& s, int l, int g, int pos, uint32_t epoch,
-                                         __amdgpu_buffer_rsrc_t rs) {
+                                         __amdgpu_buffer_rsrc_t rs, const uint32_t (&qm)[KA]) {
     MK_GLOBAL const uint8_t* const W = p.w;
     const int lane = lane_id();
     const int nq = p.nq, nkv = p.nkv;
@@ -534,16 +547,12 @@ struct Kern {
     const float gk_lo = bf16_to_f32(gk[li]), gk_hi = bf16_to_f32(gk[li + HD / 2]);
     MK_GLOBAL const float* cs = p.rope + ((size_t)pos * (HD / 2) + li) * 2;
     const float rc = cs[0], rsn = cs[1];
-    const uint32_t base = (uint32_t)(xvec(p, l, V_QKV) - p.xch);
-    const uint32_t qo = base + (uint32_t)(g * NOUT), ko = base + (uint32_t)((nq + g) * HD),
-                   vo = base + (uint32_t)((nq + nkv + g) * HD);
     constexpr int NP = KV ? (GS + 2) * HD / 2 : NOUT / 2;   // pairs gathered
     constexpr int K = (NP + 63) / 64;
-    uint32_t lo[K], hi[K];
-    if (!gather_pairs<K>(p, rs, NP, make_tag(epoch, vec_id(l, V_QKV)), lo, hi, [=](int j) {
-          const int w = 2 * j;
-          return w < NOUT ? qo + w : (w < NOUT + HD ? ko + (w - NOUT) : vo + (w - NOUT - HD));
-        }))
+    uint32_t lo[K], hi[K], off[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) off[k] = qm[k];
+    if (!gather_pairs_at<K>(p, rs, NP, make_tag(epoch, vec_id(l, V_QKV)), lo, hi, xword(p, l, V_QKV), off))
       return false;
     XR_PUT(s, 2 + 6 * l + 1, XR_READY);
 #pragma unroll
@@ -718,7 +727,7 @@ struct Kern {
       for (int k = 0; k < kMaxQKV; ++k) {
         const int r = u[S_QKV + k];
         const float v = wrow_dot(w.q[k], xa);
-        st_xword(rx, ok && r >= 0 && l0 ? 8u * (base + r) : kOOB, __float_as_uint(v), tag);
+        st_xword(rx, ok && r >= 0 && l0 ? 8u * (base + (uint32_t)u[S_QKVW + k]) : kOOB, __float_as_uint(v), tag);
       }
       XR_MAX(s, ph + 0, XR_DONE);
       }
@@ -1241,9 +1250,9 @@ struct Kern {
       if (!courier(p, s, hdr, token, pos, ns, epoch, d_next)) return;
     } else {
       const int cw = wave - 1;
-      int u[16];
+      int u[kUnitInts];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) u[i] = __builtin_amdgcn_readfirstlane(tab[kSchedInts * wave + i]);
+      for (int i = 0; i < kUnitInts; ++i) u[i] = __builtin_amdgcn_readfirstlane(tab[kSchedInts * wave + i]);
       const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w, p.w_bytes);
       bool ok = hdr[S_ATT] >= 0 ? att_waves(p, s, hdr[S_ATT], pos, ns, cw, epoch, rx)
                                 : gemv_waves(p, s, hdr, u, pos, ns, cw, epoch, rw, rx);

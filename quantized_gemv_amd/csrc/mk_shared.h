@@ -80,6 +80,8 @@ struct Xch {
   uint64_t err;               // error word (uint32 in a 64-bit slot)
   uint64_t amax;              // packing scratch: tensor abs-max (uint32 bits)
   uint64_t sched;             // the work table (int32)
+  uint64_t qmap;              // per KV head: word offset (in the q/k/v vector) of each pair of
+                              // its q rows, k rows and v rows, in that order (int32)
   uint64_t words;             // total words
 };
 
@@ -108,8 +110,11 @@ enum : int {
 };
 constexpr int kMaxSplit = 32;   // helpers per KV head (the home merges their partials in LDS)
 constexpr int kSplitGatherK = 5;    // partial word pairs per lane and round of the home's gather
-// Per compute wave: units of each phase (-1 = none), at these offsets.
-enum : int { S_QKV = 0, S_O = 4, S_GU = 8, S_D = 12 };
+// Per compute wave: units of each phase (-1 = none), at these offsets, and
+// the word each QKV unit stores (the q/k/v vector is laid out per producer
+// too: per XCD, the rows of its KV heads are dealt in even blocks over its
+// GEMV workgroups, each block starting a 128-byte line).
+enum : int { S_QKV = 0, S_O = 4, S_GU = 8, S_D = 12, S_QKVW = 16, kUnitInts = 20 };
 
 struct Params {
   MK_GLOBAL const uint8_t* w;   // weight arena

@@ -19,8 +19,8 @@ def lib_path(xray: bool = False) -> str:
     return os.path.join(HERE, "libmk_xray.so" if xray else "libmk.so")
 
 
-def build(xray: bool = False, verbose: bool = False) -> str:
-    out = lib_path(xray)
+def build(xray: bool = False, verbose: bool = False, out: str = "") -> str:
+    out = out or lib_path(xray)
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            # no packed-FP32 instructions anywhere in the device code
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

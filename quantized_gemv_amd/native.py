@@ -61,10 +61,11 @@ _VP = ctypes.c_void_p
 
 
 def load(xray: bool = False) -> ctypes.CDLL:
-    """Load libmk.so (or libmk_xray.so).  Raises if it has not been built."""
+    """Load libmk.so (or libmk_xray.so; MK_LIBRARY / MK_LIBRARY_XRAY name
+    another build of the same library).  Raises if it has not been built."""
     if xray in _LIBS:
         return _LIBS[xray]
-    path = lib_path(xray)
+    path = os.environ.get("MK_LIBRARY_XRAY" if xray else "MK_LIBRARY") or lib_path(xray)
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with quantized_gemv_amd/build.py "
                            "(there is no fallback path)")

@@ -95,7 +95,7 @@ __device__ __forceinline__ bool wait_seq(const Params& p, const uint32_t* seq, u
   if (s >= want) return s != kAbort;
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   for (uint32_t n = 1;; ++n) {
-    __builtin_amdgcn_s_sleep(1);   // yield issue slots (spinning slowed the split-attention path)
+    __builtin_amdgcn_s_sleep(1);
     s = __builtin_amdgcn_readfirstlane(lds_ld(seq));
     if (s >= want) return s != kAbort;
     if ((n & 255u) == 0 && __builtin_amdgcn_s_memrealtime() - t0 > p.spin_limit) {

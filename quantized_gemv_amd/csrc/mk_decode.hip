@@ -1172,7 +1172,9 @@ struct Kern {
   // smallest index).  Rows past the wave's last are clamped to it and their
   // results dropped (no branch around a load or a store).
   static constexpr int UBH = F_8 == FMT_BF16 ? 4 : 8;
-  static constexpr int NBH = 4;
+  // FP8 rows carry a scale register each: two batches keep them within the
+  // register file (four pushed the split variant's scalars into scratch)
+  static constexpr int NBH = F_8 == FMT_BF16 ? 4 : 2;
   static __device__ __forceinline__ bool lm_head(const Params& p, S& s, const int* hdr, int cw, float* d_logits,
                                                  __amdgpu_buffer_rsrc_t rw, bool ok, float& best, int& bidx) {
     const bool l0 = lane_id() == 0;

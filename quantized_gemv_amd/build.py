@@ -27,6 +27,7 @@ def build(xray: bool = False, verbose: bool = False, out: str = "") -> str:
            "-I", os.path.join(ROOT, "include"), "-I", CSRC]
     if xray:
         cmd.append("-DMK_XRAY")
+    cmd.append("-Rpass-analysis=kernel-resource-usage")
     cmd += [os.path.join(CSRC, s) for s in SOURCES]
     cmd += ["-o", out + ".tmp"]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -35,7 +36,35 @@ def build(xray: bool = False, verbose: bool = False, out: str = "") -> str:
         raise RuntimeError(f"hipcc failed building {os.path.basename(out)}")
     if verbose:
         sys.stderr.write(r.stderr)
+    bad = [f"{k}: {v}" for k, v in resource_usage(r.stderr).items()
+           if "decode_kernel" in k and (v.get("scratch", 0) or v.get("vgpr_spill", 0))]
+    if bad and not xray:   # the X-ray stamps may spill; that build is for diagnosis only
+        os.remove(out + ".tmp")
+        raise RuntimeError("decode kernel spills to scratch memory (slow in the layer loop):\n" + "\n".join(bad))
     os.replace(out + ".tmp", out)
+    return out
+
+
+def resource_usage(remarks: str) -> dict:
+    """Per kernel: VGPRs, spills and scratch bytes from the compiler's
+    kernel-resource-usage remarks."""
+    out, cur = {}, None
+    keys = {"VGPRs": "vgpr", "SGPRs Spill": "sgpr_spill", "VGPRs Spill": "vgpr_spill",
+            "ScratchSize [bytes/lane]": "scratch"}
+    for line in remarks.splitlines():
+        if "remark:" not in line:
+            continue
+        text = line.split("remark:", 1)[1].split("[-Rpass", 1)[0].strip()
+        if text.startswith("Function Name:"):
+            cur = text.split(":", 1)[1].strip()
+            out[cur] = {}
+        elif cur and ":" in text:
+            k, v = text.rsplit(":", 1)
+            if k.strip() in keys:
+                try:
+                    out[cur][keys[k.strip()]] = int(v.strip())
+                except ValueError:
+                    pass
     return out
 
 

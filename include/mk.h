@@ -132,7 +132,11 @@ int mk_bind(mk_model* m, void* d_weights, void* d_kv, void* d_rope, void* d_scra
  * [H].  Quantization follows the page's formats: FP8 per-row scale
  * s = absmax/448 and codes e4m3(w/s); NVFP4 tensor scale ts = absmax/2688,
  * block scale bs = e4m3(blockmax/(6*ts)) and codes e2m1(w/(e4m3(bs)*ts)); all
- * encodes round to nearest even and saturate.  The tensors are read during
+ * encodes round to nearest even and saturate.  With option 9 = k > 0 each
+ * NVFP4 block's scale code is instead the one within +-k of that bs (and in
+ * 0..0x7E) whose block squared error sum_i (w_i - w_hat_i)^2 is least, the
+ * error summed in float64 in element order, the smaller code on a tie (the
+ * page's per-block MSE scale search).  The tensors are read during
  * the call only.  Errors: MK_E_INVALID, MK_E_STATE (not bound), MK_E_HIP. */
 int mk_pack_weights(mk_model* m, const void* const* d_tensors, int32_t n_tensors, mk_stream_t s);
 
@@ -218,7 +222,9 @@ int mk_decode_codes(int32_t codec, const uint8_t* d_codes, int32_t n, float* d_o
  * GEMV workgroups there, at most 32 per head), each taking an equal slice;
  * the home merges their partial (maximum, sum, output) triples with the
  * log-sum-exp rule.  c = 0 turns it off.  (On MI355X at the 0.6B shape the
- * split path is faster from about 450 cached positions on.)
+ * split path is faster from about 450 cached positions on.)  Key 9, NVFP4
+ * block scale search radius 0..126 [0], set before mk_pack_weights (see
+ * there); 0 keeps the absolute-maximum recipe.
  * Keys 1 and 2 are reserved.
  * Errors: MK_E_INVALID (unknown key, value out of range), MK_E_STATE. */
 int mk_set_option(mk_model* m, int32_t key, int64_t value);

@@ -50,17 +50,18 @@ def tensor_format(wfmt: int, name: str) -> str:
 
 
 # ------------------------------------------------------------ primitives
-def quantize_tensor(bits: np.ndarray, fmt: str):
+def quantize_tensor(bits: np.ndarray, fmt: str, fp4_search: int = 0):
     """Store one bf16 master tensor in `fmt` ("bf16", "fp8" or "fp4") and
     return (the packed form, its float32 dequantization).  FP8 scales are per
     row, so rows of a tensor may be quantized on their own; FP4 needs the
-    whole tensor (its tensor scale)."""
+    whole tensor (its tensor scale).  `fp4_search` is the NVFP4 block scale
+    search radius (0: the absolute-maximum recipe)."""
     w = bf16_bits_to_f32(bits)
     if fmt == "fp8":
         p = quant_fp8_row(w)
         return p, p.dequant()
     if fmt == "fp4":
-        p = quant_fp4(w)
+        p = quant_fp4(w, fp4_search)
         return p, p.dequant()
     return bits, w
 
@@ -136,11 +137,13 @@ class Oracle:
 
     `dtype` is the arithmetic type (float32 by default); `round_bf16=False`
     removes the bf16 rounding points (used with float64 only, to bound the
-    oracle's own rounding)."""
+    oracle's own rounding); `fp4_search` is the NVFP4 block scale search
+    radius (0: the absolute-maximum recipe)."""
 
     def __init__(self, master, wfmt: int, max_ctx: int, dtype=np.float32,
-                 round_bf16: bool = True):
+                 round_bf16: bool = True, fp4_search: int = 0):
         sh = master.shape
+        self.fp4_search = fp4_search
         self.shape, self.wfmt, self.max_ctx = sh, wfmt, max_ctx
         self.dt, self.round_bf16 = dtype, round_bf16
         self.eps = sh.rms_eps
@@ -160,7 +163,7 @@ class Oracle:
         self.cos, self.sin = rope_table(max_ctx, sh.head_dim, sh.rope_theta)
 
     def _prepare(self, layer: int, name: str, bits: np.ndarray) -> np.ndarray:
-        p, w = quantize_tensor(bits, tensor_format(self.wfmt, name))
+        p, w = quantize_tensor(bits, tensor_format(self.wfmt, name), self.fp4_search)
         self.packed[(layer, name)] = p
         return w.astype(self.dt)
 

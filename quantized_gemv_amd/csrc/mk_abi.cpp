@@ -63,6 +63,7 @@ struct mk_model {
   int split_from = 448;         // split attention from this position on
   int split_n = 0;              // helpers per KV head in the work table
   int coresident = 0;           // decode workgroups the device holds at once (set by mk_bind)
+  int fp4_search = 0;           // NVFP4 block scale search radius (0: absolute-maximum recipe)
   uint32_t epoch = 0;
   std::string err;
 };
@@ -584,7 +585,7 @@ int mk_pack_weights(mk_model* m, const void* const* d_tensors, int32_t n_tensors
                              row_step, s);
     return launch_pack_fp4(src, N, K, codes, W + mt.scales + layer_off,
                            reinterpret_cast<float*>(W + mt.tscale + layer_off), ts_index, amax, row_off, row_step,
-                           s);
+                           m->fp4_search, s);
   };
   auto copy_vec = [&](const uint16_t* src, uint64_t off, size_t n) -> hipError_t {
     return hipMemcpyAsync(W + off, src, n * 2, hipMemcpyDeviceToDevice, s);
@@ -797,6 +798,11 @@ int mk_set_option(mk_model* m, int32_t key, int64_t value) {
     case 8:
       if (value < 0 || value > (1 << 20)) return fail(m, MK_E_INVALID, "split start position out of range");
       m->split_from = (int)value;
+      break;
+    case 9:
+      if (value < 0 || value > 0x7E) return fail(m, MK_E_INVALID, "FP4 scale search radius out of range");
+      if (m->packed) return fail(m, MK_E_STATE, "set the FP4 scale search before mk_pack_weights");
+      m->fp4_search = (int)value;
       break;
     default:
       return fail(m, MK_E_INVALID, "unknown option %d", key);

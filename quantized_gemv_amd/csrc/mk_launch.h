@@ -22,7 +22,7 @@ hipError_t launch_pack_bf16(const uint16_t* src, int N, int K, uint16_t* dst, in
 hipError_t launch_pack_fp8(const uint16_t* src, int N, int K, uint8_t* codes, float* scales, int row_off,
                            int row_step, hipStream_t s);
 hipError_t launch_pack_fp4(const uint16_t* src, int N, int K, uint8_t* codes, uint8_t* bscales, float* tscale,
-                           int ts_index, uint32_t* amax, int row_off, int row_step, hipStream_t s);
+                           int ts_index, uint32_t* amax, int row_off, int row_step, int search, hipStream_t s);
 hipError_t launch_rope(float* out, int max_ctx, int hd, double theta, hipStream_t s);
 hipError_t launch_decode_codes(int codec, const uint8_t* in, int n, float* out, hipStream_t s);
 }  // namespace mk

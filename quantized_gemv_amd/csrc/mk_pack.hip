@@ -61,10 +61,34 @@ __global__ void amax_kernel(const uint16_t* src, size_t n, uint32_t* out) {
   if (threadIdx.x == 0) atomicMax(out, __float_as_uint(a));
 }
 
-// NVFP4: ts = A/2688 (1 if A = 0); per 16-block bs = e4m3(a_b/fl32(6 ts)),
+// One E2M1 code's value (sign bit 3; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6).
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  const float m = (c & 4u) ? (float)(2u + (c & 1u)) * (float)(1u << ((c >> 1) & 1u)) : 0.5f * (float)(c & 3u);
+  return (c & 8u) ? -m : m;
+}
+
+// Squared error of one 16-wide block stored with effective scale eff:
+// sum_i (w_i - fl32(e2m1(c_i) * eff))^2 with c_i = e2m1(fl32(w_i / eff)),
+// every code 0 when eff = 0.  Differences, squares and the running sum are
+// float64 operations in index order, each rounded on its own.
+__device__ double fp4_block_sq_error(const float* w, float eff) {
+  double e = 0.0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const float q = eff != 0.f ? __fmul_rn(e2m1_value(f32_to_e2m1(w[k] / eff)), eff) : 0.f;
+    const double d = __dsub_rn((double)w[k], (double)q);
+    e = __dadd_rn(e, __dmul_rn(d, d));
+  }
+  return e;
+}
+
+// NVFP4: ts = A/2688 (1 if A = 0); per 16-block the absolute-maximum scale
+// code b0 = e4m3(a_b/fl32(6 ts)); with search > 0 the block scale is the code
+// in [b0 - search, b0 + search] (within 0..0x7E) of least block squared error,
+// the smaller code on a tie (the MSE scale search of the page's NVFP4 format);
 // eff = e4m3(bs) * ts, c = e2m1(w/eff) (all 0 when eff = 0).  One thread per block.
 __global__ void pack_fp4_kernel(const uint16_t* src, int N, int K, uint8_t* codes, uint8_t* bscales, float* tscale,
-                                int ts_index, const uint32_t* amax, int row_off, int row_step) {
+                                int ts_index, const uint32_t* amax, int row_off, int row_step, int search) {
   const int r = blockIdx.x;
   if (r >= N) return;
   const float A = __uint_as_float(*amax);
@@ -81,8 +105,19 @@ __global__ void pack_fp4_kernel(const uint16_t* src, int N, int K, uint8_t* code
       w[k] = bf16_to_f32(s[k]);
       ab = fmaxf(ab, fabsf(w[k]));
     }
-    const uint32_t bs = f32_to_e4m3(ab / six_ts);
-    const float eff = e4m3_to_f32(bs) * ts;
+    uint32_t bs = f32_to_e4m3(ab / six_ts);
+    if (search > 0) {
+      const int lo = max((int)bs - search, 0), hi = min((int)bs + search, 0x7E);
+      double best = 0.0;
+      for (int c = lo; c <= hi; ++c) {   // ascending: a tie keeps the smaller code
+        const double e = fp4_block_sq_error(w, __fmul_rn(e4m3_to_f32((uint32_t)c), ts));
+        if (c == lo || e < best) {
+          best = e;
+          bs = (uint32_t)c;
+        }
+      }
+    }
+    const float eff = __fmul_rn(e4m3_to_f32(bs), ts);
     uint32_t lo = 0, hi = 0;
     if (eff != 0.f) {
 #pragma unroll
@@ -151,13 +186,13 @@ hipError_t launch_pack_fp8(const uint16_t* src, int N, int K, uint8_t* codes, fl
 }
 
 hipError_t launch_pack_fp4(const uint16_t* src, int N, int K, uint8_t* codes, uint8_t* bscales, float* tscale,
-                           int ts_index, uint32_t* amax, int row_off, int row_step, hipStream_t s) {
+                           int ts_index, uint32_t* amax, int row_off, int row_step, int search, hipStream_t s) {
   hipError_t e = hipMemsetAsync(amax, 0, 4, s);
   if (e != hipSuccess) return e;
   const size_t n = (size_t)N * K;
   hipLaunchKernelGGL(amax_kernel, dim3(1024), dim3(256), 0, s, src, n, amax);
   hipLaunchKernelGGL(pack_fp4_kernel, dim3(N), dim3(64), 0, s, src, N, K, codes, bscales, tscale, ts_index, amax,
-                     row_off, row_step);
+                     row_off, row_step, search);
   return hipGetLastError();
 }
 

@@ -33,8 +33,8 @@ class Weights:
     on demand (FP8 scales are per row, so sampled rows are quantized alone;
     an FP4 tensor is quantized whole for its tensor scale)."""
 
-    def __init__(self, master, wfmt):
-        self.m, self.wfmt, self.full = master, wfmt, {}
+    def __init__(self, master, wfmt, fp4_search=0):
+        self.m, self.wfmt, self.full, self.search = master, wfmt, {}, fp4_search
 
     def rows(self, l, name, rows):
         bits = self.m.embed if name == "embed" else self.m.layers[l][name]
@@ -42,7 +42,7 @@ class Weights:
         if fmt == "fp4":
             key = (l, name)
             if key not in self.full:
-                self.full[key] = quantize_tensor(bits, fmt)[1]
+                self.full[key] = quantize_tensor(bits, fmt, self.search)[1]
             return self.full[key][rows]
         return quantize_tensor(bits[rows], fmt)[1]
 

@@ -11,7 +11,8 @@ It is written from the monolith project page (projects.dotslasha.me/p/monolith):
   * "Design decisions", FP8 format: E4M3 weights, one fp32 scale per output
     row, symmetric, round to nearest; activations bf16, fp32 accumulation.
   * "Design decisions", NVFP4 format: E2M1 values, one E4M3 scale per 16
-    weights, one fp32 scale per tensor, round to nearest.
+    weights, one fp32 scale per tensor, round to nearest, and a per-block
+    scale search that minimizes the squared error.
 and the e2m1 value grid printed on the TSCT super-kernel note
 (sehaxe.github.io/dormouse, section 3b, execution path 2).
 
@@ -23,4 +24,5 @@ Modules:
   codecs  bf16, e4m3 (OCP E4M3FN) and e2m1 encode / decode
   quant   FP8 per-row and NVFP4 per-16-block quantizers (canonical packed form)
   model   one decode step, prefill, greedy generation
+  quality quantization error and logit divergence on synthetic weights
 """

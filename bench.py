@@ -232,7 +232,7 @@ def main():
                    "positions": [wl.prompt_len, wl.prompt_len + K - 1],
                    "weight_format": synth.WFMT_NAMES[wl.wfmt], "accumulate": "f32", "batch": 1,
                    "grid": "one workgroup per CU: 1 courier + 7 compute waves; attention on one "
-                           "workgroup per KV head, split over the workgroups of its XCD from 448 "
+                           "workgroup per KV head, split over the workgroups of its XCD from 576 "
                            "cached positions on", "timed_runs": len(times),
                    "run_seconds": [round(t, 6) for t in times]},
         "weight_bytes_per_token": wbytes,

@@ -75,7 +75,13 @@ typedef struct mk_config {
  * measurement. */
 typedef struct mk_sizes {
   size_t weights;     /* packed weight arena */
-  size_t kv;          /* KV cache: n_layers * 2 * n_kv_heads * max_ctx * head_dim * 2 (bf16) */
+  size_t kv;          /* KV cache: n_layers * 2 * n_kv_heads * ctx4 * head_dim * 2 (bf16),
+                         ctx4 = max_ctx rounded up to a multiple of 4.  Per layer l, K then V
+                         (kv = 0, 1), per KV head g, a plane of ctx4 * head_dim values at element
+                         ((l*2 + kv) * n_kv_heads + g) * ctx4 * head_dim.  A K plane is row-major
+                         (position j, dim e at j*head_dim + e).  A V plane is tiled by 4 positions
+                         (j, e at (j/4*head_dim + e)*4 + j%4), the layout the matrix-core value
+                         product reads. */
   size_t rope;        /* RoPE table: max_ctx * head_dim/2 * 2 * 4 (fp32 cos, sin) */
   size_t scratch;     /* exchange buffers, argmax slots, error word */
   size_t trace;       /* X-ray records for one step (0 in builds without X-ray) */
@@ -118,8 +124,8 @@ int mk_query_sizes(const mk_model* m, mk_sizes* out);
  * pointers) of at least the sizes mk_query_sizes reports; `d_trace` may be
  * NULL.  Queries the current device's compute-unit count and sets the
  * launch grid to one workgroup per compute unit.  The pointers are not
- * owned and must stay valid until mk_destroy.  The scratch buffer is
- * cleared on `s`.  Errors: MK_E_INVALID (null or not 256-byte aligned),
+ * owned and must stay valid until mk_destroy.  The scratch buffer and the
+ * KV cache are cleared on `s`.  Errors: MK_E_INVALID (null or not 256-byte aligned),
  * MK_E_HIP (no device). */
 int mk_bind(mk_model* m, void* d_weights, void* d_kv, void* d_rope, void* d_scratch,
             void* d_trace, mk_stream_t s);
@@ -216,13 +222,13 @@ int mk_decode_codes(int32_t codec, const uint8_t* d_codes, int32_t n, float* d_o
  * cooperative.  The kernel's waits assume that every workgroup runs: should
  * another process hold compute units during a plain launch, they end at the
  * spin bound with MK_E_TIMEOUT instead of hanging.  Keys 7 and 8, split
- * attention [64, 448]: with key 7 = c > 0, a step at a position pos at or
+ * attention [192, 576]: with key 7 = c > 0, a step at a position pos at or
  * past key 8 spreads KV head g's cached positions over its home workgroup and
  * ns = min(helpers, pos / c) helper workgroups on the same XCD (helpers = the
  * GEMV workgroups there, at most 32 per head), each taking an equal slice;
  * the home merges their partial (maximum, sum, output) triples with the
  * log-sum-exp rule.  c = 0 turns it off.  (On MI355X at the 0.6B shape the
- * split path is faster from about 450 cached positions on.)  Key 9, NVFP4
+ * split path is faster from about 560 cached positions on.)  Key 9, NVFP4
  * block scale search radius 0..126 [0], set before mk_pack_weights (see
  * there); 0 keeps the absolute-maximum recipe.
  * Keys 1 and 2 are reserved.

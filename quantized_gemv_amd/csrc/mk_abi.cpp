@@ -59,8 +59,8 @@ struct mk_model {
   uint32_t tag_skew = 0;
   uint32_t poll_sleep = 0;
   int launch_mode = -1;         // 0 cooperative, 1 plain launch of a grid that fits at once, -1 choose
-  int split_chunk = 64;         // split attention: cached positions per participant (0: off)
-  int split_from = 448;         // split attention from this position on
+  int split_chunk = 192;        // split attention: cached positions per participant (0: off)
+  int split_from = 576;         // split attention from this position on
   int split_n = 0;              // helpers per KV head in the work table
   int coresident = 0;           // decode workgroups the device holds at once (set by mk_bind)
   int fp4_search = 0;           // NVFP4 block scale search radius (0: absolute-maximum recipe)
@@ -69,6 +69,12 @@ struct mk_model {
 };
 
 namespace {
+
+// KV cache bytes: per layer, K then V, per KV head a plane of max_ctx
+// (rounded up to 4) positions by head_dim bf16 values.
+size_t kv_bytes(const mk_config& c) {
+  return (size_t)c.n_layers * 2 * c.n_kv_heads * (size_t)((c.max_ctx + 3) & ~3) * c.head_dim * 2;
+}
 
 int fail(mk_model* m, int code, const char* fmt, ...) {
   if (m) {
@@ -505,7 +511,7 @@ int mk_query_sizes(const mk_model* m, mk_sizes* out) {
   if (!m || !out) return MK_E_INVALID;
   const mk_config& c = m->cfg;
   out->weights = m->weights_bytes;
-  out->kv = (size_t)c.n_layers * 2 * c.n_kv_heads * (size_t)c.max_ctx * c.head_dim * 2;
+  out->kv = kv_bytes(c);
   out->rope = (size_t)c.max_ctx * (c.head_dim / 2) * 2 * 4;
   out->scratch = m->scratch_reported;
   out->trace = mk_has_xray() ? sizeof(mk_trace_rec) * (size_t)sizing_grid(m) * n_phases(c) : 0;
@@ -557,6 +563,9 @@ int mk_bind(mk_model* m, void* d_weights, void* d_kv, void* d_rope, void* d_scra
   const char* why = build_sched(m->cfg, grid, m->sched, &m->split_n, &m->qkv_word);
   if (why) return fail(m, MK_E_UNSUPPORTED, "grid %d: %s", grid, why);
   HIPCK(m, hipMemsetAsync(d_scratch, 0, m->scratch_bytes, s));
+  // the attention reads whole 4-position V tiles (weight 0 past the last
+  // cached position): never-written slots must hold finite values
+  HIPCK(m, hipMemsetAsync(d_kv, 0, kv_bytes(m->cfg), s));
   HIPCK(m, hipMemcpyAsync(m->d_scratch + 8 * m->P.x.sched, m->sched.data(), m->sched.size() * sizeof(int32_t),
                           hipMemcpyHostToDevice, s));
   return sync_params(m, s);

@@ -40,6 +40,10 @@
 
 namespace mk {
 
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s4 __attribute__((ext_vector_type(4)));
+
 // This wave's index, as a value the compiler knows is uniform across the wave.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
@@ -100,7 +104,8 @@ struct Smem {
   alignas(16) float kf[HD];              // roped k before rounding
   alignas(16) uint32_t kp[HD / 2];       // this position's k, bf16 pairs
   alignas(16) uint32_t vp[HD / 2];       // this position's v, bf16 pairs
-  alignas(16) float part[kCW][4][GS * HD];  // per wave and 16-lane row: unnormalised outputs
+  alignas(16) uint16_t qa[4 * GS][HD];   // q heads as bf16 parts (per head: hi, mid, lo, 0): the score operand
+  alignas(16) float part[kCW][GS * HD];  // per wave: unnormalised outputs
   alignas(16) float wm[kCW][GS];         // per wave: running max (log2 units)
   alignas(16) float wl[kCW][GS];         // per wave: running sum
   alignas(16) float sp[GS];              // this position's scores (log2 units)
@@ -321,13 +326,6 @@ struct Kern {
   static constexpr int KH = NI * 4;            // SwiGLU output (bf16 pairs)
   static constexpr int KA = ((GS + 2) * HD / 2 + 63) / 64;   // q/k/v of one KV head
   static constexpr int KG = 16;                // argmax words of up to 1024 workgroups
-  static constexpr int DPL = HD / 8;           // attention: dims per lane (8 lanes per position)
-  static constexpr int WPL = DPL / 2;          // bf16 pairs per lane
-  static constexpr int PPW = 8;                // positions per wave per pass
-  static constexpr int PPP = PPW * kCW;        // positions per pass
-  // passes the home holds in registers (the split variant keeps fewer: its
-  // home also gathers and merges the helpers' partials)
-  static constexpr int MP = LONG ? 5 : 7;
   static constexpr int NOUT = GS * HD;         // outputs of one attention workgroup
   static constexpr int PP = (NOUT + 2 * GS) / 2;   // word pairs of one helper partial
   static constexpr int KP = kSplitGatherK;     // helper-partial pairs per lane and round of the home's gather
@@ -337,7 +335,7 @@ struct Kern {
   // ------------------------------------------------------------ courier
   // The inputs this workgroup needs, in order, for every layer; then the
   // final residual for the LM head; workgroup 0 then reduces the argmax.
-  static __device__ bool courier(const Params& p, S& s, const int* hdr, int token, int pos, int ns,
+  static __device__ __forceinline__ bool courier(const Params& p, S& s, const int* hdr, int token, int pos, int ns,
                                  uint32_t epoch, int32_t* d_next) {
     MK_GLOBAL const uint8_t* const W = p.w;
     const int lane = lane_id();
@@ -594,8 +592,17 @@ struct Kern {
       if (cw < GS) {
         const float kq = 1.4426950408889634f / sqrtf((float)HD);
         if (pl) {
-          s.q[cw * HD + li] = ra * kq;
-          s.q[cw * HD + li + HD / 2] = rb * kq;
+          const float qa = ra * kq, qb = rb * kq;
+          s.q[cw * HD + li] = qa;
+          s.q[cw * HD + li + HD / 2] = qb;
+          uint32_t pa[3], pb[3];
+          split3(qa, pa);
+          split3(qb, pb);
+#pragma unroll
+          for (int k = 0; k < 3; ++k) {
+            s.qa[4 * cw + k][li] = (uint16_t)pa[k];
+            s.qa[4 * cw + k][li + HD / 2] = (uint16_t)pb[k];
+          }
         }
       } else {
         if (pl) {
@@ -606,8 +613,7 @@ struct Kern {
         if (pl) {
           const uint32_t kw = pack_bf16(s.kf[2 * lane], s.kf[2 * lane + 1]);
           s.kp[lane] = kw;
-          const size_t plane = (size_t)p.max_ctx * HD;
-          MK_GLOBAL uint32_t* kc = GCAST(uint32_t, p.kv + ((size_t)(l * 2 + 0) * p.nkv + g) * plane);
+          MK_GLOBAL uint32_t* kc = GCAST(uint32_t, p.kv + ((size_t)(l * 2 + 0) * p.nkv + g) * kv_plane(p));
           if (ok) kc[(size_t)pos * (HD / 2) + lane] = kw;   // an aborted step leaves the cache alone
         }
       }
@@ -616,9 +622,13 @@ struct Kern {
         const float* vf = s.qraw + (GS + 1) * HD;
         const uint32_t vw = pack_bf16(vf[2 * lane], vf[2 * lane + 1]);
         s.vp[lane] = vw;
-        const size_t plane = (size_t)p.max_ctx * HD;
-        MK_GLOBAL uint32_t* vc = GCAST(uint32_t, p.kv + ((size_t)(l * 2 + 1) * p.nkv + g) * plane);
-        if (ok) vc[(size_t)pos * (HD / 2) + lane] = vw;
+        // the V plane is tiled by 4 positions: (j, e) at (j/4 * HD + e) * 4 + j%4
+        MK_GLOBAL uint16_t* vc = GCAST(uint16_t, p.kv + ((size_t)(l * 2 + 1) * p.nkv + g) * kv_plane(p));
+        const size_t e0 = ((size_t)(pos >> 2) * HD + 2 * lane) * 4 + (pos & 3);
+        if (ok) {
+          vc[e0] = (uint16_t)vw;
+          vc[e0 + 4] = (uint16_t)(vw >> 16);
+        }
       }
     }
   }
@@ -839,137 +849,219 @@ struct Kern {
   }
 
   // ---------------------------------------------- attention compute waves
-  // Wave cw takes positions 8 cw .. 8 cw + 7 of every 56-position pass, one
-  // position per 8 lanes (lane c of the 8 holds dims [c*HD/8, +HD/8)), so a
-  // wave reads eight consecutive cache rows as one coalesced run.  The home
-  // workgroup holds its first MP passes in registers, loaded a layer ahead;
-  // positions beyond, and the helpers' slices, stream through two buffers.
+  // Scores and the weighted sum of values run on the matrix cores with
+  // fp32 accumulation.  A wave takes blocks of BP = 16 consecutive cached
+  // positions; block t of wave cw starts at position (t*kCW + cw)*BP of its
+  // range.  q and the softmax weights p are fp32: each enters the bf16
+  // products as three parts (hi, mid, lo), x = hi + mid + lo exactly
+  // (split3), one operand row each, and the three rows' results are added,
+  // so every product is exact and only the order of the fp32 sums differs
+  // from a plain fp32 dot product (the cached k and v are bf16).
+  //
+  // Scores (v_mfma_f32_16x16x32_bf16, HD/32 steps): D[16 x 16] = K[16 pos x
+  // HD] * Qop[HD x 16].  Qop's column 4h + k holds part k of q head h (k = 3:
+  // zeros).  Lane l holds D rows 4(l/16)..+3 (positions) of column l%16, so
+  // the four lanes of a quad l%16 = 4h..4h+3 hold head h's parts of the same
+  // four positions; two DPP steps add them, leaving the score in each.  Those
+  // lanes then hold exactly the A operand of the value product
+  // (v_mfma_f32_16x16x16_bf16, HD/16 steps): row 4h + k = part k of head
+  // h's weights, positions 4(l/16)..+3.  So the weights never leave the
+  // registers: O[16 x HD] += P[16 x 16 pos] * V[16 pos x HD], O's rows 4h..4h+2
+  // being head h's parts.  The value operand wants four consecutive
+  // positions of one dimension per lane, so the V cache is stored in tiles
+  // of 4 positions: element (j, e) of a KV head's plane sits at
+  // (j/4 * HD + e) * 4 + j%4.
+  static constexpr int BP = 16;                // positions per block
+  static constexpr int NKC = HD / 32;          // score steps (32 dims each)
+  static constexpr int NVC = HD / 16;          // value steps (16 dims each)
+  static constexpr int PPB = BP * kCW;         // positions per pass (one block per wave)
+  // blocks the home holds in registers, loaded a layer ahead (the split
+  // variant's home also gathers and merges the helpers' partials)
+  static constexpr int MB = LONG ? 2 : 4;
+  static_assert(MB >= 2, "the home streams through two of its register blocks");
+  static_assert(GS == 2 && HD % 32 == 0, "matrix-core attention: two q heads per KV head");
+
+  // x = hi + mid + lo, each a bf16 (bits in the low half), exactly: each
+  // part rounds what the previous ones left, and 3 x 8 significant bits
+  // cover an fp32 value.
+  static __device__ __forceinline__ void split3(float x, uint32_t (&part)[3]) {
+    part[0] = f32_to_bf16(x);
+    const float r1 = x - bf16_to_f32((uint16_t)part[0]);
+    part[1] = f32_to_bf16(r1);
+    part[2] = f32_to_bf16(r1 - bf16_to_f32((uint16_t)part[1]));
+  }
+
+  struct KVBlock {
+    v4u k[NKC];   // A operand of the scores: row j0 + l%16, dims 32c + 8(l/16) .. +7
+    v2u v[NVC];   // B operand of the value product: positions j0 + 4(l/16) .. +3 of dim 16c + l%16
+  };
   struct KVRegs {
-    v4u k[MP][WPL / 4];
-    v4u v[MP][WPL / 4];
+    KVBlock b[MB];
   };
 
-  // K and V rows of the pass starting at position j0 (this wave's eight
-  // positions); rows past `last` read row `last` instead (weight 0 at use).
-  static __device__ __forceinline__ void kv_load_at(const Params& p, int l, int g, int j0, int last, int cw,
-                                                    v4u (&kk)[WPL / 4], v4u (&vv)[WPL / 4]) {
-    const int lane = lane_id();
-    const int j = j0 + cw * PPW + (lane >> 3);
-    const int jc = max(min(j, last), 0);
-    const size_t plane = (size_t)p.max_ctx * HD;
-    MK_GLOBAL const v4u* kp = GCAST(const v4u, p.kv + ((size_t)(l * 2 + 0) * p.nkv + g) * plane +
-                                                   (size_t)jc * HD + (lane & 7) * DPL);
-    MK_GLOBAL const v4u* vp = GCAST(const v4u, p.kv + ((size_t)(l * 2 + 1) * p.nkv + g) * plane +
-                                                   (size_t)jc * HD + (lane & 7) * DPL);
+  static __device__ __forceinline__ size_t kv_plane(const Params& p) { return (size_t)((p.max_ctx + 3) & ~3) * HD; }
+
+  // The block at positions j0 .. j0+15 (j0 a multiple of 4).  Rows past
+  // `last` read row `last`, and tiles past its tile that tile: finite
+  // values, weight 0 at use.
+  static __device__ __forceinline__ void kv_block_load(const Params& p, int l, int g, int j0, int last, KVBlock& kb) {
+    const int lane = lane_id(), r = lane & 15, q = lane >> 4;
+    const size_t plane = kv_plane(p);
+    // one buffer resource per plane (base in scalar registers, 32-bit lane offsets)
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.kv + ((size_t)(l * 2 + 0) * p.nkv + g) * plane, (uint32_t)(2 * plane));
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.kv + ((size_t)(l * 2 + 1) * p.nkv + g) * plane, (uint32_t)(2 * plane));
+    const int lc = max(last, 0);
+    const uint32_t ok = 2u * (uint32_t)(min(j0 + r, lc) * HD + 8 * q);
 #pragma unroll
-    for (int i = 0; i < WPL / 4; ++i) {
-      kk[i] = kp[i];
-      vv[i] = vp[i];
-    }
+    for (int c = 0; c < NKC; ++c)
+      kb.k[c] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rk, ok + 64u * c, 0, 0));
+    const uint32_t ov = 8u * (uint32_t)(min((j0 >> 2) + q, lc >> 2) * HD + r);
+#pragma unroll
+    for (int c = 0; c < NVC; ++c)
+      kb.v[c] = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(rv, ov + 128u * c, 0, 0));
   }
-  // the home's register passes cover positions 0 .. MP*PPP-1 of its slice
+  // the home's register blocks cover positions 0 .. MB*PPB-1 of its slice
   static __device__ __forceinline__ void kv_prefetch(const Params& p, int l, int g, int pos, int cw, KVRegs& kv) {
 #pragma unroll
-    for (int t = 0; t < MP; ++t) kv_load_at(p, l, g, t * PPP, pos - 1, cw, kv.k[t], kv.v[t]);
+    for (int t = 0; t < MB; ++t) kv_block_load(p, l, g, (t * kCW + cw) * BP, pos - 1, kv.b[t]);
   }
 
-  // Scores of one pass (both q heads) for the lanes' position j; -inf past pos.
-  static __device__ __forceinline__ void att_scores(const S& s, const v4u (&kk)[WPL / 4], bool act, float (&sc)[GS]) {
-    const int c = lane_id() & 7;
-    asm volatile("" ::: "memory");   // re-read q from LDS for every pass (keeps it out of registers)
+  // The q operand (B of the scores) of this lane, from the part rows in LDS.
+  static __device__ __forceinline__ void att_qop(const S& s, v4u (&qop)[NKC]) {
+    const int lane = lane_id(), r = lane & 15, q = lane >> 4;
+    const bool live = r < 4 * GS && (r & 3) != 3;
 #pragma unroll
-    for (int h = 0; h < GS; ++h) {
-      const float4* qp = reinterpret_cast<const float4*>(s.q + h * HD + c * DPL);
-      float d = 0.f;
+    for (int c = 0; c < NKC; ++c)
+      qop[c] = live ? *reinterpret_cast<const v4u*>(&s.qa[r][32 * c + 8 * q]) : v4u{0u, 0u, 0u, 0u};
+  }
+
+  // Scores of block j0 in log2 units: sc[i] for position j0 + 4(l/16) + i
+  // of this lane's head ((l%16) / 4), -inf outside [a, b) and in lanes past
+  // the two heads' quads.
+  static __device__ __forceinline__ void att_block_scores(const S& s, const KVBlock& kb, int j0, int a, int b,
+                                                          float (&sc)[4]) {
+    const int lane = lane_id(), r = lane & 15, q = lane >> 4;
+    v4u qop[NKC];
+    att_qop(s, qop);   // from LDS for every block: no registers held across blocks
+    f4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < WPL / 4; ++i) {
-        const float4 q0 = qp[2 * i], q1 = qp[2 * i + 1];
-        const v4u kw = kk[i];
-        d = fmaf(q0.x, bf16_lo(kw.x), d);
-        d = fmaf(q0.y, bf16_hi(kw.x), d);
-        d = fmaf(q0.z, bf16_lo(kw.y), d);
-        d = fmaf(q0.w, bf16_hi(kw.y), d);
-        d = fmaf(q1.x, bf16_lo(kw.z), d);
-        d = fmaf(q1.y, bf16_hi(kw.z), d);
-        d = fmaf(q1.z, bf16_lo(kw.w), d);
-        d = fmaf(q1.w, bf16_hi(kw.w), d);
-      }
-      d = sum8(d);
-      sc[h] = act ? d : -INFINITY;
+    for (int c = 0; c < NKC; ++c)
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb.k[c]), __builtin_bit_cast(bf16x8, qop[c]),
+                                                  d, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = d[i] + dpp<0xB1>(d[i]);   // (hi + mid), (lo + 0)
+      v = v + dpp<0x4E>(v);               // the quad's sum, in every lane of it
+      const int j = j0 + 4 * q + i;
+      sc[i] = r < 4 * GS && j >= a && j < b ? v : -INFINITY;
     }
   }
-  // acc += p * v for one pass.  Lanes past the slice carry p = 0 and a row
-  // the cache holds (finite), so they add nothing.
-  static __device__ __forceinline__ void att_accum(const v4u (&vv)[WPL / 4], const float (&pr)[GS],
-                                                   float (&acc)[GS][DPL]) {
-#pragma unroll
-    for (int i = 0; i < WPL / 4; ++i) {
-      const uint32_t w4[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int h = 0; h < GS; ++h) {
-          acc[h][8 * i + 2 * q] = fmaf(pr[h], bf16_lo(w4[q]), acc[h][8 * i + 2 * q]);
-          acc[h][8 * i + 2 * q + 1] = fmaf(pr[h], bf16_hi(w4[q]), acc[h][8 * i + 2 * q + 1]);
-        }
-    }
+  // The entry of a per-head pair (wave-uniform values) for head `odd`.
+  // Read out through readfirstlane: a plain select between two array
+  // elements is turned into an indexed load from private memory.
+  static __device__ __forceinline__ float head_pick(const float (&v)[GS], bool odd) {
+    const float v0 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v[0])));
+    const float v1 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v[1])));
+    return odd ? v1 : v0;
   }
-  // Online softmax step: fold a new maximum candidate into (m, lsum, acc).
-  static __device__ __forceinline__ void att_rescale(float bm, float& m, float& lsum, float (&acc)[DPL]) {
-    const float mn = fmaxf(m, wave_max(bm));
-    const float scale = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
-    m = mn;
-    lsum *= scale;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[e] *= scale;
+  // Maximum of a lane value over head h's lanes (l%16 = 4h), uniform.
+  static __device__ __forceinline__ float head_max(float v, int h) {
+    return fmaxf(fmaxf(lane_f(v, 4 * h), lane_f(v, 16 + 4 * h)), fmaxf(lane_f(v, 32 + 4 * h), lane_f(v, 48 + 4 * h)));
   }
-  // One streamed pass (scores, rescale, accumulate) at position base j0.
-  static __device__ __forceinline__ void att_pass(const S& s, const v4u (&kk)[WPL / 4], const v4u (&vv)[WPL / 4],
-                                                  int j0, int b, int cw, float (&m)[GS], float (&lsum)[GS],
-                                                  float (&acc)[GS][DPL]) {
-    const int j = j0 + cw * PPW + (lane_id() >> 3);
-    float sc[GS], pr[GS];
-    att_scores(s, kk, j < b, sc);
-#pragma unroll
-    for (int h = 0; h < GS; ++h) {
-      att_rescale(sc[h], m[h], lsum[h], acc[h]);
-      pr[h] = sc[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[h] - m[h]);
-      lsum[h] += pr[h];
-    }
-    att_accum(vv, pr, acc);
+  static __device__ __forceinline__ float block_max(const float (&sc)[4]) {
+    return fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
   }
-  // Positions [a, b) of the cache in passes of PPP, two passes in flight.
-  static __device__ __forceinline__ void att_stream(const Params& p, const S& s, int l, int g, int a, int b, int cw,
-                                                    float (&m)[GS], float (&lsum)[GS], float (&acc)[GS][DPL]) {
-    if (b <= a) return;
-    v4u k0[WPL / 4], v0[WPL / 4], k1[WPL / 4], v1[WPL / 4];
-    kv_load_at(p, l, g, a, b - 1, cw, k0, v0);
-    for (int j0 = a; j0 < b; j0 += 2 * PPP) {
-      kv_load_at(p, l, g, j0 + PPP, b - 1, cw, k1, v1);
-      att_pass(s, k0, v0, j0, b, cw, m, lsum, acc);
-      kv_load_at(p, l, g, j0 + 2 * PPP, b - 1, cw, k0, v0);
-      att_pass(s, k1, v1, j0 + PPP, b, cw, m, lsum, acc);
-    }
-  }
-  // This wave's outputs to LDS: the two 8-lane halves of each 16-lane row
-  // with one DPP step, then the four rows; the wave's max and sum.
-  static __device__ __forceinline__ void att_wave_part(S& s, int cw, const float (&m)[GS], const float (&lsum)[GS],
-                                                       float (&acc)[GS][DPL]) {
+  // Online-softmax step for both heads: fold the candidates bm (uniform)
+  // into (m, lsum, acc).  lsum lives in the score lanes (head (l%16)/4), acc
+  // rows in the lanes of head l/16.
+  static __device__ __forceinline__ void att_rescale(const float (&bm)[GS], float (&m)[GS], float& lsum,
+                                                     f4 (&acc)[NVC]) {
     const int lane = lane_id();
-    const int c = lane & 7;
+    float sc[GS];
 #pragma unroll
-    for (int h = 0; h < GS; ++h)
+    for (int h = 0; h < GS; ++h) {
+      const float mn = fmaxf(m[h], bm[h]);
+      sc[h] = m[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[h] - mn);
+      m[h] = mn;
+    }
+    lsum *= head_pick(sc, (lane & 4) != 0);
+    const float sa = head_pick(sc, (lane & 16) != 0);
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[h][e] += dpp<0x128>(acc[h][e]);
-    if ((lane & 8) == 0) {
+    for (int c = 0; c < NVC; ++c)
 #pragma unroll
-      for (int h = 0; h < GS; ++h)
+      for (int i = 0; i < 4; ++i) acc[c][i] *= sa;
+  }
+  // Weights of one block under the maxima m, and the value product.  The
+  // lanes of the hi parts add their weights to lsum (each weight once).
+  // The parts come from the hardware bf16 pair conversion (round to nearest
+  // even), two positions at a time.
+  static __device__ __forceinline__ void att_block_accum(const KVBlock& kb, const float (&sc)[4], const float (&m)[GS],
+                                                         float& lsum, f4 (&acc)[NVC]) {
+    const int k = lane_id() & 3;
+    const float mh = head_pick(m, (lane_id() & 4) != 0);
+    float pv[4];
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) s.part[cw][lane >> 4][h * HD + c * DPL + e] = acc[h][e];
+    for (int i = 0; i < 4; ++i) {
+      pv[i] = sc[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[i] - mh);
+      lsum += k == 0 ? pv[i] : 0.f;
+    }
+    v2u part[3];   // (positions 0,1), (2,3) of each part
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      part[t] = v2u{pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3])};
+      pv[0] -= bf16_lo(part[t].x);
+      pv[1] -= bf16_hi(part[t].x);
+      pv[2] -= bf16_lo(part[t].y);
+      pv[3] -= bf16_hi(part[t].y);
+    }
+    // lanes past the two heads' quads have pv = 0: every part is 0
+    const v2u pa = k == 0 ? part[0] : (k == 1 ? part[1] : (k == 2 ? part[2] : v2u{0u, 0u}));
+#pragma unroll
+    for (int c = 0; c < NVC; ++c)
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, pa), __builtin_bit_cast(s4, kb.v[c]),
+                                                         acc[c], 0, 0, 0);
+  }
+  // One block, streamed: scores, rescale, accumulate.
+  static __device__ __forceinline__ void att_block(const S& s, const KVBlock& kb, int j0, int a, int b, float (&m)[GS],
+                                                   float& lsum, f4 (&acc)[NVC]) {
+    float sc[4];
+    att_block_scores(s, kb, j0, a, b, sc);
+    const float v = block_max(sc);
+    float bm[GS];
+#pragma unroll
+    for (int h = 0; h < GS; ++h) bm[h] = head_max(v, h);
+    att_rescale(bm, m, lsum, acc);
+    att_block_accum(kb, sc, m, lsum, acc);
+  }
+  // Positions [a, b) of the cache, blocks from a0 (a multiple of 4, at most
+  // a), one pass of kCW blocks at a time, two blocks in flight in k0 and k1
+  // (the home passes two of its register blocks, whose values are used up).
+  static __device__ __forceinline__ void att_stream(const Params& p, const S& s, int l, int g, int a0, int a, int b,
+                                                    int cw, float (&m)[GS], float& lsum, f4 (&acc)[NVC], KVBlock& k0,
+                                                    KVBlock& k1) {
+    if (b <= a) return;
+    kv_block_load(p, l, g, a0 + cw * BP, b - 1, k0);
+    for (int j0 = a0; j0 < b; j0 += 2 * PPB) {
+      kv_block_load(p, l, g, j0 + PPB + cw * BP, b - 1, k1);
+      att_block(s, k0, j0 + cw * BP, a, b, m, lsum, acc);
+      kv_block_load(p, l, g, j0 + 2 * PPB + cw * BP, b - 1, k0);
+      att_block(s, k1, j0 + PPB + cw * BP, a, b, m, lsum, acc);
+    }
+  }
+  // This wave's unnormalised outputs (lanes 16h + i: head h, dims 16c + i),
+  // maxima and sums to LDS.
+  static __device__ __forceinline__ void att_wave_part(S& s, int cw, const float (&m)[GS], float lsum,
+                                                       const f4 (&acc)[NVC]) {
+    const int lane = lane_id();
+    if (lane < 16 * GS) {
+      const int h = lane >> 4, e = lane & 15;
+#pragma unroll
+      for (int c = 0; c < NVC; ++c) s.part[cw][h * HD + 16 * c + e] = (acc[c][0] + acc[c][1]) + acc[c][2];
     }
 #pragma unroll
     for (int h = 0; h < GS; ++h) {
-      const float lt = wave_sum(c == 0 ? lsum[h] : 0.f);
+      const float lt =
+          (lane_f(lsum, 4 * h) + lane_f(lsum, 16 + 4 * h)) + (lane_f(lsum, 32 + 4 * h) + lane_f(lsum, 48 + 4 * h));
       if (lane == 0) {
         s.wm[cw][h] = m[h];
         s.wl[cw][h] = lt;
@@ -994,60 +1086,45 @@ struct Kern {
     att_prepare<true>(p, s, l, g, pos, cw, ok);
     lds_barrier();
     if (cw == 0) att_current_scores(s);   // read in the merge, after the next barrier
-    float acc[GS][DPL], m[GS], lsum[GS];
+    f4 acc[NVC];
+    float m[GS], lsum = 0.f;
 #pragma unroll
-    for (int h = 0; h < GS; ++h) {
-      m[h] = -INFINITY;
-      lsum[h] = 0.f;
+    for (int h = 0; h < GS; ++h) m[h] = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
-    }
+    for (int c = 0; c < NVC; ++c) acc[c] = f4{0.f, 0.f, 0.f, 0.f};
     const int P = LONG && ns > 0 ? (pos + ns) / (ns + 1) : pos;   // the home's slice: slice 0
-    const int npass = (P + PPP - 1) / PPP;
+    const int nblk = (P + PPB - 1) / PPB;   // passes of one block per wave
 #ifdef MK_XRAY
     {  // X-ray: when the prefetched rows are all in registers
       uint32_t z = 0;
 #pragma unroll
-      for (int t = 0; t < MP; ++t) z ^= kv.k[t][0].x ^ kv.v[t][WPL / 4 - 1].w;
+      for (int t = 0; t < MB; ++t) z ^= kv.b[t].k[0].x ^ kv.b[t].v[NVC - 1].y;
       asm volatile("" ::"v"(z));   // wait until they have arrived
       XR_MAX(s, ph + 1, XR_M0 + 1);
     }
 #endif
-    // ---- the passes held in registers (loaded a layer ahead)
-    if (npass > 0) {
-      float sc[MP][GS];
+    // ---- the blocks held in registers (loaded a layer ahead): all scores,
+    // one maximum, then the weights and the value products
+    if (nblk > 0) {
+      float sc[MB][4];
+      float v = -INFINITY;
 #pragma unroll
-      for (int t = 0; t < MP; ++t) {
-#pragma unroll
-        for (int h = 0; h < GS; ++h) sc[t][h] = -INFINITY;
-        if (t < npass) {
-          const int j = t * PPP + cw * PPW + (lane >> 3);
-          att_scores(s, kv.k[t], j < P, sc[t]);
+      for (int t = 0; t < MB; ++t) {
+        if (t < nblk) {
+          att_block_scores(s, kv.b[t], (t * kCW + cw) * BP, 0, P, sc[t]);
+          v = fmaxf(v, block_max(sc[t]));
         }
       }
+      float bm[GS];
 #pragma unroll
-      for (int h = 0; h < GS; ++h) {
-        float bm = sc[0][h];
+      for (int h = 0; h < GS; ++h) bm[h] = head_max(v, h);
+      att_rescale(bm, m, lsum, acc);
 #pragma unroll
-        for (int t = 1; t < MP; ++t) bm = fmaxf(bm, sc[t][h]);
-        att_rescale(bm, m[h], lsum[h], acc[h]);
-      }
-#pragma unroll
-      for (int t = 0; t < MP; ++t) {
-        if (t < npass) {
-          float pr[GS];
-#pragma unroll
-          for (int h = 0; h < GS; ++h) {
-            // sc = -inf past P (and m may still be -inf in a wave with no position yet)
-            pr[h] = sc[t][h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[t][h] - m[h]);
-            lsum[h] += pr[h];
-          }
-          att_accum(kv.v[t], pr, acc);
-        }
-      }
+      for (int t = 0; t < MB; ++t)
+        if (t < nblk) att_block_accum(kv.b[t], sc[t], m, lsum, acc);
     }
-    // ---- longer slices: the remaining passes stream
-    if (npass > MP) att_stream(p, s, l, g, MP * PPP, P, cw, m, lsum, acc);
+    // ---- longer slices: the remaining blocks stream
+    if (nblk > MB) att_stream(p, s, l, g, MB * PPB, MB * PPB, P, cw, m, lsum, acc, kv.b[0], kv.b[1]);
     att_wave_part(s, cw, m, lsum, acc);
     XR_MAX(s, ph + 1, XR_M0);
     lds_barrier();
@@ -1088,7 +1165,7 @@ struct Kern {
     for (int w = 0; w < kCW; ++w) {
       const float e = att_weight(s.wm[w][h], M);
       Lt = fmaf(s.wl[w][h], e, Lt);
-      O = fmaf((s.part[w][0][tc] + s.part[w][1][tc]) + (s.part[w][2][tc] + s.part[w][3][tc]), e, O);
+      O = fmaf(s.part[w][tc], e, O);
     }
     if (LONG)
       for (int i = 0; i < ns; ++i) {
@@ -1130,15 +1207,14 @@ struct Kern {
     lds_barrier();
     const int chunk = (pos + ns) / (ns + 1);
     const int a = min(pos, i * chunk), b = min(pos, a + chunk);
-    float acc[GS][DPL], m[GS], lsum[GS];
+    f4 acc[NVC];
+    float m[GS], lsum = 0.f;
 #pragma unroll
-    for (int h = 0; h < GS; ++h) {
-      m[h] = -INFINITY;
-      lsum[h] = 0.f;
+    for (int h = 0; h < GS; ++h) m[h] = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
-    }
-    att_stream(p, s, l, g, a, b, cw, m, lsum, acc);
+    for (int c = 0; c < NVC; ++c) acc[c] = f4{0.f, 0.f, 0.f, 0.f};
+    KVBlock k0, k1;
+    att_stream(p, s, l, g, a & ~3, a, b, cw, m, lsum, acc, k0, k1);
     att_wave_part(s, cw, m, lsum, acc);
     lds_barrier();
     const int t = cw * 64 + lane;
@@ -1152,7 +1228,7 @@ struct Kern {
     for (int w = 0; w < kCW; ++w) {
       const float e = att_weight(s.wm[w][h], M);
       Lt = fmaf(s.wl[w][h], e, Lt);
-      O = fmaf((s.part[w][0][tc] + s.part[w][1][tc]) + (s.part[w][2][tc] + s.part[w][3][tc]), e, O);
+      O = fmaf(s.part[w][tc], e, O);
     }
     const uint32_t base = 8u * (xword(p, l, V_ATT) + (uint32_t)((g * p.split_max + i - 1) * p.split_pw));
     const uint32_t tag = make_tag(epoch, vec_id(l, V_ATT));
@@ -1226,7 +1302,7 @@ struct Kern {
   }
 
   // -------------------------------------------------------------- kernel
-  static __device__ void run(const Params& p, S& s, const int32_t* d_token, int pos, int ns, uint32_t epoch,
+  static __device__ __forceinline__ void run(const Params& p, S& s, const int32_t* d_token, int pos, int ns, uint32_t epoch,
                              int32_t* d_next, float* d_logits) {
     const int wave = wave_id(), lane = lane_id();
     const int wg = blockIdx.x;

@@ -201,6 +201,20 @@ class Decoder:
                                               out.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), n))
         return out
 
+    def kv_cache_bits(self) -> np.ndarray:
+        """The KV cache as bf16 bit patterns [n_layers, 2, n_kv_heads, max_ctx,
+        head_dim] (K then V), read back from the device layout mk.h states:
+        planes of ctx4 = max_ctx rounded up to 4 positions, K row-major, V in
+        tiles of 4 positions."""
+        sh = self.shape
+        c4 = (self.max_ctx + 3) & ~3
+        n = sh.n_layers * 2 * sh.n_kv_heads * c4 * sh.head_dim
+        raw = self.kv[: 2 * n].cpu().numpy().view(np.uint16).reshape(sh.n_layers, 2, sh.n_kv_heads, c4 * sh.head_dim)
+        k = raw[:, 0].reshape(sh.n_layers, sh.n_kv_heads, c4, sh.head_dim)
+        v = raw[:, 1].reshape(sh.n_layers, sh.n_kv_heads, c4 // 4, sh.head_dim, 4).transpose(0, 1, 2, 4, 3)
+        v = v.reshape(sh.n_layers, sh.n_kv_heads, c4, sh.head_dim)
+        return np.stack([k, v], axis=1)[:, :, :, : self.max_ctx].copy()
+
     def prefill(self, tokens: Sequence[int]) -> int:
         arr = (ctypes.c_int32 * len(tokens))(*[int(t) for t in tokens])
         return self._check(self.lib.mk_prefill(self.h, arr, len(tokens), _stream()))

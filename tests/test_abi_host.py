@@ -15,6 +15,8 @@ import json
 import os
 import re
 
+import numpy as np
+
 import pytest
 
 import synth
@@ -180,3 +182,27 @@ def test_byte_budget_matches_the_page(lib):
     assert round(page_mix / 1e9, 2) == g["bytes_per_token_nvfp4_GB_approx"]
     # KV bytes per cached position: L * 2 * nkv * hd * 2
     assert bf16.kv_bytes_per_position == L * 2 * sh.n_kv_heads * hd * 2 == 114_688
+
+
+def test_kv_cache_read_back_layout():
+    """The binding's KV read-back inverts the device layout mk.h states (K
+    planes row-major, V planes in tiles of 4 positions, planes of max_ctx
+    rounded up to 4), written here element by element from that statement."""
+    import types
+    import torch
+    L, nkv, hd, ctx = 2, 3, 8, 6
+    c4 = 8
+    sh = types.SimpleNamespace(n_layers=L, n_kv_heads=nkv, head_dim=hd)
+    want = np.random.default_rng(0).integers(0, 1 << 16, (L, 2, nkv, ctx, hd)).astype(np.uint16)
+    flat = np.zeros(L * 2 * nkv * c4 * hd, np.uint16)
+    for l in range(L):
+        for kv in range(2):
+            for g in range(nkv):
+                base = ((l * 2 + kv) * nkv + g) * c4 * hd
+                for j in range(ctx):
+                    for e in range(hd):
+                        off = j * hd + e if kv == 0 else (j // 4 * hd + e) * 4 + j % 4
+                        flat[base + off] = want[l, kv, g, j, e]
+    fake = types.SimpleNamespace(shape=sh, max_ctx=ctx, kv=torch.from_numpy(flat.view(np.uint8).copy()))
+    got = native.Decoder.kv_cache_bits(fake)
+    assert got.shape == want.shape and np.array_equal(got, want)

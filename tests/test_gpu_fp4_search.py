@@ -107,8 +107,7 @@ def test_ops_tiny_searched_weights(native, master):
             return d.read_exchange(layer, vec)
 
         def kv_bits(self):
-            raw = d.kv[: sh.n_layers * 2 * sh.n_kv_heads * d.max_ctx * sh.head_dim * 2].cpu().numpy()
-            return raw.view(np.uint16).reshape(sh.n_layers, 2, sh.n_kv_heads, d.max_ctx, sh.head_dim)
+            return d.kv_cache_bits()
 
     check_step(Step(), Weights(master, synth.FP4_MIX, fp4_search=4), sh, int(toks[39]), 39, lg.cpu().numpy(),
                range(sh.n_layers), np.random.default_rng(0))

@@ -40,9 +40,7 @@ class GpuStep:
         return self.dec.read_exchange(layer, vec)
 
     def kv_bits(self):
-        sh, d = self.sh, self.dec
-        raw = d.kv[: sh.n_layers * 2 * sh.n_kv_heads * d.max_ctx * sh.head_dim * 2].cpu().numpy()
-        return raw.view(np.uint16).reshape(sh.n_layers, 2, sh.n_kv_heads, d.max_ctx, sh.head_dim)
+        return self.dec.kv_cache_bits()
 
 
 def _step(dec, sh, token, pos):
@@ -82,19 +80,20 @@ def test_ops_tiny_every_output(native, tiny_master, wfmt):
 
 
 def test_ops_tiny_streamed_attention(native, tiny_master):
-    """Positions 400 and 470 without split attention: one and two cache
-    passes stream after the seven held in registers."""
+    """Positions 470 and 700 without split attention: one and three cache
+    passes stream after the four held in registers (max_ctx 702, not a
+    multiple of the 4-position V tile)."""
     sh = synth.TINY
-    toks = synth.make_prompt(sh.vocab, 471, 12)
-    d = _decoder(native, sh, tiny_master, synth.BF16, 480, split_chunk=0)
+    toks = synth.make_prompt(sh.vocab, 701, 12)
+    d = _decoder(native, sh, tiny_master, synth.BF16, 702, split_chunk=0)
     W = Weights(tiny_master, synth.BF16)
-    d.prefill(toks[:400])
-    logits = _step(d, sh, int(toks[400]), 400)
-    check_step(GpuStep(d, sh), W, sh, int(toks[400]), 400, logits, range(sh.n_layers), np.random.default_rng(0))
-    for pos in range(401, 470):
-        _step(d, sh, int(toks[pos]), pos)
+    d.prefill(toks[:470])
     logits = _step(d, sh, int(toks[470]), 470)
     check_step(GpuStep(d, sh), W, sh, int(toks[470]), 470, logits, range(sh.n_layers), np.random.default_rng(0))
+    for pos in range(471, 700):
+        _step(d, sh, int(toks[pos]), pos)
+    logits = _step(d, sh, int(toks[700]), 700)
+    check_step(GpuStep(d, sh), W, sh, int(toks[700]), 700, logits, range(sh.n_layers), np.random.default_rng(0))
     d.close()
 
 
@@ -172,19 +171,19 @@ def test_ops_qwen3_0p6b_sampled(native, q_master, wfmt):
 
 @pytest.mark.timeout(900)
 def test_ops_qwen3_0p6b_streamed_attention(native, q_master):
-    """Positions 400 and 460 without split attention (one and two streamed
+    """Positions 460 and 600 without split attention (one and two streamed
     cache passes), bf16."""
     sh = synth.QWEN3_0P6B
-    toks = synth.make_prompt(sh.vocab, 461, 13)
-    d = _decoder(native, sh, q_master, synth.BF16, 512, split_chunk=0)
+    toks = synth.make_prompt(sh.vocab, 601, 13)
+    d = _decoder(native, sh, q_master, synth.BF16, 640, split_chunk=0)
     W = Weights(q_master, synth.BF16)
-    d.prefill(toks[:400])
-    logits = _step(d, sh, int(toks[400]), 400)
-    check_step(GpuStep(d, sh), W, sh, int(toks[400]), 400, logits, Q_LAYERS, np.random.default_rng(2), n_sample=96)
-    for pos in range(401, 460):
-        _step(d, sh, int(toks[pos]), pos)
+    d.prefill(toks[:460])
     logits = _step(d, sh, int(toks[460]), 460)
-    check_step(GpuStep(d, sh), W, sh, int(toks[460]), 460, logits, Q_LAYERS, np.random.default_rng(3), n_sample=96)
+    check_step(GpuStep(d, sh), W, sh, int(toks[460]), 460, logits, Q_LAYERS, np.random.default_rng(2), n_sample=96)
+    for pos in range(461, 600):
+        _step(d, sh, int(toks[pos]), pos)
+    logits = _step(d, sh, int(toks[600]), 600)
+    check_step(GpuStep(d, sh), W, sh, int(toks[600]), 600, logits, Q_LAYERS, np.random.default_rng(3), n_sample=96)
     d.close()
 
 

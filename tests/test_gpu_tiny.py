@@ -179,10 +179,10 @@ def test_split_attention_long_positions(native, master, wfmt):
 
 @pytest.mark.parametrize("wfmt,split", [(synth.BF16, 0), (synth.FP4_MIX, 0), (synth.FP8_ROW, None)])
 def test_streamed_attention_beyond_register_passes(native, master, wfmt, split):
-    """Past the positions an attention workgroup holds in registers (7
-    passes of 56), the rest of the cache streams in pairs of passes: positions
-    392..529 take 1, 2 and 3 extra passes (odd and even counts).  Every step
-    is checked against the oracle.
+    """Past the positions an attention workgroup holds in registers (4
+    passes of 112), the rest of the cache streams in pairs of passes: positions
+    440..799 take 0 to 4 extra passes (odd and even counts).  Every step is
+    checked against the oracle.
 
     On random weights the logits are nearly flat, and at this depth of
     context the oracle's own rounding noise (float32 against float64, same
@@ -191,14 +191,14 @@ def test_streamed_attention_beyond_register_passes(native, master, wfmt, split):
     where the oracle's top-2 gap clears both 1e-3 and twice that step's
     measured noise; otherwise it must be a valid argmax: its oracle logit
     within that margin of the maximum.  split 0: the home workgroup alone;
-    None: the library default (split attention from position 448 on)."""
-    n = 530
+    None: the library default (split attention from position 576 on)."""
+    n = 800
     toks = synth.make_prompt(synth.TINY.vocab, n, 9)
     d = _decoder(native, master, wfmt, max_ctx=n + 2, split_chunk=split)
     orc = Oracle(master, wfmt, n + 2)
     o64 = Oracle(master, wfmt, n + 2, dtype=np.float64)
     cache, c64 = orc.new_cache(), o64.new_cache()
-    start = 380
+    start = 440
     nxt = d.prefill(toks[:start])
     want, last = orc.prefill_batched(cache, toks[:start])
     o64.prefill_batched(c64, toks[:start])

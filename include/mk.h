@@ -155,9 +155,12 @@ int mk_pack_weights(mk_model* m, const void* const* d_tensors, int32_t n_tensors
 int mk_read_packed(mk_model* m, int32_t layer, int32_t matrix, void* h_codes, void* h_scales,
                    void* h_block_scales, float* h_tensor_scale);
 
-/* Run the prompt: one decode step per position 0..n-1, writing the KV cache;
- * return the greedy token that follows the prompt (>= 0), or a negative
- * mk_status.  Synchronous. */
+/* Run the prompt through positions 0..n-1, writing the KV cache; return the
+ * greedy token that follows the prompt (>= 0), or a negative mk_status.
+ * By default one decode step per position; with option 10 = 1 the batched
+ * prefill (chunks of positions, projections on the matrix cores).  The
+ * monolith page's benchmark protocol ("Design decisions") times decode with
+ * prefill excluded, so either path serves it.  Synchronous. */
 int32_t mk_prefill(mk_model* m, const int32_t* h_tokens, int32_t n, mk_stream_t s);
 
 /* One decode step: consume `token` at position `pos` (writing its K/V into
@@ -230,7 +233,14 @@ int mk_decode_codes(int32_t codec, const uint8_t* d_codes, int32_t n, float* d_o
  * log-sum-exp rule.  c = 0 turns it off.  (On MI355X at the 0.6B shape the
  * split path is faster from about 560 cached positions on.)  Key 9, NVFP4
  * block scale search radius 0..126 [0], set before mk_pack_weights (see
- * there); 0 keeps the absolute-maximum recipe.
+ * there); 0 keeps the absolute-maximum recipe.  Key 10, prefill path [0]:
+ * 0 runs mk_prefill as one decode launch per prompt position; 1 runs the
+ * prompt through each layer in chunks of 256 positions, the projections as
+ * matrix products on the matrix cores (bf16 operands, fp32 accumulation,
+ * weights dequantized exactly), with the decode path's rounding points; it
+ * writes the same KV cache up to summation order.  1 needs hidden,
+ * intermediate and n_q_heads*head_dim divisible by 32, hidden <= 4096 and
+ * head_dim <= 256 and a multiple of 8 (else MK_E_UNSUPPORTED).
  * Keys 1 and 2 are reserved.
  * Errors: MK_E_INVALID (unknown key, value out of range), MK_E_STATE. */
 int mk_set_option(mk_model* m, int32_t key, int64_t value);

@@ -10,7 +10,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["mk_decode.hip", "mk_pack.hip", "mk_abi.cpp"]
+SOURCES = ["mk_decode.hip", "mk_pack.hip", "mk_prefill.hip", "mk_abi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

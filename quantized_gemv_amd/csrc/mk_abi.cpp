@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <algorithm>
+#include <cstddef>
 #include <cstring>
 #include <new>
 #include <string>
@@ -64,6 +65,8 @@ struct mk_model {
   int split_n = 0;              // helpers per KV head in the work table
   int coresident = 0;           // decode workgroups the device holds at once (set by mk_bind)
   int fp4_search = 0;           // NVFP4 block scale search radius (0: absolute-maximum recipe)
+  int prefill_mode = 0;         // mk_prefill: 0 one decode launch per position, 1 batched (matrix cores)
+  size_t pf_off = 0;            // batched-prefill workspace in the scratch buffer
   uint32_t epoch = 0;
   std::string err;
 };
@@ -153,6 +156,33 @@ void layout_weights(mk_model* m) {
   m->algo_bytes = algo;
 }
 
+// Batched prefill workspace: per chunk row the residual, the q/k/v outputs,
+// the GEMM input (normed residual or attention output) and the SwiGLU
+// output; then the LM head's per-wave maxima.
+struct PfLayout {
+  size_t x, qkv, a, h, bv, bi, total;
+};
+PfLayout prefill_layout(const mk_config& c) {
+  const size_t C = kPrefillChunk, H = c.hidden, I = c.intermediate, hd = c.head_dim;
+  const size_t nq = c.n_q_heads, nkv = c.n_kv_heads;
+  PfLayout L;
+  L.x = 0;
+  L.qkv = align_up(L.x + 4 * C * H);
+  L.a = align_up(L.qkv + 4 * C * (nq + 2 * nkv) * hd);
+  L.h = align_up(L.a + 2 * C * std::max(H, nq * hd));
+  L.bv = align_up(L.h + 2 * C * I);
+  L.bi = align_up(L.bv + 4ull * kPrefillHeadGroups * 4);
+  L.total = align_up(L.bi + 4ull * kPrefillHeadGroups * 4);
+  return L;
+}
+size_t prefill_workspace(const mk_config& c) { return prefill_layout(c).total; }
+// The batched prefill's kernels assume K % 32 == 0 for every matrix (the
+// GEMM's K step), hidden <= 4096 (the LM head's LDS row) and an even head_dim.
+bool prefill_supported(const mk_config& c) {
+  const int H = c.hidden, I = c.intermediate, q = c.n_q_heads * c.head_dim;
+  return H % 32 == 0 && I % 32 == 0 && q % 32 == 0 && H <= 4096 && c.head_dim % 8 == 0 && c.head_dim <= 256;
+}
+
 // Lay out the scratch buffer: per-layer exchange vectors, argmax words, the
 // error word, the zero page, the work table, the params copy, token slots.
 // Words of one split-attention partial: the outputs of the KV head's q heads,
@@ -231,7 +261,8 @@ void layout_scratch(mk_model* m, int grid, bool for_sizing = true) {
   X.words = w;
   m->params_off = align_up(w * 8);
   m->tok_off = align_up(m->params_off + sizeof(Params));
-  m->scratch_bytes = align_up(m->tok_off + 4ull * ((size_t)c.max_ctx + 4));
+  m->pf_off = align_up(m->tok_off + 4ull * ((size_t)c.max_ctx + 4));
+  m->scratch_bytes = align_up(m->pf_off + prefill_workspace(c));
   if (for_sizing) m->scratch_reported = m->scratch_bytes;
 }
 
@@ -688,6 +719,54 @@ int32_t mk_decode_step(mk_model* m, int32_t token, int32_t pos, mk_stream_t stre
   return read_token_and_error(m, tok + 1, s);
 }
 
+// Positions 0..n-1 through every layer in chunks of kPrefillChunk (matrix
+// products on the matrix cores), then the LM head of position n-1 and its
+// argmax into d_next (and its logits into d_logits when non-null).
+int prefill_batched(mk_model* m, const int32_t* d_prompt, int n, int32_t* d_next, float* d_logits, hipStream_t s) {
+  const mk_config& c = m->cfg;
+  {
+    const int rc = sync_params(m, s);
+    if (rc) return rc;
+  }
+  const PfLayout Lo = prefill_layout(c);
+  uint8_t* ws = m->d_scratch + m->pf_off;
+  const Params* dp = reinterpret_cast<const Params*>(m->d_scratch + m->params_off);
+  const char* dl = reinterpret_cast<const char*>(dp) + offsetof(Params, layer0);
+  PrefillArgs a;
+  a.params = dp;
+  a.mat_qkv = reinterpret_cast<const Mat*>(dl + offsetof(Layer, qkv));
+  a.mat_o = reinterpret_cast<const Mat*>(dl + offsetof(Layer, o));
+  a.mat_gu = reinterpret_cast<const Mat*>(dl + offsetof(Layer, gu));
+  a.mat_down = reinterpret_cast<const Mat*>(dl + offsetof(Layer, down));
+  a.fmt_lin = m->P.layer0.qkv.fmt;
+  a.fmt_down = m->P.layer0.down.fmt;
+  a.layer_stride = m->P.layer_stride;
+  a.in_norm = m->P.layer0.in_norm;
+  a.post_norm = m->P.layer0.post_norm;
+  a.L = c.n_layers;
+  a.H = c.hidden;
+  a.hd = c.head_dim;
+  a.nq = c.n_q_heads;
+  a.nkv = c.n_kv_heads;
+  a.I = c.intermediate;
+  a.X = reinterpret_cast<float*>(ws + Lo.x);
+  a.QKV = reinterpret_cast<float*>(ws + Lo.qkv);
+  a.A = reinterpret_cast<uint16_t*>(ws + Lo.a);
+  a.Hb = reinterpret_cast<uint16_t*>(ws + Lo.h);
+  a.best_v = reinterpret_cast<float*>(ws + Lo.bv);
+  a.best_i = reinterpret_cast<int32_t*>(ws + Lo.bi);
+  a.next = d_next;
+  a.logits = d_logits;
+  for (int c0 = 0; c0 < n; c0 += kPrefillChunk) {
+    a.c0 = c0;
+    a.cn = std::min(kPrefillChunk, n - c0);
+    a.last = c0 + a.cn == n;
+    a.tokens = d_prompt + c0;
+    HIPCK(m, launch_prefill_chunk(a, s));
+  }
+  return MK_OK;
+}
+
 int32_t mk_prefill(mk_model* m, const int32_t* h_tokens, int32_t n, mk_stream_t stream) {
   if (!m) return MK_E_INVALID;
   if (!h_tokens || n <= 0 || n > m->cfg.max_ctx) return fail(m, MK_E_INVALID, "mk_prefill: bad prompt length %d", n);
@@ -699,6 +778,11 @@ int32_t mk_prefill(mk_model* m, const int32_t* h_tokens, int32_t n, mk_stream_t 
   int32_t* tok = reinterpret_cast<int32_t*>(m->d_scratch + m->tok_off);
   int32_t* prompt = tok + 2;
   HIPCK(m, hipMemcpyAsync(prompt, h_tokens, 4ull * n, hipMemcpyHostToDevice, s));
+  if (m->prefill_mode == 1) {
+    const int rc = prefill_batched(m, prompt, n, tok + 1, nullptr, s);
+    if (rc) return rc;
+    return read_token_and_error(m, tok + 1, s);
+  }
   for (int i = 0; i < n; ++i) {
     int rc = launch_step(m, prompt + i, i, tok + 1, nullptr, s);
     if (rc) return rc;
@@ -807,6 +891,11 @@ int mk_set_option(mk_model* m, int32_t key, int64_t value) {
     case 8:
       if (value < 0 || value > (1 << 20)) return fail(m, MK_E_INVALID, "split start position out of range");
       m->split_from = (int)value;
+      break;
+    case 10:
+      if (value < 0 || value > 1) return fail(m, MK_E_INVALID, "prefill mode must be 0 or 1");
+      if (value == 1 && !prefill_supported(m->cfg)) return fail(m, MK_E_UNSUPPORTED, "batched prefill: shape not supported");
+      m->prefill_mode = (int)value;
       break;
     case 9:
       if (value < 0 || value > 0x7E) return fail(m, MK_E_INVALID, "FP4 scale search radius out of range");

@@ -25,4 +25,28 @@ hipError_t launch_pack_fp4(const uint16_t* src, int N, int K, uint8_t* codes, ui
                            int ts_index, uint32_t* amax, int row_off, int row_step, int search, hipStream_t s);
 hipError_t launch_rope(float* out, int max_ctx, int hd, double theta, hipStream_t s);
 hipError_t launch_decode_codes(int codec, const uint8_t* in, int n, float* out, hipStream_t s);
+
+// Batched prefill (mk_prefill.hip): positions [c0, c0 + cn) of a prompt
+// through every layer; with `last`, also the LM head of position c0+cn-1 and
+// its argmax into *next.  Device pointers; the workspace buffers hold
+// kPrefillChunk rows.
+constexpr int kPrefillChunk = 256;
+constexpr int kPrefillHeadGroups = 256;   // LM-head workgroups (4 waves each)
+struct PrefillArgs {
+  const Params* params;
+  const Mat *mat_qkv, *mat_o, *mat_gu, *mat_down;   // inside the device Params
+  uint32_t fmt_lin, fmt_down;
+  uint64_t layer_stride, in_norm, post_norm;
+  int L, H, hd, nq, nkv, I;
+  int c0, cn;
+  bool last;
+  const int32_t* tokens;   // the chunk's tokens
+  float *X, *QKV;          // [chunk][H], [chunk][(nq + 2 nkv) hd]
+  uint16_t *A, *Hb;        // [chunk][max(H, nq hd)], [chunk][I] bf16
+  float* best_v;           // [kPrefillHeadGroups * 4]
+  int32_t* best_i;
+  int32_t* next;
+  float* logits;           // [vocab] or null
+};
+hipError_t launch_prefill_chunk(const PrefillArgs& a, hipStream_t s);
 }  // namespace mk

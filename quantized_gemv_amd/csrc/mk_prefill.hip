@@ -1,0 +1,442 @@
+// Batched prefill for gfx950: a prompt's positions run through each layer
+// together, in chunks of up to kPrefillChunk positions, so the projections are
+// matrix-matrix products on the matrix cores (bf16 operands, fp32
+// accumulation) instead of one decode launch per position.  Every step keeps
+// the decode path's rounding points (GEMM inputs, K, V and the attention
+// output in bf16; residuals, q and logits in fp32) and writes the same KV
+// cache, so a decode step may follow at position n.
+//
+// Per chunk of positions [c0, c0 + cn):
+//   embed -> per layer: RMSNorm -> QKV GEMM -> q/k RMSNorm, RoPE, KV append ->
+//   causal attention over the cache -> O GEMM + residual -> RMSNorm ->
+//   gate/up GEMM + SwiGLU -> down GEMM + residual
+// then, after the last chunk, the final RMSNorm, the LM head of the last
+// position and its argmax.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "mk_codec.h"
+#include "mk_launch.h"
+#include "mk_shared.h"
+
+namespace mk {
+namespace {
+
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ int lane() { return (int)(threadIdx.x & 63); }
+__device__ __forceinline__ int wave() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
+__device__ __forceinline__ float wsum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wmax(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t arena(const Params& p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>((const uint8_t*)p.w), (short)0, (int)p.w_bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ float gain(__amdgpu_buffer_rsrc_t rw, uint64_t off, int i) {
+  return bf16_to_f32((uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rw, (uint32_t)(off + 2ull * i), 0, 0));
+}
+__device__ __forceinline__ size_t kv_plane(const Params& p, int hd) { return (size_t)((p.max_ctx + 3) & ~3) * hd; }
+
+// ------------------------------------------------------------------ embed
+// X[i, :] = the token's embedding row (bf16, or FP8 codes times the row scale).
+__global__ __launch_bounds__(256) void pf_embed(const Params* pp, const int32_t* tokens, int cn, float* X) {
+  const Params& p = *pp;
+  const int i = blockIdx.x;
+  if (i >= cn) return;
+  const __amdgpu_buffer_rsrc_t rw = arena(p);
+  const uint32_t t = (uint32_t)tokens[i];
+  const int H = p.H;
+  if (p.embed.fmt == FMT_BF16) {
+    for (int e = threadIdx.x; e < H; e += blockDim.x)
+      X[(size_t)i * H + e] = gain(rw, p.embed.codes + 2ull * t * H, e);
+  } else {
+    const float sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, (uint32_t)(p.embed.scales + 4ull * t), 0, 0));
+    for (int e = threadIdx.x; e < H; e += blockDim.x) {
+      const uint32_t c = __builtin_amdgcn_raw_buffer_load_b8(rw, (uint32_t)(p.embed.codes + (uint64_t)t * H + e), 0, 0);
+      X[(size_t)i * H + e] = e4m3_to_f32(c) * sc;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- RMSNorm
+// A[i, :] = bf16(g * (x * r)), r = 1/sqrt(mean(x^2) + eps); one workgroup per row.
+__global__ __launch_bounds__(256) void pf_rmsnorm(const Params* pp, const float* X, int cn, int H, uint64_t g_off,
+                                                  uint16_t* A) {
+  const Params& p = *pp;
+  __shared__ float red[4];
+  const int i = blockIdx.x;
+  if (i >= cn) return;
+  const float* x = X + (size_t)i * H;
+  float ss = 0.f;
+  for (int e = threadIdx.x; e < H; e += blockDim.x) ss += x[e] * x[e];
+  ss = wsum(ss);
+  if (lane() == 0) red[wave()] = ss;
+  __syncthreads();
+  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  const float r = 1.0f / sqrtf(tot / (float)H + p.eps);
+  const __amdgpu_buffer_rsrc_t rw = arena(p);
+  for (int e = threadIdx.x; e < H; e += blockDim.x) {
+    const float v = gain(rw, g_off, e) * (x[e] * r);
+    A[(size_t)i * H + e] = (uint16_t)f32_to_bf16(v);
+  }
+}
+
+// ------------------------------------------------------------------- GEMM
+// C[M x N] = A[M x K] (bf16, row-major) * W[N x K]^T, W dequantized to bf16
+// exactly in registers (FP8 codes; FP4 codes times their E4M3 block scale),
+// then each column n times its row scale (FP8) or tensor scale (FP4).  A
+// 256-thread workgroup computes a 64 x 64 tile; wave w the 32 x 32 quarter
+// (w&1, w>>1) as 2 x 2 v_mfma_f32_16x16x32_bf16 tiles; K in steps of 32
+// through LDS.  Epilogues: store C (fp32), add C into the residual X, or
+// SwiGLU over interleaved (gate, up) column pairs into bf16 H.
+enum : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+constexpr int BM = 64, BN = 64, BK = 32, LDA = BK + 8;
+
+template <uint32_t FMT>
+__device__ __forceinline__ u4 load_w8(__amdgpu_buffer_rsrc_t rw, const Mat& m, uint64_t lo, int n, int k) {
+  // 8 consecutive weights (n, k..k+7) as bf16; n < N and k + 8 <= K (callers clamp)
+  const uint64_t el = (uint64_t)n * m.K + k;
+  if (FMT == FMT_BF16) {
+    return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rw, (uint32_t)(m.codes + lo + 2 * el), 0, 0));
+  } else if (FMT == FMT_FP8) {
+    const u2 c = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(rw, (uint32_t)(m.codes + lo + el), 0, 0));
+    return u4{e4m3x2_to_bf16x2<false>(c.x), e4m3x2_to_bf16x2<true>(c.x), e4m3x2_to_bf16x2<false>(c.y),
+              e4m3x2_to_bf16x2<true>(c.y)};
+  } else {
+    const uint32_t c = __builtin_amdgcn_raw_buffer_load_b32(rw, (uint32_t)(m.codes + lo + el / 2), 0, 0);
+    const uint32_t bs = __builtin_amdgcn_raw_buffer_load_b8(rw, (uint32_t)(m.scales + lo + el / 16), 0, 0);
+    const float s = e4m3_to_f32(bs);
+    const uint32_t w2[4] = {e2m1x2_to_bf16x2<0>(c), e2m1x2_to_bf16x2<1>(c), e2m1x2_to_bf16x2<2>(c),
+                            e2m1x2_to_bf16x2<3>(c)};
+    u4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // e2m1 * e4m3 has at most 6 significant bits: exact in bf16
+      const uint32_t v = pack_bf16(bf16_lo(w2[j]) * s, bf16_hi(w2[j]) * s);
+      o[j] = v;
+    }
+    return o;
+  }
+}
+
+template <uint32_t FMT>
+__device__ __forceinline__ float col_scale(__amdgpu_buffer_rsrc_t rw, const Mat& m, uint64_t lo, int n) {
+  if (FMT == FMT_FP8)
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, (uint32_t)(m.scales + lo + 4ull * n), 0, 0));
+  if (FMT == FMT_FP4) {
+    uint32_t idx = 0;
+    if (m.ts_mode == 1) idx = (uint32_t)n < m.ts_b0 ? 0u : ((uint32_t)n < m.ts_b1 ? 1u : 2u);
+    else if (m.ts_mode == 2) idx = (uint32_t)n & 1u;
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, (uint32_t)(m.tscale + lo + 4ull * idx), 0, 0));
+  }
+  return 1.0f;
+}
+
+template <uint32_t FMT, int EPI>
+__global__ __launch_bounds__(256) void pf_gemm(const Params* pp, const Mat* mat, uint64_t lo, const uint16_t* A, int M,
+                                               float* C, uint16_t* Hout) {
+  const Params& p = *pp;
+  const Mat m = *mat;
+  const int N = (int)m.N, K = (int)m.K;
+  __shared__ __attribute__((aligned(16))) uint16_t sa[BM][LDA];
+  __shared__ __attribute__((aligned(16))) uint16_t sw[BN][LDA];
+  __shared__ float sc[BM][BN + 1];
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int t = threadIdx.x, w = wave(), l = lane();
+  const __amdgpu_buffer_rsrc_t rw = arena(p);
+  // the 8-element pieces this thread stages: row t/4, columns 8*(t%4)
+  const int sr = t >> 2, sk = 8 * (t & 3);
+  const int am = min(m0 + sr, M - 1), wn = min(n0 + sr, N - 1);
+  f4v acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f4v{0.f, 0.f, 0.f, 0.f};
+  const int wr = 32 * (w & 1), wc = 32 * (w >> 1);
+  for (int k0 = 0; k0 < K; k0 += BK) {
+    const u4 av = *reinterpret_cast<const u4*>(A + (size_t)am * K + k0 + sk);
+    const u4 wv = load_w8<FMT>(rw, m, lo, wn, k0 + sk);
+    __syncthreads();   // the previous step's operands are consumed
+    *reinterpret_cast<u4*>(&sa[sr][sk]) = av;
+    *reinterpret_cast<u4*>(&sw[sr][sk]) = wv;
+    __syncthreads();
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const u4 ao = *reinterpret_cast<const u4*>(&sa[wr + 16 * a + (l & 15)][8 * (l >> 4)]);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const u4 bo = *reinterpret_cast<const u4*>(&sw[wc + 16 * b + (l & 15)][8 * (l >> 4)]);
+        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, ao), __builtin_bit_cast(bf8v, bo),
+                                                            acc[a][b], 0, 0, 0);
+      }
+    }
+  }
+  // D: lane l holds rows 4(l/16)+i of column l%16 of each 16 x 16 tile
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int cc = wc + 16 * b + (l & 15);
+      const float s = col_scale<FMT>(rw, m, lo, min(n0 + cc, N - 1));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[wr + 16 * a + 4 * (l >> 4) + i][cc] = acc[a][b][i] * s;
+    }
+  __syncthreads();
+  if (EPI == EPI_SWIGLU) {
+    // columns (2j, 2j+1) = (gate j, up j): h_j = silu(gate) * up, bf16
+    const int I = N / 2;
+    for (int e = t; e < BM * BN / 2; e += 256) {
+      const int r = e / (BN / 2), j = e % (BN / 2);
+      const int gm = m0 + r, gj = n0 / 2 + j;
+      if (gm < M && gj < I) Hout[(size_t)gm * I + gj] = (uint16_t)f32_to_bf16(silu_f(sc[r][2 * j]) * sc[r][2 * j + 1]);
+    }
+  } else {
+    for (int e = t; e < BM * BN; e += 256) {
+      const int r = e / BN, c = e % BN;
+      const int gm = m0 + r, gn = n0 + c;
+      if (gm < M && gn < N) {
+        if (EPI == EPI_STORE) C[(size_t)gm * N + gn] = sc[r][c];
+        else C[(size_t)gm * N + gn] += sc[r][c];
+      }
+    }
+  }
+}
+
+// -------------------------------------------- q/k RMSNorm, RoPE, KV append
+// One wave per (position, head slot): slots 0..nq-1 q heads (normed, roped,
+// times log2(e)/sqrt(hd), written back in place), nq..nq+nkv-1 k heads
+// (normed, roped, bf16, appended), then the v heads (bf16, appended).  Lane
+// i < hd/2 owns the RoPE pair (i, i + hd/2).
+__global__ __launch_bounds__(256) void pf_qkv_post(const Params* pp, int l, int c0, int cn, float* QKV) {
+  const Params& p = *pp;
+  const int hd = p.hd, nq = p.nq, nkv = p.nkv, slots = nq + 2 * nkv;
+  const int idx = blockIdx.x * 4 + wave();
+  if (idx >= cn * slots) return;
+  const int i = idx / slots, h = idx % slots, pos = c0 + i;
+  const int ln = lane(), li = min(ln, hd / 2 - 1);
+  const bool pl = ln < hd / 2;
+  float* x = QKV + (size_t)i * slots * hd + (size_t)h * hd;
+  const float xa = pl ? x[li] : 0.f, xb = pl ? x[li + hd / 2] : 0.f;
+  const size_t plane = kv_plane(p, hd);
+  if (h >= nq + nkv) {   // v: round and append (V planes are tiled by 4 positions)
+    const int g = h - nq - nkv;
+    uint16_t* vc = p.kv + ((size_t)(l * 2 + 1) * nkv + g) * plane;
+    if (pl) {
+      vc[((size_t)(pos >> 2) * hd + li) * 4 + (pos & 3)] = (uint16_t)f32_to_bf16(xa);
+      vc[((size_t)(pos >> 2) * hd + li + hd / 2) * 4 + (pos & 3)] = (uint16_t)f32_to_bf16(xb);
+    }
+    return;
+  }
+  const __amdgpu_buffer_rsrc_t rw = arena(p);
+  const uint64_t lo = (uint64_t)l * p.layer_stride;
+  const bool isq = h < nq;
+  const uint64_t goff = (isq ? p.layer0.q_norm : p.layer0.k_norm) + lo;
+  const float r = 1.0f / sqrtf(wsum(xa * xa + xb * xb) / (float)hd + p.eps);
+  const float a = gain(rw, goff, li) * (xa * r), b = gain(rw, goff, li + hd / 2) * (xb * r);
+  const float cs = p.rope[((size_t)pos * (hd / 2) + li) * 2], sn = p.rope[((size_t)pos * (hd / 2) + li) * 2 + 1];
+  const float ra = a * cs - b * sn, rb = b * cs + a * sn;
+  if (isq) {
+    const float kq = 1.4426950408889634f / sqrtf((float)hd);
+    if (pl) {
+      x[li] = ra * kq;
+      x[li + hd / 2] = rb * kq;
+    }
+  } else {
+    const int g = h - nq;
+    uint16_t* kc = p.kv + ((size_t)(l * 2 + 0) * nkv + g) * plane + (size_t)pos * hd;
+    if (pl) {
+      kc[li] = (uint16_t)f32_to_bf16(ra);
+      kc[li + hd / 2] = (uint16_t)f32_to_bf16(rb);
+    }
+  }
+}
+
+// -------------------------------------------------------------- attention
+// One wave per (position i of the chunk, q head h): scores against cached
+// positions 0..c0+i in blocks of 64 (one key per lane, q read from LDS),
+// online softmax in log2 units, then each lane accumulates its two output
+// dimensions over the block's weights.  Output bf16 into O[i][h*hd ..].
+__global__ __launch_bounds__(256) void pf_attention(const Params* pp, int l, int c0, int cn, const float* QKV,
+                                                    uint16_t* O) {
+  const Params& p = *pp;
+  const int hd = p.hd, nq = p.nq, nkv = p.nkv, slots = nq + 2 * nkv;
+  __shared__ float sq[4][256];
+  __shared__ float spw[4][64];
+  const int w = wave(), ln = lane();
+  const int idx = blockIdx.x * 4 + w;
+  const bool live = idx < cn * nq;   // wave-uniform
+  const int i = live ? idx / nq : 0, h = idx % nq, pos = c0 + i, g = h / (nq / nkv);
+  const float* q = QKV + (size_t)i * slots * hd + (size_t)h * hd;
+  for (int e = ln; e < hd; e += 64) sq[w][e] = q[e];
+  __syncthreads();
+  const size_t plane = kv_plane(p, hd);
+  const uint16_t* kc = p.kv + ((size_t)(l * 2 + 0) * nkv + g) * plane;
+  const uint16_t* vc = p.kv + ((size_t)(l * 2 + 1) * nkv + g) * plane;
+  float m = -INFINITY, lsum = 0.f, o0 = 0.f, o1 = 0.f;
+  const int e0 = min(2 * ln, hd - 2);
+  const int nblk = live ? pos / 64 + 1 : 0;
+  for (int b = 0; b < nblk; ++b) {
+    const int j = 64 * b + ln;
+    const int jc = min(j, pos);
+    const u4* kr = reinterpret_cast<const u4*>(kc + (size_t)jc * hd);
+    float s = 0.f;
+    for (int c = 0; c < hd / 8; ++c) {
+      const u4 kw = kr[c];
+      const float* qq = &sq[w][8 * c];
+      s = fmaf(qq[0], bf16_lo(kw.x), s);
+      s = fmaf(qq[1], bf16_hi(kw.x), s);
+      s = fmaf(qq[2], bf16_lo(kw.y), s);
+      s = fmaf(qq[3], bf16_hi(kw.y), s);
+      s = fmaf(qq[4], bf16_lo(kw.z), s);
+      s = fmaf(qq[5], bf16_hi(kw.z), s);
+      s = fmaf(qq[6], bf16_lo(kw.w), s);
+      s = fmaf(qq[7], bf16_hi(kw.w), s);
+    }
+    s = j <= pos ? s : -INFINITY;
+    const float mn = fmaxf(m, wmax(s));
+    const float scale = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+    const float pw = s == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s - mn);
+    m = mn;
+    lsum = lsum * scale + wsum(pw);
+    o0 *= scale;
+    o1 *= scale;
+    spw[w][ln] = pw;
+    __builtin_amdgcn_wave_barrier();
+    // four positions of one dimension per 8-byte load (the V tile); weights
+    // past pos are 0 and the tile slots past it hold finite values
+    const int jn = min(64, pos + 1 - 64 * b);
+    for (int jq = 0; jq < jn; jq += 4) {
+      const size_t tile = (size_t)((64 * b + jq) >> 2);
+      const u2 d0 = *reinterpret_cast<const u2*>(vc + (tile * hd + e0) * 4);
+      const u2 d1 = *reinterpret_cast<const u2*>(vc + (tile * hd + e0 + 1) * 4);
+      const float* pj = &spw[w][jq];
+      o0 = fmaf(pj[0], bf16_lo(d0.x), o0);
+      o0 = fmaf(pj[1], bf16_hi(d0.x), o0);
+      o0 = fmaf(pj[2], bf16_lo(d0.y), o0);
+      o0 = fmaf(pj[3], bf16_hi(d0.y), o0);
+      o1 = fmaf(pj[0], bf16_lo(d1.x), o1);
+      o1 = fmaf(pj[1], bf16_hi(d1.x), o1);
+      o1 = fmaf(pj[2], bf16_lo(d1.y), o1);
+      o1 = fmaf(pj[3], bf16_hi(d1.y), o1);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  if (live && 2 * ln < hd) {
+    const uint32_t pr = pack_bf16(o0 / lsum, o1 / lsum);
+    *reinterpret_cast<uint32_t*>(O + (size_t)i * nq * hd + (size_t)h * hd + 2 * ln) = pr;
+  }
+}
+
+// ---------------------------------------------------------------- LM head
+// The last position's final RMSNorm (bf16) against every vocabulary row;
+// each wave keeps its best (value, lowest index); logits optional.
+__global__ __launch_bounds__(256) void pf_lm_head(const Params* pp, const float* x, float* logits, float* best_v,
+                                                  int32_t* best_i) {
+  const Params& p = *pp;
+  __shared__ float xn[4096];
+  __shared__ float red[4];
+  const int H = p.H, ln = lane(), w = wave();
+  float ss = 0.f;
+  for (int e = threadIdx.x; e < H; e += 256) ss += x[e] * x[e];
+  ss = wsum(ss);
+  if (ln == 0) red[w] = ss;
+  __syncthreads();
+  const float r = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)H + p.eps);
+  const __amdgpu_buffer_rsrc_t rw = arena(p);
+  for (int e = threadIdx.x; e < H; e += 256) xn[e] = bf16_to_f32((uint16_t)f32_to_bf16(gain(rw, p.final_norm, e) * (x[e] * r)));
+  __syncthreads();
+  float bv = -INFINITY;
+  int bi = 0x7FFFFFFF;
+  const int nw = gridDim.x * 4;
+  for (int row = blockIdx.x * 4 + w; row < p.V; row += nw) {
+    float d = 0.f;
+    if (p.embed.fmt == FMT_BF16) {
+      for (int e = ln; e < H; e += 64) d = fmaf(xn[e], gain(rw, p.embed.codes + 2ull * row * H, e), d);
+      d = wsum(d);
+    } else {
+      for (int e = ln; e < H; e += 64) {
+        const uint32_t c = __builtin_amdgcn_raw_buffer_load_b8(rw, (uint32_t)(p.embed.codes + (uint64_t)row * H + e), 0, 0);
+        d = fmaf(xn[e], e4m3_to_f32(c), d);
+      }
+      d = wsum(d) * __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, (uint32_t)(p.embed.scales + 4ull * row), 0, 0));
+    }
+    if (logits && ln == 0) logits[row] = d;
+    if (d > bv) {   // rows ascend: a tie keeps the lower index
+      bv = d;
+      bi = row;
+    }
+  }
+  if (ln == 0) {
+    best_v[blockIdx.x * 4 + w] = bv;
+    best_i[blockIdx.x * 4 + w] = bi;
+  }
+}
+
+__global__ void pf_argmax(const float* best_v, const int32_t* best_i, int n, int32_t* out) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  float b = best_v[0];
+  int bi = best_i[0];
+  for (int k = 1; k < n; ++k)
+    if (best_v[k] > b || (best_v[k] == b && best_i[k] < bi)) {
+      b = best_v[k];
+      bi = best_i[k];
+    }
+  *out = bi;
+}
+
+template <int EPI>
+hipError_t gemm(uint32_t fmt, const Params* pp, const Mat* mat, int N, uint64_t lo, const uint16_t* A, int M, float* C,
+                uint16_t* Hout, hipStream_t s) {
+  const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
+  if (fmt == FMT_BF16) hipLaunchKernelGGL((pf_gemm<FMT_BF16, EPI>), grid, dim3(256), 0, s, pp, mat, lo, A, M, C, Hout);
+  else if (fmt == FMT_FP8) hipLaunchKernelGGL((pf_gemm<FMT_FP8, EPI>), grid, dim3(256), 0, s, pp, mat, lo, A, M, C, Hout);
+  else hipLaunchKernelGGL((pf_gemm<FMT_FP4, EPI>), grid, dim3(256), 0, s, pp, mat, lo, A, M, C, Hout);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_chunk(const PrefillArgs& a, hipStream_t s) {
+  const Params* pp = a.params;
+  const int cn = a.cn, H = a.H, hd = a.hd, nq = a.nq, nkv = a.nkv, I = a.I;
+  const int nqkv = (nq + 2 * nkv) * hd;
+  hipLaunchKernelGGL(pf_embed, dim3(cn), dim3(256), 0, s, pp, a.tokens, cn, a.X);
+  for (int l = 0; l < a.L; ++l) {
+    const uint64_t lo = (uint64_t)l * a.layer_stride;
+    hipLaunchKernelGGL(pf_rmsnorm, dim3(cn), dim3(256), 0, s, pp, a.X, cn, H, a.in_norm + lo, a.A);
+    hipError_t e = gemm<EPI_STORE>(a.fmt_lin, pp, a.mat_qkv, nqkv, lo, a.A, cn, a.QKV, nullptr, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(pf_qkv_post, dim3((cn * (nq + 2 * nkv) + 3) / 4), dim3(256), 0, s, pp, l, a.c0, cn, a.QKV);
+    hipLaunchKernelGGL(pf_attention, dim3((cn * nq + 3) / 4), dim3(256), 0, s, pp, l, a.c0, cn, a.QKV, a.A);
+    e = gemm<EPI_RESID>(a.fmt_lin, pp, a.mat_o, H, lo, a.A, cn, a.X, nullptr, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(pf_rmsnorm, dim3(cn), dim3(256), 0, s, pp, a.X, cn, H, a.post_norm + lo, a.A);
+    e = gemm<EPI_SWIGLU>(a.fmt_lin, pp, a.mat_gu, 2 * I, lo, a.A, cn, nullptr, a.Hb, s);
+    if (e != hipSuccess) return e;
+    e = gemm<EPI_RESID>(a.fmt_down, pp, a.mat_down, H, lo, a.Hb, cn, a.X, nullptr, s);
+    if (e != hipSuccess) return e;
+  }
+  if (a.last) {
+    hipLaunchKernelGGL(pf_lm_head, dim3(kPrefillHeadGroups), dim3(256), 0, s, pp, a.X + (size_t)(cn - 1) * H, a.logits,
+                       a.best_v, a.best_i);
+    hipLaunchKernelGGL(pf_argmax, dim3(1), dim3(64), 0, s, a.best_v, a.best_i, kPrefillHeadGroups * 4, a.next);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mk

@@ -24,6 +24,7 @@ EXCHANGE = {"qkv": 0, "attn": 1, "x_o": 2, "h": 3, "x_d": 4}
 OPT_GRID, OPT_SPIN_LIMIT, OPT_TAG_SKEW, OPT_POLL_SLEEP, OPT_LAUNCH_MODE, OPT_SPLIT_CHUNK, OPT_SPLIT_FROM = \
     0, 3, 4, 5, 6, 7, 8
 OPT_FP4_SEARCH = 9
+OPT_PREFILL_MODE = 10
 
 
 class MkError(RuntimeError):
@@ -117,7 +118,8 @@ class Decoder:
     def __init__(self, shape, wfmt: int, max_ctx: int, xray: bool = False, grid: int = 0,
                  spin_limit: Optional[int] = None, poll_sleep: Optional[int] = None,
                  launch_mode: Optional[int] = None, split_chunk: Optional[int] = None,
-                 split_from: Optional[int] = None, fp4_search: Optional[int] = None):
+                 split_from: Optional[int] = None, fp4_search: Optional[int] = None,
+                 prefill_mode: Optional[int] = None):
         import torch
         self.lib = load(xray)
         self.shape, self.wfmt, self.max_ctx = shape, wfmt, max_ctx
@@ -139,6 +141,8 @@ class Decoder:
             self._check(self.lib.mk_set_option(self.h, OPT_SPLIT_FROM, split_from))
         if fp4_search is not None:
             self._check(self.lib.mk_set_option(self.h, OPT_FP4_SEARCH, fp4_search))
+        if prefill_mode is not None:
+            self._check(self.lib.mk_set_option(self.h, OPT_PREFILL_MODE, prefill_mode))
         self.sizes = mk_sizes()
         self._check(self.lib.mk_query_sizes(self.h, ctypes.byref(self.sizes)))
         dev = torch.device("cuda", torch.cuda.current_device())

@@ -43,10 +43,31 @@ def parse():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="before decoding, run a plain device copy of this many MiB three times (the "
                          "known-size reference for scaling HBM traffic counters under rocprofv3 --pmc)")
+    ap.add_argument("--prefill-bench", action="store_true",
+                    help="also time mk_prefill of the workload's prompt both ways (one decode launch per "
+                         "position, and the batched matrix-core prefill) and add a 'prefill' object")
     ap.add_argument("--xray", action="store_true",
                     help="X-ray build: print the per-phase budget of the step at position P + K/2 "
                          "instead of the headline line")
     return ap.parse_args()
+
+
+def prefill_bench(dec, native, prompt, repeats=3):
+    """Wall time of mk_prefill (synchronous) for the prompt, per path: the
+    median of `repeats` runs after one untimed run."""
+    res = {"prompt_len": int(len(prompt))}
+    for mode, name in ((0, "decode_launches"), (1, "batched")):
+        dec._check(dec.lib.mk_set_option(dec.h, native.OPT_PREFILL_MODE, mode))
+        dec.prefill(prompt)
+        ts = []
+        for _ in range(repeats):
+            t0 = time.perf_counter()
+            dec.prefill(prompt)
+            ts.append(time.perf_counter() - t0)
+        t = sorted(ts)[len(ts) // 2]
+        res[name] = {"ms": round(t * 1e3, 3), "tokens_per_s": round(len(prompt) / t, 1)}
+    dec._check(dec.lib.mk_set_option(dec.h, native.OPT_PREFILL_MODE, 0))
+    return res
 
 
 def xray_report(dec, wl, K, prompt, dump=""):
@@ -243,6 +264,8 @@ def main():
                      "bytes_per_launch": int(algo)},
         "greedy_tokens_head": [int(t) for t in tokens_ref[:8]],
     }
+    if args.prefill_bench:
+        out["prefill"] = prefill_bench(dec, native, prompt)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(master, wl, K, prompt, args.cpu_seconds)
     dec.close()

@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void pf_rmsnorm(const Params* pp, const float*
 // through LDS.  Epilogues: store C (fp32), add C into the residual X, or
 // SwiGLU over interleaved (gate, up) column pairs into bf16 H.
 enum : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
-constexpr int BM = 64, BN = 64, BK = 32, LDA = BK + 8;
+constexpr int BK = 32, LDA = BK + 8;
 
 template <uint32_t FMT>
 __device__ __forceinline__ u4 load_w8(__amdgpu_buffer_rsrc_t rw, const Mat& m, uint64_t lo, int n, int k) {
@@ -147,39 +147,44 @@ __device__ __forceinline__ float col_scale(__amdgpu_buffer_rsrc_t rw, const Mat&
   return 1.0f;
 }
 
-template <uint32_t FMT, int EPI>
+template <uint32_t FMT, int EPI, int T>
 __global__ __launch_bounds__(256) void pf_gemm(const Params* pp, const Mat* mat, uint64_t lo, const uint16_t* A, int M,
                                                float* C, uint16_t* Hout) {
+  // T x T tile: each wave owns a (T/2) x (T/2) quarter of (T/32)^2 MFMA tiles
+  constexpr int NT = T / 32;
   const Params& p = *pp;
   const Mat m = *mat;
   const int N = (int)m.N, K = (int)m.K;
-  __shared__ __attribute__((aligned(16))) uint16_t sa[BM][LDA];
-  __shared__ __attribute__((aligned(16))) uint16_t sw[BN][LDA];
-  __shared__ float sc[BM][BN + 1];
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  __shared__ __attribute__((aligned(16))) uint16_t sa[T][LDA];
+  __shared__ __attribute__((aligned(16))) uint16_t sw[T][LDA];
+  __shared__ float sc[T][T + 1];
+  const int m0 = blockIdx.y * T, n0 = blockIdx.x * T;
   const int t = threadIdx.x, w = wave(), l = lane();
   const __amdgpu_buffer_rsrc_t rw = arena(p);
-  // the 8-element pieces this thread stages: row t/4, columns 8*(t%4)
-  const int sr = t >> 2, sk = 8 * (t & 3);
+  // the 8-element pieces thread t < 4T stages: row t/4, columns 8*(t%4)
+  const bool stager = t < 4 * T;
+  const int sr = min(t >> 2, T - 1), sk = 8 * (t & 3);
   const int am = min(m0 + sr, M - 1), wn = min(n0 + sr, N - 1);
-  f4v acc[2][2];
+  f4v acc[NT][NT];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < NT; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f4v{0.f, 0.f, 0.f, 0.f};
-  const int wr = 32 * (w & 1), wc = 32 * (w >> 1);
+    for (int b = 0; b < NT; ++b) acc[a][b] = f4v{0.f, 0.f, 0.f, 0.f};
+  const int wr = (T / 2) * (w & 1), wc = (T / 2) * (w >> 1);
   for (int k0 = 0; k0 < K; k0 += BK) {
     const u4 av = *reinterpret_cast<const u4*>(A + (size_t)am * K + k0 + sk);
     const u4 wv = load_w8<FMT>(rw, m, lo, wn, k0 + sk);
     __syncthreads();   // the previous step's operands are consumed
-    *reinterpret_cast<u4*>(&sa[sr][sk]) = av;
-    *reinterpret_cast<u4*>(&sw[sr][sk]) = wv;
+    if (stager) {
+      *reinterpret_cast<u4*>(&sa[sr][sk]) = av;
+      *reinterpret_cast<u4*>(&sw[sr][sk]) = wv;
+    }
     __syncthreads();
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
+    for (int a = 0; a < NT; ++a) {
       const u4 ao = *reinterpret_cast<const u4*>(&sa[wr + 16 * a + (l & 15)][8 * (l >> 4)]);
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
+      for (int b = 0; b < NT; ++b) {
         const u4 bo = *reinterpret_cast<const u4*>(&sw[wc + 16 * b + (l & 15)][8 * (l >> 4)]);
         acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, ao), __builtin_bit_cast(bf8v, bo),
                                                             acc[a][b], 0, 0, 0);
@@ -188,9 +193,9 @@ __global__ __launch_bounds__(256) void pf_gemm(const Params* pp, const Mat* mat,
   }
   // D: lane l holds rows 4(l/16)+i of column l%16 of each 16 x 16 tile
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < NT; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < NT; ++b) {
       const int cc = wc + 16 * b + (l & 15);
       const float s = col_scale<FMT>(rw, m, lo, min(n0 + cc, N - 1));
 #pragma unroll
@@ -200,14 +205,14 @@ __global__ __launch_bounds__(256) void pf_gemm(const Params* pp, const Mat* mat,
   if (EPI == EPI_SWIGLU) {
     // columns (2j, 2j+1) = (gate j, up j): h_j = silu(gate) * up, bf16
     const int I = N / 2;
-    for (int e = t; e < BM * BN / 2; e += 256) {
-      const int r = e / (BN / 2), j = e % (BN / 2);
+    for (int e = t; e < T * T / 2; e += 256) {
+      const int r = e / (T / 2), j = e % (T / 2);
       const int gm = m0 + r, gj = n0 / 2 + j;
       if (gm < M && gj < I) Hout[(size_t)gm * I + gj] = (uint16_t)f32_to_bf16(silu_f(sc[r][2 * j]) * sc[r][2 * j + 1]);
     }
   } else {
-    for (int e = t; e < BM * BN; e += 256) {
-      const int r = e / BN, c = e % BN;
+    for (int e = t; e < T * T; e += 256) {
+      const int r = e / T, c = e % T;
       const int gm = m0 + r, gn = n0 + c;
       if (gm < M && gn < N) {
         if (EPI == EPI_STORE) C[(size_t)gm * N + gn] = sc[r][c];
@@ -268,44 +273,46 @@ __global__ __launch_bounds__(256) void pf_qkv_post(const Params* pp, int l, int 
 
 // -------------------------------------------------------------- attention
 // One wave per (position i of the chunk, q head h): scores against cached
-// positions 0..c0+i in blocks of 64 (one key per lane, q read from LDS),
-// online softmax in log2 units, then each lane accumulates its two output
-// dimensions over the block's weights.  Output bf16 into O[i][h*hd ..].
+// positions 0..c0+i in blocks of 64 (one key per lane, q in every lane's
+// registers), online softmax in log2 units, then each lane accumulates its
+// two output dimensions over the block's weights (the block's weights pass
+// through LDS).  Output bf16 into O[i][h*HD ..].
+template <int HD>
 __global__ __launch_bounds__(256) void pf_attention(const Params* pp, int l, int c0, int cn, const float* QKV,
                                                     uint16_t* O) {
   const Params& p = *pp;
-  const int hd = p.hd, nq = p.nq, nkv = p.nkv, slots = nq + 2 * nkv;
-  __shared__ float sq[4][256];
+  const int nq = p.nq, nkv = p.nkv, slots = nq + 2 * nkv;
   __shared__ float spw[4][64];
   const int w = wave(), ln = lane();
   const int idx = blockIdx.x * 4 + w;
   const bool live = idx < cn * nq;   // wave-uniform
   const int i = live ? idx / nq : 0, h = idx % nq, pos = c0 + i, g = h / (nq / nkv);
-  const float* q = QKV + (size_t)i * slots * hd + (size_t)h * hd;
-  for (int e = ln; e < hd; e += 64) sq[w][e] = q[e];
-  __syncthreads();
-  const size_t plane = kv_plane(p, hd);
+  const float4* q4 = reinterpret_cast<const float4*>(QKV + (size_t)i * slots * HD + (size_t)h * HD);
+  float4 q[HD / 4];
+#pragma unroll
+  for (int c = 0; c < HD / 4; ++c) q[c] = q4[c];
+  const size_t plane = kv_plane(p, HD);
   const uint16_t* kc = p.kv + ((size_t)(l * 2 + 0) * nkv + g) * plane;
   const uint16_t* vc = p.kv + ((size_t)(l * 2 + 1) * nkv + g) * plane;
   float m = -INFINITY, lsum = 0.f, o0 = 0.f, o1 = 0.f;
-  const int e0 = min(2 * ln, hd - 2);
+  const int e0 = min(2 * ln, HD - 2);
   const int nblk = live ? pos / 64 + 1 : 0;
   for (int b = 0; b < nblk; ++b) {
     const int j = 64 * b + ln;
-    const int jc = min(j, pos);
-    const u4* kr = reinterpret_cast<const u4*>(kc + (size_t)jc * hd);
+    const u4* kr = reinterpret_cast<const u4*>(kc + (size_t)min(j, pos) * HD);
     float s = 0.f;
-    for (int c = 0; c < hd / 8; ++c) {
+#pragma unroll
+    for (int c = 0; c < HD / 8; ++c) {
       const u4 kw = kr[c];
-      const float* qq = &sq[w][8 * c];
-      s = fmaf(qq[0], bf16_lo(kw.x), s);
-      s = fmaf(qq[1], bf16_hi(kw.x), s);
-      s = fmaf(qq[2], bf16_lo(kw.y), s);
-      s = fmaf(qq[3], bf16_hi(kw.y), s);
-      s = fmaf(qq[4], bf16_lo(kw.z), s);
-      s = fmaf(qq[5], bf16_hi(kw.z), s);
-      s = fmaf(qq[6], bf16_lo(kw.w), s);
-      s = fmaf(qq[7], bf16_hi(kw.w), s);
+      const float4 qa = q[2 * c], qb = q[2 * c + 1];
+      s = fmaf(qa.x, bf16_lo(kw.x), s);
+      s = fmaf(qa.y, bf16_hi(kw.x), s);
+      s = fmaf(qa.z, bf16_lo(kw.y), s);
+      s = fmaf(qa.w, bf16_hi(kw.y), s);
+      s = fmaf(qb.x, bf16_lo(kw.z), s);
+      s = fmaf(qb.y, bf16_hi(kw.z), s);
+      s = fmaf(qb.z, bf16_lo(kw.w), s);
+      s = fmaf(qb.w, bf16_hi(kw.w), s);
     }
     s = j <= pos ? s : -INFINITY;
     const float mn = fmaxf(m, wmax(s));
@@ -322,8 +329,8 @@ __global__ __launch_bounds__(256) void pf_attention(const Params* pp, int l, int
     const int jn = min(64, pos + 1 - 64 * b);
     for (int jq = 0; jq < jn; jq += 4) {
       const size_t tile = (size_t)((64 * b + jq) >> 2);
-      const u2 d0 = *reinterpret_cast<const u2*>(vc + (tile * hd + e0) * 4);
-      const u2 d1 = *reinterpret_cast<const u2*>(vc + (tile * hd + e0 + 1) * 4);
+      const u2 d0 = *reinterpret_cast<const u2*>(vc + (tile * HD + e0) * 4);
+      const u2 d1 = *reinterpret_cast<const u2*>(vc + (tile * HD + e0 + 1) * 4);
       const float* pj = &spw[w][jq];
       o0 = fmaf(pj[0], bf16_lo(d0.x), o0);
       o0 = fmaf(pj[1], bf16_hi(d0.x), o0);
@@ -336,9 +343,9 @@ __global__ __launch_bounds__(256) void pf_attention(const Params* pp, int l, int
     }
     __builtin_amdgcn_wave_barrier();
   }
-  if (live && 2 * ln < hd) {
+  if (live && 2 * ln < HD) {
     const uint32_t pr = pack_bf16(o0 / lsum, o1 / lsum);
-    *reinterpret_cast<uint32_t*>(O + (size_t)i * nq * hd + (size_t)h * hd + 2 * ln) = pr;
+    *reinterpret_cast<uint32_t*>(O + (size_t)i * nq * HD + (size_t)h * HD + 2 * ln) = pr;
   }
 }
 
@@ -399,14 +406,22 @@ __global__ void pf_argmax(const float* best_v, const int32_t* best_i, int n, int
   *out = bi;
 }
 
+template <int EPI, int T>
+hipError_t gemm_t(uint32_t fmt, const Params* pp, const Mat* mat, int N, uint64_t lo, const uint16_t* A, int M, float* C,
+                  uint16_t* Hout, hipStream_t s) {
+  const dim3 grid((N + T - 1) / T, (M + T - 1) / T);
+  if (fmt == FMT_BF16) hipLaunchKernelGGL((pf_gemm<FMT_BF16, EPI, T>), grid, dim3(256), 0, s, pp, mat, lo, A, M, C, Hout);
+  else if (fmt == FMT_FP8) hipLaunchKernelGGL((pf_gemm<FMT_FP8, EPI, T>), grid, dim3(256), 0, s, pp, mat, lo, A, M, C, Hout);
+  else hipLaunchKernelGGL((pf_gemm<FMT_FP4, EPI, T>), grid, dim3(256), 0, s, pp, mat, lo, A, M, C, Hout);
+  return hipGetLastError();
+}
+// 64 x 64 tiles where they give at least one workgroup per compute unit, else
+// 32 x 32 (the N = hidden products of a chunk)
 template <int EPI>
 hipError_t gemm(uint32_t fmt, const Params* pp, const Mat* mat, int N, uint64_t lo, const uint16_t* A, int M, float* C,
                 uint16_t* Hout, hipStream_t s) {
-  const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
-  if (fmt == FMT_BF16) hipLaunchKernelGGL((pf_gemm<FMT_BF16, EPI>), grid, dim3(256), 0, s, pp, mat, lo, A, M, C, Hout);
-  else if (fmt == FMT_FP8) hipLaunchKernelGGL((pf_gemm<FMT_FP8, EPI>), grid, dim3(256), 0, s, pp, mat, lo, A, M, C, Hout);
-  else hipLaunchKernelGGL((pf_gemm<FMT_FP4, EPI>), grid, dim3(256), 0, s, pp, mat, lo, A, M, C, Hout);
-  return hipGetLastError();
+  if ((long)((N + 63) / 64) * ((M + 63) / 64) >= 256) return gemm_t<EPI, 64>(fmt, pp, mat, N, lo, A, M, C, Hout, s);
+  return gemm_t<EPI, 32>(fmt, pp, mat, N, lo, A, M, C, Hout, s);
 }
 
 }  // namespace
@@ -422,7 +437,12 @@ hipError_t launch_prefill_chunk(const PrefillArgs& a, hipStream_t s) {
     hipError_t e = gemm<EPI_STORE>(a.fmt_lin, pp, a.mat_qkv, nqkv, lo, a.A, cn, a.QKV, nullptr, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(pf_qkv_post, dim3((cn * (nq + 2 * nkv) + 3) / 4), dim3(256), 0, s, pp, l, a.c0, cn, a.QKV);
-    hipLaunchKernelGGL(pf_attention, dim3((cn * nq + 3) / 4), dim3(256), 0, s, pp, l, a.c0, cn, a.QKV, a.A);
+    if (hd == 128)
+      hipLaunchKernelGGL(pf_attention<128>, dim3((cn * nq + 3) / 4), dim3(256), 0, s, pp, l, a.c0, cn, a.QKV, a.A);
+    else if (hd == 64)
+      hipLaunchKernelGGL(pf_attention<64>, dim3((cn * nq + 3) / 4), dim3(256), 0, s, pp, l, a.c0, cn, a.QKV, a.A);
+    else
+      return hipErrorInvalidValue;
     e = gemm<EPI_RESID>(a.fmt_lin, pp, a.mat_o, H, lo, a.A, cn, a.X, nullptr, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(pf_rmsnorm, dim3(cn), dim3(256), 0, s, pp, a.X, cn, H, a.post_norm + lo, a.A);

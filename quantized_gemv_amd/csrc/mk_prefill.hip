@@ -8,7 +8,7 @@
 //
 // Per chunk of positions [c0, c0 + cn):
 //   embed -> per layer: RMSNorm -> QKV GEMM -> q/k RMSNorm, RoPE, KV append ->
-//   causal attention over the cache -> O GEMM + residual -> RMSNorm ->
+//   causal attention over the cache (matrix cores) -> O GEMM + residual -> RMSNorm ->
 //   gate/up GEMM + SwiGLU -> down GEMM + residual
 // then, after the last chunk, the final RMSNorm, the LM head of the last
 // position and its argmax.
@@ -27,6 +27,7 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef float f4v __attribute__((ext_vector_type(4)));
 typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
+typedef short s4v __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int lane() { return (int)(threadIdx.x & 63); }
 __device__ __forceinline__ int wave() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
@@ -271,81 +272,146 @@ __global__ __launch_bounds__(256) void pf_qkv_post(const Params* pp, int l, int 
   }
 }
 
-// -------------------------------------------------------------- attention
-// One wave per (position i of the chunk, q head h): scores against cached
-// positions 0..c0+i in blocks of 64 (one key per lane, q in every lane's
-// registers), online softmax in log2 units, then each lane accumulates its
-// two output dimensions over the block's weights (the block's weights pass
-// through LDS).  Output bf16 into O[i][h*HD ..].
+// --------------------------------------------- attention on the matrix cores
+// x = hi + mid + lo exactly, each a bf16 (bits in the low half): each part
+// rounds what the previous ones left; 3 x 8 significant bits cover fp32.
+__device__ __forceinline__ void split3(float x, uint32_t (&part)[3]) {
+  part[0] = f32_to_bf16(x);
+  const float r1 = x - bf16_to_f32((uint16_t)part[0]);
+  part[1] = f32_to_bf16(r1);
+  part[2] = f32_to_bf16(r1 - bf16_to_f32((uint16_t)part[1]));
+}
+
+// One workgroup per (block of 16 chunk positions, q head); its 4 waves take
+// every 4th block of 16 cached keys and merge their partial softmax states
+// in LDS (fixed order).  Per key block, transposed so that the weights stay
+// in registers:
+//   S^T[16 keys x 16 queries] = K[16 x HD] * Q^T (v_mfma_f32_16x16x32_bf16;
+//     q enters as its three exact bf16 parts, three products per step);
+//   lane l then holds query l%16's scores for keys 4(l/16)..+3: exactly the
+//   B operand of O^T[HD x 16 queries] += V^T[HD x 16 keys] * P^T
+//     (v_mfma_f32_16x16x16_bf16, the weights in three exact parts), whose A
+//     operand is four consecutive keys of one dimension: one 4-position V tile.
 template <int HD>
-__global__ __launch_bounds__(256) void pf_attention(const Params* pp, int l, int c0, int cn, const float* QKV,
-                                                    uint16_t* O) {
+__global__ __launch_bounds__(256) void pf_attention_mc(const Params* pp, int l, int c0, int cn, const float* QKV,
+                                                       uint16_t* O) {
+  constexpr int NKC = HD / 32, NVC = HD / 16;
   const Params& p = *pp;
   const int nq = p.nq, nkv = p.nkv, slots = nq + 2 * nkv;
-  __shared__ float spw[4][64];
-  const int w = wave(), ln = lane();
-  const int idx = blockIdx.x * 4 + w;
-  const bool live = idx < cn * nq;   // wave-uniform
-  const int i = live ? idx / nq : 0, h = idx % nq, pos = c0 + i, g = h / (nq / nkv);
-  const float4* q4 = reinterpret_cast<const float4*>(QKV + (size_t)i * slots * HD + (size_t)h * HD);
-  float4 q[HD / 4];
+  __shared__ float sm[4][16], sl[4][16];
+  __shared__ float so[4][16][HD + 1];
+  const int w = wave(), ln = lane(), r = ln & 15, qg = ln >> 4;
+  const int qb = blockIdx.x / nq, h = blockIdx.x % nq, g = h / (nq / nkv);
+  const int i0 = 16 * qb;
+  const int qi = i0 + r;                       // this lane's query (column)
+  const bool qv = qi < cn;
+  const int pos_q = c0 + min(qi, cn - 1);
+  const int pos_max = c0 + min(i0 + 15, cn - 1);
+  // Q^T operand parts: query r, dims 32c + 8qg .. +7
+  u4 qp[3][NKC];
+  {
+    const float* q = QKV + (size_t)min(qi, cn - 1) * slots * HD + (size_t)h * HD;
 #pragma unroll
-  for (int c = 0; c < HD / 4; ++c) q[c] = q4[c];
+    for (int c = 0; c < NKC; ++c) {
+      uint32_t pr[3][8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint32_t pt[3];
+        split3(q[32 * c + 8 * qg + e], pt);
+        pr[0][e] = pt[0];
+        pr[1][e] = pt[1];
+        pr[2][e] = pt[2];
+      }
+#pragma unroll
+      for (int k = 0; k < 3; ++k)
+        qp[k][c] = u4{pr[k][0] | (pr[k][1] << 16), pr[k][2] | (pr[k][3] << 16), pr[k][4] | (pr[k][5] << 16),
+                      pr[k][6] | (pr[k][7] << 16)};
+    }
+  }
   const size_t plane = kv_plane(p, HD);
   const uint16_t* kc = p.kv + ((size_t)(l * 2 + 0) * nkv + g) * plane;
   const uint16_t* vc = p.kv + ((size_t)(l * 2 + 1) * nkv + g) * plane;
-  float m = -INFINITY, lsum = 0.f, o0 = 0.f, o1 = 0.f;
-  const int e0 = min(2 * ln, HD - 2);
-  const int nblk = live ? pos / 64 + 1 : 0;
-  for (int b = 0; b < nblk; ++b) {
-    const int j = 64 * b + ln;
-    const u4* kr = reinterpret_cast<const u4*>(kc + (size_t)min(j, pos) * HD);
-    float s = 0.f;
+  f4v acc[NVC];
 #pragma unroll
-    for (int c = 0; c < HD / 8; ++c) {
-      const u4 kw = kr[c];
-      const float4 qa = q[2 * c], qb = q[2 * c + 1];
-      s = fmaf(qa.x, bf16_lo(kw.x), s);
-      s = fmaf(qa.y, bf16_hi(kw.x), s);
-      s = fmaf(qa.z, bf16_lo(kw.y), s);
-      s = fmaf(qa.w, bf16_hi(kw.y), s);
-      s = fmaf(qb.x, bf16_lo(kw.z), s);
-      s = fmaf(qb.y, bf16_hi(kw.z), s);
-      s = fmaf(qb.z, bf16_lo(kw.w), s);
-      s = fmaf(qb.w, bf16_hi(kw.w), s);
+  for (int c = 0; c < NVC; ++c) acc[c] = f4v{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, lsum = 0.f;
+  const int nkb = pos_max / 16 + 1;
+  for (int kb = w; kb < nkb; kb += 4) {
+    const int j0 = 16 * kb;
+    f4v d = {0.f, 0.f, 0.f, 0.f};
+    const u4* kr = reinterpret_cast<const u4*>(kc + (size_t)min(j0 + r, pos_max) * HD + 8 * qg);
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) {
+      const bf8v ka = __builtin_bit_cast(bf8v, kr[4 * c]);
+#pragma unroll
+      for (int k = 0; k < 3; ++k) d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, __builtin_bit_cast(bf8v, qp[k][c]), d, 0, 0, 0);
     }
-    s = j <= pos ? s : -INFINITY;
-    const float mn = fmaxf(m, wmax(s));
+    float sc[4];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = j0 + 4 * qg + i;
+      sc[i] = qv && j <= pos_q ? d[i] : -INFINITY;
+      bm = fmaxf(bm, sc[i]);
+    }
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float mn = fmaxf(m, bm);
     const float scale = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
-    const float pw = s == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s - mn);
     m = mn;
-    lsum = lsum * scale + wsum(pw);
-    o0 *= scale;
-    o1 *= scale;
-    spw[w][ln] = pw;
-    __builtin_amdgcn_wave_barrier();
-    // four positions of one dimension per 8-byte load (the V tile); weights
-    // past pos are 0 and the tile slots past it hold finite values
-    const int jn = min(64, pos + 1 - 64 * b);
-    for (int jq = 0; jq < jn; jq += 4) {
-      const size_t tile = (size_t)((64 * b + jq) >> 2);
-      const u2 d0 = *reinterpret_cast<const u2*>(vc + (tile * HD + e0) * 4);
-      const u2 d1 = *reinterpret_cast<const u2*>(vc + (tile * HD + e0 + 1) * 4);
-      const float* pj = &spw[w][jq];
-      o0 = fmaf(pj[0], bf16_lo(d0.x), o0);
-      o0 = fmaf(pj[1], bf16_hi(d0.x), o0);
-      o0 = fmaf(pj[2], bf16_lo(d0.y), o0);
-      o0 = fmaf(pj[3], bf16_hi(d0.y), o0);
-      o1 = fmaf(pj[0], bf16_lo(d1.x), o1);
-      o1 = fmaf(pj[1], bf16_hi(d1.x), o1);
-      o1 = fmaf(pj[2], bf16_lo(d1.y), o1);
-      o1 = fmaf(pj[3], bf16_hi(d1.y), o1);
+    lsum *= scale;
+#pragma unroll
+    for (int c = 0; c < NVC; ++c) acc[c] *= scale;
+    uint32_t pp3[3][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pv = sc[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[i] - mn);
+      lsum += pv;
+      uint32_t pt[3];
+      split3(pv, pt);
+      pp3[0][i] = pt[0];
+      pp3[1][i] = pt[1];
+      pp3[2][i] = pt[2];
     }
-    __builtin_amdgcn_wave_barrier();
+    const int t = min((j0 >> 2) + qg, pos_max >> 2);
+#pragma unroll
+    for (int c = 0; c < NVC; ++c) {
+      const u2 va = *reinterpret_cast<const u2*>(vc + ((size_t)t * HD + 16 * c + r) * 4);
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const u2 pb = {pp3[k][0] | (pp3[k][1] << 16), pp3[k][2] | (pp3[k][3] << 16)};
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4v, va), __builtin_bit_cast(s4v, pb),
+                                                           acc[c], 0, 0, 0);
+      }
+    }
   }
-  if (live && 2 * ln < HD) {
-    const uint32_t pr = pack_bf16(o0 / lsum, o1 / lsum);
-    *reinterpret_cast<uint32_t*>(O + (size_t)i * nq * HD + (size_t)h * HD + 2 * ln) = pr;
+  // the query's sum over the four lane groups
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  if (qg == 0) {
+    sm[w][r] = m;
+    sl[w][r] = lsum;
+  }
+  // acc: lane l holds O^T rows (dims) 16c + 4(l/16) + i of column (query) l%16
+#pragma unroll
+  for (int c = 0; c < NVC; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) so[w][r][16 * c + 4 * qg + i] = acc[c][i];
+  __syncthreads();
+  for (int e = threadIdx.x; e < 16 * HD; e += 256) {
+    const int qr = e / HD, dd = e % HD;
+    if (i0 + qr >= cn) continue;
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) M = fmaxf(M, sm[v][qr]);
+    float L = 0.f, acc_o = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float wgt = sm[v][qr] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm[v][qr] - M);
+      L = fmaf(sl[v][qr], wgt, L);
+      acc_o = fmaf(so[v][qr][dd], wgt, acc_o);
+    }
+    O[(size_t)(i0 + qr) * nq * HD + (size_t)h * HD + dd] = (uint16_t)f32_to_bf16(acc_o / L);
   }
 }
 
@@ -437,10 +503,11 @@ hipError_t launch_prefill_chunk(const PrefillArgs& a, hipStream_t s) {
     hipError_t e = gemm<EPI_STORE>(a.fmt_lin, pp, a.mat_qkv, nqkv, lo, a.A, cn, a.QKV, nullptr, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(pf_qkv_post, dim3((cn * (nq + 2 * nkv) + 3) / 4), dim3(256), 0, s, pp, l, a.c0, cn, a.QKV);
+    const dim3 ga(((cn + 15) / 16) * nq);
     if (hd == 128)
-      hipLaunchKernelGGL(pf_attention<128>, dim3((cn * nq + 3) / 4), dim3(256), 0, s, pp, l, a.c0, cn, a.QKV, a.A);
+      hipLaunchKernelGGL(pf_attention_mc<128>, ga, dim3(256), 0, s, pp, l, a.c0, cn, a.QKV, a.A);
     else if (hd == 64)
-      hipLaunchKernelGGL(pf_attention<64>, dim3((cn * nq + 3) / 4), dim3(256), 0, s, pp, l, a.c0, cn, a.QKV, a.A);
+      hipLaunchKernelGGL(pf_attention_mc<64>, ga, dim3(256), 0, s, pp, l, a.c0, cn, a.QKV, a.A);
     else
       return hipErrorInvalidValue;
     e = gemm<EPI_RESID>(a.fmt_lin, pp, a.mat_o, H, lo, a.A, cn, a.X, nullptr, s);

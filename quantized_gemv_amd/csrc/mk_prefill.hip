@@ -14,6 +14,8 @@
 // position and its argmax.
 #include <hip/hip_runtime.h>
 #include <math.h>
+
+#include <algorithm>
 #include <stdint.h>
 
 #include "mk_codec.h"
@@ -105,7 +107,7 @@ __global__ __launch_bounds__(256) void pf_rmsnorm(const Params* pp, const float*
 // (w&1, w>>1) as 2 x 2 v_mfma_f32_16x16x32_bf16 tiles; K in steps of 32
 // through LDS.  Epilogues: store C (fp32), add C into the residual X, or
 // SwiGLU over interleaved (gate, up) column pairs into bf16 H.
-enum : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+enum : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_PARTIAL = 3 };
 constexpr int BK = 32, LDA = BK + 8;
 
 template <uint32_t FMT>
@@ -172,7 +174,9 @@ __global__ __launch_bounds__(256) void pf_gemm(const Params* pp, const Mat* mat,
 #pragma unroll
     for (int b = 0; b < NT; ++b) acc[a][b] = f4v{0.f, 0.f, 0.f, 0.f};
   const int wr = (T / 2) * (w & 1), wc = (T / 2) * (w >> 1);
-  for (int k0 = 0; k0 < K; k0 += BK) {
+  // split K (EPI_PARTIAL): workgroup z sums K range [z*K/Z, (z+1)*K/Z)
+  const int kz = K / (int)gridDim.z, kbeg = (int)blockIdx.z * kz;
+  for (int k0 = kbeg; k0 < kbeg + kz; k0 += BK) {
     const u4 av = *reinterpret_cast<const u4*>(A + (size_t)am * K + k0 + sk);
     const u4 wv = load_w8<FMT>(rw, m, lo, wn, k0 + sk);
     __syncthreads();   // the previous step's operands are consumed
@@ -217,6 +221,7 @@ __global__ __launch_bounds__(256) void pf_gemm(const Params* pp, const Mat* mat,
       const int gm = m0 + r, gn = n0 + c;
       if (gm < M && gn < N) {
         if (EPI == EPI_STORE) C[(size_t)gm * N + gn] = sc[r][c];
+        else if (EPI == EPI_PARTIAL) C[((size_t)blockIdx.z * M + gm) * N + gn] = sc[r][c];
         else C[(size_t)gm * N + gn] += sc[r][c];
       }
     }
@@ -472,22 +477,47 @@ __global__ void pf_argmax(const float* best_v, const int32_t* best_i, int n, int
   *out = bi;
 }
 
+// X[i] += P[0][i] + P[1][i] + ... (the split-K partials, in order)
+__global__ __launch_bounds__(256) void pf_add_partials(const float* P, int nz, size_t n, float* X) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    float v = P[i];
+    for (int z = 1; z < nz; ++z) v += P[(size_t)z * n + i];
+    X[i] += v;
+  }
+}
+
 template <int EPI, int T>
 hipError_t gemm_t(uint32_t fmt, const Params* pp, const Mat* mat, int N, uint64_t lo, const uint16_t* A, int M, float* C,
-                  uint16_t* Hout, hipStream_t s) {
-  const dim3 grid((N + T - 1) / T, (M + T - 1) / T);
+                  uint16_t* Hout, hipStream_t s, int nz = 1) {
+  const dim3 grid((N + T - 1) / T, (M + T - 1) / T, nz);
   if (fmt == FMT_BF16) hipLaunchKernelGGL((pf_gemm<FMT_BF16, EPI, T>), grid, dim3(256), 0, s, pp, mat, lo, A, M, C, Hout);
   else if (fmt == FMT_FP8) hipLaunchKernelGGL((pf_gemm<FMT_FP8, EPI, T>), grid, dim3(256), 0, s, pp, mat, lo, A, M, C, Hout);
   else hipLaunchKernelGGL((pf_gemm<FMT_FP4, EPI, T>), grid, dim3(256), 0, s, pp, mat, lo, A, M, C, Hout);
   return hipGetLastError();
 }
 // 64 x 64 tiles where they give at least one workgroup per compute unit, else
-// 32 x 32 (the N = hidden products of a chunk)
+// 32 x 32
 template <int EPI>
 hipError_t gemm(uint32_t fmt, const Params* pp, const Mat* mat, int N, uint64_t lo, const uint16_t* A, int M, float* C,
                 uint16_t* Hout, hipStream_t s) {
   if ((long)((N + 63) / 64) * ((M + 63) / 64) >= 256) return gemm_t<EPI, 64>(fmt, pp, mat, N, lo, A, M, C, Hout, s);
   return gemm_t<EPI, 32>(fmt, pp, mat, N, lo, A, M, C, Hout, s);
+}
+// A product added into the residual X [M x N].  Where 64 x 64 tiles leave
+// compute units idle, K is split over nz workgroups (nz <= 4, partials in
+// `ws`, which holds ws_floats) and the partials are added in a fixed order.
+hipError_t gemm_resid(uint32_t fmt, const Params* pp, const Mat* mat, int N, int K, uint64_t lo, const uint16_t* A, int M,
+                      float* X, float* ws, size_t ws_floats, hipStream_t s) {
+  const long tiles = (long)((N + 63) / 64) * ((M + 63) / 64);
+  int nz = 1;
+  while (nz < 4 && tiles * nz * 2 <= 256 && (K / (2 * nz)) % BK == 0 && (size_t)2 * nz * M * N <= ws_floats) nz *= 2;
+  if (nz == 1) return gemm<EPI_RESID>(fmt, pp, mat, N, lo, A, M, X, nullptr, s);
+  hipError_t e = gemm_t<EPI_PARTIAL, 64>(fmt, pp, mat, N, lo, A, M, ws, nullptr, s, nz);
+  if (e != hipSuccess) return e;
+  const size_t n = (size_t)M * N;
+  hipLaunchKernelGGL(pf_add_partials, dim3((unsigned)std::min<size_t>((n + 255) / 256, 1024)), dim3(256), 0, s, ws, nz, n,
+                     X);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -510,12 +540,14 @@ hipError_t launch_prefill_chunk(const PrefillArgs& a, hipStream_t s) {
       hipLaunchKernelGGL(pf_attention_mc<64>, ga, dim3(256), 0, s, pp, l, a.c0, cn, a.QKV, a.A);
     else
       return hipErrorInvalidValue;
-    e = gemm<EPI_RESID>(a.fmt_lin, pp, a.mat_o, H, lo, a.A, cn, a.X, nullptr, s);
+    // the QKV outputs are used up: their buffer holds the split-K partials
+    const size_t ws = (size_t)kPrefillChunk * nqkv;
+    e = gemm_resid(a.fmt_lin, pp, a.mat_o, H, nq * hd, lo, a.A, cn, a.X, a.QKV, ws, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(pf_rmsnorm, dim3(cn), dim3(256), 0, s, pp, a.X, cn, H, a.post_norm + lo, a.A);
     e = gemm<EPI_SWIGLU>(a.fmt_lin, pp, a.mat_gu, 2 * I, lo, a.A, cn, nullptr, a.Hb, s);
     if (e != hipSuccess) return e;
-    e = gemm<EPI_RESID>(a.fmt_down, pp, a.mat_down, H, lo, a.Hb, cn, a.X, nullptr, s);
+    e = gemm_resid(a.fmt_down, pp, a.mat_down, H, I, lo, a.Hb, cn, a.X, a.QKV, ws, s);
     if (e != hipSuccess) return e;
   }
   if (a.last) {

@@ -239,8 +239,8 @@ int mk_decode_codes(int32_t codec, const uint8_t* d_codes, int32_t n, float* d_o
  * matrix products on the matrix cores (bf16 operands, fp32 accumulation,
  * weights dequantized exactly), with the decode path's rounding points; it
  * writes the same KV cache up to summation order.  1 needs hidden,
- * intermediate and n_q_heads*head_dim divisible by 32, hidden <= 4096 and
- * head_dim <= 256 and a multiple of 8 (else MK_E_UNSUPPORTED).
+ * intermediate and n_q_heads*head_dim divisible by 64, hidden <= 4096 and
+ * head_dim 64 or 128 (else MK_E_UNSUPPORTED).
  * Keys 1 and 2 are reserved.
  * Errors: MK_E_INVALID (unknown key, value out of range), MK_E_STATE. */
 int mk_set_option(mk_model* m, int32_t key, int64_t value);

@@ -176,11 +176,12 @@ PfLayout prefill_layout(const mk_config& c) {
   return L;
 }
 size_t prefill_workspace(const mk_config& c) { return prefill_layout(c).total; }
-// The batched prefill's kernels assume K % 32 == 0 for every matrix (the
-// GEMM's K step), hidden <= 4096 (the LM head's LDS row) and an even head_dim.
+// The batched prefill's kernels assume K % 64 == 0 for every matrix (the
+// GEMM's K stage), hidden <= 4096 (the LM head's LDS row) and head_dim 64 or
+// 128 (the attention's instantiations).
 bool prefill_supported(const mk_config& c) {
   const int H = c.hidden, I = c.intermediate, q = c.n_q_heads * c.head_dim;
-  return H % 32 == 0 && I % 32 == 0 && q % 32 == 0 && H <= 4096 && c.head_dim % 8 == 0 && c.head_dim <= 256;
+  return H % 64 == 0 && I % 64 == 0 && q % 64 == 0 && H <= 4096 && (c.head_dim == 64 || c.head_dim == 128);
 }
 
 // Lay out the scratch buffer: per-layer exchange vectors, argmax words, the

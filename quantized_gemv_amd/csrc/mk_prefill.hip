@@ -153,18 +153,21 @@ __device__ __forceinline__ float col_scale(__amdgpu_buffer_rsrc_t rw, const Mat&
 template <uint32_t FMT, int EPI, int T>
 __global__ __launch_bounds__(256) void pf_gemm(const Params* pp, const Mat* mat, uint64_t lo, const uint16_t* A, int M,
                                                float* C, uint16_t* Hout) {
-  // T x T tile: each wave owns a (T/2) x (T/2) quarter of (T/32)^2 MFMA tiles
-  constexpr int NT = T / 32;
+  // T x T tile: each wave owns a (T/2) x (T/2) quarter of (T/32)^2 MFMA
+  // tiles.  K advances by KS = 2 * BK per LDS stage, two buffers: the next
+  // stage's operands are loaded into registers while the current one is
+  // multiplied, so one barrier per stage.
+  constexpr int NT = T / 32, KS = 2 * BK, LDK = KS + 8;
   const Params& p = *pp;
   const Mat m = *mat;
   const int N = (int)m.N, K = (int)m.K;
-  __shared__ __attribute__((aligned(16))) uint16_t sa[T][LDA];
-  __shared__ __attribute__((aligned(16))) uint16_t sw[T][LDA];
+  __shared__ __attribute__((aligned(16))) uint16_t sa[2][T][LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t sw[2][T][LDK];
   __shared__ float sc[T][T + 1];
   const int m0 = blockIdx.y * T, n0 = blockIdx.x * T;
   const int t = threadIdx.x, w = wave(), l = lane();
   const __amdgpu_buffer_rsrc_t rw = arena(p);
-  // the 8-element pieces thread t < 4T stages: row t/4, columns 8*(t%4)
+  // thread t < 4T stages row t/4, columns 8*(t%4) and 32 + 8*(t%4) of a stage
   const bool stager = t < 4 * T;
   const int sr = min(t >> 2, T - 1), sk = 8 * (t & 3);
   const int am = min(m0 + sr, M - 1), wn = min(n0 + sr, N - 1);
@@ -174,27 +177,51 @@ __global__ __launch_bounds__(256) void pf_gemm(const Params* pp, const Mat* mat,
 #pragma unroll
     for (int b = 0; b < NT; ++b) acc[a][b] = f4v{0.f, 0.f, 0.f, 0.f};
   const int wr = (T / 2) * (w & 1), wc = (T / 2) * (w >> 1);
-  // split K (EPI_PARTIAL): workgroup z sums K range [z*K/Z, (z+1)*K/Z)
-  const int kz = K / (int)gridDim.z, kbeg = (int)blockIdx.z * kz;
-  for (int k0 = kbeg; k0 < kbeg + kz; k0 += BK) {
-    const u4 av = *reinterpret_cast<const u4*>(A + (size_t)am * K + k0 + sk);
-    const u4 wv = load_w8<FMT>(rw, m, lo, wn, k0 + sk);
-    __syncthreads();   // the previous step's operands are consumed
-    if (stager) {
-      *reinterpret_cast<u4*>(&sa[sr][sk]) = av;
-      *reinterpret_cast<u4*>(&sw[sr][sk]) = wv;
+  // split K (EPI_PARTIAL): workgroup z sums K range [z*K/Z, (z+1)*K/Z); the
+  // range is a multiple of KS (host)
+  const int kz = K / (int)gridDim.z, kbeg = (int)blockIdx.z * kz, nst = kz / KS;
+  const uint16_t* arow = A + (size_t)am * K;
+  u4 av0 = *reinterpret_cast<const u4*>(arow + kbeg + sk);
+  u4 av1 = *reinterpret_cast<const u4*>(arow + kbeg + BK + sk);
+  u4 wv0 = load_w8<FMT>(rw, m, lo, wn, kbeg + sk);
+  u4 wv1 = load_w8<FMT>(rw, m, lo, wn, kbeg + BK + sk);
+  if (stager) {
+    *reinterpret_cast<u4*>(&sa[0][sr][sk]) = av0;
+    *reinterpret_cast<u4*>(&sa[0][sr][BK + sk]) = av1;
+    *reinterpret_cast<u4*>(&sw[0][sr][sk]) = wv0;
+    *reinterpret_cast<u4*>(&sw[0][sr][BK + sk]) = wv1;
+  }
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int cur = st & 1;
+    const bool more = st + 1 < nst;   // uniform
+    if (more) {
+      const int k1 = kbeg + (st + 1) * KS;
+      av0 = *reinterpret_cast<const u4*>(arow + k1 + sk);
+      av1 = *reinterpret_cast<const u4*>(arow + k1 + BK + sk);
+      wv0 = load_w8<FMT>(rw, m, lo, wn, k1 + sk);
+      wv1 = load_w8<FMT>(rw, m, lo, wn, k1 + BK + sk);
     }
-    __syncthreads();
 #pragma unroll
-    for (int a = 0; a < NT; ++a) {
-      const u4 ao = *reinterpret_cast<const u4*>(&sa[wr + 16 * a + (l & 15)][8 * (l >> 4)]);
+    for (int kk = 0; kk < KS; kk += BK) {
 #pragma unroll
-      for (int b = 0; b < NT; ++b) {
-        const u4 bo = *reinterpret_cast<const u4*>(&sw[wc + 16 * b + (l & 15)][8 * (l >> 4)]);
-        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, ao), __builtin_bit_cast(bf8v, bo),
-                                                            acc[a][b], 0, 0, 0);
+      for (int a = 0; a < NT; ++a) {
+        const u4 ao = *reinterpret_cast<const u4*>(&sa[cur][wr + 16 * a + (l & 15)][kk + 8 * (l >> 4)]);
+#pragma unroll
+        for (int b = 0; b < NT; ++b) {
+          const u4 bo = *reinterpret_cast<const u4*>(&sw[cur][wc + 16 * b + (l & 15)][kk + 8 * (l >> 4)]);
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, ao), __builtin_bit_cast(bf8v, bo),
+                                                              acc[a][b], 0, 0, 0);
+        }
       }
     }
+    if (more && stager) {
+      *reinterpret_cast<u4*>(&sa[cur ^ 1][sr][sk]) = av0;
+      *reinterpret_cast<u4*>(&sa[cur ^ 1][sr][BK + sk]) = av1;
+      *reinterpret_cast<u4*>(&sw[cur ^ 1][sr][sk]) = wv0;
+      *reinterpret_cast<u4*>(&sw[cur ^ 1][sr][BK + sk]) = wv1;
+    }
+    __syncthreads();
   }
   // D: lane l holds rows 4(l/16)+i of column l%16 of each 16 x 16 tile
 #pragma unroll
@@ -510,7 +537,7 @@ hipError_t gemm_resid(uint32_t fmt, const Params* pp, const Mat* mat, int N, int
                       float* X, float* ws, size_t ws_floats, hipStream_t s) {
   const long tiles = (long)((N + 63) / 64) * ((M + 63) / 64);
   int nz = 1;
-  while (nz < 4 && tiles * nz * 2 <= 256 && (K / (2 * nz)) % BK == 0 && (size_t)2 * nz * M * N <= ws_floats) nz *= 2;
+  while (nz < 4 && tiles * nz * 2 <= 256 && (K / (2 * nz)) % (2 * BK) == 0 && (size_t)2 * nz * M * N <= ws_floats) nz *= 2;
   if (nz == 1) return gemm<EPI_RESID>(fmt, pp, mat, N, lo, A, M, X, nullptr, s);
   hipError_t e = gemm_t<EPI_PARTIAL, 64>(fmt, pp, mat, N, lo, A, M, ws, nullptr, s, nz);
   if (e != hipSuccess) return e;

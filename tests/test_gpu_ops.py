@@ -120,6 +120,28 @@ def test_ops_tiny_split_attention(native, tiny_master, wfmt, chunk, positions):
     d.close()
 
 
+@pytest.mark.parametrize("split", [0, 16])
+def test_ops_tiny_block_boundaries(native, tiny_master, split):
+    """Every output of every layer at the positions where the attention's
+    block structure changes: position 0 (no cached position), the ends of the
+    first 16-position block and of the first pass of 7 blocks (112), the end
+    of the held range (448 = 4 passes) and the first streamed pass; with the
+    home workgroup alone and with helpers taking slices of 16 (split attention
+    from position 0, slice boundaries inside blocks)."""
+    sh = synth.TINY
+    positions = (0, 1, 15, 16, 17, 111, 112, 113, 447, 448, 449)
+    n = positions[-1] + 1
+    toks = synth.make_prompt(sh.vocab, n, 18)
+    d = _decoder(native, sh, tiny_master, synth.FP8_ROW, n + 3, split_chunk=split, split_from=0)
+    W = Weights(tiny_master, synth.FP8_ROW)
+    for pos in range(n):
+        logits = _step(d, sh, int(toks[pos]), pos)
+        if pos in positions:
+            check_step(GpuStep(d, sh), W, sh, int(toks[pos]), pos, logits, range(sh.n_layers),
+                       np.random.default_rng(pos))
+    d.close()
+
+
 def test_split_attention_deterministic(native, tiny_master):
     """The split path's merge order is fixed: two runs, identical bits."""
     sh = synth.TINY

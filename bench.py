@@ -162,7 +162,7 @@ def cpu_baseline(master, wl, n_steps, prompt, budget_s):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (one model replica per GPU; no multi-GPU path); "
+        print("bench.py: this benchmark runs on one GPU only (one model replica per GPU; no multi-GPU path); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import numpy as np

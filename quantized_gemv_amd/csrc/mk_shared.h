@@ -119,7 +119,8 @@ enum : int { S_QKV = 0, S_O = 4, S_GU = 8, S_D = 12, S_QKVW = 16, kUnitInts = 20
 struct Params {
   MK_GLOBAL const uint8_t* w;   // weight arena
   uint32_t w_bytes;             // its size (read through a buffer resource: below 2 GB)
-  MK_GLOBAL uint16_t* kv;       // [L][2][nkv][max_ctx][hd] bf16
+  MK_GLOBAL uint16_t* kv;       // per layer K then V, per KV head a plane of ctx4 x hd bf16 (ctx4 = max_ctx
+                                // rounded up to 4): K row-major, V in tiles of 4 positions
   MK_GLOBAL const float* rope;  // [max_ctx][hd/2][2] cos, sin
   MK_GLOBAL uint64_t* xch;      // scratch
   void* trace;                  // mk_trace_rec records, or null

@@ -8,8 +8,8 @@ that size to what the counter reads for it scales the decode kernel's
 readings.  The timed launches are the last `steps` decode dispatches.
 
     python -m quantized_gemv_amd.traffic --workload qwen3_0p6b_bf16 --steps 256 \\
-        --fetch gpurun_out/pmc_fetch/run_counter_collection.csv \\
-        --write gpurun_out/pmc_write/run_counter_collection.csv \\
+        --fetch <fetch run dir>/run_counter_collection.csv \\
+        --write <write run dir>/run_counter_collection.csv \\
         --out profiles/decode_kernel_traffic.json
 """
 from __future__ import annotations

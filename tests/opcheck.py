@@ -14,7 +14,7 @@ accumulated over the layers before it, so the tolerances are tight:
   rounding), the K row within one bf16 step (norm and rotation in another
   order).
 
-tests/test_opcheck.py pins the checker on the CPU (it accepts the oracle's
+tests/test_opcheck.py pins these comparisons on the CPU (it accepts the oracle's
 own intermediates and rejects planted mistakes); tests/test_gpu_ops.py
 applies it to the GPU.
 """

@@ -154,9 +154,9 @@ template <uint32_t FMT, int EPI, int T>
 __global__ __launch_bounds__(256) void pf_gemm(const Params* pp, const Mat* mat, uint64_t lo, const uint16_t* A, int M,
                                                float* C, uint16_t* Hout) {
   // T x T tile: each wave owns a (T/2) x (T/2) quarter of (T/32)^2 MFMA
-  // tiles.  K advances by KS = 2 * BK per LDS stage, two buffers: the next
-  // stage's operands are loaded into registers while the current one is
-  // multiplied, so one barrier per stage.
+  // tiles.  K advances by KS = 2 * BK per stage: two LDS buffers (one
+  // barrier per stage) fed from three stages of operands in registers, so
+  // global loads are issued three stages ahead of their use.
   constexpr int NT = T / 32, KS = 2 * BK, LDK = KS + 8;
   const Params& p = *pp;
   const Mat m = *mat;
@@ -181,47 +181,61 @@ __global__ __launch_bounds__(256) void pf_gemm(const Params* pp, const Mat* mat,
   // range is a multiple of KS (host)
   const int kz = K / (int)gridDim.z, kbeg = (int)blockIdx.z * kz, nst = kz / KS;
   const uint16_t* arow = A + (size_t)am * K;
-  u4 av0 = *reinterpret_cast<const u4*>(arow + kbeg + sk);
-  u4 av1 = *reinterpret_cast<const u4*>(arow + kbeg + BK + sk);
-  u4 wv0 = load_w8<FMT>(rw, m, lo, wn, kbeg + sk);
-  u4 wv1 = load_w8<FMT>(rw, m, lo, wn, kbeg + BK + sk);
-  if (stager) {
-    *reinterpret_cast<u4*>(&sa[0][sr][sk]) = av0;
-    *reinterpret_cast<u4*>(&sa[0][sr][BK + sk]) = av1;
-    *reinterpret_cast<u4*>(&sw[0][sr][sk]) = wv0;
-    *reinterpret_cast<u4*>(&sw[0][sr][BK + sk]) = wv1;
-  }
-  __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    const int cur = st & 1;
-    const bool more = st + 1 < nst;   // uniform
-    if (more) {
-      const int k1 = kbeg + (st + 1) * KS;
-      av0 = *reinterpret_cast<const u4*>(arow + k1 + sk);
-      av1 = *reinterpret_cast<const u4*>(arow + k1 + BK + sk);
-      wv0 = load_w8<FMT>(rw, m, lo, wn, k1 + sk);
-      wv1 = load_w8<FMT>(rw, m, lo, wn, k1 + BK + sk);
+  // stage operands in registers, three stages in flight (a ring of three,
+  // the loop unrolled by three so every index is static)
+  struct Stage {
+    u4 a0, a1, w0, w1;
+  };
+  auto load = [&](int stg, Stage& r) {
+    const int k = kbeg + stg * KS;
+    r.a0 = *reinterpret_cast<const u4*>(arow + k + sk);
+    r.a1 = *reinterpret_cast<const u4*>(arow + k + BK + sk);
+    r.w0 = load_w8<FMT>(rw, m, lo, wn, k + sk);
+    r.w1 = load_w8<FMT>(rw, m, lo, wn, k + BK + sk);
+  };
+  auto put = [&](const Stage& r, int buf) {
+    if (stager) {
+      *reinterpret_cast<u4*>(&sa[buf][sr][sk]) = r.a0;
+      *reinterpret_cast<u4*>(&sa[buf][sr][BK + sk]) = r.a1;
+      *reinterpret_cast<u4*>(&sw[buf][sr][sk]) = r.w0;
+      *reinterpret_cast<u4*>(&sw[buf][sr][BK + sk]) = r.w1;
     }
+  };
+  auto mul = [&](int buf) {
 #pragma unroll
     for (int kk = 0; kk < KS; kk += BK) {
 #pragma unroll
       for (int a = 0; a < NT; ++a) {
-        const u4 ao = *reinterpret_cast<const u4*>(&sa[cur][wr + 16 * a + (l & 15)][kk + 8 * (l >> 4)]);
+        const u4 ao = *reinterpret_cast<const u4*>(&sa[buf][wr + 16 * a + (l & 15)][kk + 8 * (l >> 4)]);
 #pragma unroll
         for (int b = 0; b < NT; ++b) {
-          const u4 bo = *reinterpret_cast<const u4*>(&sw[cur][wc + 16 * b + (l & 15)][kk + 8 * (l >> 4)]);
+          const u4 bo = *reinterpret_cast<const u4*>(&sw[buf][wc + 16 * b + (l & 15)][kk + 8 * (l >> 4)]);
           acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, ao), __builtin_bit_cast(bf8v, bo),
                                                               acc[a][b], 0, 0, 0);
         }
       }
     }
-    if (more && stager) {
-      *reinterpret_cast<u4*>(&sa[cur ^ 1][sr][sk]) = av0;
-      *reinterpret_cast<u4*>(&sa[cur ^ 1][sr][BK + sk]) = av1;
-      *reinterpret_cast<u4*>(&sw[cur ^ 1][sr][sk]) = wv0;
-      *reinterpret_cast<u4*>(&sw[cur ^ 1][sr][BK + sk]) = wv1;
+  };
+  // step s: multiply stage s (LDS buffer s&1), move stage s+1 (registers,
+  // ring slot (s+1)%3) to the other buffer, load stage s+3 into slot s%3
+  auto step = [&](int st, Stage& nxt, Stage& freed) {
+    if (st < nst) {   // uniform
+      mul(st & 1);
+      if (st + 1 < nst) put(nxt, (st + 1) & 1);
+      if (st + 3 < nst) load(st + 3, freed);
+      __syncthreads();
     }
-    __syncthreads();
+  };
+  Stage r0, r1, r2;
+  load(0, r0);
+  if (nst > 1) load(1, r1);
+  if (nst > 2) load(2, r2);
+  put(r0, 0);
+  __syncthreads();
+  for (int st = 0; st < nst; st += 3) {
+    step(st, r1, r0);
+    step(st + 1, r2, r1);
+    step(st + 2, r0, r2);
   }
   // D: lane l holds rows 4(l/16)+i of column l%16 of each 16 x 16 tile
 #pragma unroll

@@ -158,19 +158,30 @@ __global__ __launch_bounds__(256) void pf_gemm(const Params* pp, const Mat* mat,
   // barrier per stage) fed from three stages of operands in registers, so
   // global loads are issued three stages ahead of their use.
   constexpr int NT = T / 32, KS = 2 * BK, LDK = KS + 8;
+  constexpr int RP = T >= 64 ? T / 64 : 1;   // rows a thread stages
+  constexpr int OPB = 2 * 2 * T * LDK * 2, EPB = T * (T + 1) * 4;
   const Params& p = *pp;
   const Mat m = *mat;
   const int N = (int)m.N, K = (int)m.K;
-  __shared__ __attribute__((aligned(16))) uint16_t sa[2][T][LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t sw[2][T][LDK];
-  __shared__ float sc[T][T + 1];
+  // the operand buffers (two stages of A and W) and, after the main loop,
+  // the fp32 tile for the epilogue share one LDS block
+  __shared__ __attribute__((aligned(16))) uint8_t smem[OPB > EPB ? OPB : EPB];
+  uint16_t(*sa)[T][LDK] = reinterpret_cast<uint16_t(*)[T][LDK]>(smem);
+  uint16_t(*sw)[T][LDK] = sa + 2;
+  float(*sc)[T + 1] = reinterpret_cast<float(*)[T + 1]>(smem);
   const int m0 = blockIdx.y * T, n0 = blockIdx.x * T;
   const int t = threadIdx.x, w = wave(), l = lane();
   const __amdgpu_buffer_rsrc_t rw = arena(p);
-  // thread t < 4T stages row t/4, columns 8*(t%4) and 32 + 8*(t%4) of a stage
+  // thread t < 4T stages rows t/4 + 64i, columns 8*(t%4) and 32 + 8*(t%4) of a stage
   const bool stager = t < 4 * T;
-  const int sr = min(t >> 2, T - 1), sk = 8 * (t & 3);
-  const int am = min(m0 + sr, M - 1), wn = min(n0 + sr, N - 1);
+  const int sk = 8 * (t & 3);
+  int srw[RP], am[RP], wn[RP];
+#pragma unroll
+  for (int i = 0; i < RP; ++i) {
+    srw[i] = min((t >> 2) + 64 * i, T - 1);
+    am[i] = min(m0 + srw[i], M - 1);
+    wn[i] = min(n0 + srw[i], N - 1);
+  }
   f4v acc[NT][NT];
 #pragma unroll
   for (int a = 0; a < NT; ++a)
@@ -180,25 +191,31 @@ __global__ __launch_bounds__(256) void pf_gemm(const Params* pp, const Mat* mat,
   // split K (EPI_PARTIAL): workgroup z sums K range [z*K/Z, (z+1)*K/Z); the
   // range is a multiple of KS (host)
   const int kz = K / (int)gridDim.z, kbeg = (int)blockIdx.z * kz, nst = kz / KS;
-  const uint16_t* arow = A + (size_t)am * K;
   // stage operands in registers, three stages in flight (a ring of three,
   // the loop unrolled by three so every index is static)
   struct Stage {
-    u4 a0, a1, w0, w1;
+    u4 a0[RP], a1[RP], w0[RP], w1[RP];
   };
   auto load = [&](int stg, Stage& r) {
     const int k = kbeg + stg * KS;
-    r.a0 = *reinterpret_cast<const u4*>(arow + k + sk);
-    r.a1 = *reinterpret_cast<const u4*>(arow + k + BK + sk);
-    r.w0 = load_w8<FMT>(rw, m, lo, wn, k + sk);
-    r.w1 = load_w8<FMT>(rw, m, lo, wn, k + BK + sk);
+#pragma unroll
+    for (int i = 0; i < RP; ++i) {
+      const uint16_t* arow = A + (size_t)am[i] * K;
+      r.a0[i] = *reinterpret_cast<const u4*>(arow + k + sk);
+      r.a1[i] = *reinterpret_cast<const u4*>(arow + k + BK + sk);
+      r.w0[i] = load_w8<FMT>(rw, m, lo, wn[i], k + sk);
+      r.w1[i] = load_w8<FMT>(rw, m, lo, wn[i], k + BK + sk);
+    }
   };
   auto put = [&](const Stage& r, int buf) {
     if (stager) {
-      *reinterpret_cast<u4*>(&sa[buf][sr][sk]) = r.a0;
-      *reinterpret_cast<u4*>(&sa[buf][sr][BK + sk]) = r.a1;
-      *reinterpret_cast<u4*>(&sw[buf][sr][sk]) = r.w0;
-      *reinterpret_cast<u4*>(&sw[buf][sr][BK + sk]) = r.w1;
+#pragma unroll
+      for (int i = 0; i < RP; ++i) {
+        *reinterpret_cast<u4*>(&sa[buf][srw[i]][sk]) = r.a0[i];
+        *reinterpret_cast<u4*>(&sa[buf][srw[i]][BK + sk]) = r.a1[i];
+        *reinterpret_cast<u4*>(&sw[buf][srw[i]][sk]) = r.w0[i];
+        *reinterpret_cast<u4*>(&sw[buf][srw[i]][BK + sk]) = r.w1[i];
+      }
     }
   };
   auto mul = [&](int buf) {
@@ -541,24 +558,34 @@ hipError_t gemm_t(uint32_t fmt, const Params* pp, const Mat* mat, int N, uint64_
 template <int EPI>
 hipError_t gemm(uint32_t fmt, const Params* pp, const Mat* mat, int N, uint64_t lo, const uint16_t* A, int M, float* C,
                 uint16_t* Hout, hipStream_t s) {
+  if ((long)((N + 127) / 128) * ((M + 127) / 128) >= 256) return gemm_t<EPI, 128>(fmt, pp, mat, N, lo, A, M, C, Hout, s);
   if ((long)((N + 63) / 64) * ((M + 63) / 64) >= 256) return gemm_t<EPI, 64>(fmt, pp, mat, N, lo, A, M, C, Hout, s);
   return gemm_t<EPI, 32>(fmt, pp, mat, N, lo, A, M, C, Hout, s);
 }
-// A product added into the residual X [M x N].  Where 64 x 64 tiles leave
-// compute units idle, K is split over nz workgroups (nz <= 4, partials in
-// `ws`, which holds ws_floats) and the partials are added in a fixed order.
-hipError_t gemm_resid(uint32_t fmt, const Params* pp, const Mat* mat, int N, int K, uint64_t lo, const uint16_t* A, int M,
-                      float* X, float* ws, size_t ws_floats, hipStream_t s) {
-  const long tiles = (long)((N + 63) / 64) * ((M + 63) / 64);
+template <int T>
+hipError_t gemm_resid_t(uint32_t fmt, const Params* pp, const Mat* mat, int N, int K, uint64_t lo, const uint16_t* A,
+                        int M, float* X, float* ws, size_t ws_floats, hipStream_t s) {
+  const long tiles = (long)((N + T - 1) / T) * ((M + T - 1) / T);
   int nz = 1;
   while (nz < 4 && tiles * nz * 2 <= 256 && (K / (2 * nz)) % (2 * BK) == 0 && (size_t)2 * nz * M * N <= ws_floats) nz *= 2;
-  if (nz == 1) return gemm<EPI_RESID>(fmt, pp, mat, N, lo, A, M, X, nullptr, s);
-  hipError_t e = gemm_t<EPI_PARTIAL, 64>(fmt, pp, mat, N, lo, A, M, ws, nullptr, s, nz);
+  if (nz == 1) return gemm_t<EPI_RESID, T>(fmt, pp, mat, N, lo, A, M, X, nullptr, s);
+  hipError_t e = gemm_t<EPI_PARTIAL, T>(fmt, pp, mat, N, lo, A, M, ws, nullptr, s, nz);
   if (e != hipSuccess) return e;
   const size_t n = (size_t)M * N;
   hipLaunchKernelGGL(pf_add_partials, dim3((unsigned)std::min<size_t>((n + 255) / 256, 1024)), dim3(256), 0, s, ws, nz, n,
                      X);
   return hipGetLastError();
+}
+// A product added into the residual X [M x N].  Where the tiles leave
+// compute units idle, K is split over nz workgroups (nz <= 4, partials in
+// `ws`, which holds ws_floats) and the partials are added in a fixed order.
+// 128 x 128 tiles once four K slices of them fill the device, else 64 x 64.
+hipError_t gemm_resid(uint32_t fmt, const Params* pp, const Mat* mat, int N, int K, uint64_t lo, const uint16_t* A, int M,
+                      float* X, float* ws, size_t ws_floats, hipStream_t s) {
+  if ((long)((N + 127) / 128) * ((M + 127) / 128) * 4 >= 256 && (K / 4) % (2 * BK) == 0 &&
+      (size_t)4 * M * N <= ws_floats)
+    return gemm_resid_t<128>(fmt, pp, mat, N, K, lo, A, M, X, ws, ws_floats, s);
+  return gemm_resid_t<64>(fmt, pp, mat, N, K, lo, A, M, X, ws, ws_floats, s);
 }
 
 }  // namespace

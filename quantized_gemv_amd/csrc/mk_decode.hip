@@ -750,13 +750,20 @@ struct Kern {
     // attention slice, so that the slice has the registers of the gate/up,
     // down and next QKV rows.
     lds_barrier();
-    load_layer_o(p, rw, u, l, w);
     if (!LONG) {
+      load_layer_o(p, rw, u, l, w);
       load_layer_mlp(p, rw, u, l, w);
       if (NEXT) load_layer_qkv(p, rw, u, l + 1, w);
     } else {
-      if (hdr[S_SPLIT] >= 0 && hdr[S_SPLIT_IDX] <= ns)
-        ok = att_help(p, s, l, hdr[S_SPLIT], hdr[S_SPLIT_IDX], pos, ns, cw, sbase + hdr[S_IQS_L], epoch, rx, ok);
+      // a helper's first two passes of cached rows go out ahead of the O
+      // rows: they do not depend on this step's q
+      const bool help = hdr[S_SPLIT] >= 0 && hdr[S_SPLIT_IDX] <= ns;
+      KVBlock k0, k1;
+      if (help) help_issue(p, l, hdr[S_SPLIT], hdr[S_SPLIT_IDX], pos, ns, cw, k0, k1);
+      load_layer_o(p, rw, u, l, w);
+      if (help)
+        ok = att_help(p, s, l, hdr[S_SPLIT], hdr[S_SPLIT_IDX], pos, ns, cw, sbase + hdr[S_IQS_L], epoch, rx, ok,
+                      k0, k1);
       load_layer_mlp(p, rw, u, l, w);
       if (NEXT) load_layer_qkv(p, rw, u, l + 1, w);
     }
@@ -1048,6 +1055,18 @@ struct Kern {
       att_block(s, k1, j0 + PPB + cw * BP, a, b, m, lsum, acc);
     }
   }
+  // att_stream with the first two passes' blocks already issued into k0, k1.
+  static __device__ __forceinline__ void att_stream_issued(const Params& p, const S& s, int l, int g, int a0, int a,
+                                                           int b, int cw, float (&m)[GS], float& lsum,
+                                                           f4 (&acc)[NVC], KVBlock& k0, KVBlock& k1) {
+    if (b <= a) return;
+    for (int j0 = a0; j0 < b; j0 += 2 * PPB) {
+      if (j0 != a0) kv_block_load(p, l, g, j0 + PPB + cw * BP, b - 1, k1);
+      att_block(s, k0, j0 + cw * BP, a, b, m, lsum, acc);
+      kv_block_load(p, l, g, j0 + 2 * PPB + cw * BP, b - 1, k0);
+      att_block(s, k1, j0 + PPB + cw * BP, a, b, m, lsum, acc);
+    }
+  }
   // This wave's unnormalised outputs (lanes 16h + i: head h, dims 16c + i),
   // maxima and sums to LDS.
   static __device__ __forceinline__ void att_wave_part(S& s, int cw, const float (&m)[GS], float lsum,
@@ -1156,8 +1175,10 @@ struct Kern {
     float M = sp;
 #pragma unroll
     for (int w = 0; w < kCW; ++w) M = fmaxf(M, s.wm[w][h]);
-    if (LONG)
+    if (LONG) {
+#pragma unroll 8
       for (int i = 0; i < ns; ++i) M = fmaxf(M, s.spart[i][NOUT + h]);
+    }
     const uint32_t vpw = s.vp[(tc % HD) / 2];
     const float ec = __builtin_amdgcn_exp2f(sp - M);
     float Lt = ec, O = ec * ((tc & 1) ? bf16_hi(vpw) : bf16_lo(vpw));
@@ -1167,12 +1188,16 @@ struct Kern {
       Lt = fmaf(s.wl[w][h], e, Lt);
       O = fmaf(s.part[w][tc], e, O);
     }
-    if (LONG)
+    if (LONG) {
+      // unrolled so that the LDS reads of several partials are in flight
+      // together; the sums keep the helpers' order
+#pragma unroll 8
       for (int i = 0; i < ns; ++i) {
         const float e = att_weight(s.spart[i][NOUT + h], M);
         Lt = fmaf(s.spart[i][NOUT + GS + h], e, Lt);
         O = fmaf(s.spart[i][tc], e, O);
       }
+    }
     const float o = O / Lt;
     const float o1 = dpp<0xB1>(o);   // the neighbouring output (t ^ 1)
     st_xword(rx, ok && t < NOUT && (t & 1) == 0 ? 8u * (xword(p, l, V_O) + (g * NOUT + t) / 2) : kOOB,
@@ -1192,29 +1217,46 @@ struct Kern {
     return att_layer<false>(p, s, p.L - 1, g, pos, ns, cw, kv, epoch, rx, ok);
   }
 
+  // Slice i of KV head g's cached positions for split attention: [a, b).
+  static __device__ __forceinline__ void help_slice(int i, int pos, int ns, int& a, int& b) {
+    const int chunk = (pos + ns) / (ns + 1);
+    a = min(pos, i * chunk);
+    b = min(pos, a + chunk);
+  }
+  // The first two passes of a helper's slice, issued before its q is there.
+  static __device__ __forceinline__ void help_issue(const Params& p, int l, int g, int i, int pos, int ns, int cw,
+                                                    KVBlock& k0, KVBlock& k1) {
+    int a, b;
+    help_slice(i, pos, ns, a, b);
+    if (b <= a) return;
+    const int a0 = a & ~3;
+    kv_block_load(p, l, g, a0 + cw * BP, b - 1, k0);
+    kv_block_load(p, l, g, a0 + PPB + cw * BP, b - 1, k1);
+  }
+
   // Split-attention helper (a GEMV workgroup's compute waves, between their
   // weight burst and the O-projection): slice i of KV head g's cached
   // positions, merged over the waves and published as (unnormalised
-  // outputs, per-head maximum, per-head sum) for the head's home.
+  // outputs, per-head maximum, per-head sum) for the head's home.  k0 and
+  // k1 hold the slice's first two passes (help_issue).
   static __device__ __forceinline__ bool att_help(const Params& p, S& s, int l, int g, int i, int pos, int ns,
                                                   int cw, uint32_t want, uint32_t epoch, __amdgpu_buffer_rsrc_t rx,
-                                                  bool ok) {
+                                                  bool ok, KVBlock& k0, KVBlock& k1) {
     const int lane = lane_id();
     const int ph = 2 + 6 * l;
     ok = ok && wait_seq(p, &s.seq, want);
     XR_MIN(s, ph + 1, XR_SEEN);
     att_prepare<false>(p, s, l, g, pos, cw, ok);
     lds_barrier();
-    const int chunk = (pos + ns) / (ns + 1);
-    const int a = min(pos, i * chunk), b = min(pos, a + chunk);
+    int a, b;
+    help_slice(i, pos, ns, a, b);
     f4 acc[NVC];
     float m[GS], lsum = 0.f;
 #pragma unroll
     for (int h = 0; h < GS; ++h) m[h] = -INFINITY;
 #pragma unroll
     for (int c = 0; c < NVC; ++c) acc[c] = f4{0.f, 0.f, 0.f, 0.f};
-    KVBlock k0, k1;
-    att_stream(p, s, l, g, a & ~3, a, b, cw, m, lsum, acc, k0, k1);
+    att_stream_issued(p, s, l, g, a & ~3, a, b, cw, m, lsum, acc, k0, k1);
     att_wave_part(s, cw, m, lsum, acc);
     lds_barrier();
     const int t = cw * 64 + lane;

@@ -109,7 +109,7 @@ enum : int {
   kHdrInts = 16,
 };
 constexpr int kMaxSplit = 32;   // helpers per KV head (the home merges their partials in LDS)
-constexpr int kSplitGatherK = 5;    // partial word pairs per lane and round of the home's gather
+constexpr int kSplitGatherK = 10;   // partial word pairs per lane and round of the home's gather
 // Per compute wave: units of each phase (-1 = none), at these offsets, and
 // the word each QKV unit stores (the q/k/v vector is laid out per producer
 // too: per XCD, the rows of its KV heads are dealt in even blocks over its

@@ -746,24 +746,22 @@ struct Kern {
     // issued its QKV stores (the courier joins this barrier after handing
     // over the layer's input): a burst queued ahead of another wave's stores
     // would delay the attention workgroups' input by the burst's issue time.
-    // With split attention the burst is cut in two around this workgroup's
-    // attention slice, so that the slice has the registers of the gate/up,
-    // down and next QKV rows.
+    // With split attention a helper's slice runs before the burst, so that
+    // it has the registers of the O, gate/up, down and next QKV rows; its
+    // first pass of cached rows goes out before the wait for q.
     lds_barrier();
     if (!LONG) {
       load_layer_o(p, rw, u, l, w);
       load_layer_mlp(p, rw, u, l, w);
       if (NEXT) load_layer_qkv(p, rw, u, l + 1, w);
     } else {
-      // a helper's first two passes of cached rows go out ahead of the O
-      // rows: they do not depend on this step's q
+      // a helper's first pass of cached rows does not depend on this step's q
       const bool help = hdr[S_SPLIT] >= 0 && hdr[S_SPLIT_IDX] <= ns;
-      KVBlock k0, k1;
-      if (help) help_issue(p, l, hdr[S_SPLIT], hdr[S_SPLIT_IDX], pos, ns, cw, k0, k1);
-      load_layer_o(p, rw, u, l, w);
+      KVBlock k0;
+      if (help) help_issue(p, l, hdr[S_SPLIT], hdr[S_SPLIT_IDX], pos, ns, cw, k0);
       if (help)
-        ok = att_help(p, s, l, hdr[S_SPLIT], hdr[S_SPLIT_IDX], pos, ns, cw, sbase + hdr[S_IQS_L], epoch, rx, ok,
-                      k0, k1);
+        ok = att_help(p, s, l, hdr[S_SPLIT], hdr[S_SPLIT_IDX], pos, ns, cw, sbase + hdr[S_IQS_L], epoch, rx, ok, k0);
+      load_layer_o(p, rw, u, l, w);
       load_layer_mlp(p, rw, u, l, w);
       if (NEXT) load_layer_qkv(p, rw, u, l + 1, w);
     }
@@ -1055,13 +1053,14 @@ struct Kern {
       att_block(s, k1, j0 + PPB + cw * BP, a, b, m, lsum, acc);
     }
   }
-  // att_stream with the first two passes' blocks already issued into k0, k1.
+  // att_stream with the first pass's block already issued into k0.
   static __device__ __forceinline__ void att_stream_issued(const Params& p, const S& s, int l, int g, int a0, int a,
                                                            int b, int cw, float (&m)[GS], float& lsum,
-                                                           f4 (&acc)[NVC], KVBlock& k0, KVBlock& k1) {
+                                                           f4 (&acc)[NVC], KVBlock& k0) {
     if (b <= a) return;
+    KVBlock k1;
     for (int j0 = a0; j0 < b; j0 += 2 * PPB) {
-      if (j0 != a0) kv_block_load(p, l, g, j0 + PPB + cw * BP, b - 1, k1);
+      kv_block_load(p, l, g, j0 + PPB + cw * BP, b - 1, k1);
       att_block(s, k0, j0 + cw * BP, a, b, m, lsum, acc);
       kv_block_load(p, l, g, j0 + 2 * PPB + cw * BP, b - 1, k0);
       att_block(s, k1, j0 + PPB + cw * BP, a, b, m, lsum, acc);
@@ -1150,7 +1149,7 @@ struct Kern {
     // ---- the helpers' partials (split attention): every compute wave
     // gathers a share into LDS; nothing else of this workgroup is in flight
     if (LONG && ns > 0) {
-      XR_MIN(s, ph + 2, XR_START);
+      XR_PUT(s, ph + 2, XR_START);
       const uint32_t pb = xword(p, l, V_ATT) + (uint32_t)(g * p.split_max * p.split_pw);
       const int pw = p.split_pw;
       const __amdgpu_buffer_rsrc_t rs = xch_rsrc(p);
@@ -1165,6 +1164,7 @@ struct Kern {
                        r0 + cw * 64, kCW * 64);
       XR_MAX(s, ph + 2, XR_READY);
       lds_barrier();
+      XR_MIN(s, ph + 2, XR_SEEN);
     }
     // merge the seven waves (fixed order), the helpers and the current
     // position; thread t < NOUT owns output t
@@ -1189,16 +1189,31 @@ struct Kern {
       O = fmaf(s.part[w][tc], e, O);
     }
     if (LONG) {
-      // unrolled so that the LDS reads of several partials are in flight
-      // together; the sums keep the helpers' order
-#pragma unroll 8
-      for (int i = 0; i < ns; ++i) {
-        const float e = att_weight(s.spart[i][NOUT + h], M);
-        Lt = fmaf(s.spart[i][NOUT + GS + h], e, Lt);
-        O = fmaf(s.spart[i][tc], e, O);
+      // eight partials at a time: their LDS reads all go out before the
+      // first is used (rows past the last re-read it and are not added);
+      // the sums keep the helpers' order
+      for (int i0 = 0; i0 < ns; i0 += 8) {
+        float mw[8], lw[8], ow[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int i = min(i0 + k, ns - 1);
+          mw[k] = s.spart[i][NOUT + h];
+          lw[k] = s.spart[i][NOUT + GS + h];
+          ow[k] = s.spart[i][tc];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          if (i0 + k < ns) {
+            const float e = att_weight(mw[k], M);
+            Lt = fmaf(lw[k], e, Lt);
+            O = fmaf(ow[k], e, O);
+          }
+        }
       }
     }
     const float o = O / Lt;
+    XR_MAX(s, ph + 2, XR_M0);
     const float o1 = dpp<0xB1>(o);   // the neighbouring output (t ^ 1)
     st_xword(rx, ok && t < NOUT && (t & 1) == 0 ? 8u * (xword(p, l, V_O) + (g * NOUT + t) / 2) : kOOB,
              pack_bf16(o, o1), make_tag(epoch, vec_id(l, V_O)));
@@ -1223,25 +1238,24 @@ struct Kern {
     a = min(pos, i * chunk);
     b = min(pos, a + chunk);
   }
-  // The first two passes of a helper's slice, issued before its q is there.
+  // The first pass of a helper's slice, issued before its q is there.
   static __device__ __forceinline__ void help_issue(const Params& p, int l, int g, int i, int pos, int ns, int cw,
-                                                    KVBlock& k0, KVBlock& k1) {
+                                                    KVBlock& k0) {
     int a, b;
     help_slice(i, pos, ns, a, b);
     if (b <= a) return;
     const int a0 = a & ~3;
     kv_block_load(p, l, g, a0 + cw * BP, b - 1, k0);
-    kv_block_load(p, l, g, a0 + PPB + cw * BP, b - 1, k1);
   }
 
-  // Split-attention helper (a GEMV workgroup's compute waves, between their
-  // weight burst and the O-projection): slice i of KV head g's cached
-  // positions, merged over the waves and published as (unnormalised
-  // outputs, per-head maximum, per-head sum) for the head's home.  k0 and
-  // k1 hold the slice's first two passes (help_issue).
+  // Split-attention helper (a GEMV workgroup's compute waves, after their
+  // QKV rows and before the layer's weight burst): slice i of KV head g's
+  // cached positions, merged over the waves and published as (unnormalised
+  // outputs, per-head maximum, per-head sum) for the head's home.  k0 holds
+  // the slice's first pass (help_issue).
   static __device__ __forceinline__ bool att_help(const Params& p, S& s, int l, int g, int i, int pos, int ns,
                                                   int cw, uint32_t want, uint32_t epoch, __amdgpu_buffer_rsrc_t rx,
-                                                  bool ok, KVBlock& k0, KVBlock& k1) {
+                                                  bool ok, KVBlock& k0) {
     const int lane = lane_id();
     const int ph = 2 + 6 * l;
     ok = ok && wait_seq(p, &s.seq, want);
@@ -1256,7 +1270,7 @@ struct Kern {
     for (int h = 0; h < GS; ++h) m[h] = -INFINITY;
 #pragma unroll
     for (int c = 0; c < NVC; ++c) acc[c] = f4{0.f, 0.f, 0.f, 0.f};
-    att_stream_issued(p, s, l, g, a & ~3, a, b, cw, m, lsum, acc, k0, k1);
+    att_stream_issued(p, s, l, g, a & ~3, a, b, cw, m, lsum, acc, k0);
     att_wave_part(s, cw, m, lsum, acc);
     lds_barrier();
     const int t = cw * 64 + lane;

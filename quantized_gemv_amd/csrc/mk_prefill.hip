@@ -364,7 +364,9 @@ __global__ __launch_bounds__(256) void pf_attention_mc(const Params* pp, int l, 
   __shared__ float sm[4][16], sl[4][16];
   __shared__ float so[4][16][HD + 1];
   const int w = wave(), ln = lane(), r = ln & 15, qg = ln >> 4;
-  const int qb = blockIdx.x / nq, h = blockIdx.x % nq, g = h / (nq / nkv);
+  // the last query blocks see the most keys: they go out first, so that the
+  // short ones fill in behind them
+  const int qb = (int)(gridDim.x / nq) - 1 - (int)(blockIdx.x / nq), h = blockIdx.x % nq, g = h / (nq / nkv);
   const int i0 = 16 * qb;
   const int qi = i0 + r;                       // this lane's query (column)
   const bool qv = qi < cn;

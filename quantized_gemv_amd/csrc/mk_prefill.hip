@@ -538,6 +538,43 @@ __global__ void pf_argmax(const float* best_v, const int32_t* best_i, int n, int
 }
 
 // X[i] += P[0][i] + P[1][i] + ... (the split-K partials, in order)
+// The split-K partials added into the residual rows, fused with the next
+// RMSNorm: one workgroup per row of H <= 4096, each thread keeping its
+// elements (e = thread + 256k) in registers.  The sums, the sum of squares
+// and the scaling take the same order as pf_add_partials then pf_rmsnorm.
+__global__ __launch_bounds__(256) void pf_add_partials_norm(const Params* pp, const float* P, int nz, int H, size_t n,
+                                                            float* X, uint64_t g_off, uint16_t* A) {
+  const Params& p = *pp;
+  __shared__ float red[4];
+  const int i = blockIdx.x;
+  float xr[16];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int e = threadIdx.x + 256 * k;
+    if (e < H) {
+      const size_t j = (size_t)i * H + e;
+      float v = P[j];
+      for (int z = 1; z < nz; ++z) v += P[(size_t)z * n + j];
+      const float x = X[j] + v;
+      X[j] = x;
+      xr[k] = x;
+      ss += x * x;
+    }
+  }
+  ss = wsum(ss);
+  if (lane() == 0) red[wave()] = ss;
+  __syncthreads();
+  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  const float r = 1.0f / sqrtf(tot / (float)H + p.eps);
+  const __amdgpu_buffer_rsrc_t rw = arena(p);
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int e = threadIdx.x + 256 * k;
+    if (e < H) A[(size_t)i * H + e] = (uint16_t)f32_to_bf16(gain(rw, g_off, e) * (xr[k] * r));
+  }
+}
+
 __global__ __launch_bounds__(256) void pf_add_partials(const float* P, int nz, size_t n, float* X) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
     float v = P[i];
@@ -566,28 +603,38 @@ hipError_t gemm(uint32_t fmt, const Params* pp, const Mat* mat, int N, uint64_t 
 }
 template <int T>
 hipError_t gemm_resid_t(uint32_t fmt, const Params* pp, const Mat* mat, int N, int K, uint64_t lo, const uint16_t* A,
-                        int M, float* X, float* ws, size_t ws_floats, hipStream_t s) {
+                        int M, float* X, float* ws, size_t ws_floats, uint64_t g_off, uint16_t* An, hipStream_t s) {
   const long tiles = (long)((N + T - 1) / T) * ((M + T - 1) / T);
   int nz = 1;
   while (nz < 4 && tiles * nz * 2 <= 256 && (K / (2 * nz)) % (2 * BK) == 0 && (size_t)2 * nz * M * N <= ws_floats) nz *= 2;
-  if (nz == 1) return gemm_t<EPI_RESID, T>(fmt, pp, mat, N, lo, A, M, X, nullptr, s);
+  if (nz == 1) {
+    hipError_t e = gemm_t<EPI_RESID, T>(fmt, pp, mat, N, lo, A, M, X, nullptr, s);
+    if (e != hipSuccess || !An) return e;
+    hipLaunchKernelGGL(pf_rmsnorm, dim3(M), dim3(256), 0, s, pp, X, M, N, g_off, An);
+    return hipGetLastError();
+  }
   hipError_t e = gemm_t<EPI_PARTIAL, T>(fmt, pp, mat, N, lo, A, M, ws, nullptr, s, nz);
   if (e != hipSuccess) return e;
   const size_t n = (size_t)M * N;
-  hipLaunchKernelGGL(pf_add_partials, dim3((unsigned)std::min<size_t>((n + 255) / 256, 1024)), dim3(256), 0, s, ws, nz, n,
-                     X);
+  if (An)
+    hipLaunchKernelGGL(pf_add_partials_norm, dim3(M), dim3(256), 0, s, pp, ws, nz, N, n, X, g_off, An);
+  else
+    hipLaunchKernelGGL(pf_add_partials, dim3((unsigned)std::min<size_t>((n + 255) / 256, 1024)), dim3(256), 0, s, ws,
+                       nz, n, X);
   return hipGetLastError();
 }
 // A product added into the residual X [M x N].  Where the tiles leave
 // compute units idle, K is split over nz workgroups (nz <= 4, partials in
 // `ws`, which holds ws_floats) and the partials are added in a fixed order.
 // 128 x 128 tiles once four K slices of them fill the device, else 64 x 64.
+// With An, the RMSNorm of the new residual (gains at g_off) follows into An,
+// fused with the partials' sum where K is split.
 hipError_t gemm_resid(uint32_t fmt, const Params* pp, const Mat* mat, int N, int K, uint64_t lo, const uint16_t* A, int M,
-                      float* X, float* ws, size_t ws_floats, hipStream_t s) {
+                      float* X, float* ws, size_t ws_floats, uint64_t g_off, uint16_t* An, hipStream_t s) {
   if ((long)((N + 127) / 128) * ((M + 127) / 128) * 4 >= 256 && (K / 4) % (2 * BK) == 0 &&
       (size_t)4 * M * N <= ws_floats)
-    return gemm_resid_t<128>(fmt, pp, mat, N, K, lo, A, M, X, ws, ws_floats, s);
-  return gemm_resid_t<64>(fmt, pp, mat, N, K, lo, A, M, X, ws, ws_floats, s);
+    return gemm_resid_t<128>(fmt, pp, mat, N, K, lo, A, M, X, ws, ws_floats, g_off, An, s);
+  return gemm_resid_t<64>(fmt, pp, mat, N, K, lo, A, M, X, ws, ws_floats, g_off, An, s);
 }
 
 }  // namespace
@@ -599,7 +646,8 @@ hipError_t launch_prefill_chunk(const PrefillArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(pf_embed, dim3(cn), dim3(256), 0, s, pp, a.tokens, cn, a.X);
   for (int l = 0; l < a.L; ++l) {
     const uint64_t lo = (uint64_t)l * a.layer_stride;
-    hipLaunchKernelGGL(pf_rmsnorm, dim3(cn), dim3(256), 0, s, pp, a.X, cn, H, a.in_norm + lo, a.A);
+    // later layers' input norms come with the previous layer's down product
+    if (l == 0) hipLaunchKernelGGL(pf_rmsnorm, dim3(cn), dim3(256), 0, s, pp, a.X, cn, H, a.in_norm + lo, a.A);
     hipError_t e = gemm<EPI_STORE>(a.fmt_lin, pp, a.mat_qkv, nqkv, lo, a.A, cn, a.QKV, nullptr, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(pf_qkv_post, dim3((cn * (nq + 2 * nkv) + 3) / 4), dim3(256), 0, s, pp, l, a.c0, cn, a.QKV);
@@ -612,12 +660,13 @@ hipError_t launch_prefill_chunk(const PrefillArgs& a, hipStream_t s) {
       return hipErrorInvalidValue;
     // the QKV outputs are used up: their buffer holds the split-K partials
     const size_t ws = (size_t)kPrefillChunk * nqkv;
-    e = gemm_resid(a.fmt_lin, pp, a.mat_o, H, nq * hd, lo, a.A, cn, a.X, a.QKV, ws, s);
+    e = gemm_resid(a.fmt_lin, pp, a.mat_o, H, nq * hd, lo, a.A, cn, a.X, a.QKV, ws, a.post_norm + lo, a.A, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(pf_rmsnorm, dim3(cn), dim3(256), 0, s, pp, a.X, cn, H, a.post_norm + lo, a.A);
     e = gemm<EPI_SWIGLU>(a.fmt_lin, pp, a.mat_gu, 2 * I, lo, a.A, cn, nullptr, a.Hb, s);
     if (e != hipSuccess) return e;
-    e = gemm_resid(a.fmt_down, pp, a.mat_down, H, I, lo, a.Hb, cn, a.X, a.QKV, ws, s);
+    const bool next = l + 1 < a.L;
+    e = gemm_resid(a.fmt_down, pp, a.mat_down, H, I, lo, a.Hb, cn, a.X, a.QKV, ws,
+                   next ? a.in_norm + lo + a.layer_stride : 0, next ? a.A : nullptr, s);
     if (e != hipSuccess) return e;
   }
   if (a.last) {

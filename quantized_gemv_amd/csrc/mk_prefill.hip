@@ -501,6 +501,76 @@ __global__ __launch_bounds__(256) void pf_lm_head(const Params* pp, const float*
   float bv = -INFINITY;
   int bi = 0x7FFFFFFF;
   const int nw = gridDim.x * 4;
+  const bool f8 = p.embed.fmt != FMT_BF16;
+  // 16-byte loads: 16 FP8 codes or 8 bf16 weights per lane and load, and a
+  // wave's consecutive lanes cover consecutive bytes of a row; R rows in
+  // flight per wave.  Other row widths take the per-element loop below.
+  if (H % (f8 ? 1024 : 512) == 0) {
+    constexpr int R = 8;
+    const int epl = f8 ? 16 : 8, nk = H / (64 * epl);
+    for (int row0 = (blockIdx.x * 4 + w) * R; row0 < p.V; row0 += nw * R) {
+      float d[R];
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) d[rr] = 0.f;
+      for (int k = 0; k < nk; ++k) {
+        const int e0 = epl * (ln + 64 * k);
+        u4 c[R];
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
+          const uint64_t row = (uint64_t)min(row0 + rr, p.V - 1);
+          const uint64_t off = p.embed.codes + (f8 ? row * H + e0 : 2 * (row * H + e0));
+          c[rr] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rw, (uint32_t)off, 0, 0));
+        }
+        if (f8) {
+          float xv[16];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) xv[j] = xn[e0 + j];
+#pragma unroll
+          for (int rr = 0; rr < R; ++rr) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              float wv[4];
+              e4m3x4_to_f32(c[rr][q], wv);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) d[rr] = fmaf(xv[4 * q + j], wv[j], d[rr]);
+            }
+          }
+        } else {
+          float xv[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) xv[j] = xn[e0 + j];
+#pragma unroll
+          for (int rr = 0; rr < R; ++rr) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              d[rr] = fmaf(xv[2 * q], bf16_lo(c[rr][q]), d[rr]);
+              d[rr] = fmaf(xv[2 * q + 1], bf16_hi(c[rr][q]), d[rr]);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) {
+        const int row = row0 + rr;
+        float v = wsum(d[rr]);
+        if (f8)
+          v *= __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                             rw, (uint32_t)(p.embed.scales + 4ull * min(row, p.V - 1)), 0, 0));
+        if (row < p.V) {
+          if (logits && ln == 0) logits[row] = v;
+          if (v > bv) {   // rows ascend: a tie keeps the lower index
+            bv = v;
+            bi = row;
+          }
+        }
+      }
+    }
+    if (ln == 0) {
+      best_v[blockIdx.x * 4 + w] = bv;
+      best_i[blockIdx.x * 4 + w] = bi;
+    }
+    return;
+  }
   for (int row = blockIdx.x * 4 + w; row < p.V; row += nw) {
     float d = 0.f;
     if (p.embed.fmt == FMT_BF16) {
@@ -537,7 +607,6 @@ __global__ void pf_argmax(const float* best_v, const int32_t* best_i, int n, int
   *out = bi;
 }
 
-// X[i] += P[0][i] + P[1][i] + ... (the split-K partials, in order)
 // The split-K partials added into the residual rows, fused with the next
 // RMSNorm: one workgroup per row of H <= 4096, each thread keeping its
 // elements (e = thread + 256k) in registers.  The sums, the sum of squares
@@ -575,6 +644,7 @@ __global__ __launch_bounds__(256) void pf_add_partials_norm(const Params* pp, co
   }
 }
 
+// X[i] += P[0][i] + P[1][i] + ... (the split-K partials, in order)
 __global__ __launch_bounds__(256) void pf_add_partials(const float* P, int nz, size_t n, float* X) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
     float v = P[i];

@@ -595,16 +595,31 @@ __global__ __launch_bounds__(256) void pf_lm_head(const Params* pp, const float*
   }
 }
 
+// One wave: each lane scans every 64th entry, then a butterfly over the
+// lanes; the larger value wins, and on equal values the lower index.
 __global__ void pf_argmax(const float* best_v, const int32_t* best_i, int n, int32_t* out) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  float b = best_v[0];
-  int bi = best_i[0];
-  for (int k = 1; k < n; ++k)
-    if (best_v[k] > b || (best_v[k] == b && best_i[k] < bi)) {
-      b = best_v[k];
-      bi = best_i[k];
+  if (blockIdx.x != 0 || threadIdx.x >= 64) return;
+  const int ln = threadIdx.x;
+  float b = -INFINITY;
+  int bi = 0x7FFFFFFF;
+  for (int k = ln; k < n; k += 64) {
+    const float v = best_v[k];
+    const int i = best_i[k];
+    if (v > b || (v == b && i < bi)) {
+      b = v;
+      bi = i;
     }
-  *out = bi;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float v = __shfl_xor(b, off);
+    const int i = __shfl_xor(bi, off);
+    if (v > b || (v == b && i < bi)) {
+      b = v;
+      bi = i;
+    }
+  }
+  if (ln == 0) *out = bi;
 }
 
 // The split-K partials added into the residual rows, fused with the next

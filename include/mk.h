@@ -235,7 +235,7 @@ int mk_decode_codes(int32_t codec, const uint8_t* d_codes, int32_t n, float* d_o
  * block scale search radius 0..126 [0], set before mk_pack_weights (see
  * there); 0 keeps the absolute-maximum recipe.  Key 10, prefill path [0]:
  * 0 runs mk_prefill as one decode launch per prompt position; 1 runs the
- * prompt through each layer in chunks of 1024 positions, the projections as
+ * prompt through each layer in chunks of 4096 positions, the projections as
  * matrix products on the matrix cores (bf16 operands, fp32 accumulation,
  * weights dequantized exactly), with the decode path's rounding points; it
  * writes the same KV cache up to summation order.  1 needs hidden,

@@ -30,7 +30,7 @@ hipError_t launch_decode_codes(int codec, const uint8_t* in, int n, float* out, 
 // through every layer; with `last`, also the LM head of position c0+cn-1 and
 // its argmax into *next.  Device pointers; the workspace buffers hold
 // kPrefillChunk rows.
-constexpr int kPrefillChunk = 1024;
+constexpr int kPrefillChunk = 4096;
 constexpr int kPrefillHeadGroups = 256;   // LM-head workgroups (4 waves each)
 struct PrefillArgs {
   const Params* params;

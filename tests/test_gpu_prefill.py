@@ -8,7 +8,7 @@ C-ABI, against the oracle's prefill of the same prompt:
   gap is at least 1e-3, else a valid argmax within 1e-2 of its maximum;
 * a decode step after it: logits within relative L2 1e-2 of the oracle's.
 
-Prompts span one chunk of 1024 positions and more (a ragged last chunk)."""
+Prompts span one chunk of 4096 positions and more (a ragged last chunk)."""
 import numpy as np
 import pytest
 import torch
@@ -70,7 +70,7 @@ def _decode_after(dec, orc, cache, sh, token, pos):
 
 
 @pytest.mark.parametrize("wfmt,n", [(synth.BF16, 39), (synth.FP8_ROW, 39), (synth.FP4_MIX, 39),
-                                    (synth.BF16, 300), (synth.FP8_ROW, 1100)])
+                                    (synth.BF16, 300), (synth.FP8_ROW, 1100), (synth.FP8_ROW, 4200)])
 def test_prefill_batched_tiny(native, tiny_master, wfmt, n):
     sh = synth.TINY
     toks = synth.make_prompt(sh.vocab, n + 1, 31)

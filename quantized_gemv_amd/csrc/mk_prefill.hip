@@ -691,7 +691,7 @@ hipError_t gemm_resid_t(uint32_t fmt, const Params* pp, const Mat* mat, int N, i
                         int M, float* X, float* ws, size_t ws_floats, uint64_t g_off, uint16_t* An, hipStream_t s) {
   const long tiles = (long)((N + T - 1) / T) * ((M + T - 1) / T);
   int nz = 1;
-  while (nz < 4 && tiles * nz * 2 <= 256 && (K / (2 * nz)) % (2 * BK) == 0 && (size_t)2 * nz * M * N <= ws_floats) nz *= 2;
+  while (nz < 4 && tiles * nz * 2 <= 512 && (K / (2 * nz)) % (2 * BK) == 0 && (size_t)2 * nz * M * N <= ws_floats) nz *= 2;
   if (nz == 1) {
     hipError_t e = gemm_t<EPI_RESID, T>(fmt, pp, mat, N, lo, A, M, X, nullptr, s);
     if (e != hipSuccess || !An) return e;
@@ -708,9 +708,10 @@ hipError_t gemm_resid_t(uint32_t fmt, const Params* pp, const Mat* mat, int N, i
                        nz, n, X);
   return hipGetLastError();
 }
-// A product added into the residual X [M x N].  Where the tiles leave
-// compute units idle, K is split over nz workgroups (nz <= 4, partials in
-// `ws`, which holds ws_floats) and the partials are added in a fixed order.
+// A product added into the residual X [M x N].  Where the tiles give fewer
+// than two workgroups per compute unit, K is split over nz workgroups
+// (nz <= 4, partials in `ws`, which holds ws_floats) and the partials are
+// added in a fixed order.
 // 128 x 128 tiles once four K slices of them fill the device, else 64 x 64.
 // With An, the RMSNorm of the new residual (gains at g_off) follows into An,
 // fused with the partials' sum where K is split.

@@ -83,7 +83,10 @@ typedef struct mk_sizes {
                          (j, e at (j/4*head_dim + e)*4 + j%4), the layout the matrix-core value
                          product reads. */
   size_t rope;        /* RoPE table: max_ctx * head_dim/2 * 2 * 4 (fp32 cos, sin) */
-  size_t scratch;     /* exchange buffers, argmax slots, error word */
+  size_t scratch;     /* exchange buffers, argmax slots, error word, and the
+                         batched prefill's buffers for 4096-position chunks
+                         (residual, q/k/v outputs, GEMM input, SwiGLU output:
+                         about 126 MB at the 0.6B shape) */
   size_t trace;       /* X-ray records for one step (0 in builds without X-ray) */
   size_t weight_bytes_per_token;  /* algorithmic weight bytes one step reads: every matrix,
                                      its scales and the norm gains, each once */

@@ -230,33 +230,32 @@ def test_ops_qwen3_0p6b_split_attention(native, q_master, wfmt, chunk):
 
 
 @pytest.mark.timeout(900)
-def test_end_to_end_qwen3_0p6b_bf16(native, q_master):
+@pytest.mark.parametrize("prefill_mode", [0, 1])
+def test_end_to_end_qwen3_0p6b_bf16(native, q_master, prefill_mode):
     """Whole-step parity at the benchmark's size: after the benchmark's
-    prompt, 4 teacher-forced steps (positions 128..131) against the full
-    oracle: logits within relative L2 1e-2, and the fused argmax equal to
-    the oracle's where the oracle's top-2 gap is at least 1e-3 (else a valid
-    argmax within 1e-2 of the oracle's maximum)."""
+    prompt (mk_prefill as one decode launch per position, or the batched
+    matrix-core prefill), 8 teacher-forced steps (positions 128..135) against
+    the full oracle: logits within relative L2 1e-2, and the fused argmax by
+    the G3 rule of tests/gates.py.  The oracle's reference is its stepwise
+    prefill; its batched prefill (another summation order) gives the margin.
+    With the batched GPU prefill, step 1 here is a near-tie (oracle gap
+    2.8e-3 against an order noise of 1.3e-2): a token that differs there is
+    a valid argmax, not a failure."""
+    from gates import check_token, rel_l2
     sh = synth.QWEN3_0P6B
     wl = synth.WORKLOADS["qwen3_0p6b_bf16"]
     prompt = synth.make_prompt(sh.vocab, wl.prompt_len, wl.prompt_seed)
     orc = Oracle(q_master, synth.BF16, 160)
-    cache = orc.new_cache()
-    want, last = orc.prefill_batched(cache, prompt)
-    d = _decoder(native, sh, q_master, synth.BF16, 160)
-    got = d.prefill(prompt)
-    top2 = np.sort(last)[-2:]
-    if top2[1] - top2[0] >= 1e-3:
-        assert got == want
-    forced = synth.make_prompt(sh.vocab, 4, 21)
+    cache, twin_cache = orc.new_cache(), orc.new_cache()
+    _, last = orc.prefill(cache, prompt)
+    _, twin = orc.prefill_batched(twin_cache, prompt)
+    d = _decoder(native, sh, q_master, synth.BF16, 160, prefill_mode=prefill_mode)
+    check_token(d.prefill(prompt), last, np.abs(last - twin).max(), "prefill")
+    forced = synth.make_prompt(sh.vocab, 8, 21)
     for i, t in enumerate(forced):
         pos = wl.prompt_len + i
         logits = _step(d, sh, int(t), pos)
-        ref = orc.step(cache, int(t), pos)
-        assert np.linalg.norm(logits - ref) / np.linalg.norm(ref) <= 1e-2, pos
-        g = argmax_lowest(logits)
-        top2 = np.sort(ref)[-2:]
-        if top2[1] - top2[0] >= 1e-3:
-            assert g == argmax_lowest(ref), pos
-        else:
-            assert ref[g] >= ref.max() - 1e-2, pos
+        ref, tw = orc.step(cache, int(t), pos), orc.step(twin_cache, int(t), pos)
+        assert rel_l2(logits, ref) <= 1e-2, pos
+        check_token(argmax_lowest(logits), ref, np.abs(ref - tw).max(), pos)
     d.close()

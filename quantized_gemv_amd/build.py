@@ -69,7 +69,10 @@ def resource_usage(remarks: str) -> dict:
 
 
 def build_all(verbose: bool = False):
-    return [build(False, verbose), build(True, verbose)]
+    """Both variants, compiled side by side."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(2) as ex:
+        return list(ex.map(lambda x: build(x, verbose), (False, True)))
 
 
 if __name__ == "__main__":

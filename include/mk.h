@@ -183,6 +183,28 @@ int32_t mk_decode_step(mk_model* m, int32_t token, int32_t pos, mk_stream_t s);
 int mk_decode_step_async(mk_model* m, const int32_t* d_token, int32_t pos, int32_t* d_next,
                          float* d_logits, mk_stream_t s);
 
+/* The same step as mk_decode_step_async, for callers that cannot allocate
+ * device memory around it (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): its scratch (exchange words,
+ * argmax words, error word, work table, kernel parameters) is a static
+ * device array of the library, 32 MiB on each GPU, held until the process
+ * ends, instead of the bound scratch buffer.  The model must be bound and
+ * packed (its weights, KV cache and RoPE table are used as usual); the
+ * caller passes the token buffers and the optional logits as for
+ * mk_decode_step_async.  The call allocates nothing: no hipMalloc, hipFree or
+ * allocating library routine; it enqueues a one-word clear of the array's
+ * error word, and the first call on a device, or the first after another
+ * model used the array, also copies the model's parameters and work table
+ * into it.  Every call on one GPU shares that GPU's array: calls that overlap
+ * on one GPU (two streams, two threads, two models) race and must be
+ * serialised by the caller.  A failed step leaves -1 in d_next; its error
+ * code is not kept.  Errors (immediate): MK_E_INVALID (as for
+ * mk_decode_step_async, or another device current than the model's),
+ * MK_E_STATE, MK_E_UNSUPPORTED (the model's step needs more than the array
+ * holds: the size is in mk_last_error), MK_E_HIP. */
+int mk_decode_step_async_noalloc(mk_model* m, const int32_t* d_token, int32_t pos, int32_t* d_next,
+                                 float* d_logits, mk_stream_t s);
+
 /* Read and clear the device error word (synchronous).  Returns MK_OK or the
  * first error a kernel recorded. */
 int mk_check_device_error(mk_model* m, mk_stream_t s);

@@ -7,7 +7,9 @@
 #include <cstdio>
 #include <algorithm>
 #include <cstddef>
+#include <atomic>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -68,6 +70,9 @@ struct mk_model {
   int prefill_mode = 0;         // mk_prefill: 0 one decode launch per position, 1 batched (matrix cores)
   size_t pf_off = 0;            // batched-prefill workspace in the scratch buffer
   uint32_t epoch = 0;
+  uint64_t uid = 0;             // unique per model handle (owner of the static scratch contents)
+  bool static_dirty = true;     // parameters changed since they were last put in the static scratch
+  Params P_static;              // the parameter block of the no-allocation path (held for its upload)
   std::string err;
 };
 
@@ -444,8 +449,7 @@ int check_grid(mk_model* m, int grid) {
 
 // Fill the kernel parameters that depend on the grid and the bound buffers,
 // and upload them.
-int sync_params(mk_model* m, hipStream_t s) {
-  if (!m->params_dirty) return MK_OK;
+void fill_params(mk_model* m) {
   const mk_config& c = m->cfg;
   Params& P = m->P;
   // C-style casts: in the device pass of this file these fields are global pointers
@@ -470,7 +474,12 @@ int sync_params(mk_model* m, hipStream_t s) {
   P.n_phases = n_phases(c);
   P.split_max = kMaxSplit;
   P.split_pw = (int)split_pw(c);
-  HIPCK(m, hipMemcpyAsync(m->d_scratch + m->params_off, &P, sizeof(Params), hipMemcpyHostToDevice, s));
+}
+
+int sync_params(mk_model* m, hipStream_t s) {
+  if (!m->params_dirty) return MK_OK;
+  fill_params(m);
+  HIPCK(m, hipMemcpyAsync(m->d_scratch + m->params_off, &m->P, sizeof(Params), hipMemcpyHostToDevice, s));
   HIPCK(m, hipStreamSynchronize(s));  // the host copy is a stack-independent member, but keep ordering simple
   m->params_dirty = false;
   return MK_OK;
@@ -491,15 +500,10 @@ int32_t read_token_and_error(mk_model* m, const int32_t* d_next, hipStream_t s) 
   return tok;
 }
 
-int launch_step(mk_model* m, const int32_t* d_token, int pos, int32_t* d_next, float* d_logits, hipStream_t s) {
-  int rc = sync_params(m, s);
-  if (rc) return rc;
-  m->epoch = (m->epoch + 1) & kEpochMask;
-  if (m->epoch == 0) {  // tags would repeat: clear the exchange words and restart
-    HIPCK(m, hipMemsetAsync(m->d_scratch, 0, 8 * m->P.x.err, s));
-    m->epoch = 1;
-  }
-  const Params* dp = reinterpret_cast<const Params*>(m->d_scratch + m->params_off);
+// One decode launch with the parameter block at `dp` (device memory) and
+// exchange tags of `epoch`.
+int launch_with(mk_model* m, const Params* dp, uint32_t epoch, const int32_t* d_token, int pos, int32_t* d_next,
+                float* d_logits, hipStream_t s) {
   const mk_config& c = m->cfg;
   const bool coop = m->launch_mode == 0 || (m->launch_mode < 0 && m->P.grid > m->coresident);
   const int ns = m->split_chunk > 0 && pos >= m->split_from ? std::min(m->split_n, pos / m->split_chunk) : 0;
@@ -507,9 +511,47 @@ int launch_step(mk_model* m, const int32_t* d_token, int pos, int32_t* d_next, f
     return fail(m, MK_E_UNSUPPORTED, "plain launch: grid %d exceeds the %d workgroups the device holds at once",
                 m->P.grid, m->coresident);
   HIPCK(m, launch_decode(dp, c.wfmt, c.head_dim, c.n_q_heads / c.n_kv_heads, c.hidden, c.n_q_heads * c.head_dim,
-                         c.intermediate, m->P.grid, coop, d_token, pos, ns, m->epoch, d_next, d_logits, s));
+                         c.intermediate, m->P.grid, coop, d_token, pos, ns, epoch, d_next, d_logits, s));
   return MK_OK;
 }
+
+int launch_step(mk_model* m, const int32_t* d_token, int pos, int32_t* d_next, float* d_logits, hipStream_t s) {
+  int rc = sync_params(m, s);
+  if (rc) return rc;
+  m->epoch = (m->epoch + 1) & kEpochMask;
+  if (m->epoch == 0) {  // tags would repeat: clear the exchange words and restart
+    HIPCK(m, launch_zero_words(reinterpret_cast<uint64_t*>(m->d_scratch), m->P.x.err, s));
+    m->epoch = 1;
+  }
+  const Params* dp = reinterpret_cast<const Params*>(m->d_scratch + m->params_off);
+  return launch_with(m, dp, m->epoch, d_token, pos, d_next, d_logits, s);
+}
+
+// ---- the no-allocation step (mk_decode_step_async_noalloc)
+// Its scratch (exchange words, argmax words, error word, work table and the
+// kernel parameter block, laid out as in the bound scratch buffer) is this
+// file-scope device array.  Each device holds its own copy, at the address
+// hipGetSymbolAddress reports with that device current; the array's name in
+// host code is only a handle for that lookup.
+constexpr size_t kStaticScratchBytes = 32ull << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+// Per device: the array's device address, the exchange epoch of the last
+// step run in it (tags stay unique across every model that uses the array),
+// which model's work table and parameters it holds, and how much of it any
+// model has used.
+struct StaticSlot {
+  uint8_t* ptr = nullptr;
+  uint32_t epoch = 0;
+  uint64_t owner = 0;
+  size_t extent = 0;
+};
+std::mutex g_static_mu;
+std::vector<StaticSlot> g_static;
+std::atomic<uint64_t> g_next_uid{1};
+
+// Bytes of the static array one step of this model uses.
+size_t static_need(const mk_model* m) { return m->params_off + sizeof(Params); }
 
 }  // namespace
 
@@ -523,6 +565,7 @@ int mk_create(const mk_config* cfg, mk_model** out) {
   mk_model* m = new (std::nothrow) mk_model();
   if (!m) return MK_E_INVALID;
   m->cfg = *cfg;
+  m->uid = g_next_uid.fetch_add(1);
   std::memset(&m->P, 0, sizeof(Params));
   if (cfg->wfmt == MK_WFMT_FP8_ROW) m->fmt_lin = m->fmt_down = m->fmt_embed = FMT_FP8;
   if (cfg->wfmt == MK_WFMT_FP4_MIX) {
@@ -591,6 +634,7 @@ int mk_bind(mk_model* m, void* d_weights, void* d_kv, void* d_rope, void* d_scra
   m->d_trace = mk_has_xray() ? d_trace : nullptr;
   m->bound = true;
   m->params_dirty = true;
+  m->static_dirty = true;
   m->epoch = 0;
   const char* why = build_sched(m->cfg, grid, m->sched, &m->split_n, &m->qkv_word);
   if (why) return fail(m, MK_E_UNSUPPORTED, "grid %d: %s", grid, why);
@@ -705,6 +749,56 @@ int mk_decode_step_async(mk_model* m, const int32_t* d_token, int32_t pos, int32
   if (pos < 0 || pos >= m->cfg.max_ctx) return fail(m, MK_E_INVALID, "position %d outside [0, %d)", pos, m->cfg.max_ctx);
   if (!m->bound || !m->packed) return fail(m, MK_E_STATE, "decode before mk_bind and mk_pack_weights");
   return launch_step(m, d_token, pos, d_next, d_logits, reinterpret_cast<hipStream_t>(stream));
+}
+
+int mk_decode_step_async_noalloc(mk_model* m, const int32_t* d_token, int32_t pos, int32_t* d_next,
+                                 float* d_logits, mk_stream_t stream) {
+  if (!m) return MK_E_INVALID;
+  if (!d_token || !d_next || d_token == d_next)
+    return fail(m, MK_E_INVALID, "mk_decode_step_async_noalloc: token buffers must be distinct and non-null");
+  if (pos < 0 || pos >= m->cfg.max_ctx) return fail(m, MK_E_INVALID, "position %d outside [0, %d)", pos, m->cfg.max_ctx);
+  if (!m->bound || !m->packed) return fail(m, MK_E_STATE, "decode before mk_bind and mk_pack_weights");
+  if (static_need(m) > kStaticScratchBytes)
+    return fail(m, MK_E_UNSUPPORTED,
+                "mk_decode_step_async_noalloc: this model's step needs %zu bytes of scratch, more than the "
+                "library's static %zu",
+                static_need(m), (size_t)kStaticScratchBytes);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int dev = -1;
+  HIPCK(m, hipGetDevice(&dev));
+  if (dev != m->device)
+    return fail(m, MK_E_INVALID, "mk_decode_step_async_noalloc: device %d is current, the model is bound on %d", dev,
+                m->device);
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (g_static.size() <= (size_t)dev) g_static.resize((size_t)dev + 1);
+  StaticSlot& slot = g_static[(size_t)dev];
+  if (!slot.ptr) {   // first use on this device: look up this device's copy of the array
+    void* p = nullptr;
+    HIPCK(m, hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    slot.ptr = static_cast<uint8_t*>(p);
+  }
+  if (slot.owner != m->uid || m->static_dirty) {
+    // this model's parameter block (exchange base = the array) and work table
+    fill_params(m);
+    m->P_static = m->P;
+    m->P_static.xch = (decltype(m->P_static.xch))slot.ptr;
+    HIPCK(m, hipMemcpyAsync(slot.ptr + m->params_off, &m->P_static, sizeof(Params), hipMemcpyHostToDevice, s));
+    HIPCK(m, hipMemcpyAsync(slot.ptr + 8 * m->P.x.sched, m->sched.data(), m->sched.size() * sizeof(int32_t),
+                            hipMemcpyHostToDevice, s));
+    slot.owner = m->uid;
+    slot.extent = std::max(slot.extent, (size_t)(8 * m->P.x.err));
+    m->static_dirty = false;
+  }
+  uint32_t epoch = (slot.epoch + 1) & kEpochMask;
+  if (epoch == 0) {   // tags would repeat: clear every exchange word used so far
+    HIPCK(m, launch_zero_words(reinterpret_cast<uint64_t*>(slot.ptr), slot.extent / 8, s));
+    epoch = 1;
+  }
+  slot.epoch = epoch;
+  // a failed earlier step leaves its code in the error word: start clean
+  HIPCK(m, launch_zero_words(reinterpret_cast<uint64_t*>(slot.ptr) + m->P.x.err, 1, s));
+  return launch_with(m, reinterpret_cast<const Params*>(slot.ptr + m->params_off), epoch, d_token, pos, d_next,
+                     d_logits, s);
 }
 
 int32_t mk_decode_step(mk_model* m, int32_t token, int32_t pos, mk_stream_t stream) {
@@ -907,6 +1001,7 @@ int mk_set_option(mk_model* m, int32_t key, int64_t value) {
       return fail(m, MK_E_INVALID, "unknown option %d", key);
   }
   m->params_dirty = true;
+  m->static_dirty = true;
   return MK_OK;
 }
 

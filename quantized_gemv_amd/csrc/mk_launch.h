@@ -25,6 +25,9 @@ hipError_t launch_pack_fp4(const uint16_t* src, int N, int K, uint8_t* codes, ui
                            int ts_index, uint32_t* amax, int row_off, int row_step, int search, hipStream_t s);
 hipError_t launch_rope(float* out, int max_ctx, int hd, double theta, hipStream_t s);
 hipError_t launch_decode_codes(int codec, const uint8_t* in, int n, float* out, hipStream_t s);
+// Set n 64-bit words to zero with a kernel (no hipMemsetAsync, so the clear
+// is an ordinary kernel node when the caller captures the stream).
+hipError_t launch_zero_words(uint64_t* p, size_t n, hipStream_t s);
 
 // Batched prefill (mk_prefill.hip): positions [c0, c0 + cn) of a prompt
 // through every layer; with `last`, also the LM head of position c0+cn-1 and

@@ -1,6 +1,8 @@
 // gfx950 kernels that run once per model: the weight packers (the page's
 // FP8 and NVFP4 recipes), the RoPE table builder, and a codec test hook.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <math.h>
 #include <stdint.h>
 
@@ -172,6 +174,18 @@ __global__ void round_bf16_kernel(const float* in, int n, float* out) {
 }
 
 // ------------------------------------------------------- launch wrappers
+__global__ void zero_words_kernel(uint64_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+hipError_t launch_zero_words(uint64_t* p, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const size_t blocks = std::min<size_t>(1024, (n + 255) / 256);
+  hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack_bf16(const uint16_t* src, int N, int K, uint16_t* dst, int row_off, int row_step,
                             hipStream_t s) {
   if (N <= 0) return hipSuccess;

@@ -85,6 +85,7 @@ def load(xray: bool = False) -> ctypes.CDLL:
         "mk_prefill": (ctypes.c_int32, [_VP, P(ctypes.c_int32), ctypes.c_int32, _VP]),
         "mk_decode_step": (ctypes.c_int32, [_VP, ctypes.c_int32, ctypes.c_int32, _VP]),
         "mk_decode_step_async": (ctypes.c_int, [_VP, _VP, ctypes.c_int32, _VP, _VP, _VP]),
+        "mk_decode_step_async_noalloc": (ctypes.c_int, [_VP, _VP, ctypes.c_int32, _VP, _VP, _VP]),
         "mk_check_device_error": (ctypes.c_int, [_VP, _VP]),
         "mk_get_trace": (ctypes.c_int, [_VP, _VP, ctypes.c_size_t, P(ctypes.c_size_t)]),
         "mk_decode_codes": (ctypes.c_int, [ctypes.c_int32, _VP, ctypes.c_int32, _VP, _VP]),
@@ -230,6 +231,13 @@ class Decoder:
         self._check(self.lib.mk_decode_step_async(self.h, d_token.data_ptr(), int(pos), d_next.data_ptr(),
                                                   d_logits.data_ptr() if d_logits is not None else None,
                                                   _stream()))
+
+    def decode_step_async_noalloc(self, d_token, pos: int, d_next, d_logits=None) -> None:
+        """mk_decode_step_async_noalloc: the step with the library's static
+        scratch array in place of the bound scratch buffer."""
+        self._check(self.lib.mk_decode_step_async_noalloc(self.h, d_token.data_ptr(), int(pos), d_next.data_ptr(),
+                                                          d_logits.data_ptr() if d_logits is not None else None,
+                                                          _stream()))
 
     def check_device_error(self) -> None:
         self._check(self.lib.mk_check_device_error(self.h, _stream()))

@@ -14,12 +14,16 @@ the seeded synthetic Qwen3-0.6B-shaped weights, with the oracle alone:
           whether the top-1 token equals bf16's, and the relative L2
           distance of the logits, for FP8 per row and FP4-mix (without and
           with the search).
+  greedy  the page's first-64-token greedy agreement: per prompt, each
+          format decodes 64 tokens greedily on its own; the agreement is the
+          fraction of those positions whose token equals bf16's, averaged
+          over the prompts.
 
 Random weights give flat, nearly uninformative output distributions, so
 these figures flag gross breakage and compare recipes on equal terms; they
 say nothing of a trained model's quality.
 
-    python -m oracle.quality [--layers 0,13,27] [--radii 1,2,4,8] [--steps 64]
+    python -m oracle.quality [--layers 0,13,27] [--radii 1,2,4,8] [--steps 64] [--prompts 8]
 """
 from __future__ import annotations
 
@@ -63,9 +67,28 @@ def mse_report(master, layers, radii):
 
 
 def softmax64(x: np.ndarray) -> np.ndarray:
+    """The softmax of a logit vector, in float64."""
     z = x.astype(np.float64) - np.max(x)
     e = np.exp(z)
     return e / e.sum()
+
+
+def kl_divergence(ref_logits: np.ndarray, logits: np.ndarray) -> float:
+    """KL(p || q) in nats, p and q the softmax distributions of the
+    reference logits and of the other logits: sum_i p_i (log p_i - log q_i),
+    a term with p_i = 0 counting 0."""
+    p, q = softmax64(ref_logits), softmax64(logits)
+    t = np.where(p > 0, p * (np.log(np.where(p > 0, p, 1.0)) - np.log(q)), 0.0)
+    return float(np.sum(t))
+
+
+def greedy_agreement(ref_tokens, tokens, n: int = 64) -> float:
+    """The fraction of the first n positions at which two greedy decodes of
+    the same prompt chose the same token (the page's agreement measure)."""
+    a, b = np.asarray(ref_tokens)[:n], np.asarray(tokens)[:n]
+    if len(a) < n or len(b) < n:
+        raise ValueError(f"need {n} tokens from each decode")
+    return float(np.mean(a == b))
 
 
 def teacher_forced_logits(master, wfmt, prompt, forced, fp4_search=0):
@@ -86,12 +109,29 @@ def logits_report(master, prompt, forced, variants):
         got = teacher_forced_logits(master, wfmt, prompt, forced, k)
         kl, top1, rel = [], [], []
         for a, b in zip(ref, got):
-            p, q = softmax64(a), softmax64(b)
-            kl.append(float(np.sum(p * (np.log(p) - np.log(q)))))
+            kl.append(kl_divergence(a, b))
             top1.append(int(np.argmax(a)) == int(np.argmax(b)))
             rel.append(float(np.linalg.norm(b - a) / np.linalg.norm(a)))
         rows.append((name, float(np.mean(kl)), float(np.max(kl)), float(np.mean(top1)), float(np.mean(rel))))
     return rows
+
+
+def greedy_report(master, prompts, n, variants):
+    """Mean first-n greedy agreement with bf16 over the prompts, per format."""
+    import synth
+
+    def decode(wfmt, k):
+        orc = Oracle(master, wfmt, max(len(p) for p in prompts) + n, fp4_search=k)
+        return [orc.generate(p, n - 1, batched_prefill=True)[0] for p in prompts]
+
+    ref = decode(synth.BF16, 0)
+    rows = []
+    for name, wfmt, k in variants:
+        got = decode(wfmt, k)
+        agree = [greedy_agreement(a, b, n) for a, b in zip(ref, got)]
+        distinct = np.mean([len(set(t)) for t in got])
+        rows.append((name, float(np.mean(agree)), float(np.min(agree)), float(distinct)))
+    return rows, float(np.mean([len(set(t)) for t in ref]))
 
 
 def main():
@@ -100,6 +140,8 @@ def main():
     ap.add_argument("--radii", default="1,2,4,8")
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--search", type=int, default=4, help="radius of the searched FP4-mix variant")
+    ap.add_argument("--prompts", type=int, default=8, help="prompts of the greedy agreement")
+    ap.add_argument("--greedy-len", type=int, default=64)
     args = ap.parse_args()
     sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     import synth
@@ -124,6 +166,14 @@ def main():
     print("|---|---:|---:|---:|---:|")
     for name, kl, klmax, top1, rel in logits_report(master, prompt, forced, variants):
         print(f"| {name} | {kl:.3e} | {klmax:.3e} | {top1:.3f} | {rel:.4f} |")
+    prompts = [synth.make_prompt(sh.vocab, wl.prompt_len, 100 + i) for i in range(args.prompts)]
+    rows, ref_distinct = greedy_report(master, prompts, args.greedy_len, variants)
+    print(f"\nfirst-{args.greedy_len}-token greedy agreement with bf16, {args.prompts} prompts of "
+          f"{wl.prompt_len} tokens (bf16 itself: {ref_distinct:.1f} distinct tokens per decode)")
+    print("| format | mean agreement | min agreement | distinct tokens per decode |")
+    print("|---|---:|---:|---:|")
+    for name, mean, low, distinct in rows:
+        print(f"| {name} | {mean:.3f} | {low:.3f} | {distinct:.1f} |")
     print(f"\n({time.time() - t0:.0f} s)")
 
 

@@ -181,6 +181,84 @@ def test_batched_prefill_equals_stepwise():
         assert np.allclose(c1.k, c2.k, rtol=1e-10, atol=1e-12)
 
 
+# the bf16 rounding points of one layer in the batched prefill, in the order
+# it takes them (GEMV input, K, V, attention output, post-attention GEMV
+# input, SwiGLU output), then the final norm's output
+ROUNDING_POINTS = ("xn", "k", "v", "o", "xn2", "h", "final")
+
+
+def _prefill_skipping(o, toks, skip):
+    """The batched prefill with rounding point `skip` (an index into
+    ROUNDING_POINTS) left out in every layer: a planted mistake."""
+    L = o.shape.n_layers
+    orig, calls = M.Oracle._r, [0]
+
+    def r(self, x):
+        i = calls[0]
+        calls[0] += 1
+        hit = i % 6 == skip if i < 6 * L else skip == 6
+        return x.astype(self.dt) if hit else orig(self, x)
+
+    c = o.new_cache()
+    M.Oracle._r = r
+    try:
+        _, logits = o.prefill_batched(c, toks)
+    finally:
+        M.Oracle._r = orig
+    assert calls[0] == 6 * L + 1
+    return c, logits
+
+
+@pytest.mark.parametrize("wfmt", [synth.BF16, synth.FP8_ROW, synth.FP4_MIX])
+def test_batched_prefill_rounding_points(wfmt):
+    """The batched prefill takes every bf16 rounding point of the stepwise
+    decode.  In float64 a change of summation order moves a value by about
+    1e-16 of itself, far too little to move any float32 or bf16 rounding, so
+    with the rounding points on, the batched and stepwise prefills must give
+    bit-identical caches and logits.  Leaving out any one rounding point of
+    the batched prefill (each planted in turn) breaks that."""
+    master = synth.make_weights(synth.TINY, 0)
+    toks = synth.make_prompt(synth.TINY.vocab, 48, seed=31)
+    o = M.Oracle(master, wfmt, 64, dtype=F64)
+    a, b = o.new_cache(), o.new_cache()
+    ta, la = o.prefill(a, toks)
+    tb, lb = o.prefill_batched(b, toks)
+    assert ta == tb
+    assert np.array_equal(a.k, b.k) and np.array_equal(a.v, b.v)
+    assert np.array_equal(la, lb)
+    for skip, name in enumerate(ROUNDING_POINTS):
+        c, lc = _prefill_skipping(o, toks, skip)
+        same = np.array_equal(a.k, c.k) and np.array_equal(a.v, c.v) and np.array_equal(la, lc)
+        assert not same, ("planted mistake not caught", name)
+
+
+@pytest.mark.parametrize("wfmt", [synth.BF16, synth.FP8_ROW, synth.FP4_MIX])
+def test_batched_prefill_float32(wfmt):
+    """In float32 (the arithmetic of the references the GPU tests use) the
+    batched and stepwise prefills differ only by summation order: both
+    caches hold bf16 values; layer 0, where both start from the same
+    embeddings, is within one bf16 step per element and at least 99.9 %
+    bit-equal; every cached row of every layer is within relative L2 1e-2;
+    the logits too."""
+    from oracle.codecs import bf16_round
+    master = synth.make_weights(synth.TINY, 0)
+    toks = synth.make_prompt(synth.TINY.vocab, 48, seed=31)
+    o = M.Oracle(master, wfmt, 64)
+    a, b = o.new_cache(), o.new_cache()
+    _, la = o.prefill(a, toks)
+    _, lb = o.prefill_batched(b, toks)
+    for x, y in ((a.k, b.k), (a.v, b.v)):
+        x, y = x[:, :, :48], y[:, :, :48]
+        assert np.array_equal(bf16_round(y), y) and np.array_equal(bf16_round(x), x)
+        x64, y64 = x.astype(F64), y.astype(F64)
+        step = 2.0 ** -7 * np.maximum(np.abs(x64[0]), np.abs(y64[0]))
+        assert np.all(np.abs(x64[0] - y64[0]) <= step)
+        assert np.mean(x[0] == y[0]) >= 0.999
+        rel = np.linalg.norm(x64 - y64, axis=-1) / np.linalg.norm(x64, axis=-1)
+        assert rel.max() <= 1e-2
+    assert np.linalg.norm(la - lb) / np.linalg.norm(la) <= 1e-2
+
+
 def test_step_rejects_out_of_range():
     _, o = _oracle(synth.TINY, synth.BF16, max_ctx=8)
     c = o.new_cache()

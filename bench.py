@@ -46,6 +46,12 @@ def parse():
     ap.add_argument("--prefill-bench", action="store_true",
                     help="also time mk_prefill of the workload's prompt both ways (one decode launch per "
                          "position, and the batched matrix-core prefill) and add a 'prefill' object")
+    ap.add_argument("--grid", type=int, default=0, help="workgroups per launch (0: one per compute unit)")
+    ap.add_argument("--sync", type=int, default=0,
+                    help="0 tagged exchange words (the default); 1 one grid barrier per phase hand-off with "
+                         "relaxed counters; 2 the same barrier with agent-scope release/acquire fences")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="with the bf16 workload, skip the FP8 workload's figure that the line carries too")
     ap.add_argument("--xray", action="store_true",
                     help="X-ray build: print the per-phase budget of the step at position P + K/2 "
                          "instead of the headline line")
@@ -139,24 +145,72 @@ def cpu_baseline(master, wl, n_steps, prompt, budget_s):
         threads = len(os.sched_getaffinity(0))
     orc = Oracle(master, wl.wfmt, wl.prompt_len + n_steps + 1)
     done, spent, last = 0, 0.0, wl.prompt_len
-    for _ in range(2):
+    tokens, gaps = [], []   # the first pass's greedy tokens and the top-2 gap behind each
+    for rep in range(2):
         cache = orc.new_cache()
-        tok, _ = orc.prefill_batched(cache, prompt)
+        tok, lg = orc.prefill_batched(cache, prompt)
+        if rep == 0:
+            tokens.append(tok)
+            gaps.append(top2_gap(lg))
         for i in range(n_steps):
             t0 = time.perf_counter()
             lg = orc.step(cache, tok, wl.prompt_len + i)
-            tok = int(np.argmax(lg))
+            tok = argmax_lowest(lg)
             spent += time.perf_counter() - t0
             done += 1
             last = max(last, wl.prompt_len + i)
+            if rep == 0:
+                tokens.append(tok)
+                gaps.append(top2_gap(lg))
             if spent >= budget_s:
                 break
         if spent >= budget_s:
             break
-    return {"value": done / spent, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} greedy decode steps at positions {wl.prompt_len}..{last} (the timed positions, "
-                      f"in up to two passes, each after an untimed batched prefill of the same "
-                      f"{wl.prompt_len}-token prompt); {spent:.1f} s of numpy float32 on the host"}
+    out = {"value": done / spent, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{done} greedy decode steps at positions {wl.prompt_len}..{last} (the timed positions, "
+                     f"in up to two passes, each after an untimed batched prefill of the same "
+                     f"{wl.prompt_len}-token prompt); {spent:.1f} s of numpy float32 on the host"}
+    return out, tokens, gaps
+
+
+# Largest logit difference between two orders of summation of the oracle
+# itself (its batched against its stepwise prefill, then the same tokens) at
+# the 0.6B shape after the 128-token prompt; twice it is the margin below
+# which a top-2 gap counts as a near-tie (the parity tests measure it per
+# step).
+ORDER_NOISE = 1.5e-2
+
+
+def top2_gap(logits) -> float:
+    import numpy as np
+    t = np.partition(logits, -2)[-2:]
+    return float(t[1] - t[0])
+
+
+def argmax_lowest(logits) -> int:
+    import numpy as np
+    return int(np.flatnonzero(logits == np.max(logits))[0])
+
+
+def greedy_gate(gpu_tokens, oracle_tokens, oracle_gaps):
+    """The same-session correctness gate (the page's "Hard constraints": no
+    speed number counts unless that build passed the correctness check in
+    the same session): the timed run's greedy tokens against the oracle's
+    own greedy decode of the same prompt.  They must agree up to the first
+    step whose oracle top-2 gap is below the near-tie margin; past a
+    divergence the two sequences are no longer comparable."""
+    n = min(len(gpu_tokens), len(oracle_tokens))
+    margin = max(1e-3, 2 * ORDER_NOISE)
+    agree = 0
+    while agree < n and int(gpu_tokens[agree]) == int(oracle_tokens[agree]):
+        agree += 1
+    first_tie = next((i for i in range(n) if oracle_gaps[i] < margin), None)
+    res = {"compared": n, "agree_prefix": agree, "near_tie_margin": margin, "first_near_tie": first_tie}
+    if agree < n:
+        res["divergence_oracle_gap"] = round(float(oracle_gaps[agree]), 6)
+    # a divergence is allowed only at or after the first near-tie
+    res["pass"] = bool(agree == n or (first_tie is not None and agree >= first_tie))
+    return res
 
 
 def main():
@@ -183,7 +237,7 @@ def main():
     master = synth.make_weights(sh, wl.weight_seed)
     prompt = synth.make_prompt(sh.vocab, wl.prompt_len, wl.prompt_seed)
 
-    dec = native.Decoder(sh, wl.wfmt, max_ctx, xray=args.xray,
+    dec = native.Decoder(sh, wl.wfmt, max_ctx, xray=args.xray, grid=args.grid, sync_mode=args.sync or None,
                          poll_sleep=None if args.poll_sleep < 0 else args.poll_sleep,
                          launch_mode=None if args.launch < 0 else args.launch,
                          split_chunk=None if args.split_chunk < 0 else args.split_chunk,
@@ -205,11 +259,73 @@ def main():
         print(json.dumps({"workload": wl.name, **xray_report(dec, wl, K, prompt, args.xray_dump)}), flush=True)
         dec.close()
         return
+    res = time_decode(dec, wl, prompt, K, W, args.repeats)
+    dec.close()
+    del dec
+    out = {
+        "metric": "batch-1 decode tokens/s (0.6B shape); % of HBM roofline on weight bytes",
+        "value": res["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {0: "bf16", 1: "fp8_e4m3", 2: "fp4_e2m1+fp8_e4m3"}[wl.wfmt],
+        "data": "synthetic (seeded random weights N(0,0.02), uniform random prompt)",
+        "config": {"workload": wl.name, "prompt_len": wl.prompt_len, "decode_steps": K,
+                   "positions": [wl.prompt_len, wl.prompt_len + K - 1],
+                   "weight_format": synth.WFMT_NAMES[wl.wfmt], "accumulate": "f32", "batch": 1,
+                   "grid": "one workgroup per CU: 1 courier + 7 compute waves; attention on one "
+                           "workgroup per KV head, split over the workgroups of its XCD from 576 "
+                           "cached positions on" if not args.grid else f"{args.grid} workgroups",
+                   "timed_runs": len(res["times"]),
+                   "run_seconds": [round(t, 6) for t in res["times"]]},
+        "weight_bytes_per_token": res["weight_bytes"],
+        "weight_roofline_pct": res["weight_roofline_pct"],
+        "roofline": res["roofline"],
+        "greedy_tokens_head": [int(t) for t in res["tokens"][:8]],
+    }
+    if wl.name == "qwen3_0p6b_bf16" and not args.no_fp8 and args.prompt_len <= 0:
+        # the FP8 workload (same master, same prompt and positions), timed the same way
+        wl8 = synth.WORKLOADS["qwen3_0p6b_fp8"]
+        d8 = native.Decoder(sh, wl8.wfmt, max_ctx, grid=args.grid)
+        dev_master = native.master_to_device(master)
+        d8.pack(dev_master)
+        del dev_master
+        torch.cuda.empty_cache()
+        r8 = time_decode(d8, wl8, prompt, K, W, args.repeats)
+        d8.close()
+        del d8
+        out["fp8"] = {"workload": wl8.name, "value": r8["value"], "unit": "tokens/s", "ms_per_step": r8["ms_per_step"],
+                      "dtype": "fp8_e4m3", "weight_bytes_per_token": r8["weight_bytes"],
+                      "weight_roofline_pct": r8["weight_roofline_pct"], "roofline": r8["roofline"],
+                      "run_seconds": [round(t, 6) for t in r8["times"]]}
+    if args.prefill_bench:
+        dp = native.Decoder(sh, wl.wfmt, max_ctx, grid=args.grid)
+        dp.pack(native.master_to_device(master))
+        out["prefill"] = prefill_bench(dp, native, prompt)
+        dp.close()
+    if not args.no_cpu_baseline:
+        cpu, o_tokens, o_gaps = cpu_baseline(master, wl, K, prompt, args.cpu_seconds)
+        out["cpu_baseline"] = cpu
+        out["greedy_gate"] = greedy_gate(res["tokens"], o_tokens, o_gaps)
+    torch.cuda.synchronize()
+    print(json.dumps(out), flush=True)
+
+
+def time_decode(dec, wl, prompt, K, W, repeats):
+    """W untimed warm-up steps, then `repeats` timed runs of K steps, each
+    after an untimed prefill: HIP events on the stream the kernel runs on
+    around the K chained launches.  Returns the median figures."""
+    import numpy as np
+    import torch
     stream = torch.cuda.current_stream()
     toks = torch.zeros(max(K, W) + 1, dtype=torch.int32, device="cuda")
 
     def run(n):
-        """Prefill, then n chained decode steps; returns elapsed seconds."""
         first = dec.prefill(prompt)
         toks[0] = first
         torch.cuda.synchronize()
@@ -224,8 +340,8 @@ def main():
         return e0.elapsed_time(e1) / 1e3
 
     run(W)                       # warm-up pass
-    times = [run(K) for _ in range(max(1, args.repeats))]
-    tokens_ref = toks[:K + 1].cpu().numpy().copy()
+    times = [run(K) for _ in range(max(1, repeats))]
+    tokens = toks[:K + 1].cpu().numpy().copy()
     dt = float(np.median(times))
     tps = K / dt
     sizes = dec.sizes
@@ -233,43 +349,13 @@ def main():
     # algorithmic bytes per launch: every weight byte once, plus the KV cache
     # read over positions 0..pos (mean over the timed positions)
     mean_ctx = wl.prompt_len + (K - 1) / 2.0 + 1
-    kv_bytes = float(sizes.kv_bytes_per_position) * mean_ctx
-    algo = wbytes + kv_bytes
+    algo = wbytes + float(sizes.kv_bytes_per_position) * mean_ctx
     achieved = algo / (dt / K) / 1e9
-    out = {
-        "metric": "batch-1 decode tokens/s (0.6B shape); % of HBM roofline on weight bytes",
-        "value": round(tps, 2),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
-        "ms_per_step": round(dt / K * 1e3, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": {0: "bf16", 1: "fp8_e4m3", 2: "fp4_e2m1+fp8_e4m3"}[wl.wfmt],
-        "data": "synthetic (seeded random weights N(0,0.02), uniform random prompt)",
-        "config": {"workload": wl.name, "prompt_len": wl.prompt_len, "decode_steps": K,
-                   "positions": [wl.prompt_len, wl.prompt_len + K - 1],
-                   "weight_format": synth.WFMT_NAMES[wl.wfmt], "accumulate": "f32", "batch": 1,
-                   "grid": "one workgroup per CU: 1 courier + 7 compute waves; attention on one "
-                           "workgroup per KV head, split over the workgroups of its XCD from 576 "
-                           "cached positions on", "timed_runs": len(times),
-                   "run_seconds": [round(t, 6) for t in times]},
-        "weight_bytes_per_token": wbytes,
-        "weight_roofline_pct": round(100.0 * wbytes * tps / (PEAK_HBM_GBPS * 1e9), 2),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(wl.name),
-                     "kernel": "mk::decode_kernel",
-                     "bytes_per_launch": int(algo)},
-        "greedy_tokens_head": [int(t) for t in tokens_ref[:8]],
-    }
-    if args.prefill_bench:
-        out["prefill"] = prefill_bench(dec, native, prompt)
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(master, wl, K, prompt, args.cpu_seconds)
-    dec.close()
-    print(json.dumps(out), flush=True)
+    return {"value": round(tps, 2), "ms_per_step": round(dt / K * 1e3, 5), "times": times, "tokens": tokens,
+            "weight_bytes": wbytes, "weight_roofline_pct": round(100.0 * wbytes * tps / (PEAK_HBM_GBPS * 1e9), 2),
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                         "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(wl.name),
+                         "kernel": "mk::decode_kernel", "bytes_per_launch": int(algo)}}
 
 
 if __name__ == "__main__":

@@ -266,6 +266,19 @@ int mk_decode_codes(int32_t codec, const uint8_t* d_codes, int32_t n, float* d_o
  * writes the same KV cache up to summation order.  1 needs hidden,
  * intermediate and n_q_heads*head_dim divisible by 64, hidden <= 4096 and
  * head_dim 64 or 128 (else MK_E_UNSUPPORTED).
+ * Key 11, synchronisation between phases [0]: 0 tagged exchange words (each
+ * consumer waits for exactly the values it reads); 1 and 2 one grid-wide
+ * barrier per phase hand-off, the monolith page's baseline kept for
+ * comparison ("Upstream facts": four full-grid atomic barriers per layer;
+ * "Design decisions": the sync experiments measure the counters against
+ * them): every workgroup arrives at an agent-scope counter once its stores
+ * of the phase are complete, and every consumer waits for the last arrival
+ * before reading.  Mode 1 uses relaxed counter atomics (the values travel in
+ * device-coherent words); mode 2 arrives with an agent-scope release and
+ * leaves with an agent-scope acquire, the literal reading of the page's
+ * release/acquire counters (on MI355X an L2 write-back and an L2 invalidate
+ * of the workgroup's XCD at every barrier).  Modes 1 and 2 turn split
+ * attention off and are refused by mk_decode_step_async_noalloc.
  * Keys 1 and 2 are reserved.
  * Errors: MK_E_INVALID (unknown key, value out of range), MK_E_STATE. */
 int mk_set_option(mk_model* m, int32_t key, int64_t value);

@@ -68,6 +68,7 @@ struct mk_model {
   int coresident = 0;           // decode workgroups the device holds at once (set by mk_bind)
   int fp4_search = 0;           // NVFP4 block scale search radius (0: absolute-maximum recipe)
   int prefill_mode = 0;         // mk_prefill: 0 one decode launch per position, 1 batched (matrix cores)
+  int sync_mode = 0;            // 0 tagged exchange words, 1 one grid barrier per phase hand-off
   size_t pf_off = 0;            // batched-prefill workspace in the scratch buffer
   uint32_t epoch = 0;
   uint64_t uid = 0;             // unique per model handle (owner of the static scratch contents)
@@ -255,6 +256,8 @@ void layout_scratch(mk_model* m, int grid, bool for_sizing = true) {
   uint64_t w = lw * (uint64_t)c.n_layers;
   X.arg = al(w);
   w = X.arg + 2ull * grid;
+  X.bar = al(w);
+  w = X.bar + 5ull * c.n_layers + 1;
   X.err = al(w);
   X.amax = X.err + 1;
   w = X.amax + 1;
@@ -474,6 +477,7 @@ void fill_params(mk_model* m) {
   P.n_phases = n_phases(c);
   P.split_max = kMaxSplit;
   P.split_pw = (int)split_pw(c);
+  P.bar_fence = m->sync_mode == 2 ? 1u : 0u;
 }
 
 int sync_params(mk_model* m, hipStream_t s) {
@@ -494,6 +498,11 @@ int32_t read_token_and_error(mk_model* m, const int32_t* d_next, hipStream_t s) 
   if (err) {
     uint32_t zero = 0;
     HIPCK(m, hipMemcpy(m->d_scratch + 8 * m->P.x.err, &zero, 4, hipMemcpyHostToDevice));
+    // a step that failed may have left workgroups short of some barriers:
+    // restart the grid-barrier counters
+    HIPCK(m, launch_zero_words(reinterpret_cast<uint64_t*>(m->d_scratch) + m->P.x.bar, 5ull * m->cfg.n_layers + 1,
+                               s));
+    HIPCK(m, hipStreamSynchronize(s));
     if (err & 1u) return fail(m, MK_E_TIMEOUT, "a kernel wait exceeded its spin bound");
     return fail(m, MK_E_INVALID, "the kernel read a token outside the vocabulary");
   }
@@ -506,12 +515,14 @@ int launch_with(mk_model* m, const Params* dp, uint32_t epoch, const int32_t* d_
                 float* d_logits, hipStream_t s) {
   const mk_config& c = m->cfg;
   const bool coop = m->launch_mode == 0 || (m->launch_mode < 0 && m->P.grid > m->coresident);
-  const int ns = m->split_chunk > 0 && pos >= m->split_from ? std::min(m->split_n, pos / m->split_chunk) : 0;
+  const bool barrier = m->sync_mode != 0;
+  const int ns = !barrier && m->split_chunk > 0 && pos >= m->split_from ? std::min(m->split_n, pos / m->split_chunk)
+                                                                        : 0;
   if (!coop && m->P.grid > m->coresident)
     return fail(m, MK_E_UNSUPPORTED, "plain launch: grid %d exceeds the %d workgroups the device holds at once",
                 m->P.grid, m->coresident);
   HIPCK(m, launch_decode(dp, c.wfmt, c.head_dim, c.n_q_heads / c.n_kv_heads, c.hidden, c.n_q_heads * c.head_dim,
-                         c.intermediate, m->P.grid, coop, d_token, pos, ns, epoch, d_next, d_logits, s));
+                         c.intermediate, m->P.grid, coop, barrier, d_token, pos, ns, epoch, d_next, d_logits, s));
   return MK_OK;
 }
 
@@ -758,6 +769,9 @@ int mk_decode_step_async_noalloc(mk_model* m, const int32_t* d_token, int32_t po
     return fail(m, MK_E_INVALID, "mk_decode_step_async_noalloc: token buffers must be distinct and non-null");
   if (pos < 0 || pos >= m->cfg.max_ctx) return fail(m, MK_E_INVALID, "position %d outside [0, %d)", pos, m->cfg.max_ctx);
   if (!m->bound || !m->packed) return fail(m, MK_E_STATE, "decode before mk_bind and mk_pack_weights");
+  if (m->sync_mode != 0)
+    return fail(m, MK_E_UNSUPPORTED, "mk_decode_step_async_noalloc: the grid-barrier variant (option 11) needs the "
+                                     "bound scratch buffer");
   if (static_need(m) > kStaticScratchBytes)
     return fail(m, MK_E_UNSUPPORTED,
                 "mk_decode_step_async_noalloc: this model's step needs %zu bytes of scratch, more than the "
@@ -991,6 +1005,10 @@ int mk_set_option(mk_model* m, int32_t key, int64_t value) {
       if (value < 0 || value > 1) return fail(m, MK_E_INVALID, "prefill mode must be 0 or 1");
       if (value == 1 && !prefill_supported(m->cfg)) return fail(m, MK_E_UNSUPPORTED, "batched prefill: shape not supported");
       m->prefill_mode = (int)value;
+      break;
+    case 11:
+      if (value < 0 || value > 2) return fail(m, MK_E_INVALID, "sync mode must be 0, 1 or 2");
+      m->sync_mode = (int)value;
       break;
     case 9:
       if (value < 0 || value > 0x7E) return fail(m, MK_E_INVALID, "FP4 scale search radius out of range");

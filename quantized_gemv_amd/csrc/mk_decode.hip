@@ -28,6 +28,8 @@
 // per token).  No MFMA: these are matrix-vector products, bound by HBM
 // bandwidth.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <math.h>
 #include <stdint.h>
 
@@ -119,6 +121,7 @@ struct Smem {
   alignas(16) int32_t bidx[kCW];
   float r_xd, r_xo;                      // 1/rms of xd_raw and xo_raw
   uint32_t seq;                          // inputs handed over by the courier (kAbort: abort)
+  uint32_t arr[kCW];                     // grid-barrier variant: barriers each compute wave has finished its part of
   XR_FIELD
 };
 
@@ -317,7 +320,14 @@ __device__ __forceinline__ void gain_load(__amdgpu_buffer_rsrc_t rw, uint32_t of
 // LONG: the split-attention variant (for long contexts): every GEMV
 // workgroup on a KV head's XCD also takes a slice of that head's cached
 // positions, and the head's home workgroup merges the slices.
-template <int WF, int HD, int GS, int NH, int NQ, int NI, bool LONG>
+// BAR: the grid-barrier variant, the page's baseline synchronisation kept
+// for comparison: every hand-off between phases is one grid-wide barrier
+// (each workgroup arrives once its compute waves' stores of the phase are
+// complete, with an agent-scope release; all wait for the last arrival, then
+// an agent-scope acquire) before any consumer reads the phase's outputs.
+// The tagged words are still read after it, so the values are the same
+// either way; only the waiting differs.  Not combined with LONG.
+template <int WF, int HD, int GS, int NH, int NQ, int NI, bool LONG, bool BAR>
 struct Kern {
   static constexpr uint32_t F_LIN = WF == 0 ? FMT_BF16 : (WF == 1 ? FMT_FP8 : FMT_FP4);  // q, k, v, o, gate, up
   static constexpr uint32_t F_8 = WF == 0 ? FMT_BF16 : FMT_FP8;                          // down, embed / LM head
@@ -330,7 +340,69 @@ struct Kern {
   static constexpr int PP = (NOUT + 2 * GS) / 2;   // word pairs of one helper partial
   static constexpr int KP = kSplitGatherK;     // helper-partial pairs per lane and round of the home's gather
   static_assert(NOUT <= kCW * 64, "one merge thread per attention output");
+  static_assert(!(LONG && BAR), "the grid-barrier variant has no split attention");
   typedef Smem<HD, GS, NH, NQ, NI> S;
+
+  // ------------------------------------------------- grid-barrier variant
+  // Barriers of one step, in order: per layer l, 5l + {0: q/k/v, 1: attention
+  // output, 2: residual after O, 3: SwiGLU output, 4: residual after down};
+  // then 5L: the argmax words.  A compute wave records in s.arr[cw] how many
+  // barriers it has finished its part of: after its stores of a phase
+  // (waited for with vmcnt(0), which on gfx9 also waits for its loads in
+  // flight), or at once for a phase in which it stores nothing.
+  static __device__ __forceinline__ void arrive(S& s, int cw, uint32_t upto, bool stored) {
+    if (!BAR) return;
+    if (stored) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores are complete
+    asm volatile("" ::: "memory");
+    if (lane_id() == 0) lds_st(&s.arr[cw], upto);
+  }
+
+  // Courier: barrier b.  Wait until this workgroup's compute waves have
+  // finished their part, then arrive at the grid-wide counter of barrier b
+  // and wait until every workgroup of this launch has arrived (the counter
+  // reaches the next multiple of the grid).  With p.bar_fence the arrival is
+  // an agent-scope release and the departure an agent-scope acquire (on
+  // gfx950 an L2 write-back and an L2 invalidate of the workgroup's XCD);
+  // without, the counter operations are relaxed agent-scope atomics: the
+  // values themselves travel in device-coherent words whose stores the
+  // producing waves have waited for.  Bounded like every other wait.
+  static __device__ bool grid_barrier(const Params& p, S& s, uint32_t b) {
+    const int lane = lane_id();
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (true) {
+      const uint32_t a = lane < kCW ? lds_ld(&s.arr[lane]) : 0xFFFFFFFFu;
+      if (__builtin_amdgcn_ballot_w64(a < b + 1) == 0) break;
+      if (__builtin_amdgcn_s_memrealtime() - t0 > p.spin_limit) {
+        raise_error(p, ERR_TIMEOUT);
+        return false;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    MK_GLOBAL uint64_t* ctr = p.xch + p.x.bar + b;
+    uint64_t old = 0;
+    if (lane == 0) {
+      if (p.bar_fence)
+        old = __hip_atomic_fetch_add(ctr, 1ull, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        old = __hip_atomic_fetch_add(ctr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    old = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(old >> 32)) << 32) |
+          (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)old);
+    const uint64_t G = (uint64_t)p.grid, target = (old / G + 1) * G;
+    for (uint32_t n = 1;; ++n) {
+      const uint64_t v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__builtin_amdgcn_ballot_w64(v < target) == 0) break;
+      if (__builtin_amdgcn_s_memrealtime() - t0 > p.spin_limit) {
+        raise_error(p, ERR_TIMEOUT);
+        return false;
+      }
+      if ((n & 63u) == 0 && __hip_atomic_load(err_word(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+        return false;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (p.bar_fence) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return true;
+  }
 
   // ------------------------------------------------------------ courier
   // The inputs this workgroup needs, in order, for every layer; then the
@@ -386,7 +458,9 @@ struct Kern {
     for (int l = 0; l < L; ++l) {
       const uint64_t loff = (uint64_t)l * p.layer_stride;
       const int ph = 2 + 6 * l;
+      const uint32_t bq = 5u * (uint32_t)l;
       // ---- residual entering layer l (layer 0: the embedding above)
+      if (BAR && l > 0 && !grid_barrier(p, s, bq - 1)) return abort(s);
       if ((flags & 1) && l > 0) {
         XR_PUT(s, ph + 0, XR_START);
         if (!gather_pairs_at<KX>(p, rs, H / 2, make_tag(epoch, vec_id(l - 1, V_XD)), lo, hi, xword(p, l - 1, V_XD),
@@ -398,6 +472,7 @@ struct Kern {
         XR_PUT(s, ph + 0, XR_HANDOFF);
       }
       if (att < 0) lds_barrier();   // the compute waves' QKV stores are out; their weight burst follows
+      if (BAR && !grid_barrier(p, s, bq + 0)) return abort(s);
       // ---- q, k, v of KV head `att`: q/k RMSNorm, RoPE, KV append
       if (att >= 0) {
         XR_PUT(s, ph + 1, XR_START);
@@ -423,6 +498,7 @@ struct Kern {
         }
       }
       // ---- attention output
+      if (BAR && !grid_barrier(p, s, bq + 1)) return abort(s);
       if (flags & 2) {
         XR_PUT(s, ph + 3, XR_START);
         uint32_t ol[KO], oh[KO];
@@ -440,6 +516,7 @@ struct Kern {
         XR_PUT(s, ph + 3, XR_HANDOFF);
       }
       // ---- residual after O
+      if (BAR && !grid_barrier(p, s, bq + 2)) return abort(s);
       if (flags & 4) {
         XR_PUT(s, ph + 4, XR_START);
         if (!gather_pairs_at<KX>(p, rs, H / 2, make_tag(epoch, vec_id(l, V_XO)), lo, hi, xword(p, l, V_XO), mo))
@@ -450,6 +527,7 @@ struct Kern {
         XR_PUT(s, ph + 4, XR_HANDOFF);
       }
       // ---- SwiGLU output
+      if (BAR && !grid_barrier(p, s, bq + 3)) return abort(s);
       if (flags & 8) {
         XR_PUT(s, ph + 5, XR_START);
         uint32_t hl[KH], hh[KH];
@@ -467,6 +545,7 @@ struct Kern {
     }
     // ---- final residual -> final RMSNorm (LM-head input)
     const int ph_head = 2 + 6 * L;
+    if (BAR && !grid_barrier(p, s, 5u * (uint32_t)L - 1u)) return abort(s);
     {
       XR_PUT(s, ph_head, XR_START);
       if (!gather_pairs_at<KX>(p, rs, H / 2, make_tag(epoch, vec_id(L - 1, V_XD)), lo, hi, xword(p, L - 1, V_XD),
@@ -478,6 +557,7 @@ struct Kern {
       XR_PUT(s, ph_head, XR_HANDOFF);
     }
     lds_barrier();   // the compute waves' argmax candidates are in LDS
+    if (BAR && !grid_barrier(p, s, 5u * (uint32_t)L)) return false;
     // ---- workgroup 0: reduce every workgroup's (value, index)
     if (blockIdx.x == 0) {
       XR_PUT(s, ph_head + 1, XR_START);
@@ -742,6 +822,7 @@ struct Kern {
       XR_MAX(s, ph + 0, XR_DONE);
       }
     }
+    arrive(s, cw, 5u * (uint32_t)l + 2u, true);   // q/k/v stored; nothing of the attention output
     // ---- the layer's weight burst, once every wave of the workgroup has
     // issued its QKV stores (the courier joins this barrier after handing
     // over the layer's input): a burst queued ahead of another wave's stores
@@ -784,6 +865,7 @@ struct Kern {
       XR_MAX(s, ph + 3, XR_DONE);
       }
     }
+    arrive(s, cw, 5u * (uint32_t)l + 3u, true);
     // ---- gate/up + SwiGLU: a unit is the four rows behind one output word
     {
       if (u[S_GU] >= 0) {
@@ -812,6 +894,7 @@ struct Kern {
       XR_MAX(s, ph + 4, XR_DONE);
       }
     }
+    arrive(s, cw, 5u * (uint32_t)l + 4u, true);
     // ---- down + residual
     {
       if (u[S_D] >= 0) {
@@ -831,6 +914,7 @@ struct Kern {
       XR_MAX(s, ph + 5, XR_DONE);
       }
     }
+    arrive(s, cw, 5u * (uint32_t)l + 5u, true);
     return ok;
   }
 
@@ -1099,6 +1183,7 @@ struct Kern {
                                                    KVRegs& kv, uint32_t epoch, __amdgpu_buffer_rsrc_t rx, bool ok) {
     const int lane = lane_id();
     const int ph = 2 + 6 * l;
+    arrive(s, cw, 5u * (uint32_t)l + 1u, false);   // this workgroup stores no q/k/v
     ok = ok && wait_seq(p, &s.seq, (uint32_t)l + 1u);
     XR_MIN(s, ph + 1, XR_SEEN);
     att_prepare<true>(p, s, l, g, pos, cw, ok);
@@ -1218,6 +1303,7 @@ struct Kern {
     st_xword(rx, ok && t < NOUT && (t & 1) == 0 ? 8u * (xword(p, l, V_O) + (g * NOUT + t) / 2) : kOOB,
              pack_bf16(o, o1), make_tag(epoch, vec_id(l, V_O)));
     XR_MAX(s, ph + 1, XR_DONE);
+    arrive(s, cw, 5u * (uint32_t)l + 5u, true);   // attention output stored; nothing of the other phases
     lds_barrier();
     if (NEXT) kv_prefetch(p, l + 1, g, pos, cw, kv);
     return ok;
@@ -1363,6 +1449,7 @@ struct Kern {
     const int wave = wave_id(), lane = lane_id();
     const int wg = blockIdx.x;
     if (threadIdx.x == 0) s.seq = 0;
+    if (threadIdx.x < kCW) s.arr[threadIdx.x] = 0;
     XR_INIT(s);
     const int token = *d_token;
     if (token < 0 || token >= p.V) {
@@ -1413,6 +1500,7 @@ struct Kern {
         st_xword(rx, ok && lane == 0 ? off : kOOB, __float_as_uint(b), tag);
         st_xword(rx, ok && lane == 0 ? off + 8u : kOOB, (uint32_t)bi, tag);
       }
+      arrive(s, cw, 5u * (uint32_t)p.L + 1u, cw == 0);
     }
 #ifdef MK_XRAY
     __syncthreads();
@@ -1426,12 +1514,12 @@ struct Kern {
 // attention or not): the formats, the attention shape and every per-lane
 // register array size are compile-time constants.  `ns` is the number of
 // helpers per KV head in this step (0 without split attention).
-template <int WF, int HD, int GS, int NH, int NQ, int NI, bool LONG>
+template <int WF, int HD, int GS, int NH, int NQ, int NI, bool LONG, bool BAR>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const Params* __restrict__ pp, const int32_t* d_token,
                                                              int pos, int ns, uint32_t epoch, int32_t* d_next,
                                                              float* d_logits) {
   __shared__ Smem<HD, GS, NH, NQ, NI> s;
-  Kern<WF, HD, GS, NH, NQ, NI, LONG>::run(*pp, s, d_token, pos, ns, epoch, d_next, d_logits);
+  Kern<WF, HD, GS, NH, NQ, NI, LONG, BAR>::run(*pp, s, d_token, pos, ns, epoch, d_next, d_logits);
 }
 
 // ------------------------------------------------------- launch wrappers
@@ -1450,12 +1538,14 @@ bool decode_shape_supported(int hd, int gs, int hidden, int qdim, int inter) {
   return false;
 }
 
-static const void* decode_fn(int wfmt, int hd, int gs, int hidden, int qdim, int inter, bool split) {
+// variant: 0 the headline kernel, 1 split attention, 2 grid barriers
+static const void* decode_fn(int wfmt, int hd, int gs, int hidden, int qdim, int inter, int variant) {
   const void* fn = nullptr;
   const int nh = cdiv1024(hidden), nqd = cdiv1024(qdim), ni = cdiv1024(inter);
-#define MK_FN(W_, H_, G_, A_, B_, C_)                                                        \
-  (split ? reinterpret_cast<const void*>(decode_kernel<W_, H_, G_, A_, B_, C_, true>)         \
-         : reinterpret_cast<const void*>(decode_kernel<W_, H_, G_, A_, B_, C_, false>))
+#define MK_FN(W_, H_, G_, A_, B_, C_)                                                                  \
+  (variant == 1   ? reinterpret_cast<const void*>(decode_kernel<W_, H_, G_, A_, B_, C_, true, false>)   \
+   : variant == 2 ? reinterpret_cast<const void*>(decode_kernel<W_, H_, G_, A_, B_, C_, false, true>)   \
+                  : reinterpret_cast<const void*>(decode_kernel<W_, H_, G_, A_, B_, C_, false, false>))
 #define MK_CASE(H_, G_, A_, B_, C_)                                                                 \
   if (hd == H_ && gs == G_ && nh == A_ && nqd == B_ && ni == C_) {                                  \
     fn = wfmt == 0 ? MK_FN(0, H_, G_, A_, B_, C_) : (wfmt == 1 ? MK_FN(1, H_, G_, A_, B_, C_)       \
@@ -1468,21 +1558,22 @@ static const void* decode_fn(int wfmt, int hd, int gs, int hidden, int qdim, int
 }
 
 hipError_t decode_coresident(int wfmt, int hd, int gs, int hidden, int qdim, int inter, int* per_cu) {
-  int n[2];
-  for (int v = 0; v < 2; ++v) {
-    const void* fn = decode_fn(wfmt, hd, gs, hidden, qdim, inter, v == 1);
+  int n[3];
+  for (int v = 0; v < 3; ++v) {
+    const void* fn = decode_fn(wfmt, hd, gs, hidden, qdim, inter, v);
     if (!fn) return hipErrorInvalidValue;
     const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[v], fn, kThreads, 0);
     if (e != hipSuccess) return e;
   }
-  *per_cu = n[0] < n[1] ? n[0] : n[1];
+  *per_cu = std::min(n[0], std::min(n[1], n[2]));
   return hipSuccess;
 }
 
 hipError_t launch_decode(const Params* d_params, int wfmt, int hd, int gs, int hidden, int qdim, int inter, int grid,
-                         bool cooperative, const int32_t* d_token, int pos, int ns, uint32_t epoch, int32_t* d_next,
-                         float* d_logits, hipStream_t s) {
-  const void* fn = decode_fn(wfmt, hd, gs, hidden, qdim, inter, ns > 0);
+                         bool cooperative, bool barrier, const int32_t* d_token, int pos, int ns, uint32_t epoch,
+                         int32_t* d_next, float* d_logits, hipStream_t s) {
+  if (barrier && ns > 0) return hipErrorInvalidValue;
+  const void* fn = decode_fn(wfmt, hd, gs, hidden, qdim, inter, barrier ? 2 : (ns > 0 ? 1 : 0));
   if (!fn) return hipErrorInvalidValue;
   void* args[] = {&d_params, &d_token, &pos, &ns, &epoch, &d_next, &d_logits};
   if (cooperative) return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);

@@ -10,11 +10,12 @@ namespace mk {
 // `cooperative`: hipLaunchCooperativeKernel (the runtime guarantees that the
 // whole grid is resident) or a plain launch (the caller has checked with
 // decode_coresident() that the grid fits the device at once).
-// `ns` > 0 launches the split-attention variant with ns helpers per KV head.
+// `ns` > 0 launches the split-attention variant with ns helpers per KV head;
+// `barrier` the grid-barrier variant (needs ns == 0).
 hipError_t launch_decode(const Params* d_params, int wfmt, int hd, int gs, int hidden, int qdim, int inter, int grid,
-                         bool cooperative, const int32_t* d_token, int pos, int ns, uint32_t epoch, int32_t* d_next,
-                         float* d_logits, hipStream_t s);
-// Workgroups of the decode kernel (either variant) that one compute unit holds at once.
+                         bool cooperative, bool barrier, const int32_t* d_token, int pos, int ns, uint32_t epoch,
+                         int32_t* d_next, float* d_logits, hipStream_t s);
+// Workgroups of the decode kernel (any variant) that one compute unit holds at once.
 hipError_t decode_coresident(int wfmt, int hd, int gs, int hidden, int qdim, int inter, int* per_cu);
 bool decode_shape_supported(int hd, int gs, int hidden, int qdim, int inter);
 hipError_t launch_pack_bf16(const uint16_t* src, int N, int K, uint16_t* dst, int row_off, int row_step,

@@ -77,6 +77,7 @@ struct Xch {
   // starts a line of its own, at word i * pad_stride (0 = packed layout).
   uint32_t pad_c[kTypes], pad_stride[kTypes];
   uint64_t arg;               // argmax words [grid][2] (value, index)
+  uint64_t bar;               // grid-barrier variant: one arrival counter per barrier of a step (5L + 1)
   uint64_t err;               // error word (uint32 in a 64-bit slot)
   uint64_t amax;              // packing scratch: tensor abs-max (uint32 bits)
   uint64_t sched;             // the work table (int32)
@@ -138,6 +139,8 @@ struct Params {
   int n_phases;           // trace phases per step (trace stride per workgroup)
   int split_max;          // helper slots per KV head in the partials vector
   int split_pw;           // words per helper partial (outputs, maxima, sums; padded)
+  uint32_t bar_fence;     // grid-barrier variant: 1 arrive with an agent-scope release and leave with an
+                          // agent-scope acquire (L2 write-back and invalidate), 0 relaxed counters
 };
 
 }  // namespace mk

@@ -25,6 +25,7 @@ OPT_GRID, OPT_SPIN_LIMIT, OPT_TAG_SKEW, OPT_POLL_SLEEP, OPT_LAUNCH_MODE, OPT_SPL
     0, 3, 4, 5, 6, 7, 8
 OPT_FP4_SEARCH = 9
 OPT_PREFILL_MODE = 10
+OPT_SYNC_MODE = 11   # 0 tagged exchange words; 1, 2 one grid barrier per phase hand-off (2: with L2 fences)
 
 
 class MkError(RuntimeError):
@@ -120,7 +121,7 @@ class Decoder:
                  spin_limit: Optional[int] = None, poll_sleep: Optional[int] = None,
                  launch_mode: Optional[int] = None, split_chunk: Optional[int] = None,
                  split_from: Optional[int] = None, fp4_search: Optional[int] = None,
-                 prefill_mode: Optional[int] = None):
+                 prefill_mode: Optional[int] = None, sync_mode: Optional[int] = None):
         import torch
         self.lib = load(xray)
         self.shape, self.wfmt, self.max_ctx = shape, wfmt, max_ctx
@@ -144,6 +145,8 @@ class Decoder:
             self._check(self.lib.mk_set_option(self.h, OPT_FP4_SEARCH, fp4_search))
         if prefill_mode is not None:
             self._check(self.lib.mk_set_option(self.h, OPT_PREFILL_MODE, prefill_mode))
+        if sync_mode is not None:
+            self._check(self.lib.mk_set_option(self.h, OPT_SYNC_MODE, sync_mode))
         self.sizes = mk_sizes()
         self._check(self.lib.mk_query_sizes(self.h, ctypes.byref(self.sizes)))
         dev = torch.device("cuda", torch.cuda.current_device())

@@ -1,0 +1,128 @@
+"""The X-ray build (libmk_xray.so, compiled with the per-phase stamps) as an
+instrument, against the monolith page's milestone M2 criteria (stamps only
+behind a compile-time flag; the instrumented build within 3 % of the
+headline build's speed; the phases summing to within 5 % of the per-token
+time):
+
+* every workgroup writes one record per phase of the step, the phases it
+  takes part in are marked active, and within a record the stamps that were
+  taken are in order (gather began <= every word present <= handed over <=
+  first compute wave saw it <= last compute wave done);
+* the chain of phases (the budget of quantized_gemv_amd/xray.py) spans the
+  step: its length is within 5 % of the step's duration measured from the
+  host with events;
+* the instrumented step's logits are bit-identical to the headline build's;
+* the instrumented build runs within 3 % of the headline build.
+Run at the 0.6B shape in the benchmark's launch, bf16, tagged exchange."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from quantized_gemv_amd import xray
+
+pytestmark = pytest.mark.gpu
+
+SH = synth.QWEN3_0P6B
+
+
+@pytest.fixture(scope="module")
+def native():
+    from quantized_gemv_amd import native as n
+    assert torch.cuda.is_available()
+    return n
+
+
+@pytest.fixture(scope="module")
+def runs(native):
+    """Both builds on the same weights and prompt: the logits of 4 steps,
+    the X-ray records of the last one, and the time per step of 64 chained
+    steps (median of 3 runs, each after the same prefill)."""
+    master = synth.make_weights(SH, 0)
+    prompt = synth.make_prompt(SH.vocab, 128, 1)
+    out = {}
+    for xr in (False, True):
+        d = native.Decoder(SH, synth.BF16, 256, xray=xr)
+        d.pack(native.master_to_device(master))
+        d.prefill(prompt)
+        tok = torch.zeros(2, dtype=torch.int32, device="cuda")
+        lg = torch.zeros(SH.vocab, dtype=torch.float32, device="cuda")
+        logits = []
+        for i, t in enumerate((11, 22, 33, 44)):
+            tok[0] = t
+            d.decode_step_async(tok[0:1], 128 + i, tok[1:2], lg)
+            torch.cuda.synchronize()
+            logits.append(lg.cpu().numpy().copy())
+        rec = d.trace() if xr else None
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # one step alone, timed from the host, and its records
+        tok[0] = 55
+        e0.record()
+        d.decode_step_async(tok[0:1], 132, tok[1:2])
+        e1.record()
+        torch.cuda.synchronize()
+        one_step_ms = e0.elapsed_time(e1)
+        rec1 = d.trace() if xr else None
+        times = []
+        chain = torch.zeros(65, dtype=torch.int32, device="cuda")
+        for _ in range(3):
+            d.prefill(prompt)
+            chain[0] = 7
+            torch.cuda.synchronize()
+            e0.record()
+            for i in range(64):
+                d.decode_step_async(chain[i:i + 1], 128 + i, chain[i + 1:i + 2])
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / 64)
+        d.check_device_error()
+        out[xr] = {"logits": np.array(logits), "rec": rec, "rec1": rec1, "one_step_ms": one_step_ms,
+                   "ms": float(np.median(times)), "grid": torch.cuda.get_device_properties(0).multi_processor_count}
+        d.close()
+    return out
+
+
+def test_records_complete_and_ordered(runs):
+    rec, grid = runs[True]["rec"], runs[True]["grid"]
+    L = SH.n_layers
+    n_ph = 6 * L + 4
+    assert len(rec) == grid * n_ph
+    assert np.array_equal(np.sort(rec["wg"] * n_ph + rec["phase"]), np.arange(grid * n_ph))
+    act = rec[rec["active"] == 1]
+    # every workgroup takes part in the embedding or attention, every layer, and the LM head
+    for wg in range(grid):
+        mine = act[act["wg"] == wg]
+        assert (6 * L + 2) in mine["phase"], wg
+        for l in range(L):
+            assert np.any((mine["phase"] >= 2 + 6 * l) & (mine["phase"] < 8 + 6 * l)), (wg, l)
+    assert (6 * L + 3) in act[act["wg"] == 0]["phase"]           # workgroup 0 reduces the argmax
+    cols = ("t_start", "t_ready", "t_handoff", "t_seen", "t_done")
+    st = np.stack([act[c].astype(np.int64) for c in cols], axis=1)
+    for row, r in zip(st, act):
+        taken = row[row > 0]
+        assert taken.size >= 1, (int(r["wg"]), int(r["phase"]))
+        assert np.all(np.diff(taken) >= 0), (int(r["wg"]), int(r["phase"]), row)
+    # every XCD takes part, and the stamps of one step lie within its span
+    assert len(np.unique(act["xcc"] & 0xF)) == 8
+    assert (st[st > 0].max() - st[st > 0].min()) * xray.RT_NS < 5e6
+
+
+def test_phases_span_the_step(runs):
+    """The chain's length (first stamp to the argmax) is within 5 % of the
+    step's duration measured from the host."""
+    b = xray.budget(runs[True]["rec1"], SH.n_layers)
+    step_ms = b["step_ns"] / 1e6
+    host_ms = runs[True]["one_step_ms"]
+    assert abs(step_ms - host_ms) <= 0.05 * host_ms, (step_ms, host_ms)
+    cats = ("weight_gemv_ns", "wait_ns", "attention_ns", "lm_head_ns", "other_ns")
+    assert abs(sum(b[c] for c in cats) - b["step_ns"]) <= 0.01 * b["step_ns"]
+
+
+def test_logits_bit_identical_to_headline(runs):
+    a, b = runs[False]["logits"], runs[True]["logits"]
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_overhead_within_three_percent(runs):
+    head, xr = runs[False]["ms"], runs[True]["ms"]
+    assert xr <= 1.03 * head, (head, xr)

@@ -115,17 +115,26 @@ typedef struct mk_trace_rec {
 
 typedef struct mk_model mk_model;
 
-/* Validate `cfg` and create a host-side handle (no HIP calls).  The device
- * used is the one current at mk_bind.  Errors: MK_E_INVALID (null or
+/* Validate `cfg` and create a host-side handle (no HIP calls).  The shape
+ * is the model the monolith page decodes (Part 2, "Upstream facts": hidden
+ * 1024, intermediate 3072, 28 layers, 16 query and 8 KV heads of 128, vocab
+ * 151,936, tied embeddings, QK-norm, RoPE); the formats are its "Design
+ * decisions" (FP8 format, NVFP4 format).  The device used is the one current
+ * at mk_bind.  Errors: MK_E_INVALID (null or
  * non-positive sizes), MK_E_UNSUPPORTED (shape outside the constraints). */
 int mk_create(const mk_config* cfg, mk_model** out);
 
-/* Fill `out` with the buffer sizes for this model.  No HIP calls. */
+/* Fill `out` with the buffer sizes for this model, and the algorithmic
+ * bytes per token of the page's byte budget (Part 2, "Upstream facts":
+ * weights read per step, 1,192.1 MB at bf16, and the byte-budget block that
+ * follows it; its FP8 and NVFP4 lines are estimates).  No HIP calls. */
 int mk_query_sizes(const mk_model* m, mk_sizes* out);
 
 /* Register caller-owned device buffers (for example torch tensors' data
  * pointers) of at least the sizes mk_query_sizes reports; `d_trace` may be
- * NULL.  Queries the current device's compute-unit count and sets the
+ * NULL.  The library allocates nothing itself (the TSCT super-kernel note,
+ * section 4, "Interface discipline": no workspace allocated inside an op, no
+ * custom allocators).  Queries the current device's compute-unit count and sets the
  * launch grid to one workgroup per compute unit.  The pointers are not
  * owned and must stay valid until mk_destroy.  The scratch buffer and the
  * KV cache are cleared on `s`.  Errors: MK_E_INVALID (null or not 256-byte aligned),
@@ -134,7 +143,13 @@ int mk_bind(mk_model* m, void* d_weights, void* d_kv, void* d_rope, void* d_scra
             void* d_trace, mk_stream_t s);
 
 /* Quantize and pack the bf16 master weights into the bound arena and build
- * the RoPE table, on the GPU.  `d_tensors` holds 2 + 11*n_layers DEVICE
+ * the RoPE table, on the GPU (monolith page, Part 2, "Design decisions": FP8
+ * format, NVFP4 format with the per-block MSE scale search, and weight layout,
+ * packed in the order the kernel streams it; milestones M3 and M5, the
+ * packers).  The bf16 master is taken as device tensors, not host ones: the
+ * master already lives in device memory where the caller made it, and
+ * quantizing there needs no device allocation inside the library (packing
+ * from host memory would need a staging buffer of the library's own).  `d_tensors` holds 2 + 11*n_layers DEVICE
  * pointers to bf16 tensors in this order: embed [V,H]; per layer in_norm [H],
  * q [nq*hd,H], k [nkv*hd,H], v [nkv*hd,H], q_norm [hd], k_norm [hd],
  * o [H,nq*hd], post_norm [H], gate [I,H], up [I,H], down [H,I]; final_norm
@@ -149,7 +164,11 @@ int mk_bind(mk_model* m, void* d_weights, void* d_kv, void* d_rope, void* d_scra
  * the call only.  Errors: MK_E_INVALID, MK_E_STATE (not bound), MK_E_HIP. */
 int mk_pack_weights(mk_model* m, const void* const* d_tensors, int32_t n_tensors, mk_stream_t s);
 
-/* Test hook: copy one matrix back in canonical (row-major, un-fused) form.
+/* Test hook for the correctness gate (monolith page, Part 2, "Hard
+ * constraints": no speed number counts unless that build passed the
+ * correctness suite): copy one matrix back in canonical (row-major,
+ * un-fused) form, so its bytes can be compared with an independent quantizer
+ * whatever the streaming layout.
  * matrix: 0 q, 1 k, 2 v, 3 o, 4 gate, 5 up, 6 down, 7 embed (layer ignored).
  * h_codes: bf16 [N,K] (uint16), FP8 [N,K] bytes, or FP4 [N,K/2] bytes (element
  * 2j in the low nibble of byte j).  h_scales: FP8 fp32 [N] (else unused).
@@ -159,23 +178,30 @@ int mk_read_packed(mk_model* m, int32_t layer, int32_t matrix, void* h_codes, vo
                    void* h_block_scales, float* h_tensor_scale);
 
 /* Run the prompt through positions 0..n-1, writing the KV cache; return the
- * greedy token that follows the prompt (>= 0), or a negative mk_status.
+ * greedy token that follows the prompt (>= 0), or a negative mk_status
+ * (monolith page, Part 2, "Design decisions", benchmark protocol: prefill
+ * excluded from the timed decode).
  * By default one decode step per position; with option 10 = 1 the batched
  * prefill (chunks of positions, projections on the matrix cores).  The
  * monolith page's benchmark protocol ("Design decisions") times decode with
  * prefill excluded, so either path serves it.  Synchronous. */
 int32_t mk_prefill(mk_model* m, const int32_t* h_tokens, int32_t n, mk_stream_t s);
 
-/* One decode step: consume `token` at position `pos` (writing its K/V into
- * the cache), attend over positions 0..pos and return the next greedy token
+/* One decode step (monolith page, Part 2, "Mission": the decode
+ * megakernel; "Design decisions", sync experiment 5: the LM head and argmax
+ * folded in, so one launch yields each token): consume `token` at position
+ * `pos` (writing its K/V into the cache), attend over positions 0..pos and
+ * return the next greedy token
  * (>= 0) or a negative mk_status (MK_E_INVALID if pos >= max_ctx or token is
  * outside the vocabulary; MK_E_TIMEOUT if the kernel hit its spin bound).
  * One kernel launch; synchronous (a 4-byte readback). */
 int32_t mk_decode_step(mk_model* m, int32_t token, int32_t pos, mk_stream_t s);
 
-/* The same step without any host synchronisation: the token is read from
- * device memory `d_token` and the next token is written to `d_next` (both
- * int32, device), so steps chain on the device.  `d_logits` (fp32 [vocab],
+/* The same step without any host synchronisation (monolith page, Part 2,
+ * "Hard constraints": the timing harness times with events around the full
+ * decode loop, outside the kernel): the token is read from device memory
+ * `d_token` and the next token is written to `d_next` (both int32, device),
+ * so steps chain on the device.  `d_logits` (fp32 [vocab],
  * device) receives the logits when non-NULL.  A token outside the
  * vocabulary read from `d_token` makes the kernel record MK_E_INVALID in the
  * device error word, which the next synchronous call reports.  Errors
@@ -206,16 +232,22 @@ int mk_decode_step_async_noalloc(mk_model* m, const int32_t* d_token, int32_t po
                                  float* d_logits, mk_stream_t s);
 
 /* Read and clear the device error word (synchronous).  Returns MK_OK or the
- * first error a kernel recorded. */
+ * first error a kernel recorded.  (The pages prescribe no failure handling
+ * inside the kernel; every wait here is bounded instead of spinning forever,
+ * and this call reports a wait that hit its bound.) */
 int mk_check_device_error(mk_model* m, mk_stream_t s);
 
-/* Copy the X-ray records of the most recent step (X-ray builds only).
+/* Copy the X-ray records of the most recent step (X-ray builds only;
+ * monolith page, Part 2, "Design decisions", timing: one stamp pair per
+ * block and phase in a preallocated device buffer; milestone M2: the
+ * host-side dump of the trace for one chosen token position).
  * Writes min(cap, available) records; *n_out receives the number available
  * (0 in builds without X-ray).  Synchronous.  Errors: MK_E_INVALID if cap is
  * smaller than the number available. */
 int mk_get_trace(mk_model* m, mk_trace_rec* h_out, size_t cap, size_t* n_out);
 
-/* Test hook: copy back one activation vector of the last decode step, as
+/* Test hook for the correctness gate (monolith page, Part 2, "Hard
+ * constraints"): copy back one activation vector of the last decode step, as
  * one phase handed it to the next (the step's per-layer intermediates, for
  * op-by-op parity).  vec: 0 the q, k and v GEMV outputs before the q/k norms
  * ((nq + 2*nkv)*hd floats: the q heads, then the k heads, then the v heads);
@@ -228,7 +260,9 @@ int mk_get_trace(mk_model* m, mk_trace_rec* h_out, size_t cap, size_t* n_out);
  * the device.  Errors: MK_E_INVALID, MK_E_STATE, MK_E_HIP. */
 int mk_read_exchange(mk_model* m, int32_t layer, int32_t vec, float* h_out, size_t n);
 
-/* Test hook: decode `n` codes with the kernel's own register decoders.
+/* Test hook (monolith page, Part 2, milestone M0: run the e4m3 and e2m1
+ * converts against a CPU reference for every input value): decode `n` codes
+ * with the kernel's own register decoders.
  * codec 0: E4M3 bytes -> fp32; codec 1: E2M1 (one code per byte, low
  * nibble) -> fp32; codecs 2 and 3: the same two formats through the
  * converters the GEMVs use (to packed bf16), widened to fp32; codec 4:
@@ -238,7 +272,8 @@ int mk_read_exchange(mk_model* m, int32_t layer, int32_t vec, float* h_out, size
 int mk_decode_codes(int32_t codec, const uint8_t* d_codes, int32_t n, float* d_out, mk_stream_t s);
 
 /* Tuning knobs (defaults in brackets): key 0 grid size [compute units],
- * set before mk_bind; key 3 spin bound in 100 MHz ticks [100000000 = 1 s];
+ * set before mk_bind (monolith page, Part 2, "Design decisions", sync
+ * experiment 3: the launch-shape sweep); key 3 spin bound in 100 MHz ticks [100000000 = 1 s];
  * key 4 test hook [0]: a non-zero value shifts every tag the kernel waits
  * for, so no wait can be satisfied and each one ends at the spin bound (used
  * to test the MK_E_TIMEOUT path without hanging); key 5 poll back-off
@@ -283,11 +318,16 @@ int mk_decode_codes(int32_t codec, const uint8_t* d_codes, int32_t n, float* d_o
  * Errors: MK_E_INVALID (unknown key, value out of range), MK_E_STATE. */
 int mk_set_option(mk_model* m, int32_t key, int64_t value);
 
-/* 1 if the library was built with the X-ray stamps, else 0. */
+/* 1 if the library was built with the X-ray stamps, else 0 (monolith page,
+ * Part 2, "Hard constraints": X-ray compiles only behind a compile-time flag,
+ * and headline numbers come only from uninstrumented builds). */
 int mk_has_xray(void);
 
+/* Diagnostics: the text of a status code; the last error message of a handle
+ * (owned by the handle, valid until its next call). */
 const char* mk_status_str(int status);
 const char* mk_last_error(const mk_model* m);
+/* Free the host handle.  The caller's device buffers are not touched. */
 void mk_destroy(mk_model* m);
 
 #ifdef __cplusplus

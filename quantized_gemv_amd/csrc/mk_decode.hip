@@ -8,7 +8,9 @@
 // GEMV and the argmax, so one launch yields one token (the page's "fold the LM
 // head and argmax into the megakernel").
 //
-// Launch: cooperative, one workgroup of eight waves per compute unit.  Wave 0
+// Launch: one workgroup of eight waves per compute unit, as a plain launch
+// once the occupancy check has shown that the device holds the whole grid at
+// once (a cooperative launch otherwise).  Wave 0
 // of every workgroup is its courier (mk_sync.h): it gathers each input
 // vector the workgroup needs from the exchange words, normalises it where the
 // consumer wants that (every workgroup recomputes the RMSNorm factor itself,

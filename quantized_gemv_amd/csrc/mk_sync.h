@@ -113,7 +113,14 @@ __device__ __forceinline__ void hand_over(uint32_t* seq, uint32_t value) {
 }
 
 // 16-byte load of two consecutive exchange words with device-scope
-// coherence (sc1), through a buffer resource over the scratch buffer.
+// coherence (sc1), through a buffer resource over the scratch buffer.  Each
+// 8-byte half is checked against the tag on its own, so what this relies on
+// is that the memory system never splits an aligned 8-byte word: a half is
+// seen either before or after its producer's single 8-byte store, never
+// half-written.  The two halves may come from different moments (they are
+// two producers' words, or one word seen before it was written), which the
+// per-half tag check absorbs.  The 16-byte load is not assumed to be atomic
+// as a whole.
 __device__ __forceinline__ v4u ld_pair(__amdgpu_buffer_rsrc_t r, uint32_t word) {
   return __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(r, word * 8u, 0, 16));
 }

@@ -46,15 +46,7 @@ class mk_sizes(ctypes.Structure):
                                                "weight_bytes_per_token", "kv_bytes_per_position")]
 
 
-class mk_trace_rec(ctypes.Structure):
-    _fields_ = [("phase", ctypes.c_uint32), ("wg", ctypes.c_uint32), ("hw_id", ctypes.c_uint32),
-                ("xcc", ctypes.c_uint32), ("active", ctypes.c_uint32), ("pad", ctypes.c_uint32),
-                ("t_start", ctypes.c_uint64), ("t_wait_begin", ctypes.c_uint64),
-                ("t_wait_end", ctypes.c_uint64), ("t_end", ctypes.c_uint64),
-                ("rt_start", ctypes.c_uint64), ("rt_end", ctypes.c_uint64),
-                ("t_mark", ctypes.c_uint64 * 4)]
-
-
+# One X-ray record (mk_trace_rec in include/mk.h, 88 bytes).
 TRACE_DTYPE = np.dtype([(n, np.uint32) for n in ("phase", "wg", "hw_id", "xcc", "active", "pad")] +
                        [(n, np.uint64) for n in ("t_start", "t_ready", "t_handoff", "t_seen", "t_done")] +
                        [("t_mark", np.uint64, (3,))])
@@ -254,9 +246,18 @@ class Decoder:
         return out
 
     def close(self):
+        """Destroy the handle and release the device buffers, after the work
+        queued on them has finished.  Every script calls this itself: left
+        to garbage collection at interpreter exit, the buffers would be freed
+        while the HIP runtime (and a profiler's hooks on it) shut down."""
         if getattr(self, "h", None):
+            import torch
+            torch.cuda.synchronize()
             self.lib.mk_destroy(self.h)
             self.h = None
+            for name in ("weights", "kv", "rope", "scratch", "trace_buf"):
+                setattr(self, name, None)
+            torch.cuda.empty_cache()
 
     def __del__(self):
         try:

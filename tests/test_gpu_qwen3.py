@@ -9,8 +9,9 @@ per compute unit, library defaults):
 * free-running greedy decode (bf16, FP8) equal to the oracle's up to the
   first near-tie;
 * the default split attention (from 576 cached positions) at positions 600
-  and 1000, and the long-context workload itself (FP8, 16,384-token prompt),
-  every phase recomputed from the GPU's own inputs (tests/opcheck.py).
+  and 1000, the ends of the page's position sweep (16 and 2048), and the
+  long-context workload itself (FP8, 16,384-token prompt), every phase
+  recomputed from the GPU's own inputs (tests/opcheck.py).
 
 The G3 margin is the one tests/gates.py states: max(1e-3, twice the
 oracle's own summation-order noise at that step)."""
@@ -201,4 +202,19 @@ def test_long_context_fp8_16k(native, q_master):
     logits, _ = _step(d, first, P)
     check_step(GpuStep(d), Weights(q_master, synth.FP8_ROW), SH, first, P, logits, Q_LAYERS,
                np.random.default_rng(5), n_sample=96)
+    d.close()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("wfmt,pos", [(synth.BF16, 16), (synth.BF16, 2048), (synth.FP4_MIX, 2048)])
+def test_sweep_positions_qwen3(native, q_master, wfmt, pos):
+    """The ends of the page's position sweep (16 and 2048 cached positions)
+    not covered above, in the launch the sweep times: every phase of layers
+    0, 1, 14, 27 and the LM head recomputed from the GPU's own inputs."""
+    toks = synth.make_prompt(SH.vocab, pos + 1, 19)
+    d = _decoder(native, q_master, wfmt, pos + 8)
+    d.prefill(toks[:pos])
+    logits, _ = _step(d, int(toks[pos]), pos)
+    check_step(GpuStep(d), Weights(q_master, wfmt), SH, int(toks[pos]), pos, logits, Q_LAYERS,
+               np.random.default_rng(pos), n_sample=96)
     d.close()

@@ -1199,6 +1199,11 @@ struct Kern {
     for (int c = 0; c < NVC; ++c) acc[c] = f4{0.f, 0.f, 0.f, 0.f};
     const int P = LONG && ns > 0 ? (pos + ns) / (ns + 1) : pos;   // the home's slice: slice 0
     const int nblk = (P + PPB - 1) / PPB;   // passes of one block per wave
+    // held blocks of this wave that start before P (its others are all
+    // masked: their matrix-core work is skipped, their registers stay
+    // loaded).  Only without split attention: there the home's two held
+    // blocks are nearly always live, and the branch cost more than it saved.
+    const int nblk_w = LONG ? nblk : min(nblk, P > cw * BP ? (P - cw * BP + PPB - 1) / PPB : 0);
 #ifdef MK_XRAY
     {  // X-ray: when the prefetched rows are all in registers
       uint32_t z = 0;
@@ -1215,7 +1220,7 @@ struct Kern {
       float v = -INFINITY;
 #pragma unroll
       for (int t = 0; t < MB; ++t) {
-        if (t < nblk) {
+        if (t < nblk_w) {
           att_block_scores(s, kv.b[t], (t * kCW + cw) * BP, 0, P, sc[t]);
           v = fmaxf(v, block_max(sc[t]));
         }
@@ -1226,7 +1231,7 @@ struct Kern {
       att_rescale(bm, m, lsum, acc);
 #pragma unroll
       for (int t = 0; t < MB; ++t)
-        if (t < nblk) att_block_accum(kv.b[t], sc[t], m, lsum, acc);
+        if (t < nblk_w) att_block_accum(kv.b[t], sc[t], m, lsum, acc);
     }
     // ---- longer slices: the remaining blocks stream
     if (nblk > MB) att_stream(p, s, l, g, MB * PPB, MB * PPB, P, cw, m, lsum, acc, kv.b[0], kv.b[1]);
@@ -1392,9 +1397,9 @@ struct Kern {
   // smallest index).  Rows past the wave's last are clamped to it and their
   // results dropped (no branch around a load or a store).
   static constexpr int UBH = F_8 == FMT_BF16 ? 4 : 8;
-  // FP8 rows carry a scale register each: two batches keep them within the
-  // register file (four pushed the split variant's scalars into scratch)
-  static constexpr int NBH = F_8 == FMT_BF16 ? 4 : 2;
+  // FP8 rows carry a scale register each: the split variant keeps two
+  // batches in flight (four pushed its scalars into scratch memory)
+  static constexpr int NBH = F_8 == FMT_BF16 || !LONG ? 4 : 2;
   static __device__ __forceinline__ bool lm_head(const Params& p, S& s, const int* hdr, int cw, float* d_logits,
                                                  __amdgpu_buffer_rsrc_t rw, bool ok, float& best, int& bidx) {
     const bool l0 = lane_id() == 0;

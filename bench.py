@@ -116,18 +116,19 @@ def kernel_source_hash() -> str:
 def measured_traffic(workload: str):
     """HBM bytes per decode launch from profiles/decode_kernel_traffic.json
     (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by the same counter's
-    reading for a plain copy of known size), or None when absent or taken on
-    another version of the kernel."""
+    reading for a plain copy of known size), with the algorithmic bytes of
+    the launches they were taken over, or (None, None) when absent or taken
+    on another version of the kernel."""
     path = os.path.join(ROOT, "profiles", "decode_kernel_traffic.json")
     try:
         with open(path) as f:
             d = json.load(f)
     except (OSError, ValueError):
-        return None
+        return None, None
     e = d.get("workloads", {}).get(workload)
     if not e or d.get("kernel_source_sha256") != kernel_source_hash():
-        return None
-    return int(e["fetch_bytes_per_launch"] + e["write_bytes_per_launch"])
+        return None, None
+    return int(e["fetch_bytes_per_launch"] + e["write_bytes_per_launch"]), e.get("algorithmic_bytes_per_launch")
 
 
 def cpu_baseline(master, wl, n_steps, prompt, budget_s):
@@ -351,10 +352,17 @@ def time_decode(dec, wl, prompt, K, W, repeats):
     mean_ctx = wl.prompt_len + (K - 1) / 2.0 + 1
     algo = wbytes + float(sizes.kv_bytes_per_position) * mean_ctx
     achieved = algo / (dt / K) / 1e9
+    # the counters were taken over the 256 timed launches of the default run
+    # (positions P..P+255); their ratio to those launches' algorithmic bytes
+    # is what a reader compares, whatever window this run timed
+    traffic, traffic_algo = measured_traffic(wl.name)
     return {"value": round(tps, 2), "ms_per_step": round(dt / K * 1e3, 5), "times": times, "tokens": tokens,
             "weight_bytes": wbytes, "weight_roofline_pct": round(100.0 * wbytes * tps / (PEAK_HBM_GBPS * 1e9), 2),
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                         "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(wl.name),
+                         "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                         "traffic_over_algorithmic": round(traffic / traffic_algo, 4) if traffic and traffic_algo else None,
+                         "traffic_window": f"the 256 launches at positions {wl.prompt_len}..{wl.prompt_len + 255}"
+                                           if traffic else None,
                          "kernel": "mk::decode_kernel", "bytes_per_launch": int(algo)}}
 
 

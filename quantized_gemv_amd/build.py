@@ -1,7 +1,9 @@
 """Build libmk (the C-ABI library with the gfx950 kernels) in-tree with hipcc.
 
-Two variants: libmk.so (headline build) and libmk_xray.so (compiled with
-MK_XRAY, the per-phase timestamp stamps).
+Three variants: libmk.so (headline build), libmk_xray.so (compiled with
+MK_XRAY, the per-phase timestamp stamps) and libmk_stress.so (compiled with
+MK_STRESS: pseudo-random pauses before every exchange store and hand-over,
+for the race-detection tests).
 """
 import os
 import subprocess
@@ -15,18 +17,27 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 
-def lib_path(xray: bool = False) -> str:
-    return os.path.join(HERE, "libmk_xray.so" if xray else "libmk.so")
+VARIANTS = {"": "libmk.so", "xray": "libmk_xray.so", "stress": "libmk_stress.so"}
 
 
-def build(xray: bool = False, verbose: bool = False, out: str = "") -> str:
-    out = out or lib_path(xray)
+def lib_path(xray=False) -> str:
+    """Path of a library variant: False / "" the headline build, True / "xray"
+    the X-ray build, "stress" the stress build."""
+    kind = "xray" if xray is True else ("" if xray is False else xray)
+    return os.path.join(HERE, VARIANTS[kind])
+
+
+def build(xray=False, verbose: bool = False, out: str = "") -> str:
+    kind = "xray" if xray is True else ("" if xray is False else xray)
+    out = out or lib_path(kind)
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            # no packed-FP32 instructions anywhere in the device code
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-I", os.path.join(ROOT, "include"), "-I", CSRC]
-    if xray:
+    if kind == "xray":
         cmd.append("-DMK_XRAY")
+    if kind == "stress":
+        cmd.append("-DMK_STRESS")
     cmd.append("-Rpass-analysis=kernel-resource-usage")
     cmd += [os.path.join(CSRC, s) for s in SOURCES]
     cmd += ["-o", out + ".tmp"]
@@ -38,7 +49,7 @@ def build(xray: bool = False, verbose: bool = False, out: str = "") -> str:
         sys.stderr.write(r.stderr)
     bad = [f"{k}: {v}" for k, v in resource_usage(r.stderr).items()
            if "decode_kernel" in k and (v.get("scratch", 0) or v.get("vgpr_spill", 0))]
-    if bad and not xray:   # the X-ray stamps may spill; that build is for diagnosis only
+    if bad and kind == "":   # the X-ray stamps and stress pauses may spill; those builds are for tests
         os.remove(out + ".tmp")
         raise RuntimeError("decode kernel spills to scratch memory (slow in the layer loop):\n" + "\n".join(bad))
     os.replace(out + ".tmp", out)
@@ -69,10 +80,10 @@ def resource_usage(remarks: str) -> dict:
 
 
 def build_all(verbose: bool = False):
-    """Both variants, compiled side by side."""
+    """Every variant, compiled side by side."""
     from concurrent.futures import ThreadPoolExecutor
-    with ThreadPoolExecutor(2) as ex:
-        return list(ex.map(lambda x: build(x, verbose), (False, True)))
+    with ThreadPoolExecutor(len(VARIANTS)) as ex:
+        return list(ex.map(lambda k: build(k, verbose), list(VARIANTS)))
 
 
 if __name__ == "__main__":

@@ -35,6 +35,27 @@
 namespace mk {
 
 enum : uint32_t { ERR_TIMEOUT = 1u, ERR_TOKEN = 2u };
+
+#ifdef MK_STRESS
+// Stress build, the race-detection stand-in: a pseudo-random pause of 0 to
+// 31 x 2 s_sleep units (up to about 1.7 us) before every exchange store and
+// every courier hand-over.  The pause depends on the clock, the workgroup,
+// the wave and the store site, so every run interleaves the producers,
+// the consumers' poll rounds and the LDS hand-offs differently.  A missing
+// wait or a value read before it is complete would show as a changed
+// result; the results must stay bit-identical to the headline build's.
+__device__ __forceinline__ void stress_pause(uint32_t site) {
+  uint32_t h = site ^ (uint32_t)__builtin_amdgcn_s_memrealtime() ^ (blockIdx.x * 0x9E3779B1u) ^
+               ((threadIdx.x >> 6) * 0x85EBCA77u);
+  h ^= h >> 16;
+  h *= 0x7FEB352Du;
+  h ^= h >> 15;
+  h *= 0x846CA68Bu;
+  h ^= h >> 16;
+  const uint32_t n = __builtin_amdgcn_readfirstlane(h) & 31u;
+  for (uint32_t i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(2);
+}
+#endif
 constexpr uint32_t kAbort = 0xFFFFFFFFu;
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
@@ -107,6 +128,9 @@ __device__ __forceinline__ bool wait_seq(const Params& p, const uint32_t* seq, u
 
 // Courier: publish one more input (LDS writes first, then the counter).
 __device__ __forceinline__ void hand_over(uint32_t* seq, uint32_t value) {
+#ifdef MK_STRESS
+  stress_pause(value * 0x27D4EB2Fu);
+#endif
   lds_drain();
   if ((threadIdx.x & 63) == 0) lds_st(seq, value);
   lds_drain();
@@ -134,6 +158,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t xch_rsrc(const Params& p) {
 // store, which lets a wave skip a store without a branch.
 __device__ __forceinline__ void st_xword(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint32_t payload,
                                          uint32_t tag) {
+#ifdef MK_STRESS
+  stress_pause(__builtin_amdgcn_readfirstlane(byte_off) ^ tag);
+#endif
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, v2u{tag, payload}), r, byte_off, 0, 16);
 }
 

@@ -51,16 +51,18 @@ TRACE_DTYPE = np.dtype([(n, np.uint32) for n in ("phase", "wg", "hw_id", "xcc", 
                        [(n, np.uint64) for n in ("t_start", "t_ready", "t_handoff", "t_seen", "t_done")] +
                        [("t_mark", np.uint64, (3,))])
 
-_LIBS: Dict[bool, ctypes.CDLL] = {}
+_LIBS: Dict[object, ctypes.CDLL] = {}
 _VP = ctypes.c_void_p
 
 
-def load(xray: bool = False) -> ctypes.CDLL:
-    """Load libmk.so (or libmk_xray.so; MK_LIBRARY / MK_LIBRARY_XRAY name
-    another build of the same library).  Raises if it has not been built."""
+def load(xray=False) -> ctypes.CDLL:
+    """Load libmk.so, or with xray=True libmk_xray.so, or with xray="stress"
+    libmk_stress.so (MK_LIBRARY / MK_LIBRARY_XRAY name another build of the
+    first two).  Raises if it has not been built."""
     if xray in _LIBS:
         return _LIBS[xray]
-    path = os.environ.get("MK_LIBRARY_XRAY" if xray else "MK_LIBRARY") or lib_path(xray)
+    env = {False: "MK_LIBRARY", True: "MK_LIBRARY_XRAY"}.get(xray)
+    path = (os.environ.get(env) if env else None) or lib_path(xray)
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with quantized_gemv_amd/build.py "
                            "(there is no fallback path)")
@@ -109,7 +111,7 @@ def _stream(stream=None) -> int:
 class Decoder:
     """One model handle with its device buffers (allocated through torch)."""
 
-    def __init__(self, shape, wfmt: int, max_ctx: int, xray: bool = False, grid: int = 0,
+    def __init__(self, shape, wfmt: int, max_ctx: int, xray=False, grid: int = 0,
                  spin_limit: Optional[int] = None, poll_sleep: Optional[int] = None,
                  launch_mode: Optional[int] = None, split_chunk: Optional[int] = None,
                  split_from: Optional[int] = None, fp4_search: Optional[int] = None,

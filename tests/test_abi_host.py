@@ -44,12 +44,12 @@ def test_header_declares_the_entry_points():
         assert n in names
 
 
-@pytest.mark.parametrize("xray", [False, True])
+@pytest.mark.parametrize("xray", [False, True, "stress"])
 def test_library_exports_every_declared_symbol(xray):
     L = ctypes.CDLL(native.lib_path(xray))
     missing = [n for n in _declared() if not hasattr(L, n)]
     assert not missing, missing
-    assert native.load(xray).mk_has_xray() == (1 if xray else 0)
+    assert native.load(xray).mk_has_xray() == (1 if xray is True else 0)
 
 
 def _create(lib, shape=synth.TINY, wfmt=synth.BF16, max_ctx=64, **over):

@@ -259,24 +259,26 @@ __device__ __forceinline__ void load_act(const uint32_t* src, int K, uint32_t (&
 // ------------------------------------------------------------- courier
 // A residual vector for LDS: pairs j = l + 64k of x (fp32 bits in lo/hi) go
 // to x_raw, and 1/sqrt(mean(x^2) + eps) to *r.  The compute waves apply the
-// gains and round to bf16 themselves, each for its own slice.  Pairs past
-// H/2 hold don't-care values and are masked.
+// gains and round to bf16 themselves, each for its own slice.  x_raw holds
+// 128 * MAXK floats: lanes past H/2 store their (don't-care) pairs beyond
+// element H, where nobody reads, and add zeros to the sum of squares, so
+// there is no branch per pair.  inv_h = 1/H (exact for a power of two);
+// the reciprocal square root is v_rsq_f32 (within 1 ulp).
 template <int MAXK>
-__device__ __forceinline__ void raw_to_lds(const Params& p, const uint32_t (&lo)[MAXK], const uint32_t (&hi)[MAXK],
-                                           int H, float* x_raw, float* r) {
+__device__ __forceinline__ void raw_to_lds(const uint32_t (&lo)[MAXK], const uint32_t (&hi)[MAXK], int H,
+                                           float inv_h, float eps, float* x_raw, float* r) {
   const int lane = lane_id();
   float ss = 0.f;
 #pragma unroll
   for (int k = 0; k < MAXK; ++k) {
     const int j = lane + 64 * k;
-    if (j < H / 2) {
-      const float a = __uint_as_float(lo[k]), b = __uint_as_float(hi[k]);
-      ss = fmaf(a, a, ss);
-      ss = fmaf(b, b, ss);
-      *reinterpret_cast<v2u*>(x_raw + 2 * j) = v2u{lo[k], hi[k]};
-    }
+    const bool in = j < H / 2;
+    const float a = in ? __uint_as_float(lo[k]) : 0.f, b = in ? __uint_as_float(hi[k]) : 0.f;
+    ss = fmaf(a, a, ss);
+    ss = fmaf(b, b, ss);
+    *reinterpret_cast<v2u*>(x_raw + 2 * j) = v2u{lo[k], hi[k]};
   }
-  const float rr = 1.0f / sqrtf(wave_sum(ss) / (float)H + p.eps);
+  const float rr = __builtin_amdgcn_rsqf(wave_sum(ss) * inv_h + eps);
   if (lane == 0) *r = rr;
 }
 
@@ -350,13 +352,36 @@ struct Kern {
   // output, 2: residual after O, 3: SwiGLU output, 4: residual after down};
   // then 5L: the argmax words.  A compute wave records in s.arr[cw] how many
   // barriers it has finished its part of: after its stores of a phase
-  // (waited for with vmcnt(0), which on gfx9 also waits for its loads in
-  // flight), or at once for a phase in which it stores nothing.
+  // (in this variant waited for with vmcnt(0), which on gfx9 also waits for
+  // its loads in flight), or at once for a phase in which it stores nothing.
+  // The tagged exchange keeps the same record, without the wait: there it
+  // says that the wave has issued its stores (see stores_out).
   static __device__ __forceinline__ void arrive(S& s, int cw, uint32_t upto, bool stored) {
-    if (!BAR) return;
-    if (stored) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores are complete
+    if (BAR && stored) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores are complete
     asm volatile("" ::: "memory");
     if (lane_id() == 0) lds_st(&s.arr[cw], upto);
+  }
+
+  // Courier, tagged exchange: before polling for the vector of barrier b,
+  // wait until this workgroup's compute waves have issued their stores of
+  // that phase.  The compute unit's vector-memory path is shared by its
+  // waves in issue order, so polls issued earlier would sit ahead of the
+  // very stores other workgroups are waiting for; and a vector cannot be
+  // complete before this workgroup's part of it is out.  Bounded like every
+  // other wait.
+  static __device__ __forceinline__ bool stores_out(const Params& p, S& s, uint32_t b) {
+    if (BAR) return true;   // the grid barrier before the gather has waited for them
+    const int lane = lane_id();
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (true) {
+      const uint32_t a = lane < kCW ? lds_ld(&s.arr[lane]) : 0xFFFFFFFFu;
+      if (__builtin_amdgcn_ballot_w64(a < b + 1) == 0) return true;
+      if (__builtin_amdgcn_s_memrealtime() - t0 > p.spin_limit) {
+        raise_error(p, ERR_TIMEOUT);
+        return false;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
   }
 
   // Courier: barrier b.  Wait until this workgroup's compute waves have
@@ -419,6 +444,7 @@ struct Kern {
     const Layer& L0 = p.layer0;
     uint32_t seq = 0;
     uint32_t lo[KX], hi[KX];
+    const float eps = p.eps, inv_h = 1.0f / (float)H;
     // ---- embedding -> the residual of layer 0
     if (flags & 1) {
       XR_PUT(s, 1, XR_START);
@@ -437,7 +463,7 @@ struct Kern {
           hi[k] = __float_as_uint(e4m3_to_f32(w >> 8) * sc);
         }
       }
-      raw_to_lds<KX>(p, lo, hi, H, s.xd_raw, &s.r_xd);
+      raw_to_lds<KX>(lo, hi, H, inv_h, eps, s.xd_raw, &s.r_xd);
       hand_over(&s.seq, ++seq);
       XR_PUT(s, 1, XR_HANDOFF);
     }
@@ -464,12 +490,13 @@ struct Kern {
       // ---- residual entering layer l (layer 0: the embedding above)
       if (BAR && l > 0 && !grid_barrier(p, s, bq - 1)) return abort(s);
       if ((flags & 1) && l > 0) {
+        if (!stores_out(p, s, bq - 1)) return abort(s);
         XR_PUT(s, ph + 0, XR_START);
         if (!gather_pairs_at<KX>(p, rs, H / 2, make_tag(epoch, vec_id(l - 1, V_XD)), lo, hi, xword(p, l - 1, V_XD),
                                  mx))
           return abort(s);
         XR_PUT(s, ph + 0, XR_READY);
-        raw_to_lds<KX>(p, lo, hi, H, s.xd_raw, &s.r_xd);
+        raw_to_lds<KX>(lo, hi, H, inv_h, eps, s.xd_raw, &s.r_xd);
         hand_over(&s.seq, ++seq);
         XR_PUT(s, ph + 0, XR_HANDOFF);
       }
@@ -510,37 +537,35 @@ struct Kern {
           return abort(s);
         XR_PUT(s, ph + 3, XR_READY);
 #pragma unroll
-        for (int k = 0; k < KO; ++k) {
-          const int j = lane + 64 * k;
-          if (j < p.nq * HD / 4) *reinterpret_cast<v2u*>(s.o_in + 2 * j) = v2u{ol[k], oh[k]};
-        }
+        for (int k = 0; k < KO; ++k)   // o_in holds 64 * KO pairs: lanes past the end store don't-care pairs there
+          *reinterpret_cast<v2u*>(s.o_in + 2 * (lane + 64 * k)) = v2u{ol[k], oh[k]};
         hand_over(&s.seq, ++seq);
         XR_PUT(s, ph + 3, XR_HANDOFF);
       }
       // ---- residual after O
       if (BAR && !grid_barrier(p, s, bq + 2)) return abort(s);
       if (flags & 4) {
+        if (!stores_out(p, s, bq + 2)) return abort(s);
         XR_PUT(s, ph + 4, XR_START);
         if (!gather_pairs_at<KX>(p, rs, H / 2, make_tag(epoch, vec_id(l, V_XO)), lo, hi, xword(p, l, V_XO), mo))
           return abort(s);
         XR_PUT(s, ph + 4, XR_READY);
-        raw_to_lds<KX>(p, lo, hi, H, s.xo_raw, &s.r_xo);
+        raw_to_lds<KX>(lo, hi, H, inv_h, eps, s.xo_raw, &s.r_xo);
         hand_over(&s.seq, ++seq);
         XR_PUT(s, ph + 4, XR_HANDOFF);
       }
       // ---- SwiGLU output
       if (BAR && !grid_barrier(p, s, bq + 3)) return abort(s);
       if (flags & 8) {
+        if (!stores_out(p, s, bq + 3)) return abort(s);
         XR_PUT(s, ph + 5, XR_START);
         uint32_t hl[KH], hh[KH];
         if (!gather_pairs_at<KH>(p, rs, p.I / 4, make_tag(epoch, vec_id(l, V_H)), hl, hh, xword(p, l, V_H), mh))
           return abort(s);
         XR_PUT(s, ph + 5, XR_READY);
 #pragma unroll
-        for (int k = 0; k < KH; ++k) {
-          const int j = lane + 64 * k;
-          if (j < p.I / 4) *reinterpret_cast<v2u*>(s.h_in + 2 * j) = v2u{hl[k], hh[k]};
-        }
+        for (int k = 0; k < KH; ++k)   // h_in holds 64 * KH pairs: lanes past the end store don't-care pairs there
+          *reinterpret_cast<v2u*>(s.h_in + 2 * (lane + 64 * k)) = v2u{hl[k], hh[k]};
         hand_over(&s.seq, ++seq);
         XR_PUT(s, ph + 5, XR_HANDOFF);
       }
@@ -549,12 +574,13 @@ struct Kern {
     const int ph_head = 2 + 6 * L;
     if (BAR && !grid_barrier(p, s, 5u * (uint32_t)L - 1u)) return abort(s);
     {
+      if (!stores_out(p, s, 5u * (uint32_t)L - 1u)) return abort(s);
       XR_PUT(s, ph_head, XR_START);
       if (!gather_pairs_at<KX>(p, rs, H / 2, make_tag(epoch, vec_id(L - 1, V_XD)), lo, hi, xword(p, L - 1, V_XD),
                                mx))
         return abort(s);
       XR_PUT(s, ph_head, XR_READY);
-      raw_to_lds<KX>(p, lo, hi, H, s.xd_raw, &s.r_xd);
+      raw_to_lds<KX>(lo, hi, H, inv_h, eps, s.xd_raw, &s.r_xd);
       hand_over(&s.seq, ++seq);
       XR_PUT(s, ph_head, XR_HANDOFF);
     }
@@ -635,11 +661,9 @@ struct Kern {
     if (!gather_pairs_at<K>(p, rs, NP, make_tag(epoch, vec_id(l, V_QKV)), lo, hi, xword(p, l, V_QKV), off))
       return false;
     XR_PUT(s, 2 + 6 * l + 1, XR_READY);
+    static_assert(NP % 64 == 0, "every lane stores a pair of q/k/v");
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int j = lane + 64 * k;
-      if (j < NP) *reinterpret_cast<v2u*>(s.qraw + 2 * j) = v2u{lo[k], hi[k]};
-    }
+    for (int k = 0; k < K; ++k) *reinterpret_cast<v2u*>(s.qraw + 2 * (lane + 64 * k)) = v2u{lo[k], hi[k]};
     if (lane < HD / 2) {
       s.gq[lane] = gq_lo;
       s.gq[lane + HD / 2] = gq_hi;
@@ -666,7 +690,7 @@ struct Kern {
     if (cw < GS || (KV && cw == GS)) {
       const float* src = s.qraw + cw * HD;
       const float xa = pl ? src[li] : 0.f, xb = pl ? src[li + HD / 2] : 0.f;
-      const float r = 1.0f / sqrtf(wave_sum(xa * xa + xb * xb) / (float)HD + p.eps);
+      const float r = __builtin_amdgcn_rsqf(wave_sum(xa * xa + xb * xb) * (1.0f / HD) + p.eps);   // v_rsq_f32: within 1 ulp
       const float* gg = cw < GS ? s.gq : s.gk;
       const float a = gg[li] * (xa * r), b = gg[li + HD / 2] * (xb * r);
       const float c = s.rc[li], sn = s.rs[li];

@@ -52,25 +52,23 @@ typedef short s4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
-// Cross-lane reductions with DPP (row operations on the VALU) and
-// v_readlane.  DPP controls (gfx9): quad_perm [1,0,3,2] = 0xB1,
-// [2,3,0,1] = 0x4E, row_ror:4 = 0x124, row_ror:8 = 0x128,
-// row_half_mirror = 0x141.
+// Cross-lane reductions with DPP (row operations on the VALU), gfx950's
+// permlane swaps and v_readlane.  DPP controls (gfx9): quad_perm [1,0,3,2] =
+// 0xB1, [2,3,0,1] = 0x4E, [2,3,2,3] = 0xEE, row_ror:4 = 0x124, row_ror:8 =
+// 0x128, row_mirror = 0x140, row_half_mirror = 0x141.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
-// Sum over each 8-lane group, result in every lane of it.
-__device__ __forceinline__ float sum8(float v) {
-  v += dpp<0xB1>(v);
-  v += dpp<0x4E>(v);
-  return v + dpp<0x141>(v);
-}
+// Sum over each 16-lane row, the same bits in every lane of it: each step
+// adds a lane's value to its partner's, the partner's partner being the
+// lane itself (xor 1, xor 2, then the mirror images within 8 and 16 lanes),
+// and a + b == b + a.
 __device__ __forceinline__ float sum16(float v) {
   v += dpp<0xB1>(v);
   v += dpp<0x4E>(v);
-  v += dpp<0x124>(v);
-  return v + dpp<0x128>(v);
+  v += dpp<0x141>(v);
+  return v + dpp<0x140>(v);
 }
 __device__ __forceinline__ float max16(float v) {
   v = fmaxf(v, dpp<0xB1>(v));
@@ -78,20 +76,49 @@ __device__ __forceinline__ float max16(float v) {
   v = fmaxf(v, dpp<0x124>(v));
   return fmaxf(v, dpp<0x128>(v));
 }
+// Sum of a lane's value with those of the lanes 16, 32 and 48 apart (the
+// same position in the other 16-lane rows), the same bits in all four:
+// v_permlane32_swap pairs lanes 32 apart, v_permlane16_swap rows 16 apart.
+__device__ __forceinline__ float rows_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float w = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(w), __float_as_uint(w), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 __device__ __forceinline__ float lane_f(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
-// Sum / max over the wave, the same value in every lane (fixed order).
-__device__ __forceinline__ float wave_sum(float v) {
-  v = sum16(v);
-  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
-}
+// Sum over the wave, the same bits in every lane (fixed order).
+__device__ __forceinline__ float wave_sum(float v) { return rows_sum(sum16(v)); }
 __device__ __forceinline__ float wave_max(float v) {
   v = max16(v);
   return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
+// The row whose total wave_sum4 leaves in lane l: 2 (l & 1) + ((l >> 1) & 1).
+__device__ __forceinline__ int sum4_row(int lane) { return 2 * (lane & 1) + ((lane >> 1) & 1); }
+// Wave sums of four values at once: lane l ends with the total of value
+// sum4_row(l) (lanes 0..3 hold rows 0, 2, 1, 3).  The first two steps
+// halve the values per lane while pairing lanes (a lane keeps the rows it
+// does not send), the rest sum lanes of the same row: about the cost of one
+// full reduction instead of four.  The totals are complete in every lane
+// of a row but may differ between its lanes in the last bits (the 16-lane
+// steps rotate); callers read one lane per row.
+__device__ __forceinline__ float wave_sum4(float a, float b, float c, float d) {
+  const int lane = lane_id();
+  const bool odd = (lane & 1) != 0, hi = (lane & 2) != 0;
+  const float n0 = (odd ? c : a) + dpp<0xB1>(odd ? a : c);   // rows 0 (even lanes), 2 (odd)
+  const float n1 = (odd ? d : b) + dpp<0xB1>(odd ? b : d);   // rows 1, 3
+  float v = (hi ? n1 : n0) + dpp<0x4E>(hi ? n0 : n1);
+  v += dpp<0x124>(v);
+  v += dpp<0x128>(v);
+  return rows_sum(v);
+}
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// z * sigmoid(z) with v_exp_f32 and v_rcp_f32 (each within 1 ulp); large
+// |z| give z or -0 (exp2 overflows to inf, whose reciprocal is 0).
+__device__ __forceinline__ float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
+}
 
 // ------------------------------------------------------------------ LDS
 template <int HD, int GS, int NH, int NQ, int NI>
@@ -839,12 +866,24 @@ struct Kern {
       }
 #endif
       const uint32_t base = xword(p, l, V_QKV), tag = make_tag(epoch, vec_id(l, V_QKV));
+      static_assert(kMaxQKV <= 4, "one wave_sum4 for the q/k/v rows");
+      float y[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < kMaxQKV; ++k) {
-        const int r = u[S_QKV + k];
-        const float v = wrow_dot(w.q[k], xa);
-        st_xword(rx, ok && r >= 0 && l0 ? 8u * (base + (uint32_t)u[S_QKVW + k]) : kOOB, __float_as_uint(v), tag);
+      for (int k = 0; k < kMaxQKV; ++k) y[k] = wrow_partial(w.q[k], xa);
+      // lane q < kMaxQKV (q = sum4_row(lane), lanes 0..3) stores row q
+      const int q = sum4_row(lane_id());
+      float v = wave_sum4(y[0], y[1], y[2], y[3]);
+      int r = u[S_QKV];
+      uint32_t wo = (uint32_t)u[S_QKVW];
+      float sc = w.q[0].s;
+#pragma unroll
+      for (int k = 1; k < kMaxQKV; ++k) {
+        r = q == k ? u[S_QKV + k] : r;
+        wo = q == k ? (uint32_t)u[S_QKVW + k] : wo;
+        sc = q == k ? w.q[k].s : sc;
       }
+      if (F_LIN != FMT_BF16) v *= sc;
+      st_xword(rx, ok && lane_id() < 4 && q < kMaxQKV && r >= 0 ? 8u * (base + wo) : kOOB, __float_as_uint(v), tag);
       XR_MAX(s, ph + 0, XR_DONE);
       }
     }
@@ -909,13 +948,13 @@ struct Kern {
         float y[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) y[r] = wrow_partial(w.gu[k][r], xa);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          y[r] = wave_sum(y[r]);
-          if (F_LIN != FMT_BF16) y[r] *= w.gu[k][r].s;
-        }
-        const float h0 = silu(y[0]) * y[1], h1 = silu(y[2]) * y[3];
-        st_xword(rx, ok && t >= 0 && l0 ? 8u * (base + w.sg[k]) : kOOB, pack_bf16(h0, h1), tag);
+        // rows (gate, up, gate, up): lanes 0, 2, 1, 3 end with their totals
+        const int q = sum4_row(lane_id());
+        float v = wave_sum4(y[0], y[1], y[2], y[3]);
+        if (F_LIN != FMT_BF16)
+          v *= q == 0 ? w.gu[k][0].s : (q == 1 ? w.gu[k][1].s : (q == 2 ? w.gu[k][2].s : w.gu[k][3].s));
+        const float h = silu(v) * dpp<0xEE>(v);   // lane 0: gate 0 with up 0 (lane 2); lane 1: rows 2, 3
+        st_xword(rx, ok && t >= 0 && l0 ? 8u * (base + w.sg[k]) : kOOB, pack_bf16(h, dpp<0xB1>(h)), tag);
       }
       XR_MAX(s, ph + 4, XR_DONE);
       }

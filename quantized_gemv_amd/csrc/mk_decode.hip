@@ -126,8 +126,10 @@ struct Smem {
   // every array starts on a 16-byte boundary: the compute waves read them
   // with 16-byte LDS loads
   alignas(16) float xd_raw[NH * 1024];   // residual entering the layer (fp32)
+  alignas(16) uint32_t xd_act[NH * 512]; // its RMSNorm with the layer's input gains, bf16 pairs (QKV input)
   alignas(16) uint32_t o_in[NQ * 512];   // attention output, bf16 pairs (O input)
   alignas(16) float xo_raw[NH * 1024];   // residual after O (fp32)
+  alignas(16) uint32_t xo_act[NH * 512]; // its RMSNorm with the post-attention gains (gate/up input)
   alignas(16) uint32_t h_in[NI * 512];   // SwiGLU output, bf16 pairs (down input)
   // attention workgroups
   alignas(16) float qraw[(GS + 2) * HD]; // gathered q heads, k, v of the KV head
@@ -148,7 +150,6 @@ struct Smem {
   // argmax
   alignas(16) float best[kCW];
   alignas(16) int32_t bidx[kCW];
-  float r_xd, r_xo;                      // 1/rms of xd_raw and xo_raw
   uint32_t seq;                          // inputs handed over by the courier (kAbort: abort)
   uint32_t arr[kCW];                     // grid-barrier variant: barriers each compute wave has finished its part of
   XR_FIELD
@@ -284,16 +285,20 @@ __device__ __forceinline__ void load_act(const uint32_t* src, int K, uint32_t (&
 }
 
 // ------------------------------------------------------------- courier
-// A residual vector for LDS: pairs j = l + 64k of x (fp32 bits in lo/hi) go
-// to x_raw, and 1/sqrt(mean(x^2) + eps) to *r.  The compute waves apply the
-// gains and round to bf16 themselves, each for its own slice.  x_raw holds
-// 128 * MAXK floats: lanes past H/2 store their (don't-care) pairs beyond
+// A residual vector for LDS and its RMSNorm: pairs j = l + 64k of x (fp32
+// bits in lo/hi) go to x_raw (for the residual add after the next
+// projection) and bf16(g * (x * r)), r = 1/sqrt(mean(x^2) + eps), to act as
+// bf16 pairs in the same order (the GEMVs' input); g[k] holds the gains of
+// pair j as a bf16 pair.  The courier does this once for the workgroup, so
+// the compute waves only load act.  x_raw holds 128 * MAXK floats and act
+// 64 * MAXK pairs: lanes past H/2 store their (don't-care) pairs beyond
 // element H, where nobody reads, and add zeros to the sum of squares, so
-// there is no branch per pair.  inv_h = 1/H (exact for a power of two);
-// the reciprocal square root is v_rsq_f32 (within 1 ulp).
+// there is no branch per pair.  inv_h = 1/H (exact for a power of two); the
+// reciprocal square root is v_rsq_f32 (within 1 ulp).
 template <int MAXK>
-__device__ __forceinline__ void raw_to_lds(const uint32_t (&lo)[MAXK], const uint32_t (&hi)[MAXK], int H,
-                                           float inv_h, float eps, float* x_raw, float* r) {
+__device__ __forceinline__ void norm_to_lds(const uint32_t (&lo)[MAXK], const uint32_t (&hi)[MAXK],
+                                            const uint32_t (&g)[MAXK], int H, float inv_h, float eps, float* x_raw,
+                                            uint32_t* act) {
   const int lane = lane_id();
   float ss = 0.f;
 #pragma unroll
@@ -305,47 +310,19 @@ __device__ __forceinline__ void raw_to_lds(const uint32_t (&lo)[MAXK], const uin
     ss = fmaf(b, b, ss);
     *reinterpret_cast<v2u*>(x_raw + 2 * j) = v2u{lo[k], hi[k]};
   }
-  const float rr = __builtin_amdgcn_rsqf(wave_sum(ss) * inv_h + eps);
-  if (lane == 0) *r = rr;
+  const float r = __builtin_amdgcn_rsqf(wave_sum(ss) * inv_h + eps);
+#pragma unroll
+  for (int k = 0; k < MAXK; ++k)
+    act[lane + 64 * k] = pack_bf16(bf16_lo(g[k]) * (__uint_as_float(lo[k]) * r),
+                                   bf16_hi(g[k]) * (__uint_as_float(hi[k]) * r));
 }
 
-// Compute waves: the lane's slice of bf16(g * x * r) (RMSNorm with gains g,
-// bf16 pairs in gw) from the raw vector in LDS; lanes past K read zeros.
-template <int NCH>
-__device__ __forceinline__ void norm_act(const float* x_raw, float r, const uint32_t (&gw)[NCH][8], int K,
-                                         uint32_t (&xa)[NCH][8]) {
-  const int lane = lane_id();
+// The gains (bf16 pairs) of the courier's pairs j = l + 64k of a norm whose
+// weights sit at byte `off` of the arena (pairs past H/2 repeat the last).
+template <int MAXK>
+__device__ __forceinline__ void courier_gains(MK_GLOBAL const uint8_t* W, uint64_t off, int H, uint32_t (&g)[MAXK]) {
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const int e0 = c * 1024 + 16 * lane;
-    const bool in = e0 < K;
-    const float4* xp = reinterpret_cast<const float4*>(x_raw + min(e0, K - 16));
-    float x[16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 v = xp[q];
-      x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      xa[c][j] = in ? pack_bf16(bf16_lo(gw[c][j]) * (x[2 * j] * r), bf16_hi(gw[c][j]) * (x[2 * j + 1] * r)) : 0u;
-  }
-}
-
-// The lane's gains (bf16 pairs) for norm_act, from the weight arena (have =
-// false: kOOB, zeros).
-template <int NCH>
-__device__ __forceinline__ void gain_load(__amdgpu_buffer_rsrc_t rw, uint32_t off, int K, bool have,
-                                          uint32_t (&gw)[NCH][8]) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const uint32_t o = have ? off + 2u * (uint32_t)min(c * 1024 + 16 * lane, K - 16) : kOOB;
-    const v4u a = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rw, o, 0, 0));
-    const v4u b = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rw, o + 16, 0, 0));
-    gw[c][0] = a.x; gw[c][1] = a.y; gw[c][2] = a.z; gw[c][3] = a.w;
-    gw[c][4] = b.x; gw[c][5] = b.y; gw[c][6] = b.z; gw[c][7] = b.w;
-  }
+  for (int k = 0; k < MAXK; ++k) g[k] = GCAST(const uint32_t, W + off)[min(lane_id() + 64 * k, H / 2 - 1)];
 }
 
 // LONG: the split-attention variant (for long contexts): every GEMV
@@ -472,6 +449,11 @@ struct Kern {
     uint32_t seq = 0;
     uint32_t lo[KX], hi[KX];
     const float eps = p.eps, inv_h = 1.0f / (float)H;
+    // the lane's input-norm and post-attention-norm gains of the current
+    // layer, loaded at the top of the layer (the loads land while the
+    // courier waits for this workgroup's stores)
+    uint32_t gq[KX], gg[KX];
+    if (flags & 1) courier_gains<KX>(W, p.layer0.in_norm, H, gq);
     // ---- embedding -> the residual of layer 0
     if (flags & 1) {
       XR_PUT(s, 1, XR_START);
@@ -490,7 +472,7 @@ struct Kern {
           hi[k] = __float_as_uint(e4m3_to_f32(w >> 8) * sc);
         }
       }
-      raw_to_lds<KX>(lo, hi, H, inv_h, eps, s.xd_raw, &s.r_xd);
+      norm_to_lds<KX>(lo, hi, gq, H, inv_h, eps, s.xd_raw, s.xd_act);
       hand_over(&s.seq, ++seq);
       XR_PUT(s, 1, XR_HANDOFF);
     }
@@ -514,6 +496,8 @@ struct Kern {
       const uint64_t loff = (uint64_t)l * p.layer_stride;
       const int ph = 2 + 6 * l;
       const uint32_t bq = 5u * (uint32_t)l;
+      if ((flags & 1) && l > 0) courier_gains<KX>(W, p.layer0.in_norm + loff, H, gq);
+      if (flags & 4) courier_gains<KX>(W, p.layer0.post_norm + loff, H, gg);
       // ---- residual entering layer l (layer 0: the embedding above)
       if (BAR && l > 0 && !grid_barrier(p, s, bq - 1)) return abort(s);
       if ((flags & 1) && l > 0) {
@@ -523,7 +507,7 @@ struct Kern {
                                  mx))
           return abort(s);
         XR_PUT(s, ph + 0, XR_READY);
-        raw_to_lds<KX>(lo, hi, H, inv_h, eps, s.xd_raw, &s.r_xd);
+        norm_to_lds<KX>(lo, hi, gq, H, inv_h, eps, s.xd_raw, s.xd_act);
         hand_over(&s.seq, ++seq);
         XR_PUT(s, ph + 0, XR_HANDOFF);
       }
@@ -577,7 +561,7 @@ struct Kern {
         if (!gather_pairs_at<KX>(p, rs, H / 2, make_tag(epoch, vec_id(l, V_XO)), lo, hi, xword(p, l, V_XO), mo))
           return abort(s);
         XR_PUT(s, ph + 4, XR_READY);
-        raw_to_lds<KX>(lo, hi, H, inv_h, eps, s.xo_raw, &s.r_xo);
+        norm_to_lds<KX>(lo, hi, gg, H, inv_h, eps, s.xo_raw, s.xo_act);
         hand_over(&s.seq, ++seq);
         XR_PUT(s, ph + 4, XR_HANDOFF);
       }
@@ -601,13 +585,14 @@ struct Kern {
     const int ph_head = 2 + 6 * L;
     if (BAR && !grid_barrier(p, s, 5u * (uint32_t)L - 1u)) return abort(s);
     {
+      courier_gains<KX>(W, p.final_norm, H, gq);
       if (!stores_out(p, s, 5u * (uint32_t)L - 1u)) return abort(s);
       XR_PUT(s, ph_head, XR_START);
       if (!gather_pairs_at<KX>(p, rs, H / 2, make_tag(epoch, vec_id(L - 1, V_XD)), lo, hi, xword(p, L - 1, V_XD),
                                mx))
         return abort(s);
       XR_PUT(s, ph_head, XR_READY);
-      raw_to_lds<KX>(lo, hi, H, inv_h, eps, s.xd_raw, &s.r_xd);
+      norm_to_lds<KX>(lo, hi, gq, H, inv_h, eps, s.xd_raw, s.xd_act);
       hand_over(&s.seq, ++seq);
       XR_PUT(s, ph_head, XR_HANDOFF);
     }
@@ -802,8 +787,6 @@ struct Kern {
     WRow<F_LIN, NQ> o[kMaxO];
     WRow<F_LIN, NH> gu[kMaxGU][4];
     WRow<F_8, NI> d[kMaxD];
-    uint32_t gin[NH][8];     // input-norm gains of the QKV rows' layer (lane slice)
-    uint32_t gpost[NH][8];   // post-attention-norm gains (gate/up input)
     uint32_t so[kMaxO], sg[kMaxGU], sd[kMaxD];   // output word of each O / gate-up / down unit
   };
 
@@ -813,7 +796,6 @@ struct Kern {
     const GMat g = gmat(p.layer0.qkv, lo);
 #pragma unroll
     for (int k = 0; k < kMaxQKV; ++k) wrow_load(rw, g, u[S_QKV + k], w.q[k]);
-    gain_load<NH>(rw, (uint32_t)(p.layer0.in_norm + lo), p.H, u[S_QKV] >= 0, w.gin);
   }
   static __device__ __forceinline__ void load_layer_o(const Params& p, __amdgpu_buffer_rsrc_t rw, const int* u,
                                                       int l, GemvW& w) {
@@ -829,7 +811,6 @@ struct Kern {
     for (int k = 0; k < kMaxGU; ++k)
 #pragma unroll
       for (int r = 0; r < 4; ++r) wrow_load(rw, gg, u[S_GU + k] >= 0 ? 4 * u[S_GU + k] + r : -1, w.gu[k][r]);
-    gain_load<NH>(rw, (uint32_t)(p.layer0.post_norm + lo), p.H, u[S_GU] >= 0, w.gpost);
     const GMat gd = gmat(p.layer0.down, lo);
 #pragma unroll
     for (int k = 0; k < kMaxD; ++k) wrow_load(rw, gd, u[S_D + k], w.d[k]);
@@ -855,7 +836,7 @@ struct Kern {
       }
       if (u[S_QKV] >= 0) {
       uint32_t xa[NH][8];
-      norm_act<NH>(s.xd_raw, s.r_xd, w.gin, H, xa);
+      load_act<NH>(s.xd_act, H, xa);
 #ifdef MK_XRAY
       {  // X-ray: when this wave's QKV rows are all in registers
         uint32_t z = 0;
@@ -939,7 +920,7 @@ struct Kern {
       }
       if (u[S_GU] >= 0) {
       uint32_t xa[NH][8];
-      norm_act<NH>(s.xo_raw, s.r_xo, w.gpost, H, xa);
+      load_act<NH>(s.xo_act, H, xa);
       const uint32_t base = xword(p, l, V_H), tag = make_tag(epoch, vec_id(l, V_H));
 #pragma unroll
       for (int k = 0; k < kMaxGU; ++k) {
@@ -1478,12 +1459,10 @@ struct Kern {
 #pragma unroll
       for (int b = 0; b < UBH; ++b) wrow_load(rw, g, row(q * UBH + b), B[q][b]);
     asm volatile("" ::: "memory");
-    uint32_t gf[NH][8];
-    gain_load<NH>(rw, (uint32_t)p.final_norm, p.H, true, gf);
     ok = ok && wait_seq(p, &s.seq, (uint32_t)(p.L * (LONG ? hdr[S_NIN_L] : hdr[S_NIN])) + 1u);
     XR_MIN(s, 2 + 6 * p.L, XR_SEEN);
     uint32_t xa[NH][8];
-    norm_act<NH>(s.xd_raw, s.r_xd, gf, p.H, xa);
+    load_act<NH>(s.xd_act, p.H, xa);
     best = -INFINITY;
     bidx = 0x7FFFFFFF;
     auto use = [&](const WRow<F_8, NH>(&Bq)[UBH], int k0) {

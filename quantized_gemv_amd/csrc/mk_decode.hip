@@ -1013,7 +1013,7 @@ struct Kern {
   // blocks the home holds in registers, loaded a layer ahead (the split
   // variant's home also gathers and merges the helpers' partials)
   static constexpr int MB = LONG ? 2 : 4;
-  static_assert(MB >= 2, "the home streams through two of its register blocks");
+  static_assert(MB >= 2 && MB % 2 == 0, "the home streams through two of its register blocks; scores go in pairs");
   static_assert(GS == 2 && HD % 32 == 0, "matrix-core attention: two q heads per KV head");
 
   // x = hi + mid + lo, each a bf16 (bits in the low half), exactly: each
@@ -1070,19 +1070,11 @@ struct Kern {
       qop[c] = live ? *reinterpret_cast<const v4u*>(&s.qa[r][32 * c + 8 * q]) : v4u{0u, 0u, 0u, 0u};
   }
 
-  // Scores of block j0 in log2 units: sc[i] for position j0 + 4(l/16) + i
-  // of this lane's head ((l%16) / 4), -inf outside [a, b) and in lanes past
-  // the two heads' quads.
-  static __device__ __forceinline__ void att_block_scores(const S& s, const KVBlock& kb, int j0, int a, int b,
-                                                          float (&sc)[4]) {
+  // Scores of block j0 in log2 units from its product d: sc[i] for position
+  // j0 + 4(l/16) + i of this lane's head ((l%16) / 4), -inf outside [a, b)
+  // and in lanes past the two heads' quads.
+  static __device__ __forceinline__ void att_score_out(const f4& d, int j0, int a, int b, float (&sc)[4]) {
     const int lane = lane_id(), r = lane & 15, q = lane >> 4;
-    v4u qop[NKC];
-    att_qop(s, qop);   // from LDS for every block: no registers held across blocks
-    f4 d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < NKC; ++c)
-      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb.k[c]), __builtin_bit_cast(bf16x8, qop[c]),
-                                                  d, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float v = d[i] + dpp<0xB1>(d[i]);   // (hi + mid), (lo + 0)
@@ -1090,6 +1082,33 @@ struct Kern {
       const int j = j0 + 4 * q + i;
       sc[i] = r < 4 * GS && j >= a && j < b ? v : -INFINITY;
     }
+  }
+  static __device__ __forceinline__ void att_block_scores(const S& s, const KVBlock& kb, int j0, int a, int b,
+                                                          float (&sc)[4]) {
+    v4u qop[NKC];
+    att_qop(s, qop);   // from LDS for every streamed block: no registers held across blocks
+    f4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NKC; ++c)
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb.k[c]), __builtin_bit_cast(bf16x8, qop[c]),
+                                                  d, 0, 0, 0);
+    att_score_out(d, j0, a, b, sc);
+  }
+  // Two held blocks' scores at once (q operand in registers): their
+  // matrix-core chains interleave instead of waiting on each other.
+  static __device__ __forceinline__ void att_pair_scores(const v4u (&qop)[NKC], const KVBlock& ka, const KVBlock& kb,
+                                                         int ja, int jb, int a, int b, float (&sa)[4],
+                                                         float (&sb)[4]) {
+    f4 da = {0.f, 0.f, 0.f, 0.f}, db = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) {
+      da = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka.k[c]), __builtin_bit_cast(bf16x8, qop[c]),
+                                                   da, 0, 0, 0);
+      db = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb.k[c]), __builtin_bit_cast(bf16x8, qop[c]),
+                                                   db, 0, 0, 0);
+    }
+    att_score_out(da, ja, a, b, sa);
+    att_score_out(db, jb, a, b, sb);
   }
   // The entry of a per-head pair (wave-uniform values) for head `odd`.
   // Read out through readfirstlane: a plain select between two array
@@ -1260,13 +1279,19 @@ struct Kern {
     // ---- the blocks held in registers (loaded a layer ahead): all scores,
     // one maximum, then the weights and the value products
     if (nblk > 0) {
+      v4u qop[NKC];
+      att_qop(s, qop);
       float sc[MB][4];
       float v = -INFINITY;
+      // in pairs: a block past P scores -inf everywhere (its registers hold
+      // finite values), so a pair with one live block still gives the
+      // right maximum
 #pragma unroll
-      for (int t = 0; t < MB; ++t) {
+      for (int t = 0; t < MB; t += 2) {
         if (t < nblk_w) {
-          att_block_scores(s, kv.b[t], (t * kCW + cw) * BP, 0, P, sc[t]);
-          v = fmaxf(v, block_max(sc[t]));
+          att_pair_scores(qop, kv.b[t], kv.b[t + 1], (t * kCW + cw) * BP, ((t + 1) * kCW + cw) * BP, 0, P, sc[t],
+                          sc[t + 1]);
+          v = fmaxf(v, fmaxf(block_max(sc[t]), block_max(sc[t + 1])));
         }
       }
       float bm[GS];
@@ -1307,22 +1332,30 @@ struct Kern {
     const int t = cw * 64 + lane;
     const int tc = min(t, NOUT - 1);
     const int h = tc / HD;
+    // every LDS read of the merge goes out before the first is used
+    float wm[kCW], wl[kCW], wp[kCW];
+#pragma unroll
+    for (int w = 0; w < kCW; ++w) {
+      wm[w] = s.wm[w][h];
+      wl[w] = s.wl[w][h];
+      wp[w] = s.part[w][tc];
+    }
     const float sp = s.sp[h];
+    const uint32_t vpw = s.vp[(tc % HD) / 2];
     float M = sp;
 #pragma unroll
-    for (int w = 0; w < kCW; ++w) M = fmaxf(M, s.wm[w][h]);
+    for (int w = 0; w < kCW; ++w) M = fmaxf(M, wm[w]);
     if (LONG) {
 #pragma unroll 8
       for (int i = 0; i < ns; ++i) M = fmaxf(M, s.spart[i][NOUT + h]);
     }
-    const uint32_t vpw = s.vp[(tc % HD) / 2];
     const float ec = __builtin_amdgcn_exp2f(sp - M);
     float Lt = ec, O = ec * ((tc & 1) ? bf16_hi(vpw) : bf16_lo(vpw));
 #pragma unroll
     for (int w = 0; w < kCW; ++w) {
-      const float e = att_weight(s.wm[w][h], M);
-      Lt = fmaf(s.wl[w][h], e, Lt);
-      O = fmaf(s.part[w][tc], e, O);
+      const float e = att_weight(wm[w], M);
+      Lt = fmaf(wl[w], e, Lt);
+      O = fmaf(wp[w], e, O);
     }
     if (LONG) {
       // eight partials at a time: their LDS reads all go out before the
@@ -1348,7 +1381,7 @@ struct Kern {
         }
       }
     }
-    const float o = O / Lt;
+    const float o = O * __builtin_amdgcn_rcpf(Lt);   // v_rcp_f32: within 1 ulp
     XR_MAX(s, ph + 2, XR_M0);
     const float o1 = dpp<0xB1>(o);   // the neighbouring output (t ^ 1)
     st_xword(rx, ok && t < NOUT && (t & 1) == 0 ? 8u * (xword(p, l, V_O) + (g * NOUT + t) / 2) : kOOB,

@@ -74,7 +74,7 @@ typedef struct mk_config {
 /* Byte sizes of the caller-owned device buffers, plus figures used for
  * measurement. */
 typedef struct mk_sizes {
-  size_t weights;     /* packed weight arena */
+  size_t weights;     /* packed weight arena (and the work table mk_bind writes after it) */
   size_t kv;          /* KV cache: n_layers * 2 * n_kv_heads * ctx4 * head_dim * 2 (bf16),
                          ctx4 = max_ctx rounded up to a multiple of 4.  Per layer l, K then V
                          (kv = 0, 1), per KV head g, a plane of ctx4 * head_dim values at element
@@ -212,7 +212,7 @@ int mk_decode_step_async(mk_model* m, const int32_t* d_token, int32_t pos, int32
 /* The same step as mk_decode_step_async, for callers that cannot allocate
  * device memory around it (code under HIP graph capture, tight serving
  * loops, harnesses that forbid allocation): its scratch (exchange words,
- * argmax words, error word, work table, kernel parameters) is a static
+ * argmax words, error word, kernel parameters) is a static
  * device array of the library, 32 MiB on each GPU, held until the process
  * ends, instead of the bound scratch buffer.  The model must be bound and
  * packed (its weights, KV cache and RoPE table are used as usual); the
@@ -220,8 +220,8 @@ int mk_decode_step_async(mk_model* m, const int32_t* d_token, int32_t pos, int32
  * mk_decode_step_async.  The call allocates nothing: no hipMalloc, hipFree or
  * allocating library routine; it enqueues a one-word clear of the array's
  * error word, and the first call on a device, or the first after another
- * model used the array, also copies the model's parameters and work table
- * into it.  Every call on one GPU shares that GPU's array: calls that overlap
+ * model used the array, also copies the model's parameters into it (the
+ * work table lives in the weight arena, written by mk_bind).  Every call on one GPU shares that GPU's array: calls that overlap
  * on one GPU (two streams, two threads, two models) race and must be
  * serialised by the caller.  A failed step leaves -1 in d_next; its error
  * code is not kept.  Errors (immediate): MK_E_INVALID (as for

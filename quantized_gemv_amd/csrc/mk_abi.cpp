@@ -109,6 +109,16 @@ int hip_fail(mk_model* m, hipError_t e, const char* what) {
 
 bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) % kAlign) == 0; }
 
+// The largest grid the library launches.
+constexpr int kMaxGrid = 1024;
+
+// Ints of the work table for `grid` workgroups and of the q/k/v pair map
+// that follows it (per KV head, one word offset per pair of its rows).
+size_t sched_ints(const mk_config& c, int grid) {
+  return (size_t)grid * kWaves * kSchedInts +
+         (size_t)c.n_kv_heads * (c.n_q_heads / c.n_kv_heads + 2) * c.head_dim / 2;
+}
+
 // Lay out the weight arena and fill the matrix descriptors.
 void layout_weights(mk_model* m) {
   const mk_config& c = m->cfg;
@@ -158,6 +168,10 @@ void layout_weights(mk_model* m) {
   algo = algo_before + layer_algo * c.n_layers;
   place_vec(P.final_norm, H);
   P.layer_stride = m->layer_stride;
+  // the work table and q/k/v pair map (written at bind), sized for the
+  // largest grid
+  P.sched = off;
+  off = align_up(off + sched_ints(m->cfg, kMaxGrid) * sizeof(int32_t));
   m->weights_bytes = off;
   m->algo_bytes = algo;
 }
@@ -191,7 +205,7 @@ bool prefill_supported(const mk_config& c) {
 }
 
 // Lay out the scratch buffer: per-layer exchange vectors, argmax words, the
-// error word, the zero page, the work table, the params copy, token slots.
+// error word, the params copy, token slots.
 // Words of one split-attention partial: the outputs of the KV head's q heads,
 // their maxima and sums, padded to 128 bytes.
 uint64_t split_pw(const mk_config& c) {
@@ -261,12 +275,7 @@ void layout_scratch(mk_model* m, int grid, bool for_sizing = true) {
   X.err = al(w);
   X.amax = X.err + 1;
   w = X.amax + 1;
-  X.sched = (w + 31) / 32 * 32;                 // 256-byte boundary
-  w = X.sched;
-  w += (uint64_t)grid * kWaves * kSchedInts / 2;
-  X.qmap = w;
-  w += (nkv * (uint64_t)(nq / nkv + 2) * hd / 2 + 1) / 2;
-  w = (w + 31) / 32 * 32;
+  w = (w + 31) / 32 * 32;   // 256-byte boundary
   X.words = w;
   m->params_off = align_up(w * 8);
   m->tok_off = align_up(m->params_off + sizeof(Params));
@@ -420,7 +429,6 @@ int n_phases(const mk_config& c) { return 6 * c.n_layers + 4; }
 
 // Before mk_bind the compute-unit count is unknown, so sizes are reported for
 // the grid option if set, else for the largest grid the library launches.
-constexpr int kMaxGrid = 1024;
 int sizing_grid(const mk_model* m) { return m->grid_opt > 0 ? m->grid_opt : kMaxGrid; }
 
 int validate_cfg(const mk_config* c) {
@@ -539,8 +547,8 @@ int launch_step(mk_model* m, const int32_t* d_token, int pos, int32_t* d_next, f
 }
 
 // ---- the no-allocation step (mk_decode_step_async_noalloc)
-// Its scratch (exchange words, argmax words, error word, work table and the
-// kernel parameter block, laid out as in the bound scratch buffer) is this
+// Its scratch (exchange words, argmax words, error word and the kernel
+// parameter block, laid out as in the bound scratch buffer) is this
 // file-scope device array.  Each device holds its own copy, at the address
 // hipGetSymbolAddress reports with that device current; the array's name in
 // host code is only a handle for that lookup.
@@ -549,7 +557,7 @@ static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
 
 // Per device: the array's device address, the exchange epoch of the last
 // step run in it (tags stay unique across every model that uses the array),
-// which model's work table and parameters it holds, and how much of it any
+// which model's parameters it holds, and how much of it any
 // model has used.
 struct StaticSlot {
   uint8_t* ptr = nullptr;
@@ -653,8 +661,9 @@ int mk_bind(mk_model* m, void* d_weights, void* d_kv, void* d_rope, void* d_scra
   // the attention reads whole 4-position V tiles (weight 0 past the last
   // cached position): never-written slots must hold finite values
   HIPCK(m, hipMemsetAsync(d_kv, 0, kv_bytes(m->cfg), s));
-  HIPCK(m, hipMemcpyAsync(m->d_scratch + 8 * m->P.x.sched, m->sched.data(), m->sched.size() * sizeof(int32_t),
-                          hipMemcpyHostToDevice, s));
+  m->P.qmap = m->P.sched + (uint64_t)grid * kWaves * kSchedInts * sizeof(int32_t);
+  HIPCK(m, hipMemcpyAsync(static_cast<uint8_t*>(d_weights) + m->P.sched, m->sched.data(),
+                          m->sched.size() * sizeof(int32_t), hipMemcpyHostToDevice, s));
   return sync_params(m, s);
 }
 
@@ -797,8 +806,6 @@ int mk_decode_step_async_noalloc(mk_model* m, const int32_t* d_token, int32_t po
     m->P_static = m->P;
     m->P_static.xch = (decltype(m->P_static.xch))slot.ptr;
     HIPCK(m, hipMemcpyAsync(slot.ptr + m->params_off, &m->P_static, sizeof(Params), hipMemcpyHostToDevice, s));
-    HIPCK(m, hipMemcpyAsync(slot.ptr + 8 * m->P.x.sched, m->sched.data(), m->sched.size() * sizeof(int32_t),
-                            hipMemcpyHostToDevice, s));
     slot.owner = m->uid;
     slot.extent = std::max(slot.extent, (size_t)(8 * m->P.x.err));
     m->static_dirty = false;

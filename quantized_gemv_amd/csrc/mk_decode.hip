@@ -640,7 +640,7 @@ struct Kern {
   // g's q, k and v rows, from the map in the work table (read once per
   // launch; pairs past the first np repeat the last one).
   static __device__ __forceinline__ void qkv_map(const Params& p, int g, int np, uint32_t (&qm)[KA]) {
-    MK_GLOBAL const int* m = GCAST(const int, p.xch + p.x.qmap) + (size_t)g * ((GS + 2) * HD / 2);
+    MK_GLOBAL const int* m = GCAST(const int, p.w + p.qmap) + (size_t)g * ((GS + 2) * HD / 2);
 #pragma unroll
     for (int k = 0; k < KA; ++k) qm[k] = (uint32_t)m[min(lane_id() + 64 * k, np - 1)];
   }
@@ -790,12 +790,15 @@ struct Kern {
     uint32_t so[kMaxO], sg[kMaxGU], sd[kMaxD];   // output word of each O / gate-up / down unit
   };
 
+  // have = false (past the last layer): the same loads at the offset past
+  // the arena (zeros, no memory access), so the last layer runs the same
+  // instructions as every other.
   static __device__ __forceinline__ void load_layer_qkv(const Params& p, __amdgpu_buffer_rsrc_t rw, const int* u,
-                                                        int l, GemvW& w) {
+                                                        int l, GemvW& w, bool have = true) {
     const uint64_t lo = (uint64_t)l * p.layer_stride;
     const GMat g = gmat(p.layer0.qkv, lo);
 #pragma unroll
-    for (int k = 0; k < kMaxQKV; ++k) wrow_load(rw, g, u[S_QKV + k], w.q[k]);
+    for (int k = 0; k < kMaxQKV; ++k) wrow_load(rw, g, have ? u[S_QKV + k] : -1, w.q[k]);
   }
   static __device__ __forceinline__ void load_layer_o(const Params& p, __amdgpu_buffer_rsrc_t rw, const int* u,
                                                       int l, GemvW& w) {
@@ -816,9 +819,10 @@ struct Kern {
     for (int k = 0; k < kMaxD; ++k) wrow_load(rw, gd, u[S_D + k], w.d[k]);
   }
 
-  // One layer of a GEMV compute wave.  NEXT: the burst also loads the next
+  // One layer of a GEMV compute wave; the burst also loads the next layer's
+  // QKV rows (past the last layer: no-op loads).  One instance serves every
+  // layer, which keeps the kernel's code within the instruction cache.
   // layer's QKV rows.
-  template <bool NEXT>
   static __device__ __forceinline__ bool gemv_layer(const Params& p, S& s, int l, const int* hdr, const int* u,
                                                     GemvW& w, int pos, int ns, int cw, uint32_t epoch,
                                                     __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rx, bool ok) {
@@ -880,7 +884,7 @@ struct Kern {
     if (!LONG) {
       load_layer_o(p, rw, u, l, w);
       load_layer_mlp(p, rw, u, l, w);
-      if (NEXT) load_layer_qkv(p, rw, u, l + 1, w);
+      load_layer_qkv(p, rw, u, l + 1, w, l + 1 < p.L);
     } else {
       // a helper's first pass of cached rows does not depend on this step's q
       const bool help = hdr[S_SPLIT] >= 0 && hdr[S_SPLIT_IDX] <= ns;
@@ -890,7 +894,7 @@ struct Kern {
         ok = att_help(p, s, l, hdr[S_SPLIT], hdr[S_SPLIT_IDX], pos, ns, cw, sbase + hdr[S_IQS_L], epoch, rx, ok, k0);
       load_layer_o(p, rw, u, l, w);
       load_layer_mlp(p, rw, u, l, w);
-      if (NEXT) load_layer_qkv(p, rw, u, l + 1, w);
+      load_layer_qkv(p, rw, u, l + 1, w, l + 1 < p.L);
     }
     // ---- O-projection + residual
     {
@@ -979,8 +983,8 @@ struct Kern {
       w.sd[k] = xpad_word((uint32_t)max(u[S_D + k], 0), p.H, p.x.pad_c[V_XD], p.x.pad_stride[V_XD]);
     load_layer_qkv(p, rw, u, 0, w);
     bool ok = true;
-    for (int l = 0; l + 1 < p.L; ++l) ok = gemv_layer<true>(p, s, l, hdr, u, w, pos, ns, cw, epoch, rw, rx, ok);
-    return gemv_layer<false>(p, s, p.L - 1, hdr, u, w, pos, ns, cw, epoch, rw, rx, ok);
+    for (int l = 0; l < p.L; ++l) ok = gemv_layer(p, s, l, hdr, u, w, pos, ns, cw, epoch, rw, rx, ok);
+    return ok;
   }
 
   // ---------------------------------------------- attention compute waves
@@ -1243,7 +1247,6 @@ struct Kern {
   // Home workgroup of KV head g.  Its slice is positions 0..P-1 of the cache
   // (all of 0..pos-1 without helpers); position `pos` itself (its k and v were
   // produced in this step) enters at the merge, with the helpers' partials.
-  template <bool NEXT>
   static __device__ __forceinline__ bool att_layer(const Params& p, S& s, int l, int g, int pos, int ns, int cw,
                                                    KVRegs& kv, uint32_t epoch, __amdgpu_buffer_rsrc_t rx, bool ok) {
     const int lane = lane_id();
@@ -1389,7 +1392,9 @@ struct Kern {
     XR_MAX(s, ph + 1, XR_DONE);
     arrive(s, cw, 5u * (uint32_t)l + 5u, true);   // attention output stored; nothing of the other phases
     lds_barrier();
-    if (NEXT) kv_prefetch(p, l + 1, g, pos, cw, kv);
+    // the next layer's held blocks (the last layer reloads its own: one
+    // instance of this code for every layer)
+    kv_prefetch(p, min(l + 1, p.L - 1), g, pos, cw, kv);
     return ok;
   }
 
@@ -1398,8 +1403,8 @@ struct Kern {
     KVRegs kv;
     kv_prefetch(p, 0, g, pos, cw, kv);
     bool ok = true;
-    for (int l = 0; l + 1 < p.L; ++l) ok = att_layer<true>(p, s, l, g, pos, ns, cw, kv, epoch, rx, ok);
-    return att_layer<false>(p, s, p.L - 1, g, pos, ns, cw, kv, epoch, rx, ok);
+    for (int l = 0; l < p.L; ++l) ok = att_layer(p, s, l, g, pos, ns, cw, kv, epoch, rx, ok);
+    return ok;
   }
 
   // Slice i of KV head g's cached positions for split attention: [a, b).
@@ -1543,7 +1548,7 @@ struct Kern {
     }
     if (wg == 0 && threadIdx.x == 0) *d_next = -1;  // overwritten on success
     // this workgroup's row of the work table, as wave-uniform values
-    MK_GLOBAL const int* tab = GCAST(const int, p.xch + p.x.sched) + (size_t)wg * kSchedInts * kWaves;
+    MK_GLOBAL const int* tab = GCAST(const int, p.w + p.sched) + (size_t)wg * kSchedInts * kWaves;
     int hdr[kHdrInts];
 #pragma unroll
     for (int i = 0; i < kHdrInts; ++i) hdr[i] = __builtin_amdgcn_readfirstlane(tab[i]);

@@ -80,9 +80,6 @@ struct Xch {
   uint64_t bar;               // grid-barrier variant: one arrival counter per barrier of a step (5L + 1)
   uint64_t err;               // error word (uint32 in a 64-bit slot)
   uint64_t amax;              // packing scratch: tensor abs-max (uint32 bits)
-  uint64_t sched;             // the work table (int32)
-  uint64_t qmap;              // per KV head: word offset (in the q/k/v vector) of each pair of
-                              // its q rows, k rows and v rows, in that order (int32)
   uint64_t words;             // total words
 };
 
@@ -131,6 +128,14 @@ struct Params {
   Layer layer0;
   uint64_t layer_stride;  // bytes between consecutive layers' matrices
   uint64_t final_norm;
+  // Read-only tables in the weight arena (byte offsets), written at bind:
+  // the work table (int32, kSchedInts per header and per compute wave) and,
+  // right after it, per KV head the word offset (in the q/k/v vector) of
+  // each pair of its q rows, k rows and v rows, in that order (int32).
+  // Every workgroup reads its rows once per launch.  Being an input of
+  // every decode entry point, the arena also serves the step that brings
+  // no scratch buffer of its own.
+  uint64_t sched, qmap;
   Xch x;
   int grid;
   uint64_t spin_limit;    // s_memrealtime ticks

@@ -2,7 +2,7 @@
 its output equals mk_decode_step_async's (same kernels, same work table and
 exchange layout, only the scratch memory differs), bit for bit, on calls in
 a row whose inputs shrink and whose models change, so the shared static
-array's parameters, work table and tags are refreshed each time."""
+array's parameters and tags are refreshed each time."""
 import numpy as np
 import pytest
 import torch

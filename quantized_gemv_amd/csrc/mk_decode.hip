@@ -288,41 +288,55 @@ __device__ __forceinline__ void load_act(const uint32_t* src, int K, uint32_t (&
 // A residual vector for LDS and its RMSNorm: pairs j = l + 64k of x (fp32
 // bits in lo/hi) go to x_raw (for the residual add after the next
 // projection) and bf16(g * (x * r)), r = 1/sqrt(mean(x^2) + eps), to act as
-// bf16 pairs in the same order (the GEMVs' input); g[k] holds the gains of
-// pair j as a bf16 pair.  The courier does this once for the workgroup, so
-// the compute waves only load act.  x_raw holds 128 * MAXK floats and act
+// bf16 pairs in the same order (the GEMVs' input); g[2k], g[2k+1] hold the
+// gains of pair j.  The courier does this once for the workgroup, so the
+// compute waves only load act.  x_raw holds 128 * MAXK floats and act
 // 64 * MAXK pairs: lanes past H/2 store their (don't-care) pairs beyond
-// element H, where nobody reads, and add zeros to the sum of squares, so
-// there is no branch per pair.  inv_h = 1/H (exact for a power of two); the
-// reciprocal square root is v_rsq_f32 (within 1 ulp).
+// element H, where nobody reads, and add zeros to the sum of squares.
+// inv_h = 1/H (exact for a power of two); the reciprocal square root is
+// v_rsq_f32 (within 1 ulp).
 template <int MAXK>
 __device__ __forceinline__ void norm_to_lds(const uint32_t (&lo)[MAXK], const uint32_t (&hi)[MAXK],
-                                            const uint32_t (&g)[MAXK], int H, float inv_h, float eps, float* x_raw,
-                                            uint32_t* act) {
+                                            const float (&g)[2 * MAXK], int H, float inv_h, float eps,
+                                            float* x_raw, uint32_t* act) {
   const int lane = lane_id();
   float ss = 0.f;
+  if (H == 128 * MAXK) {   // every lane's pairs are in the vector: no masking
 #pragma unroll
-  for (int k = 0; k < MAXK; ++k) {
-    const int j = lane + 64 * k;
-    const bool in = j < H / 2;
-    const float a = in ? __uint_as_float(lo[k]) : 0.f, b = in ? __uint_as_float(hi[k]) : 0.f;
-    ss = fmaf(a, a, ss);
-    ss = fmaf(b, b, ss);
-    *reinterpret_cast<v2u*>(x_raw + 2 * j) = v2u{lo[k], hi[k]};
+    for (int k = 0; k < MAXK; ++k) {
+      const float a = __uint_as_float(lo[k]), b = __uint_as_float(hi[k]);
+      ss = fmaf(a, a, ss);
+      ss = fmaf(b, b, ss);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < MAXK; ++k) {
+      const bool in = lane + 64 * k < H / 2;
+      const float a = in ? __uint_as_float(lo[k]) : 0.f, b = in ? __uint_as_float(hi[k]) : 0.f;
+      ss = fmaf(a, a, ss);
+      ss = fmaf(b, b, ss);
+    }
   }
+#pragma unroll
+  for (int k = 0; k < MAXK; ++k) *reinterpret_cast<v2u*>(x_raw + 2 * (lane + 64 * k)) = v2u{lo[k], hi[k]};
   const float r = __builtin_amdgcn_rsqf(wave_sum(ss) * inv_h + eps);
 #pragma unroll
   for (int k = 0; k < MAXK; ++k)
-    act[lane + 64 * k] = pack_bf16(bf16_lo(g[k]) * (__uint_as_float(lo[k]) * r),
-                                   bf16_hi(g[k]) * (__uint_as_float(hi[k]) * r));
+    act[lane + 64 * k] = pack_bf16(g[2 * k] * (__uint_as_float(lo[k]) * r), g[2 * k + 1] * (__uint_as_float(hi[k]) * r));
 }
 
-// The gains (bf16 pairs) of the courier's pairs j = l + 64k of a norm whose
-// weights sit at byte `off` of the arena (pairs past H/2 repeat the last).
+// The gains of the courier's pairs j = l + 64k of a norm whose bf16
+// weights sit at byte `off` of the arena, as fp32 (pairs past H/2 repeat
+// the last).  Loaded ahead of the hand-off they serve, so the conversion
+// stays off its path.
 template <int MAXK>
-__device__ __forceinline__ void courier_gains(MK_GLOBAL const uint8_t* W, uint64_t off, int H, uint32_t (&g)[MAXK]) {
+__device__ __forceinline__ void courier_gains(MK_GLOBAL const uint8_t* W, uint64_t off, int H, float (&g)[2 * MAXK]) {
 #pragma unroll
-  for (int k = 0; k < MAXK; ++k) g[k] = GCAST(const uint32_t, W + off)[min(lane_id() + 64 * k, H / 2 - 1)];
+  for (int k = 0; k < MAXK; ++k) {
+    const uint32_t w = GCAST(const uint32_t, W + off)[min(lane_id() + 64 * k, H / 2 - 1)];
+    g[2 * k] = bf16_lo(w);
+    g[2 * k + 1] = bf16_hi(w);
+  }
 }
 
 // LONG: the split-attention variant (for long contexts): every GEMV
@@ -452,7 +466,7 @@ struct Kern {
     // the lane's input-norm and post-attention-norm gains of the current
     // layer, loaded at the top of the layer (the loads land while the
     // courier waits for this workgroup's stores)
-    uint32_t gq[KX], gg[KX];
+    float gq[2 * KX], gg[2 * KX];
     if (flags & 1) courier_gains<KX>(W, p.layer0.in_norm, H, gq);
     // ---- embedding -> the residual of layer 0
     if (flags & 1) {
@@ -1297,10 +1311,10 @@ struct Kern {
           v = fmaxf(v, fmaxf(block_max(sc[t]), block_max(sc[t + 1])));
         }
       }
-      float bm[GS];
+      // the first fold: m is -inf and lsum, acc are 0, so the rescale of
+      // att_rescale would multiply zeros; take the maxima directly
 #pragma unroll
-      for (int h = 0; h < GS; ++h) bm[h] = head_max(v, h);
-      att_rescale(bm, m, lsum, acc);
+      for (int h = 0; h < GS; ++h) m[h] = head_max(v, h);
 #pragma unroll
       for (int t = 0; t < MB; ++t)
         if (t < nblk_w) att_block_accum(kv.b[t], sc[t], m, lsum, acc);

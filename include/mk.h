@@ -209,6 +209,28 @@ int32_t mk_decode_step(mk_model* m, int32_t token, int32_t pos, mk_stream_t s);
 int mk_decode_step_async(mk_model* m, const int32_t* d_token, int32_t pos, int32_t* d_next,
                          float* d_logits, mk_stream_t s);
 
+/* `n` greedy decode steps in one call (monolith page, Part 2, "Mission":
+ * one persistent kernel per token, and the greedy loop of its benchmark):
+ * the token read from `d_token` (int32, device) enters at position `pos`,
+ * and step i's greedy token, the input of position pos + i + 1, is written to
+ * d_next[i] (int32[n], device).  The same kernels run the steps inside as
+ * few launches as possible: a launch runs several steps, every workgroup
+ * reducing each step's argmax itself so that the next step starts without a
+ * kernel boundary; a position with split-attention helpers (from option 8's
+ * position on, when option 7 is set) runs in a launch of its own, since a
+ * helper reads KV rows that another CU wrote, and a new launch also begins
+ * every 512 steps and where the exchange tags would wrap.  Each step's results
+ * equal those of mk_decode_step_async chained on its own tokens.
+ * `d_logits` (fp32 [n][vocab], device) receives every step's logits when
+ * non-NULL.  A token outside the vocabulary read from `d_token` makes the
+ * kernel record MK_E_INVALID in the device error word and write -1 to
+ * every d_next[i] of that launch; so does a step that hits the spin bound
+ * (MK_E_TIMEOUT), for its own and the launch's later steps.  Errors
+ * (immediate): MK_E_INVALID (n < 1, pos + n > max_ctx, d_token inside
+ * d_next[0..n), a null buffer), MK_E_STATE, MK_E_HIP. */
+int mk_decode_steps_async(mk_model* m, const int32_t* d_token, int32_t pos, int32_t n, int32_t* d_next,
+                          float* d_logits, mk_stream_t s);
+
 /* The same step as mk_decode_step_async, for callers that cannot allocate
  * device memory around it (code under HIP graph capture, tight serving
  * loops, harnesses that forbid allocation): its scratch (exchange words,

@@ -517,20 +517,30 @@ int32_t read_token_and_error(mk_model* m, const int32_t* d_next, hipStream_t s) 
   return tok;
 }
 
-// One decode launch with the parameter block at `dp` (device memory) and
-// exchange tags of `epoch`.
+// Helpers per KV head of split attention at position `pos` (0: none).
+int split_helpers(const mk_model* m, int pos) {
+  const bool barrier = m->sync_mode != 0;
+  return !barrier && m->split_chunk > 0 && pos >= m->split_from ? std::min(m->split_n, pos / m->split_chunk) : 0;
+}
+
+// One decode launch of `nsteps` greedy steps from position `pos` with the
+// parameter block at `dp` (device memory) and exchange tags of epochs
+// epoch .. epoch + nsteps - 1.  A launch of more than one step has no
+// split-attention helpers at any of its positions.
 int launch_with(mk_model* m, const Params* dp, uint32_t epoch, const int32_t* d_token, int pos, int32_t* d_next,
-                float* d_logits, hipStream_t s) {
+                float* d_logits, hipStream_t s, int nsteps = 1) {
   const mk_config& c = m->cfg;
   const bool coop = m->launch_mode == 0 || (m->launch_mode < 0 && m->P.grid > m->coresident);
   const bool barrier = m->sync_mode != 0;
-  const int ns = !barrier && m->split_chunk > 0 && pos >= m->split_from ? std::min(m->split_n, pos / m->split_chunk)
-                                                                        : 0;
+  const int ns = split_helpers(m, pos);
+  if (nsteps > 1 && (ns > 0 || split_helpers(m, pos + nsteps - 1) > 0))
+    return fail(m, MK_E_INVALID, "a launch of %d steps from position %d would use split attention", nsteps, pos);
   if (!coop && m->P.grid > m->coresident)
     return fail(m, MK_E_UNSUPPORTED, "plain launch: grid %d exceeds the %d workgroups the device holds at once",
                 m->P.grid, m->coresident);
   HIPCK(m, launch_decode(dp, c.wfmt, c.head_dim, c.n_q_heads / c.n_kv_heads, c.hidden, c.n_q_heads * c.head_dim,
-                         c.intermediate, m->P.grid, coop, barrier, d_token, pos, ns, epoch, d_next, d_logits, s));
+                         c.intermediate, m->P.grid, coop, barrier, d_token, pos, nsteps, ns, epoch, d_next, d_logits,
+                         s));
   return MK_OK;
 }
 
@@ -544,6 +554,38 @@ int launch_step(mk_model* m, const int32_t* d_token, int pos, int32_t* d_next, f
   }
   const Params* dp = reinterpret_cast<const Params*>(m->d_scratch + m->params_off);
   return launch_with(m, dp, m->epoch, d_token, pos, d_next, d_logits, s);
+}
+
+// n greedy steps from position `pos` in as few launches as the exchange
+// epochs and split attention allow: a launch never lets the epoch wrap and
+// runs at most kMaxStepsPerLaunch steps, and a position with split-attention
+// helpers gets a launch of its own (a helper reads KV rows another CU wrote;
+// only a kernel boundary makes those visible to it).  A later launch reads
+// its first token from the previous one's last output, on the same stream.
+constexpr int kMaxStepsPerLaunch = 512;
+int launch_steps(mk_model* m, const int32_t* d_token, int pos, int n, int32_t* d_next, float* d_logits,
+                 hipStream_t s) {
+  int rc = sync_params(m, s);
+  if (rc) return rc;
+  const Params* dp = reinterpret_cast<const Params*>(m->d_scratch + m->params_off);
+  for (int done = 0; done < n;) {
+    uint32_t e = (m->epoch + 1) & kEpochMask;
+    if (e == 0) {   // tags would repeat: clear the exchange words and restart
+      HIPCK(m, launch_zero_words(reinterpret_cast<uint64_t*>(m->d_scratch), m->P.x.err, s));
+      e = 1;
+    }
+    const int p0 = pos + done, ns0 = split_helpers(m, p0);
+    const int cap = (int)std::min<uint64_t>({(uint64_t)(n - done), (uint64_t)kMaxStepsPerLaunch,
+                                              (uint64_t)kEpochMask - e + 1});
+    int k = 1;
+    while (ns0 == 0 && k < cap && split_helpers(m, p0 + k) == 0) ++k;
+    rc = launch_with(m, dp, e, done == 0 ? d_token : d_next + done - 1, p0, d_next + done,
+                     d_logits ? d_logits + (size_t)done * m->cfg.vocab : nullptr, s, k);
+    if (rc) return rc;
+    m->epoch = e + (uint32_t)k - 1;
+    done += k;
+  }
+  return MK_OK;
 }
 
 // ---- the no-allocation step (mk_decode_step_async_noalloc)
@@ -769,6 +811,19 @@ int mk_decode_step_async(mk_model* m, const int32_t* d_token, int32_t pos, int32
   if (pos < 0 || pos >= m->cfg.max_ctx) return fail(m, MK_E_INVALID, "position %d outside [0, %d)", pos, m->cfg.max_ctx);
   if (!m->bound || !m->packed) return fail(m, MK_E_STATE, "decode before mk_bind and mk_pack_weights");
   return launch_step(m, d_token, pos, d_next, d_logits, reinterpret_cast<hipStream_t>(stream));
+}
+
+int mk_decode_steps_async(mk_model* m, const int32_t* d_token, int32_t pos, int32_t n, int32_t* d_next,
+                          float* d_logits, mk_stream_t stream) {
+  if (!m) return MK_E_INVALID;
+  if (!d_token || !d_next) return fail(m, MK_E_INVALID, "mk_decode_steps_async: token buffers must be non-null");
+  if (n < 1) return fail(m, MK_E_INVALID, "mk_decode_steps_async: %d steps", n);
+  if (d_token >= d_next && d_token < d_next + n)
+    return fail(m, MK_E_INVALID, "mk_decode_steps_async: d_token lies inside d_next[0..n)");
+  if (pos < 0 || (int64_t)pos + n > m->cfg.max_ctx)
+    return fail(m, MK_E_INVALID, "positions %d..%d outside [0, %d)", pos, pos + n - 1, m->cfg.max_ctx);
+  if (!m->bound || !m->packed) return fail(m, MK_E_STATE, "decode before mk_bind and mk_pack_weights");
+  return launch_steps(m, d_token, pos, n, d_next, d_logits, reinterpret_cast<hipStream_t>(stream));
 }
 
 int mk_decode_step_async_noalloc(mk_model* m, const int32_t* d_token, int32_t pos, int32_t* d_next,

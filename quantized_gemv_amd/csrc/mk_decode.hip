@@ -151,6 +151,13 @@ struct Smem {
   alignas(16) float best[kCW];
   alignas(16) int32_t bidx[kCW];
   uint32_t seq;                          // inputs handed over by the courier (kAbort: abort)
+  uint32_t fail;                         // a wave's step failed: the launch's later steps do not run
+  // the launch's step state, read from here by every step (held in no
+  // register across a step): step index, steps, first position, first
+  // epoch, the next token, and the output arrays' addresses
+  uint32_t st_i, st_n, st_pos0, st_e0, st_token;
+  uint32_t st_next[2], st_logits[2];
+  int tab[kWaves * kSchedInts];          // this workgroup's row of the work table
   uint32_t arr[kCW];                     // grid-barrier variant: barriers each compute wave has finished its part of
   XR_FIELD
 };
@@ -452,8 +459,10 @@ struct Kern {
   // ------------------------------------------------------------ courier
   // The inputs this workgroup needs, in order, for every layer; then the
   // final residual for the LM head; workgroup 0 then reduces the argmax.
+  // all_argmax: every workgroup reduces the argmax (its result is the next
+  // step's token), not only workgroup 0, which writes *d_next.
   static __device__ __forceinline__ bool courier(const Params& p, S& s, const int* hdr, int token, int pos, int ns,
-                                 uint32_t epoch, int32_t* d_next) {
+                                 uint32_t epoch, int32_t* d_next, bool all_argmax, int& next_token) {
     MK_GLOBAL const uint8_t* const W = p.w;
     const int lane = lane_id();
     const int H = p.H, L = p.L;
@@ -612,8 +621,9 @@ struct Kern {
     }
     lds_barrier();   // the compute waves' argmax candidates are in LDS
     if (BAR && !grid_barrier(p, s, 5u * (uint32_t)L)) return false;
-    // ---- workgroup 0: reduce every workgroup's (value, index)
-    if (blockIdx.x == 0) {
+    // ---- workgroup 0 (every workgroup when a step follows in this launch):
+    // reduce every workgroup's (value, index)
+    if (blockIdx.x == 0 || all_argmax) {
       XR_PUT(s, ph_head + 1, XR_START);
       uint32_t vl[KG], il[KG];
       const uint32_t base = (uint32_t)p.x.arg;
@@ -639,7 +649,8 @@ struct Kern {
       int mi = best == m ? bidx : 0x7FFFFFFF;   // smallest index among the lanes holding the maximum
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) mi = min(mi, __shfl_xor(mi, o));
-      if (lane == 0) *d_next = mi;
+      next_token = __builtin_amdgcn_readfirstlane(mi);
+      if (blockIdx.x == 0 && lane == 0) *d_next = mi;
       XR_PUT(s, ph_head + 1, XR_HANDOFF);
     }
     return true;
@@ -982,10 +993,9 @@ struct Kern {
     return ok;
   }
 
-  static __device__ __forceinline__ bool gemv_waves(const Params& p, S& s, const int* hdr, const int* u, int pos,
-                                                    int ns, int cw, uint32_t epoch, __amdgpu_buffer_rsrc_t rw,
-                                                    __amdgpu_buffer_rsrc_t rx) {
-    GemvW w;
+  // The output words of the wave's O, gate/up and down units (once per
+  // launch).
+  static __device__ __forceinline__ void gemv_setup(const Params& p, const int* u, GemvW& w) {
 #pragma unroll
     for (int k = 0; k < kMaxO; ++k)
       w.so[k] = xpad_word((uint32_t)max(u[S_O + k], 0), p.H, p.x.pad_c[V_XO], p.x.pad_stride[V_XO]);
@@ -995,6 +1005,13 @@ struct Kern {
 #pragma unroll
     for (int k = 0; k < kMaxD; ++k)
       w.sd[k] = xpad_word((uint32_t)max(u[S_D + k], 0), p.H, p.x.pad_c[V_XD], p.x.pad_stride[V_XD]);
+  }
+  // The layers of one step.
+  static __device__ __forceinline__ bool gemv_waves(const Params& p, S& s, const int* hdr, const int* u, int pos,
+                                                    int ns, int cw, uint32_t epoch, __amdgpu_buffer_rsrc_t rw,
+                                                    __amdgpu_buffer_rsrc_t rx) {
+    GemvW w;
+    gemv_setup(p, u, w);
     load_layer_qkv(p, rw, u, 0, w);
     bool ok = true;
     for (int l = 0; l < p.L; ++l) ok = gemv_layer(p, s, l, hdr, u, w, pos, ns, cw, epoch, rw, rx, ok);
@@ -1493,9 +1510,11 @@ struct Kern {
   // smallest index).  Rows past the wave's last are clamped to it and their
   // results dropped (no branch around a load or a store).
   static constexpr int UBH = F_8 == FMT_BF16 ? 4 : 8;
-  // FP8 rows carry a scale register each: the split variant keeps two
-  // batches in flight (four pushed its scalars into scratch memory)
-  static constexpr int NBH = F_8 == FMT_BF16 || !LONG ? 4 : 2;
+  // FP8 rows carry a scale register each: two batches in flight (8 rows of
+  // 1 KB per wave each, still far more bytes in flight than the HBM latency
+  // needs).  With four, the step loop's registers (the GEMV's and the LM
+  // head's values live in one loop) no longer fit in 256 VGPRs.
+  static constexpr int NBH = F_8 == FMT_BF16 ? 4 : 2;
   static __device__ __forceinline__ bool lm_head(const Params& p, S& s, const int* hdr, int cw, float* d_logits,
                                                  __amdgpu_buffer_rsrc_t rw, bool ok, float& best, int& bidx) {
     const bool l0 = lane_id() == 0;
@@ -1545,42 +1564,83 @@ struct Kern {
   }
 
   // -------------------------------------------------------------- kernel
-  static __device__ __forceinline__ void run(const Params& p, S& s, const int32_t* d_token, int pos, int ns, uint32_t epoch,
-                             int32_t* d_next, float* d_logits) {
-    const int wave = wave_id(), lane = lane_id();
-    const int wg = blockIdx.x;
-    if (threadIdx.x == 0) s.seq = 0;
-    if (threadIdx.x < kCW) s.arr[threadIdx.x] = 0;
-    XR_INIT(s);
-    const int token = *d_token;
-    if (token < 0 || token >= p.V) {
-      if (wg == 0 && threadIdx.x == 0) {
-        raise_error(p, ERR_TOKEN);
-        *d_next = -1;
-      }
-      return;
+  // `nsteps` greedy steps at positions pos0, pos0 + 1, ...: step i runs with
+  // exchange epoch epoch0 + i, and its argmax, reduced by every workgroup,
+  // is step i + 1's token (d_next[i] gets it too; d_logits, if given, row i
+  // the logits).  Between steps the workgroup's waves meet at a barrier,
+  // and a failed step stops every wave there.  With nsteps > 1, ns must be
+  // 0: a KV row written in one step is read in the next only by the
+  // workgroup that wrote it (same CU), while a split-attention helper on
+  // another CU could read a stale copy of it (the kernel boundary is what
+  // makes earlier launches' rows visible to every CU).
+  // One step's state, from LDS.
+  struct Step {
+    int i, pos;
+    uint32_t epoch;
+  };
+  static __device__ __forceinline__ Step step_state(const S& s) {
+    Step t;
+    t.i = (int)__builtin_amdgcn_readfirstlane(lds_ld(&s.st_i));
+    t.pos = (int)__builtin_amdgcn_readfirstlane(lds_ld(&s.st_pos0)) + t.i;
+    t.epoch = __builtin_amdgcn_readfirstlane(lds_ld(&s.st_e0)) + (uint32_t)t.i;
+    return t;
+  }
+  template <typename T>
+  static __device__ __forceinline__ T* lds_ptr(const uint32_t (&w)[2]) {
+    // each half widened as unsigned (readfirstlane returns a signed int)
+    const uint64_t a = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(lds_ld(&w[1])) << 32 |
+                       (uint32_t)__builtin_amdgcn_readfirstlane(lds_ld(&w[0]));
+    return reinterpret_cast<T*>((uintptr_t)a);
+  }
+  // Entries [off, off + N) of the workgroup's table row, read anew by every
+  // step: nothing derived from them is computed once before the step loop
+  // and held (or spilled) across the whole step.
+  template <int N>
+  static __device__ __forceinline__ void tab_row(const S& s, int off, int (&a)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) a[i] = (int)__builtin_amdgcn_readfirstlane(lds_ld((const uint32_t*)&s.tab[off + i]));
+  }
+  static __device__ __forceinline__ bool last_step(const S& s, int i) {
+    return i + 1 >= (int)__builtin_amdgcn_readfirstlane(lds_ld(&s.st_n));
+  }
+  // The end of a step with another to follow: a failure in any wave stops
+  // every wave; else thread 0 moves the step state on and the counters and
+  // records are cleared once every wave is past the step.  Returns true to
+  // go on.
+  static __device__ __forceinline__ bool step_end(S& s, bool ok) {
+    if (!ok && lane_id() == 0) lds_st(&s.fail, 1u);
+    lds_barrier();
+    if (__builtin_amdgcn_readfirstlane(lds_ld(&s.fail)) != 0) return false;
+    if (threadIdx.x == 0) {
+      s.seq = 0;
+      lds_st(&s.st_i, lds_ld(&s.st_i) + 1u);
+#pragma unroll
+      for (int w = 0; w < kCW; ++w) s.arr[w] = 0;   // constant offsets: no address held across the step
     }
-    if (wg == 0 && threadIdx.x == 0) *d_next = -1;  // overwritten on success
-    // this workgroup's row of the work table, as wave-uniform values
-    MK_GLOBAL const int* tab = GCAST(const int, p.w + p.sched) + (size_t)wg * kSchedInts * kWaves;
-    int hdr[kHdrInts];
-#pragma unroll
-    for (int i = 0; i < kHdrInts; ++i) hdr[i] = __builtin_amdgcn_readfirstlane(tab[i]);
-    lds_barrier();   // seq and the X-ray records are initialised
-    const __amdgpu_buffer_rsrc_t rx = xch_rsrc(p);
-    if (wave == 0) {
-      if (!courier(p, s, hdr, token, pos, ns, epoch, d_next)) return;
-    } else {
-      const int cw = wave - 1;
-      int u[kUnitInts];
-#pragma unroll
-      for (int i = 0; i < kUnitInts; ++i) u[i] = __builtin_amdgcn_readfirstlane(tab[kSchedInts * wave + i]);
+    XR_INIT(s);
+    lds_barrier();
+    return true;
+  }
+
+  // The compute waves' steps: `layers(t, hdr, rx, rw)` runs a step's layers
+  // (attention or GEMV units, by the workgroup's role), then the LM head
+  // and the workgroup's argmax candidate.  Each role has its own loop, so
+  // the values either role derives once (lane masks, offsets) are held only
+  // where that role runs.
+  template <typename F>
+  static __device__ __forceinline__ void compute_steps(const Params& p, S& s, int cw, F&& layers) {
+    const int lane = lane_id(), wg = blockIdx.x;
+    for (;;) {
+      const Step t = step_state(s);
+      int hdr[kHdrInts];
+      tab_row(s, 0, hdr);
+      const __amdgpu_buffer_rsrc_t rx = xch_rsrc(p);
       const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w, p.w_bytes);
-      bool ok = hdr[S_ATT] >= 0 ? att_waves(p, s, hdr[S_ATT], pos, ns, cw, epoch, rx)
-                                : gemv_waves(p, s, hdr, u, pos, ns, cw, epoch, rw, rx);
+      bool ok = layers(t, hdr, rx, rw);
       float best;
       int bidx;
-      ok = lm_head(p, s, hdr, cw, d_logits, rw, ok, best, bidx);
+      float* lg = lds_ptr<float>(s.st_logits);
+      ok = lm_head(p, s, hdr, cw, lg ? lg + (size_t)t.i * p.V : nullptr, rw, ok, best, bidx);
       if (lane == 0) {
         s.best[cw] = best;
         s.bidx[cw] = bidx;
@@ -1596,12 +1656,86 @@ struct Kern {
             b = s.best[w];
             bi = s.bidx[w];
           }
-        const uint32_t tag = make_tag(epoch, vec_id(p.L, 0));
+        const uint32_t tag = make_tag(t.epoch, vec_id(p.L, 0));
         const uint32_t off = 8u * (uint32_t)(p.x.arg + 2ull * wg);
         st_xword(rx, ok && lane == 0 ? off : kOOB, __float_as_uint(b), tag);
         st_xword(rx, ok && lane == 0 ? off + 8u : kOOB, (uint32_t)bi, tag);
       }
       arrive(s, cw, 5u * (uint32_t)p.L + 1u, cw == 0);
+      if (last_step(s, t.i) || !step_end(s, ok)) break;
+    }
+  }
+
+  static __device__ __forceinline__ void run(const Params& p, S& s, const int32_t* d_token, int pos0, int nsteps,
+                                             int ns, uint32_t epoch0, int32_t* d_next, float* d_logits) {
+    const int wave = wave_id(), lane = lane_id();
+    const int wg = blockIdx.x;
+    const int token = __builtin_amdgcn_readfirstlane(*d_token);
+    if (token < 0 || token >= p.V) {
+      if (wg == 0 && threadIdx.x == 0) {
+        raise_error(p, ERR_TOKEN);
+        for (int i = 0; i < nsteps; ++i) d_next[i] = -1;
+      }
+      return;
+    }
+    if (wg == 0 && threadIdx.x == 0)
+      for (int i = 0; i < nsteps; ++i) d_next[i] = -1;   // overwritten on success
+    if (threadIdx.x == 0) {
+      s.seq = 0;
+      s.fail = 0;
+      s.st_i = 0;
+      s.st_n = (uint32_t)nsteps;
+      s.st_pos0 = (uint32_t)pos0;
+      s.st_e0 = epoch0;
+      s.st_token = (uint32_t)token;
+      s.st_next[0] = (uint32_t)(uintptr_t)d_next;
+      s.st_next[1] = (uint32_t)((uint64_t)(uintptr_t)d_next >> 32);
+      s.st_logits[0] = (uint32_t)(uintptr_t)d_logits;
+      s.st_logits[1] = (uint32_t)((uint64_t)(uintptr_t)d_logits >> 32);
+    }
+    if (threadIdx.x < kCW) s.arr[threadIdx.x] = 0;
+    XR_INIT(s);
+    // this workgroup's row of the work table
+    MK_GLOBAL const int* tab = GCAST(const int, p.w + p.sched) + (size_t)wg * kSchedInts * kWaves;
+    for (int i = threadIdx.x; i < kWaves * kSchedInts; i += kThreads) s.tab[i] = tab[i];
+    lds_barrier();   // seq, the step state, the table row and the X-ray records are initialised
+    if (wave == 0) {
+      for (;;) {
+        const Step t = step_state(s);
+        int hdr[kHdrInts];
+        tab_row(s, 0, hdr);
+        const bool more = !last_step(s, t.i);
+        int next = -1;
+        bool ok = courier(p, s, hdr, (int)__builtin_amdgcn_readfirstlane(lds_ld(&s.st_token)), t.pos, ns, t.epoch,
+                          lds_ptr<int32_t>(s.st_next) + t.i, more, next);
+        // the next step's token is this step's argmax: checked as a launch
+        // checks the token it reads (an index past the vocabulary would
+        // address past the embedding table)
+        if (ok && more && (next < 0 || next >= p.V)) {
+          if (lane == 0) raise_error(p, ERR_TOKEN);
+          ok = false;
+        }
+        // A courier that gave up inside the step has handed the abort value
+        // to the compute waves (their waits return at once, and they stop at
+        // the step's end) and may have skipped barriers of the step: it ends
+        // here.  A failed final argmax skipped none: it meets the compute
+        // waves at the step's end like a good step.
+        if (!ok && __builtin_amdgcn_readfirstlane(lds_ld(&s.seq)) == kAbort) return;
+        if (lane == 0) lds_st(&s.st_token, (uint32_t)next);
+        if (!more || !step_end(s, ok)) break;
+      }
+    } else if (s.tab[S_ATT] >= 0) {
+      const int g = s.tab[S_ATT];
+      compute_steps(p, s, wave - 1, [&](const Step& t, const int*, __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t) {
+        return att_waves(p, s, g, t.pos, ns, wave - 1, t.epoch, rx);
+      });
+    } else {
+      compute_steps(p, s, wave - 1,
+                    [&](const Step& t, const int* hdr, __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rw) {
+                      int u[kUnitInts];
+                      tab_row(s, kSchedInts * wave, u);
+                      return gemv_waves(p, s, hdr, u, t.pos, ns, wave - 1, t.epoch, rw, rx);
+                    });
     }
 #ifdef MK_XRAY
     __syncthreads();
@@ -1617,10 +1751,10 @@ struct Kern {
 // helpers per KV head in this step (0 without split attention).
 template <int WF, int HD, int GS, int NH, int NQ, int NI, bool LONG, bool BAR>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(const Params* __restrict__ pp, const int32_t* d_token,
-                                                             int pos, int ns, uint32_t epoch, int32_t* d_next,
-                                                             float* d_logits) {
+                                                             int pos, int nsteps, int ns, uint32_t epoch,
+                                                             int32_t* d_next, float* d_logits) {
   __shared__ Smem<HD, GS, NH, NQ, NI> s;
-  Kern<WF, HD, GS, NH, NQ, NI, LONG, BAR>::run(*pp, s, d_token, pos, ns, epoch, d_next, d_logits);
+  Kern<WF, HD, GS, NH, NQ, NI, LONG, BAR>::run(*pp, s, d_token, pos, nsteps, ns, epoch, d_next, d_logits);
 }
 
 // ------------------------------------------------------- launch wrappers
@@ -1671,12 +1805,13 @@ hipError_t decode_coresident(int wfmt, int hd, int gs, int hidden, int qdim, int
 }
 
 hipError_t launch_decode(const Params* d_params, int wfmt, int hd, int gs, int hidden, int qdim, int inter, int grid,
-                         bool cooperative, bool barrier, const int32_t* d_token, int pos, int ns, uint32_t epoch,
-                         int32_t* d_next, float* d_logits, hipStream_t s) {
+                         bool cooperative, bool barrier, const int32_t* d_token, int pos, int nsteps, int ns,
+                         uint32_t epoch, int32_t* d_next, float* d_logits, hipStream_t s) {
   if (barrier && ns > 0) return hipErrorInvalidValue;
   const void* fn = decode_fn(wfmt, hd, gs, hidden, qdim, inter, barrier ? 2 : (ns > 0 ? 1 : 0));
   if (!fn) return hipErrorInvalidValue;
-  void* args[] = {&d_params, &d_token, &pos, &ns, &epoch, &d_next, &d_logits};
+  if (nsteps < 1) return hipErrorInvalidValue;
+  void* args[] = {&d_params, &d_token, &pos, &nsteps, &ns, &epoch, &d_next, &d_logits};
   if (cooperative) return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
   return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, 0, s);
 }

@@ -13,8 +13,8 @@ namespace mk {
 // `ns` > 0 launches the split-attention variant with ns helpers per KV head;
 // `barrier` the grid-barrier variant (needs ns == 0).
 hipError_t launch_decode(const Params* d_params, int wfmt, int hd, int gs, int hidden, int qdim, int inter, int grid,
-                         bool cooperative, bool barrier, const int32_t* d_token, int pos, int ns, uint32_t epoch,
-                         int32_t* d_next, float* d_logits, hipStream_t s);
+                         bool cooperative, bool barrier, const int32_t* d_token, int pos, int nsteps, int ns,
+                         uint32_t epoch, int32_t* d_next, float* d_logits, hipStream_t s);
 // Workgroups of the decode kernel (any variant) that one compute unit holds at once.
 hipError_t decode_coresident(int wfmt, int hd, int gs, int hidden, int qdim, int inter, int* per_cu);
 bool decode_shape_supported(int hd, int gs, int hidden, int qdim, int inter);

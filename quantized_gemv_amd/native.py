@@ -81,6 +81,7 @@ def load(xray=False) -> ctypes.CDLL:
         "mk_decode_step": (ctypes.c_int32, [_VP, ctypes.c_int32, ctypes.c_int32, _VP]),
         "mk_decode_step_async": (ctypes.c_int, [_VP, _VP, ctypes.c_int32, _VP, _VP, _VP]),
         "mk_decode_step_async_noalloc": (ctypes.c_int, [_VP, _VP, ctypes.c_int32, _VP, _VP, _VP]),
+        "mk_decode_steps_async": (ctypes.c_int, [_VP, _VP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP]),
         "mk_check_device_error": (ctypes.c_int, [_VP, _VP]),
         "mk_get_trace": (ctypes.c_int, [_VP, _VP, ctypes.c_size_t, P(ctypes.c_size_t)]),
         "mk_decode_codes": (ctypes.c_int, [ctypes.c_int32, _VP, ctypes.c_int32, _VP, _VP]),
@@ -228,6 +229,14 @@ class Decoder:
         self._check(self.lib.mk_decode_step_async(self.h, d_token.data_ptr(), int(pos), d_next.data_ptr(),
                                                   d_logits.data_ptr() if d_logits is not None else None,
                                                   _stream()))
+
+    def decode_steps_async(self, d_token, pos: int, n: int, d_next, d_logits=None) -> None:
+        """mk_decode_steps_async: n greedy steps from position pos; d_next
+        (int32[n]) receives each step's token, d_logits (fp32 [n][vocab]) if
+        given each step's logits."""
+        self._check(self.lib.mk_decode_steps_async(self.h, d_token.data_ptr(), int(pos), int(n), d_next.data_ptr(),
+                                                   d_logits.data_ptr() if d_logits is not None else None,
+                                                   _stream()))
 
     def decode_step_async_noalloc(self, d_token, pos: int, d_next, d_logits=None) -> None:
         """mk_decode_step_async_noalloc: the step with the library's static

@@ -47,6 +47,9 @@ def parse():
                     help="also time mk_prefill of the workload's prompt both ways (one decode launch per "
                          "position, and the batched matrix-core prefill) and add a 'prefill' object")
     ap.add_argument("--grid", type=int, default=0, help="workgroups per launch (0: one per compute unit)")
+    ap.add_argument("--one-step-per-launch", action="store_true",
+                    help="time K single-step launches (mk_decode_step_async) instead of one call of K steps "
+                         "(mk_decode_steps_async)")
     ap.add_argument("--sync", type=int, default=0,
                     help="0 tagged exchange words (the default); 1 one grid barrier per phase hand-off with "
                          "relaxed counters; 2 the same barrier with agent-scope release/acquire fences")
@@ -114,11 +117,11 @@ def kernel_source_hash() -> str:
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per decode launch from profiles/decode_kernel_traffic.json
-    (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by the same counter's
-    reading for a plain copy of known size), with the algorithmic bytes of
-    the launches they were taken over, or (None, None) when absent or taken
-    on another version of the kernel."""
+    """HBM bytes per decode step from profiles/decode_kernel_traffic.json
+    (FETCH_SIZE and WRITE_SIZE of the timed dispatches, each scaled by the
+    same counter's reading for a plain copy of known size), with the
+    algorithmic bytes per step of the steps they were taken over, or
+    (None, None) when absent or taken on another version of the kernel."""
     path = os.path.join(ROOT, "profiles", "decode_kernel_traffic.json")
     try:
         with open(path) as f:
@@ -128,7 +131,7 @@ def measured_traffic(workload: str):
     e = d.get("workloads", {}).get(workload)
     if not e or d.get("kernel_source_sha256") != kernel_source_hash():
         return None, None
-    return int(e["fetch_bytes_per_launch"] + e["write_bytes_per_launch"]), e.get("algorithmic_bytes_per_launch")
+    return int(e["fetch_bytes_per_step"] + e["write_bytes_per_step"]), e.get("algorithmic_bytes_per_step")
 
 
 def cpu_baseline(master, wl, n_steps, prompt, budget_s):
@@ -260,7 +263,11 @@ def main():
         print(json.dumps({"workload": wl.name, **xray_report(dec, wl, K, prompt, args.xray_dump)}), flush=True)
         dec.close()
         return
-    res = time_decode(dec, wl, prompt, K, W, args.repeats)
+    # the same steps as K single-step launches, for comparison (not the
+    # value); first, so that the timed launches are the run's last decode
+    # dispatches (what the counter summaries take)
+    res1 = None if args.one_step_per_launch else time_decode(dec, wl, prompt, K, W, 3, True)
+    res = time_decode(dec, wl, prompt, K, W, args.repeats, args.one_step_per_launch)
     dec.close()
     del dec
     out = {
@@ -282,6 +289,9 @@ def main():
                    "grid": "one workgroup per CU: 1 courier + 7 compute waves; attention on one "
                            "workgroup per KV head, split over the workgroups of its XCD from 576 "
                            "cached positions on" if not args.grid else f"{args.grid} workgroups",
+                   "launch": "K single-step launches" if args.one_step_per_launch else
+                             "one mk_decode_steps_async call of K steps (one launch; positions with "
+                             "split-attention helpers launch one by one)",
                    "timed_runs": len(res["times"]),
                    "run_seconds": [round(t, 6) for t in res["times"]]},
         "weight_bytes_per_token": res["weight_bytes"],
@@ -289,6 +299,9 @@ def main():
         "roofline": res["roofline"],
         "greedy_tokens_head": [int(t) for t in res["tokens"][:8]],
     }
+    if res1 is not None:
+        out["one_step_per_launch"] = {"value": res1["value"], "ms_per_step": res1["ms_per_step"],
+                                      "tokens_match": bool(np.array_equal(res1["tokens"], res["tokens"]))}
     if wl.name == "qwen3_0p6b_bf16" and not args.no_fp8 and args.prompt_len <= 0:
         # the FP8 workload (same master, same prompt and positions), timed the same way
         wl8 = synth.WORKLOADS["qwen3_0p6b_fp8"]
@@ -297,13 +310,17 @@ def main():
         d8.pack(dev_master)
         del dev_master
         torch.cuda.empty_cache()
-        r8 = time_decode(d8, wl8, prompt, K, W, args.repeats)
+        r81 = None if args.one_step_per_launch else time_decode(d8, wl8, prompt, K, W, 3, True)
+        r8 = time_decode(d8, wl8, prompt, K, W, args.repeats, args.one_step_per_launch)
         d8.close()
         del d8
         out["fp8"] = {"workload": wl8.name, "value": r8["value"], "unit": "tokens/s", "ms_per_step": r8["ms_per_step"],
                       "dtype": "fp8_e4m3", "weight_bytes_per_token": r8["weight_bytes"],
                       "weight_roofline_pct": r8["weight_roofline_pct"], "roofline": r8["roofline"],
                       "run_seconds": [round(t, 6) for t in r8["times"]]}
+        if r81 is not None:
+            out["fp8"]["one_step_per_launch"] = {"value": r81["value"], "ms_per_step": r81["ms_per_step"],
+                                                 "tokens_match": bool(np.array_equal(r81["tokens"], r8["tokens"]))}
     if args.prefill_bench:
         dp = native.Decoder(sh, wl.wfmt, max_ctx, grid=args.grid)
         dp.pack(native.master_to_device(master))
@@ -317,10 +334,12 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def time_decode(dec, wl, prompt, K, W, repeats):
+def time_decode(dec, wl, prompt, K, W, repeats, one_per_launch=False):
     """W untimed warm-up steps, then `repeats` timed runs of K steps, each
     after an untimed prefill: HIP events on the stream the kernel runs on
-    around the K chained launches.  Returns the median figures."""
+    around one mk_decode_steps_async call of K steps (one launch; with
+    one_per_launch, K chained single-step launches).  Returns the median
+    figures."""
     import numpy as np
     import torch
     stream = torch.cuda.current_stream()
@@ -333,8 +352,11 @@ def time_decode(dec, wl, prompt, K, W, repeats):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for i in range(n):
-            dec.decode_step_async(toks[i:i + 1], wl.prompt_len + i, toks[i + 1:i + 2])
+        if one_per_launch:
+            for i in range(n):
+                dec.decode_step_async(toks[i:i + 1], wl.prompt_len + i, toks[i + 1:i + 2])
+        else:
+            dec.decode_steps_async(toks[0:1], wl.prompt_len, n, toks[1:n + 1])
         e1.record(stream)
         torch.cuda.synchronize()
         dec.check_device_error()
@@ -350,20 +372,24 @@ def time_decode(dec, wl, prompt, K, W, repeats):
     # algorithmic bytes per launch: every weight byte once, plus the KV cache
     # read over positions 0..pos (mean over the timed positions)
     mean_ctx = wl.prompt_len + (K - 1) / 2.0 + 1
-    algo = wbytes + float(sizes.kv_bytes_per_position) * mean_ctx
+    algo = wbytes + float(sizes.kv_bytes_per_position) * mean_ctx   # per step
     achieved = algo / (dt / K) / 1e9
-    # the counters were taken over the 256 timed launches of the default run
-    # (positions P..P+255); their ratio to those launches' algorithmic bytes
-    # is what a reader compares, whatever window this run timed
+    spl = 1 if one_per_launch else K   # steps per launch
+    # the counters were taken over the 256 timed steps of the default run
+    # (positions P..P+255, one launch); their ratio to those steps'
+    # algorithmic bytes is what a reader compares, whatever window this run
+    # timed
     traffic, traffic_algo = measured_traffic(wl.name)
     return {"value": round(tps, 2), "ms_per_step": round(dt / K * 1e3, 5), "times": times, "tokens": tokens,
             "weight_bytes": wbytes, "weight_roofline_pct": round(100.0 * wbytes * tps / (PEAK_HBM_GBPS * 1e9), 2),
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                         "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                         "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                         "traffic": int(traffic * spl) if traffic else None,
                          "traffic_over_algorithmic": round(traffic / traffic_algo, 4) if traffic and traffic_algo else None,
-                         "traffic_window": f"the 256 launches at positions {wl.prompt_len}..{wl.prompt_len + 255}"
+                         "traffic_window": f"the 256 steps at positions {wl.prompt_len}..{wl.prompt_len + 255}"
                                            if traffic else None,
-                         "kernel": "mk::decode_kernel", "bytes_per_launch": int(algo)}}
+                         "kernel": "mk::decode_kernel", "steps_per_launch": spl,
+                         "bytes_per_launch": int(algo * spl), "launch_us": round(dt / K * spl * 1e6, 2)}}
 
 
 if __name__ == "__main__":

@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--one-step-per-launch", action="store_true",
                     help="time K single-step launches (mk_decode_step_async) instead of one call of K steps "
                          "(mk_decode_steps_async)")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip the comparison runs of K single-step launches")
     ap.add_argument("--sync", type=int, default=0,
                     help="0 tagged exchange words (the default); 1 one grid barrier per phase hand-off with "
                          "relaxed counters; 2 the same barrier with agent-scope release/acquire fences")
@@ -266,7 +268,8 @@ def main():
     # the same steps as K single-step launches, for comparison (not the
     # value); first, so that the timed launches are the run's last decode
     # dispatches (what the counter summaries take)
-    res1 = None if args.one_step_per_launch else time_decode(dec, wl, prompt, K, W, 3, True)
+    compare = not (args.one_step_per_launch or args.no_compare)
+    res1 = time_decode(dec, wl, prompt, K, W, 3, True) if compare else None
     res = time_decode(dec, wl, prompt, K, W, args.repeats, args.one_step_per_launch)
     dec.close()
     del dec
@@ -310,7 +313,7 @@ def main():
         d8.pack(dev_master)
         del dev_master
         torch.cuda.empty_cache()
-        r81 = None if args.one_step_per_launch else time_decode(d8, wl8, prompt, K, W, 3, True)
+        r81 = time_decode(d8, wl8, prompt, K, W, 3, True) if compare else None
         r8 = time_decode(d8, wl8, prompt, K, W, args.repeats, args.one_step_per_launch)
         d8.close()
         del d8

@@ -1006,13 +1006,17 @@ struct Kern {
     for (int k = 0; k < kMaxD; ++k)
       w.sd[k] = xpad_word((uint32_t)max(u[S_D + k], 0), p.H, p.x.pad_c[V_XD], p.x.pad_stride[V_XD]);
   }
+  // bf16: layer 0's QKV rows are loaded before the step, during the
+  // previous step's argmax when one ran.  In FP8 and FP4 the same early
+  // load changed the layer loop's register allocation and cost more than it
+  // saved (measured), so there each step loads them itself.
+  static constexpr bool kQKV0Early = F_LIN == FMT_BF16;
   // The layers of one step.
   static __device__ __forceinline__ bool gemv_waves(const Params& p, S& s, const int* hdr, const int* u, int pos,
                                                     int ns, int cw, uint32_t epoch, __amdgpu_buffer_rsrc_t rw,
-                                                    __amdgpu_buffer_rsrc_t rx) {
-    GemvW w;
+                                                    __amdgpu_buffer_rsrc_t rx, GemvW& w) {
     gemv_setup(p, u, w);
-    load_layer_qkv(p, rw, u, 0, w);
+    if constexpr (!kQKV0Early) load_layer_qkv(p, rw, u, 0, w);
     bool ok = true;
     for (int l = 0; l < p.L; ++l) ok = gemv_layer(p, s, l, hdr, u, w, pos, ns, cw, epoch, rw, rx, ok);
     return ok;
@@ -1624,11 +1628,12 @@ struct Kern {
 
   // The compute waves' steps: `layers(t, hdr, rx, rw)` runs a step's layers
   // (attention or GEMV units, by the workgroup's role), then the LM head
-  // and the workgroup's argmax candidate.  Each role has its own loop, so
-  // the values either role derives once (lane masks, offsets) are held only
-  // where that role runs.
-  template <typename F>
-  static __device__ __forceinline__ void compute_steps(const Params& p, S& s, int cw, F&& layers) {
+  // and the workgroup's argmax candidate; `next(rw)` runs when another step
+  // follows, before the waves wait for its token.  Each role has its own
+  // loop, so the values either role derives once (lane masks, offsets) are
+  // held only where that role runs.
+  template <typename F, typename G>
+  static __device__ __forceinline__ void compute_steps(const Params& p, S& s, int cw, F&& layers, G&& next) {
     const int lane = lane_id(), wg = blockIdx.x;
     for (;;) {
       const Step t = step_state(s);
@@ -1662,7 +1667,9 @@ struct Kern {
         st_xword(rx, ok && lane == 0 ? off + 8u : kOOB, (uint32_t)bi, tag);
       }
       arrive(s, cw, 5u * (uint32_t)p.L + 1u, cw == 0);
-      if (last_step(s, t.i) || !step_end(s, ok)) break;
+      if (last_step(s, t.i)) break;
+      next(rw);
+      if (!step_end(s, ok)) break;
     }
   }
 
@@ -1726,16 +1733,33 @@ struct Kern {
       }
     } else if (s.tab[S_ATT] >= 0) {
       const int g = s.tab[S_ATT];
-      compute_steps(p, s, wave - 1, [&](const Step& t, const int*, __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t) {
-        return att_waves(p, s, g, t.pos, ns, wave - 1, t.epoch, rx);
-      });
+      compute_steps(
+          p, s, wave - 1,
+          [&](const Step& t, const int*, __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t) {
+            return att_waves(p, s, g, t.pos, ns, wave - 1, t.epoch, rx);
+          },
+          [](__amdgpu_buffer_rsrc_t) {});
     } else {
-      compute_steps(p, s, wave - 1,
-                    [&](const Step& t, const int* hdr, __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rw) {
-                      int u[kUnitInts];
-                      tab_row(s, kSchedInts * wave, u);
-                      return gemv_waves(p, s, hdr, u, t.pos, ns, wave - 1, t.epoch, rw, rx);
-                    });
+      // bf16: layer 0's QKV rows, the first step's now, every later step's
+      // while the step before it reduces its argmax (the rows are the same
+      // in every step)
+      GemvW w;
+      auto qkv0 = [&](__amdgpu_buffer_rsrc_t rw) {
+        if constexpr (kQKV0Early) {
+          int u[kUnitInts];
+          tab_row(s, kSchedInts * wave, u);
+          load_layer_qkv(p, rw, u, 0, w);
+        }
+      };
+      qkv0(make_rsrc(p.w, p.w_bytes));
+      compute_steps(
+          p, s, wave - 1,
+          [&](const Step& t, const int* hdr, __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rw) {
+            int u[kUnitInts];
+            tab_row(s, kSchedInts * wave, u);
+            return gemv_waves(p, s, hdr, u, t.pos, ns, wave - 1, t.epoch, rw, rx, w);
+          },
+          qkv0);
     }
 #ifdef MK_XRAY
     __syncthreads();

@@ -269,7 +269,7 @@ void layout_scratch(mk_model* m, int grid, bool for_sizing = true) {
   X.layer_words = lw;
   uint64_t w = lw * (uint64_t)c.n_layers;
   X.arg = al(w);
-  w = X.arg + 2ull * grid;
+  w = X.arg + 4ull * grid;   // per workgroup: argmax value and index, LM-head ticks, rows and XCD
   X.bar = al(w);
   w = X.bar + 5ull * c.n_layers + 1;
   X.err = al(w);

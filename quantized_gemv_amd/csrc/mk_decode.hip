@@ -90,6 +90,22 @@ __device__ __forceinline__ float lane_f(float v, int lane) {
 }
 // Sum over the wave, the same bits in every lane (fixed order).
 __device__ __forceinline__ float wave_sum(float v) { return rows_sum(sum16(v)); }
+// Integer sum over the wave, in every lane: the steps of sum16 and
+// rows_sum (exact in any order).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  v += dpp_u32<0xB1>(v);
+  v += dpp_u32<0x4E>(v);
+  v += dpp_u32<0x141>(v);
+  v += dpp_u32<0x140>(v);
+  const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = a[0] + a[1];
+  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return b[0] + b[1];
+}
 __device__ __forceinline__ float wave_max(float v) {
   v = max16(v);
   return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
@@ -121,6 +137,10 @@ __device__ __forceinline__ float silu(float z) {
 }
 
 // ------------------------------------------------------------------ LDS
+// LM-head balancing across XCDs (several steps per launch): grids of up to
+// this many workgroups.
+constexpr int kLmGrid = 256;
+
 template <int HD, int GS, int NH, int NQ, int NI>
 struct Smem {
   // every array starts on a 16-byte boundary: the compute waves read them
@@ -158,6 +178,8 @@ struct Smem {
   uint32_t st_i, st_n, st_pos0, st_e0, st_token;
   uint32_t st_next[2], st_logits[2];
   int tab[kWaves * kSchedInts];          // this workgroup's row of the work table
+  uint32_t lm_va, lm_vb;                 // this workgroup's LM-head rows [lm_va, lm_vb) in the step
+  uint32_t lm_rec[kLmGrid][2];           // the step before's records: LM-head end tick, dt << 16 | rows << 4 | XCD
   uint32_t arr[kCW];                     // grid-barrier variant: barriers each compute wave has finished its part of
   XR_FIELD
 };
@@ -365,6 +387,7 @@ struct Kern {
   static constexpr int KH = NI * 4;            // SwiGLU output (bf16 pairs)
   static constexpr int KA = ((GS + 2) * HD / 2 + 63) / 64;   // q/k/v of one KV head
   static constexpr int KG = 16;                // argmax words of up to 1024 workgroups
+  static constexpr int KL = kLmGrid / 64;      // LM-head balancing: records per lane
   static constexpr int NOUT = GS * HD;         // outputs of one attention workgroup
   static constexpr int PP = (NOUT + 2 * GS) / 2;   // word pairs of one helper partial
   static constexpr int KP = kSplitGatherK;     // helper-partial pairs per lane and round of the home's gather
@@ -461,8 +484,11 @@ struct Kern {
   // final residual for the LM head; workgroup 0 then reduces the argmax.
   // all_argmax: every workgroup reduces the argmax (its result is the next
   // step's token), not only workgroup 0, which writes *d_next.
+  // rebalance: a step before this one ran in the launch; the LM-head rows
+  // of this step follow from its records (lm_partition).
   static __device__ __forceinline__ bool courier(const Params& p, S& s, const int* hdr, int token, int pos, int ns,
-                                 uint32_t epoch, int32_t* d_next, bool all_argmax, int& next_token) {
+                                 uint32_t epoch, int32_t* d_next, bool all_argmax, bool rebalance,
+                                 int& next_token) {
     MK_GLOBAL const uint8_t* const W = p.w;
     const int lane = lane_id();
     const int H = p.H, L = p.L;
@@ -476,6 +502,11 @@ struct Kern {
     // layer, loaded at the top of the layer (the loads land while the
     // courier waits for this workgroup's stores)
     float gq[2 * KX], gg[2 * KX];
+    // where the lane's pairs of the per-producer vectors sit (the same in
+    // every layer); its loads go out first, ahead of the embedding's
+    uint32_t qm[KA];
+    qkv_map(p, att >= 0 ? att : (LONG && hdr[S_SPLIT] >= 0 ? hdr[S_SPLIT] : 0),
+            att >= 0 ? (GS + 2) * HD / 2 : NOUT / 2, qm);
     if (flags & 1) courier_gains<KX>(W, p.layer0.in_norm, H, gq);
     // ---- embedding -> the residual of layer 0
     if (flags & 1) {
@@ -499,10 +530,6 @@ struct Kern {
       hand_over(&s.seq, ++seq);
       XR_PUT(s, 1, XR_HANDOFF);
     }
-    // where the lane's pairs of the per-producer vectors sit (the same in every layer)
-    uint32_t qm[KA];
-    qkv_map(p, att >= 0 ? att : (LONG && hdr[S_SPLIT] >= 0 ? hdr[S_SPLIT] : 0),
-            att >= 0 ? (GS + 2) * HD / 2 : NOUT / 2, qm);
     uint32_t mx[KX], mo[KX], mh[KH];
 #pragma unroll
     for (int k = 0; k < KX; ++k) {
@@ -515,6 +542,12 @@ struct Kern {
       const uint32_t j = (uint32_t)min(lane + 64 * k, p.I / 4 - 1);
       mh[k] = xpad_word(2 * j, p.I / 2, p.x.pad_c[V_H], p.x.pad_stride[V_H]);
     }
+    // this step's LM-head rows: a GEMV workgroup's courier now (the compute
+    // waves' layer-0 QKV rows cover it), an attention workgroup's after its
+    // layer-0 attention, where it waits for the next layer's q, k, v
+    XR_PUT(s, 1, XR_M0);
+    if (rebalance && att < 0) lm_partition(p, s);
+    XR_PUT(s, 1, XR_M0 + 1);
     for (int l = 0; l < L; ++l) {
       const uint64_t loff = (uint64_t)l * p.layer_stride;
       const int ph = 2 + 6 * l;
@@ -546,6 +579,7 @@ struct Kern {
         lds_barrier();   // every compute wave has written its partial outputs
         if (LONG && ns > 0) lds_barrier();   // the helpers' partials are in LDS
         lds_barrier();   // and merged them: the LDS arrays may be reused
+        if (l == 0 && rebalance) lm_partition(p, s);
       }
       // ---- split attention helper: q of KV head hdr[S_SPLIT]
       if (LONG && hdr[S_SPLIT] >= 0) {
@@ -625,25 +659,46 @@ struct Kern {
     // reduce every workgroup's (value, index)
     if (blockIdx.x == 0 || all_argmax) {
       XR_PUT(s, ph_head + 1, XR_START);
-      uint32_t vl[KG], il[KG];
       const uint32_t base = (uint32_t)p.x.arg;
-      if (!gather_pairs<KG>(p, rs, p.grid, make_tag(epoch, vec_id(L, 0)), vl, il,
-                            [=](int j) { return base + 2u * j; }))
-        return false;
-      XR_PUT(s, ph_head + 1, XR_READY);
+      const uint32_t tag = make_tag(epoch, vec_id(L, 0));
       float best = -INFINITY;
       int bidx = 0x7FFFFFFF;
+      auto take = [&](uint32_t vw, uint32_t iw) {
+        const float v = __uint_as_float(vw);
+        const int i = (int)iw;
+        if (v > best || (v == best && i < bidx)) {
+          best = v;
+          bidx = i;
+        }
+      };
+      if (all_argmax && p.grid <= kLmGrid) {
+        // whole records, one round: pair 2j is workgroup j's (value, index),
+        // pair 2j + 1 its (end tick, dt << 16 | rows << 4 | XCD), kept for the
+        // next step's LM-head rows (even lanes hold the former, odd lanes the
+        // latter)
+        uint32_t al[2 * KL], ah[2 * KL];
+        if (!gather_pairs<2 * KL>(p, rs, 2 * p.grid, tag, al, ah, [=](int j) { return base + 2u * j; }))
+          return false;
+        XR_PUT(s, ph_head + 1, XR_READY);
 #pragma unroll
-      for (int k = 0; k < KG; ++k) {
-        const int j = lane + 64 * k;
-        if (j < p.grid) {
-          const float v = __uint_as_float(vl[k]);
-          const int i = (int)il[k];
-          if (v > best || (v == best && i < bidx)) {
-            best = v;
-            bidx = i;
+        for (int k = 0; k < 2 * KL; ++k) {
+          const int j = lane + 64 * k;
+          if (j < 2 * p.grid) {
+            if ((lane & 1) == 0) {
+              take(al[k], ah[k]);
+            } else {
+              s.lm_rec[j >> 1][0] = al[k];
+              s.lm_rec[j >> 1][1] = ah[k];
+            }
           }
         }
+      } else {
+        uint32_t vl[KG], il[KG];
+        if (!gather_pairs<KG>(p, rs, p.grid, tag, vl, il, [=](int j) { return base + 4u * j; })) return false;
+        XR_PUT(s, ph_head + 1, XR_READY);
+#pragma unroll
+        for (int k = 0; k < KG; ++k)
+          if (lane + 64 * k < p.grid) take(vl[k], il[k]);
       }
       const float m = wave_max(best);
       int mi = best == m ? bidx : 0x7FFFFFFF;   // smallest index among the lanes holding the maximum
@@ -654,6 +709,58 @@ struct Kern {
       XR_PUT(s, ph_head + 1, XR_HANDOFF);
     }
     return true;
+  }
+
+  // This step's LM-head rows, from every workgroup's record of the step
+  // before (gathered with the argmax into lm_rec): a damped step towards
+  // equal end times.  Each workgroup's share moves by half of its end's
+  // offset from the grid's mean end, converted to rows with its own rows per
+  // tick (the workgroups of a slower XCD all end later and all give rows
+  // away); the rows then go to workgroups in index order in proportion to
+  // their shares.  Every workgroup runs the same instructions on the same
+  // words, so all of them derive the same partition of [0, V): workgroup w's
+  // end and workgroup w+1's start are the same function of the same prefix
+  // sum.  Which workgroup computes a row changes neither its logit nor the
+  // argmax.  Equal shares when the LM head is too short to time (under a
+  // microsecond on average) or a share would not fit the record's 12 bits of
+  // rows; grids of up to kLmGrid workgroups.
+  static __device__ void lm_partition(const Params& p, S& s) {
+    const int lane = lane_id(), G = p.grid, wg = blockIdx.x;
+    if (G > kLmGrid || 2 * p.V / G > 0xFFF) return;
+    uint32_t te[KL], mt[KL];   // end ticks, dt << 16 | rows << 4 | XCD
+    const uint32_t e0 = s.lm_rec[0][0];
+    uint32_t es = 0, ds = 0;
+#pragma unroll
+    for (int k = 0; k < KL; ++k) {
+      const int j = lane + 64 * k;
+      te[k] = s.lm_rec[min(j, G - 1)][0];
+      mt[k] = s.lm_rec[min(j, G - 1)][1];
+      es += j < G ? te[k] - e0 : 0u;   // ends past workgroup 0's (two's complement: earlier ones subtract)
+      ds += j < G ? mt[k] >> 16 : 0u;
+    }
+    const float emean = (float)(int)wave_sum_u32(es) / (float)G;
+    const bool even = wave_sum_u32(ds) < 100u * (uint32_t)G;   // 100 ticks: 1 us
+    uint32_t sw = 0, sw1 = 0, st = 0;   // this lane's share of S(wg), S(wg + 1) and S(G), in 1/16 rows
+#pragma unroll
+    for (int k = 0; k < KL; ++k) {
+      const int j = lane + 64 * k;
+      const float r = (float)((mt[k] >> 4) & 0xFFFu);
+      const float d = (float)max(mt[k] >> 16, 1u);
+      const float e = (float)(int)(te[k] - e0);
+      const float w = even ? 1.f : fminf(fmaxf(r - 0.5f * (e - emean) * (r / d), 0.5f * r), 2.f * r);
+      const uint32_t wi = j < G ? (uint32_t)(w * 16.f + 0.5f) + 1u : 0u;
+      sw += j < wg ? wi : 0u;
+      sw1 += j <= wg ? wi : 0u;
+      st += wi;
+    }
+    sw = wave_sum_u32(sw);
+    sw1 = wave_sum_u32(sw1);
+    st = wave_sum_u32(st);
+    const double vs = (double)p.V / (double)st;
+    if (lane == 0) {
+      lds_st(&s.lm_va, wg == 0 ? 0u : min((uint32_t)((double)sw * vs), (uint32_t)p.V));
+      lds_st(&s.lm_vb, wg == G - 1 ? (uint32_t)p.V : min((uint32_t)((double)sw1 * vs), (uint32_t)p.V));
+    }
   }
 
   static __device__ bool abort(S& s) {
@@ -1520,10 +1627,15 @@ struct Kern {
   // head's values live in one loop) no longer fit in 256 VGPRs.
   static constexpr int NBH = F_8 == FMT_BF16 ? 4 : 2;
   static __device__ __forceinline__ bool lm_head(const Params& p, S& s, const int* hdr, int cw, float* d_logits,
-                                                 __amdgpu_buffer_rsrc_t rw, bool ok, float& best, int& bidx) {
+                                                 __amdgpu_buffer_rsrc_t rw, bool ok, float& best, int& bidx,
+                                                 uint32_t& t_in) {
     const bool l0 = lane_id() == 0;
-    const int G = p.grid, wg = blockIdx.x;
-    const int va = (int)((int64_t)p.V * wg / G), vb = (int)((int64_t)p.V * (wg + 1) / G);
+    const int va = (int)__builtin_amdgcn_readfirstlane(lds_ld(&s.lm_va));
+    const int vb = (int)__builtin_amdgcn_readfirstlane(lds_ld(&s.lm_vb));
+#ifdef MK_XRAY
+    // the record's third mark: this workgroup's rows (va << 32 | count)
+    if (cw == 0 && lane_id() == 0) s.xr.v[2 + 6 * p.L][XR_M0 + 2] = (uint64_t)va << 32 | (uint32_t)(vb - va);
+#endif
     const int n = vb > va + cw ? (vb - va - cw + kCW - 1) / kCW : 0;   // rows of this wave
     const GMat g = gmat(p.embed, 0);
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(d_logits, d_logits ? 4u * (uint32_t)p.V : 0u);
@@ -1535,6 +1647,7 @@ struct Kern {
       for (int b = 0; b < UBH; ++b) wrow_load(rw, g, row(q * UBH + b), B[q][b]);
     asm volatile("" ::: "memory");
     ok = ok && wait_seq(p, &s.seq, (uint32_t)(p.L * (LONG ? hdr[S_NIN_L] : hdr[S_NIN])) + 1u);
+    t_in = (uint32_t)__builtin_amdgcn_s_memrealtime();
     XR_MIN(s, 2 + 6 * p.L, XR_SEEN);
     uint32_t xa[NH][8];
     load_act<NH>(s.xd_act, p.H, xa);
@@ -1619,7 +1732,7 @@ struct Kern {
       s.seq = 0;
       lds_st(&s.st_i, lds_ld(&s.st_i) + 1u);
 #pragma unroll
-      for (int w = 0; w < kCW; ++w) s.arr[w] = 0;   // constant offsets: no address held across the step
+      for (int w = 0; w < kCW; ++w) lds_st(&s.arr[w], 0u);   // constant offsets, one word each: nothing held across the step
     }
     XR_INIT(s);
     lds_barrier();
@@ -1645,7 +1758,8 @@ struct Kern {
       float best;
       int bidx;
       float* lg = lds_ptr<float>(s.st_logits);
-      ok = lm_head(p, s, hdr, cw, lg ? lg + (size_t)t.i * p.V : nullptr, rw, ok, best, bidx);
+      uint32_t t_in;
+      ok = lm_head(p, s, hdr, cw, lg ? lg + (size_t)t.i * p.V : nullptr, rw, ok, best, bidx, t_in);
       if (lane == 0) {
         s.best[cw] = best;
         s.bidx[cw] = bidx;
@@ -1661,10 +1775,20 @@ struct Kern {
             b = s.best[w];
             bi = s.bidx[w];
           }
+        // the workgroup's record: its (value, index), then when its LM head
+        // ended, how long it took (ticks from its input to its last
+        // candidate), for how many rows, on which XCD: every workgroup derives
+        // the next step's LM-head rows from them
+        const uint32_t t_end = (uint32_t)__builtin_amdgcn_s_memrealtime();
+        const uint32_t dt = min(t_end - t_in, 0xFFFFu);
+        const uint32_t rows = min(lds_ld(&s.lm_vb) - lds_ld(&s.lm_va), 0xFFFu);
+        const uint32_t xcc = __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 7u;   // XCC_ID
         const uint32_t tag = make_tag(t.epoch, vec_id(p.L, 0));
-        const uint32_t off = 8u * (uint32_t)(p.x.arg + 2ull * wg);
+        const uint32_t off = 8u * (uint32_t)(p.x.arg + 4ull * wg);
         st_xword(rx, ok && lane == 0 ? off : kOOB, __float_as_uint(b), tag);
         st_xword(rx, ok && lane == 0 ? off + 8u : kOOB, (uint32_t)bi, tag);
+        st_xword(rx, ok && lane == 0 ? off + 16u : kOOB, t_end, tag);
+        st_xword(rx, ok && lane == 0 ? off + 24u : kOOB, dt << 16 | rows << 4 | xcc, tag);
       }
       arrive(s, cw, 5u * (uint32_t)p.L + 1u, cw == 0);
       if (last_step(s, t.i)) break;
@@ -1699,6 +1823,9 @@ struct Kern {
       s.st_next[1] = (uint32_t)((uint64_t)(uintptr_t)d_next >> 32);
       s.st_logits[0] = (uint32_t)(uintptr_t)d_logits;
       s.st_logits[1] = (uint32_t)((uint64_t)(uintptr_t)d_logits >> 32);
+      // the first step's LM-head rows: an equal share
+      s.lm_va = (uint32_t)((int64_t)p.V * wg / p.grid);
+      s.lm_vb = (uint32_t)((int64_t)p.V * (wg + 1) / p.grid);
     }
     if (threadIdx.x < kCW) s.arr[threadIdx.x] = 0;
     XR_INIT(s);
@@ -1714,7 +1841,7 @@ struct Kern {
         const bool more = !last_step(s, t.i);
         int next = -1;
         bool ok = courier(p, s, hdr, (int)__builtin_amdgcn_readfirstlane(lds_ld(&s.st_token)), t.pos, ns, t.epoch,
-                          lds_ptr<int32_t>(s.st_next) + t.i, more, next);
+                          lds_ptr<int32_t>(s.st_next) + t.i, more, t.i > 0, next);
         // the next step's token is this step's argmax: checked as a launch
         // checks the token it reads (an index past the vocabulary would
         // address past the embedding table)

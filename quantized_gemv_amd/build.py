@@ -33,6 +33,9 @@ def build(xray=False, verbose: bool = False, out: str = "") -> str:
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            # no packed-FP32 instructions anywhere in the device code
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # every loop starts on a 64-byte boundary: the exchange polls and
+           # the layer loops ran 0.5-1 % faster per token than unaligned
+           "-falign-loops=64",
            "-I", os.path.join(ROOT, "include"), "-I", CSRC]
     if kind == "xray":
         cmd.append("-DMK_XRAY")

@@ -336,6 +336,12 @@ int mk_decode_codes(int32_t codec, const uint8_t* d_codes, int32_t n, float* d_o
  * release/acquire counters (on MI355X an L2 write-back and an L2 invalidate
  * of the workgroup's XCD at every barrier).  Modes 1 and 2 turn split
  * attention off and are refused by mk_decode_step_async_noalloc.
+ * Key 12, LM-head balancing [0], for launches of several steps
+ * (mk_decode_steps_async): 1 moves each workgroup's share of the LM-head rows
+ * towards equal end times, from the step before's timings (a damped step;
+ * which workgroup computes a row changes no result); 0 keeps equal shares.
+ * On MI355X the balancing measured slower than equal shares (the per-XCD
+ * LM-head speed does not persist from one step to the next), hence off.
  * Keys 1 and 2 are reserved.
  * Errors: MK_E_INVALID (unknown key, value out of range), MK_E_STATE. */
 int mk_set_option(mk_model* m, int32_t key, int64_t value);

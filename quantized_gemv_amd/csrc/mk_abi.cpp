@@ -61,6 +61,7 @@ struct mk_model {
   std::vector<int32_t> qkv_word;   // word of each q/k/v row in the per-producer layout
   uint32_t tag_skew = 0;
   uint32_t poll_sleep = 0;
+  uint32_t lm_balance = 0;
   int launch_mode = -1;         // 0 cooperative, 1 plain launch of a grid that fits at once, -1 choose
   int split_chunk = 192;        // split attention: cached positions per participant (0: off)
   int split_from = 576;         // split attention from this position on
@@ -482,6 +483,7 @@ void fill_params(mk_model* m) {
   P.spin_limit = (uint64_t)m->spin_limit;
   P.tag_skew = m->tag_skew;
   P.poll_sleep = m->poll_sleep;
+  P.lm_balance = m->lm_balance;
   P.n_phases = n_phases(c);
   P.split_max = kMaxSplit;
   P.split_pw = (int)split_pw(c);
@@ -1050,6 +1052,10 @@ int mk_set_option(mk_model* m, int32_t key, int64_t value) {
     case 5:
       if (value < 0 || value > 16) return fail(m, MK_E_INVALID, "poll back-off out of range");
       m->poll_sleep = (uint32_t)value;
+      break;
+    case 12:
+      if (value < 0 || value > 1) return fail(m, MK_E_INVALID, "LM-head balancing must be 0 or 1");
+      m->lm_balance = (uint32_t)value;
       break;
     case 6:
       if (value < -1 || value > 1) return fail(m, MK_E_INVALID, "launch mode must be -1, 0 or 1");

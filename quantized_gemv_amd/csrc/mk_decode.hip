@@ -726,7 +726,7 @@ struct Kern {
   // rows; grids of up to kLmGrid workgroups.
   static __device__ void lm_partition(const Params& p, S& s) {
     const int lane = lane_id(), G = p.grid, wg = blockIdx.x;
-    if (G > kLmGrid || 2 * p.V / G > 0xFFF) return;
+    if (!p.lm_balance || G > kLmGrid || 2 * p.V / G > 0xFFF) return;
     uint32_t te[KL], mt[KL];   // end ticks, dt << 16 | rows << 4 | XCD
     const uint32_t e0 = s.lm_rec[0][0];
     uint32_t es = 0, ds = 0;

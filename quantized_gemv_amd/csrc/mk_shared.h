@@ -146,6 +146,7 @@ struct Params {
   int split_pw;           // words per helper partial (outputs, maxima, sums; padded)
   uint32_t bar_fence;     // grid-barrier variant: 1 arrive with an agent-scope release and leave with an
                           // agent-scope acquire (L2 write-back and invalidate), 0 relaxed counters
+  uint32_t lm_balance;    // several steps per launch: 1 LM-head rows balanced across XCDs, 0 equal shares (default)
 };
 
 }  // namespace mk

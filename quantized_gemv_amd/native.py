@@ -26,6 +26,7 @@ OPT_GRID, OPT_SPIN_LIMIT, OPT_TAG_SKEW, OPT_POLL_SLEEP, OPT_LAUNCH_MODE, OPT_SPL
 OPT_FP4_SEARCH = 9
 OPT_PREFILL_MODE = 10
 OPT_SYNC_MODE = 11   # 0 tagged exchange words; 1, 2 one grid barrier per phase hand-off (2: with L2 fences)
+OPT_LM_BALANCE = 12  # several steps per launch: 1 LM-head rows balanced across XCDs, 0 equal shares (default)
 
 
 class MkError(RuntimeError):
@@ -116,7 +117,8 @@ class Decoder:
                  spin_limit: Optional[int] = None, poll_sleep: Optional[int] = None,
                  launch_mode: Optional[int] = None, split_chunk: Optional[int] = None,
                  split_from: Optional[int] = None, fp4_search: Optional[int] = None,
-                 prefill_mode: Optional[int] = None, sync_mode: Optional[int] = None):
+                 prefill_mode: Optional[int] = None, sync_mode: Optional[int] = None,
+                 lm_balance: Optional[int] = None):
         import torch
         self.lib = load(xray)
         self.shape, self.wfmt, self.max_ctx = shape, wfmt, max_ctx
@@ -142,6 +144,8 @@ class Decoder:
             self._check(self.lib.mk_set_option(self.h, OPT_PREFILL_MODE, prefill_mode))
         if sync_mode is not None:
             self._check(self.lib.mk_set_option(self.h, OPT_SYNC_MODE, sync_mode))
+        if lm_balance is not None:
+            self._check(self.lib.mk_set_option(self.h, OPT_LM_BALANCE, lm_balance))
         self.sizes = mk_sizes()
         self._check(self.lib.mk_query_sizes(self.h, ctypes.byref(self.sizes)))
         dev = torch.device("cuda", torch.cuda.current_device())

@@ -134,6 +134,10 @@ def test_calls_out_of_order_and_bad_arguments(lib):
     assert lib.mk_set_option(h, native.OPT_SYNC_MODE, -1) == native.MK_E_INVALID
     assert lib.mk_set_option(h, native.OPT_SYNC_MODE, 1) == native.MK_OK
     assert lib.mk_set_option(h, native.OPT_SYNC_MODE, 0) == native.MK_OK
+    assert lib.mk_set_option(h, native.OPT_LM_BALANCE, 2) == native.MK_E_INVALID
+    assert lib.mk_set_option(h, native.OPT_LM_BALANCE, -1) == native.MK_E_INVALID
+    assert lib.mk_set_option(h, native.OPT_LM_BALANCE, 1) == native.MK_OK
+    assert lib.mk_set_option(h, native.OPT_LM_BALANCE, 0) == native.MK_OK
     assert lib.mk_set_option(h, native.OPT_SPIN_LIMIT, 1000) == native.MK_OK
     assert lib.mk_last_error(h)
     n_out = ctypes.c_size_t(7)

@@ -136,6 +136,25 @@ def test_steps_stress_build_tiny(native, master):
 
 
 @pytest.mark.timeout(600)
+@pytest.mark.parametrize("wfmt", [synth.BF16, synth.FP8_ROW])
+def test_steps_lm_balance_qwen3(native, wfmt):
+    """Option 12 on (LM-head rows moved between workgroups from step to
+    step): 24 steps after a 64-token prompt at the 0.6B shape, bit-identical
+    to single-step launches (which workgroup computes a row changes no
+    result)."""
+    m = synth.make_weights(synth.QWEN3_0P6B, 0)
+    prompt = synth.make_prompt(synth.QWEN3_0P6B.vocab, 64, 76)
+    d = _decoder(native, synth.QWEN3_0P6B, m, wfmt, 96)
+    first = d.prefill(prompt)
+    ref = _chained(d, first, 64, 24, synth.QWEN3_0P6B.vocab)
+    d.close()
+    d = _decoder(native, synth.QWEN3_0P6B, m, wfmt, 96, lm_balance=1)
+    assert d.prefill(prompt) == first
+    _same(_multi(d, first, 64, 24, synth.QWEN3_0P6B.vocab), ref)
+    d.close()
+
+
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("wfmt,plen,n", [(synth.BF16, 64, 12), (synth.FP8_ROW, 570, 10)])
 def test_steps_equal_chained_steps_qwen3(native, wfmt, plen, n):
     """The 0.6B shape: 12 bf16 steps after a 64-token prompt, and 10 FP8

@@ -671,7 +671,7 @@ struct Kern {
           bidx = i;
         }
       };
-      if (all_argmax && p.grid <= kLmGrid) {
+      if (all_argmax && p.lm_balance && p.grid <= kLmGrid) {
         // whole records, one round: pair 2j is workgroup j's (value, index),
         // pair 2j + 1 its (end tick, dt << 16 | rows << 4 | XCD), kept for the
         // next step's LM-head rows (even lanes hold the former, odd lanes the
@@ -692,6 +692,14 @@ struct Kern {
             }
           }
         }
+      } else if (p.grid <= kLmGrid) {
+        // the (value, index) pairs alone: KL loads per lane
+        uint32_t vl[KL], il[KL];
+        if (!gather_pairs<KL>(p, rs, p.grid, tag, vl, il, [=](int j) { return base + 4u * j; })) return false;
+        XR_PUT(s, ph_head + 1, XR_READY);
+#pragma unroll
+        for (int k = 0; k < KL; ++k)
+          if (lane + 64 * k < p.grid) take(vl[k], il[k]);
       } else {
         uint32_t vl[KG], il[KG];
         if (!gather_pairs<KG>(p, rs, p.grid, tag, vl, il, [=](int j) { return base + 4u * j; })) return false;

@@ -329,23 +329,17 @@ __device__ __forceinline__ void norm_to_lds(const uint32_t (&lo)[MAXK], const ui
                                             const float (&g)[2 * MAXK], int H, float inv_h, float eps,
                                             float* x_raw, uint32_t* act) {
   const int lane = lane_id();
-  float ss = 0.f;
-  if (H == 128 * MAXK) {   // every lane's pairs are in the vector: no masking
+  // four partial sums (pairs k mod 4), added in a fixed order: a quarter of
+  // the dependent chain
+  float sp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < MAXK; ++k) {
-      const float a = __uint_as_float(lo[k]), b = __uint_as_float(hi[k]);
-      ss = fmaf(a, a, ss);
-      ss = fmaf(b, b, ss);
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < MAXK; ++k) {
-      const bool in = lane + 64 * k < H / 2;
-      const float a = in ? __uint_as_float(lo[k]) : 0.f, b = in ? __uint_as_float(hi[k]) : 0.f;
-      ss = fmaf(a, a, ss);
-      ss = fmaf(b, b, ss);
-    }
+  for (int k = 0; k < MAXK; ++k) {
+    const bool in = H == 128 * MAXK || lane + 64 * k < H / 2;   // the first: every pair in the vector
+    const float a = in ? __uint_as_float(lo[k]) : 0.f, b = in ? __uint_as_float(hi[k]) : 0.f;
+    sp[k & 3] = fmaf(a, a, sp[k & 3]);
+    sp[k & 3] = fmaf(b, b, sp[k & 3]);
   }
+  const float ss = (sp[0] + sp[1]) + (sp[2] + sp[3]);
 #pragma unroll
   for (int k = 0; k < MAXK; ++k) *reinterpret_cast<v2u*>(x_raw + 2 * (lane + 64 * k)) = v2u{lo[k], hi[k]};
   const float r = __builtin_amdgcn_rsqf(wave_sum(ss) * inv_h + eps);

@@ -110,13 +110,14 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Compute waves: wait until the courier has handed over `want` inputs.
 // Returns false if the courier aborted, or (a safety net: the courier's own
-// waits are bounded) after `spin_limit` ticks.
+// waits are bounded) after `spin_limit` ticks.  The loop polls LDS without
+// sleeping between reads: a sleep of 64 clocks between polls cost 0.8 % of
+// the step (five hand-offs per layer).
 __device__ __forceinline__ bool wait_seq(const Params& p, const uint32_t* seq, uint32_t want) {
   uint32_t s = __builtin_amdgcn_readfirstlane(lds_ld(seq));
   if (s >= want) return s != kAbort;
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   for (uint32_t n = 1;; ++n) {
-    __builtin_amdgcn_s_sleep(1);
     s = __builtin_amdgcn_readfirstlane(lds_ld(seq));
     if (s >= want) return s != kAbort;
     if ((n & 255u) == 0 && __builtin_amdgcn_s_memrealtime() - t0 > p.spin_limit) {

@@ -536,6 +536,17 @@ struct Kern {
       const uint32_t j = (uint32_t)min(lane + 64 * k, p.I / 4 - 1);
       mh[k] = xpad_word(2 * j, p.I / 2, p.x.pad_c[V_H], p.x.pad_stride[V_H]);
     }
+    // attention and split-attention helper workgroups: layer 0's q/k-norm
+    // gains and the position's RoPE pair (the same in every layer)
+    const bool att_in = att >= 0 || (LONG && hdr[S_SPLIT] >= 0);
+    uint32_t ag[4] = {0u, 0u, 0u, 0u};
+    float rc = 0.f, rsn = 0.f;
+    if (att_in) {
+      att_gains(p, 0, ag);
+      MK_GLOBAL const float* cs = p.rope + ((size_t)pos * (HD / 2) + min(lane, HD / 2 - 1)) * 2;
+      rc = cs[0];
+      rsn = cs[1];
+    }
     // this step's LM-head rows: a GEMV workgroup's courier now (the compute
     // waves' layer-0 QKV rows cover it), an attention workgroup's after its
     // layer-0 attention, where it waits for the next layer's q, k, v
@@ -566,7 +577,7 @@ struct Kern {
       // ---- q, k, v of KV head `att`: q/k RMSNorm, RoPE, KV append
       if (att >= 0) {
         XR_PUT(s, ph + 1, XR_START);
-        if (!attention_input<true>(p, s, l, att, pos, epoch, rs, qm)) return abort(s);
+        if (!attention_input<true>(p, s, l, att, pos, epoch, rs, qm, ag, rc, rsn)) return abort(s);
         hand_over(&s.seq, ++seq);
         XR_PUT(s, ph + 1, XR_HANDOFF);
         lds_barrier();   // q, k and v are normed, roped and appended
@@ -579,7 +590,7 @@ struct Kern {
       if (LONG && hdr[S_SPLIT] >= 0) {
         if (hdr[S_SPLIT_IDX] <= ns) {
           XR_PUT(s, ph + 1, XR_START);
-          if (!attention_input<false>(p, s, l, hdr[S_SPLIT], pos, epoch, rs, qm)) return abort(s);
+          if (!attention_input<false>(p, s, l, hdr[S_SPLIT], pos, epoch, rs, qm, ag, rc, rsn)) return abort(s);
           hand_over(&s.seq, ++seq);
           XR_PUT(s, ph + 1, XR_HANDOFF);
           lds_barrier();   // q is normed and roped
@@ -588,6 +599,8 @@ struct Kern {
           hand_over(&s.seq, ++seq);   // no slice this step; keeps the input numbering
         }
       }
+      // the next layer's gains, while the courier waits for its q, k, v
+      if (att_in) att_gains(p, min(l + 1, L - 1), ag);
       // ---- attention output
       if (BAR && !grid_barrier(p, s, bq + 1)) return abort(s);
       if (flags & 2) {
@@ -779,26 +792,32 @@ struct Kern {
     for (int k = 0; k < KA; ++k) qm[k] = (uint32_t)m[min(lane_id() + 64 * k, np - 1)];
   }
 
+  // The q/k-norm gains of layer l at this lane's RoPE pair (lane,
+  // lane + HD/2), as loaded bf16 bits: the courier loads the next layer's
+  // while it waits, and converts them where they are used, so that no wait
+  // for them sits in front of the q/k/v gather's first poll round.
+  static __device__ __forceinline__ void att_gains(const Params& p, int l, uint32_t (&ag)[4]) {
+    const int li = min(lane_id(), HD / 2 - 1);
+    const uint64_t loff = (uint64_t)l * p.layer_stride;
+    MK_GLOBAL const uint16_t* gq = GCAST(const uint16_t, p.w + p.layer0.q_norm + loff);
+    MK_GLOBAL const uint16_t* gk = GCAST(const uint16_t, p.w + p.layer0.k_norm + loff);
+    ag[0] = gq[li];
+    ag[1] = gq[li + HD / 2];
+    ag[2] = gk[li];
+    ag[3] = gk[li + HD / 2];
+  }
+
   // Gather q (GS heads), k and v of KV head g into LDS, with this layer's
-  // q/k-norm gains and this position's RoPE pairs (loaded ahead of the
-  // gather); the compute waves norm, rope and append them (att_prepare).
-  // Without KV (a split-attention helper): q only, with the q-norm gains.
-  // qm: the word offsets of the lane's pairs (see qkv_map).
+  // q/k-norm gains and this position's RoPE pairs; the compute waves norm,
+  // rope and append them (att_prepare).  Without KV (a split-attention
+  // helper): q only, with the q-norm gains.  qm: the word offsets of the
+  // lane's pairs (see qkv_map); ag: att_gains(l); rc, rsn: the position's
+  // RoPE pair of this lane (loaded by the courier before its layer loop).
   template <bool KV>
   static __device__ bool attention_input(const Params& p, S& s, int l, int g, int pos, uint32_t epoch,
-                                         __amdgpu_buffer_rsrc_t rs, const uint32_t (&qm)[KA]) {
-    MK_GLOBAL const uint8_t* const W = p.w;
+                                         __amdgpu_buffer_rsrc_t rs, const uint32_t (&qm)[KA],
+                                         const uint32_t (&ag)[4], float rc, float rsn) {
     const int lane = lane_id();
-    const int nq = p.nq, nkv = p.nkv;
-    const uint64_t loff = (uint64_t)l * p.layer_stride;
-    const Layer& L0 = p.layer0;
-    const int li = min(lane, HD / 2 - 1);
-    MK_GLOBAL const uint16_t* gq = GCAST(const uint16_t, W + L0.q_norm + loff);
-    MK_GLOBAL const uint16_t* gk = GCAST(const uint16_t, W + L0.k_norm + loff);
-    const float gq_lo = bf16_to_f32(gq[li]), gq_hi = bf16_to_f32(gq[li + HD / 2]);
-    const float gk_lo = bf16_to_f32(gk[li]), gk_hi = bf16_to_f32(gk[li + HD / 2]);
-    MK_GLOBAL const float* cs = p.rope + ((size_t)pos * (HD / 2) + li) * 2;
-    const float rc = cs[0], rsn = cs[1];
     constexpr int NP = KV ? (GS + 2) * HD / 2 : NOUT / 2;   // pairs gathered
     constexpr int K = (NP + 63) / 64;
     uint32_t lo[K], hi[K], off[K];
@@ -811,10 +830,10 @@ struct Kern {
 #pragma unroll
     for (int k = 0; k < K; ++k) *reinterpret_cast<v2u*>(s.qraw + 2 * (lane + 64 * k)) = v2u{lo[k], hi[k]};
     if (lane < HD / 2) {
-      s.gq[lane] = gq_lo;
-      s.gq[lane + HD / 2] = gq_hi;
-      s.gk[lane] = gk_lo;
-      s.gk[lane + HD / 2] = gk_hi;
+      s.gq[lane] = bf16_to_f32((uint16_t)ag[0]);
+      s.gq[lane + HD / 2] = bf16_to_f32((uint16_t)ag[1]);
+      s.gk[lane] = bf16_to_f32((uint16_t)ag[2]);
+      s.gk[lane + HD / 2] = bf16_to_f32((uint16_t)ag[3]);
       s.rc[lane] = rc;
       s.rs[lane] = rsn;
     }

@@ -290,7 +290,7 @@ def main():
                    "positions": [wl.prompt_len, wl.prompt_len + K - 1],
                    "weight_format": synth.WFMT_NAMES[wl.wfmt], "accumulate": "f32", "batch": 1,
                    "grid": "one workgroup per CU: 1 courier + 7 compute waves; attention on one "
-                           "workgroup per KV head, split over the workgroups of its XCD from 576 "
+                           "workgroup per KV head, split over the workgroups of its XCD from 704 "
                            "cached positions on" if not args.grid else f"{args.grid} workgroups",
                    "launch": "K single-step launches" if args.one_step_per_launch else
                              "one mk_decode_steps_async call of K steps (one launch; positions with "

@@ -307,13 +307,15 @@ int mk_decode_codes(int32_t codec, const uint8_t* d_codes, int32_t n, float* d_o
  * cooperative.  The kernel's waits assume that every workgroup runs: should
  * another process hold compute units during a plain launch, they end at the
  * spin bound with MK_E_TIMEOUT instead of hanging.  Keys 7 and 8, split
- * attention [192, 576]: with key 7 = c > 0, a step at a position pos at or
+ * attention [192, 704]: with key 7 = c > 0, a step at a position pos at or
  * past key 8 spreads KV head g's cached positions over its home workgroup and
  * ns = min(helpers, pos / c) helper workgroups on the same XCD (helpers = the
  * GEMV workgroups there, at most 32 per head), each taking an equal slice;
  * the home merges their partial (maximum, sum, output) triples with the
  * log-sum-exp rule.  c = 0 turns it off.  (On MI355X at the 0.6B shape the
- * split path is faster from about 560 cached positions on.)  Key 9, NVFP4
+ * split path is faster from about 700 cached positions on, where consecutive
+ * positions run one launch each; below, the home alone within one launch of
+ * several steps is faster.)  Key 9, NVFP4
  * block scale search radius 0..126 [0], set before mk_pack_weights (see
  * there); 0 keeps the absolute-maximum recipe.  Key 10, prefill path [0]:
  * 0 runs mk_prefill as one decode launch per prompt position; 1 runs the

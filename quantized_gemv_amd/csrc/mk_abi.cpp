@@ -64,7 +64,7 @@ struct mk_model {
   uint32_t lm_balance = 0;
   int launch_mode = -1;         // 0 cooperative, 1 plain launch of a grid that fits at once, -1 choose
   int split_chunk = 192;        // split attention: cached positions per participant (0: off)
-  int split_from = 576;         // split attention from this position on
+  int split_from = 704;         // split attention from this position on
   int split_n = 0;              // helpers per KV head in the work table
   int coresident = 0;           // decode workgroups the device holds at once (set by mk_bind)
   int fp4_search = 0;           // NVFP4 block scale search radius (0: absolute-maximum recipe)

@@ -8,7 +8,7 @@ per compute unit, library defaults):
   prompt and the FP4-mix workload's 512-token prompt;
 * free-running greedy decode (bf16, FP8) equal to the oracle's up to the
   first near-tie;
-* the default split attention (from 576 cached positions) at positions 600
+* the default split attention (from 704 cached positions) at positions 720
   and 1000, the ends of the page's position sweep (16 and 2048), and the
   long-context workload itself (FP8, 16,384-token prompt), every phase
   recomputed from the GPU's own inputs (tests/opcheck.py).
@@ -171,16 +171,16 @@ def test_free_running_greedy_qwen3(native, q_master, wfmt):
 @pytest.mark.parametrize("wfmt", [synth.FP4_MIX, synth.FP8_ROW])
 def test_split_attention_default_qwen3(native, q_master, wfmt):
     """The library's default split attention at the FP4-mix workload's
-    positions: at 600 (3 helpers per KV head, slices of 150 positions: two
+    positions: at 720 (3 helpers per KV head, slices of 180 positions: two
     passes per helper) and 1000 (5 helpers, slices of 167), every phase of
     layers 0, 1, 14, 27 and the LM head recomputed from the GPU's inputs."""
     toks = synth.make_prompt(SH.vocab, 1001, 17)
     d = _decoder(native, q_master, wfmt, 1024)
     W = Weights(q_master, wfmt)
-    d.prefill(toks[:600])
-    for pos in range(600, 1001):
+    d.prefill(toks[:720])
+    for pos in range(720, 1001):
         logits, _ = _step(d, int(toks[pos]), pos)
-        if pos in (600, 1000):
+        if pos in (720, 1000):
             check_step(GpuStep(d), W, SH, int(toks[pos]), pos, logits, Q_LAYERS, np.random.default_rng(pos),
                        n_sample=96)
     d.close()
@@ -190,7 +190,7 @@ def test_split_attention_default_qwen3(native, q_master, wfmt):
 def test_long_context_fp8_16k(native, q_master):
     """The long-context workload: the FP8 model, a 16,384-token prompt run
     through mk_prefill (one decode launch per position: split attention from
-    576 on), then the first decode step at position 16,384 (31 helpers per KV
+    704 on), then the first decode step at position 16,384 (31 helpers per KV
     head, slices of 512 positions: five passes each), every phase of layers
     0, 1, 14, 27 and the LM head recomputed from the GPU's own cache and
     inputs."""

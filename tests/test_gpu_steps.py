@@ -106,15 +106,15 @@ def test_steps_equal_chained_steps_tiny(native, master, wfmt, case):
 
 
 def test_steps_launch_cap_and_split_boundary_tiny(native, master):
-    """600 steps after an 8-token prompt with the default split attention
-    (helpers from position 576): launches of 512 steps (8..519) and 56 steps
-    (520..575), then one launch per position."""
+    """720 steps after an 8-token prompt with the default split attention
+    (helpers from position 704): launches of 512 steps (8..519) and 184
+    steps (520..703), then one launch per position."""
     prompt = synth.make_prompt(synth.TINY.vocab, 8, 72)
     runs = []
     for fn in (_chained, _multi):
-        d = _decoder(native, synth.TINY, master, synth.FP8_ROW, 640)
+        d = _decoder(native, synth.TINY, master, synth.FP8_ROW, 736)
         first = d.prefill(prompt)
-        runs.append(fn(d, first, 8, 600, synth.TINY.vocab))
+        runs.append(fn(d, first, 8, 720, synth.TINY.vocab))
         d.close()
     _same(runs[1], runs[0])
 
@@ -155,11 +155,11 @@ def test_steps_lm_balance_qwen3(native, wfmt):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("wfmt,plen,n", [(synth.BF16, 64, 12), (synth.FP8_ROW, 570, 10)])
+@pytest.mark.parametrize("wfmt,plen,n", [(synth.BF16, 64, 12), (synth.FP8_ROW, 698, 10)])
 def test_steps_equal_chained_steps_qwen3(native, wfmt, plen, n):
     """The 0.6B shape: 12 bf16 steps after a 64-token prompt, and 10 FP8
-    steps from position 570 (six in one launch, then split attention from
-    576 one launch per position)."""
+    steps from position 698 (six in one launch, then split attention from
+    704 one launch per position)."""
     m = synth.make_weights(synth.QWEN3_0P6B, 0)
     prompt = synth.make_prompt(synth.QWEN3_0P6B.vocab, plen, 74)
     d = _decoder(native, synth.QWEN3_0P6B, m, wfmt, plen + n + 4)

@@ -200,7 +200,7 @@ def test_streamed_attention_beyond_register_passes(native, master, wfmt, split):
     where the oracle's top-2 gap clears both 1e-3 and twice that step's
     measured noise; otherwise it must be a valid argmax: its oracle logit
     within that margin of the maximum.  split 0: the home workgroup alone;
-    None: the library default (split attention from position 576 on)."""
+    None: the library default (split attention from position 704 on)."""
     n = 800
     toks = synth.make_prompt(synth.TINY.vocab, n, 9)
     d = _decoder(native, master, wfmt, max_ctx=n + 2, split_chunk=split)
